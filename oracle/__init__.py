@@ -1,0 +1,168 @@
+"""CPU oracle for the ring AllReduce: test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never imports,
+links or calls it, and it imports nothing from the product.
+
+``ring_oracle.c`` is the reduction itself (a sequential simulation of the ring
+schedule, see its header for the passages it follows); ``select.py`` is the
+alpha-beta protocol model.  This module builds the C file with gcc and wraps it
+with ctypes over numpy arrays.  bfloat16 arrays are carried as raw ``uint16``
+bit patterns, since numpy has no bfloat16 type.
+
+Parity pins (what ties this oracle to something other than itself) live in
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_mutations.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ring_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libring_oracle.so")
+
+# name -> (code in ring_oracle.c, numpy storage dtype, element bytes)
+DTYPES = {
+    "int8": (0, np.int8, 1),
+    "int32": (1, np.int32, 4),
+    "float16": (2, np.float16, 2),
+    "bfloat16": (3, np.uint16, 2),
+    "float32": (4, np.float32, 4),
+    "float64": (5, np.float64, 8),
+}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle C file into a shared library (gcc, no fast-math)."""
+    cmd = ["gcc", *CFLAGS, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    sz = ctypes.c_size_t
+    vp = ctypes.c_void_p
+    lib.oracle_ring_allreduce.argtypes = [
+        ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz,
+        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.oracle_ring_allreduce.restype = ctypes.c_int
+    lib.oracle_element_chunks.argtypes = [sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz, vp]
+    lib.oracle_element_chunks.restype = ctypes.c_int
+    lib.oracle_channel_range.argtypes = [sz, sz, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.oracle_channel_range.restype = None
+    lib.oracle_loop_chunk.argtypes = [sz, sz, sz, ctypes.c_int, sz]
+    lib.oracle_loop_chunk.restype = sz
+    for name in ("oracle_f16_decode_array", "oracle_bf16_decode_array",
+                 "oracle_f16_encode_array", "oracle_bf16_encode_array"):
+        getattr(lib, name).argtypes = [vp, vp, sz]
+        getattr(lib, name).restype = None
+    return lib
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the oracle library, building it first if it is not there.
+
+    With ``path`` given, load that file instead (the mutation tests load
+    deliberately broken copies this way) without caching it.
+    """
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def ring_allreduce(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
+                   ring=None, lib: ctypes.CDLL | None = None, out=None):
+    """Ring AllReduce of the n input arrays ``xs`` (one per rank).
+
+    Returns the n output arrays (fresh ones unless ``out`` is given; ``out``
+    may be ``xs`` itself for the in-place form).  ``ring[i]`` is the rank at
+    ring index i (None = identity).  ``chunk_elems`` is the per-rank,
+    per-channel chunk of a full loop and must be a multiple of 16 bytes.
+    """
+    lib = lib or load()
+    code, npt, esize = DTYPES[dtype]
+    n = len(xs)
+    xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
+    count = xs[0].size if n else 0
+    assert all(x.size == count for x in xs)
+    ys = out if out is not None else [np.empty(count, dtype=npt) for _ in range(n)]
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    rp = None
+    if ring is not None:
+        rp = (ctypes.c_int * n)(*[int(r) for r in ring])
+    rc = lib.oracle_ring_allreduce(n, count, code, OPS[op], nchannels, chunk_elems, rp, xp, yp)
+    if rc != 0:
+        raise ValueError("oracle_ring_allreduce rejected its arguments")
+    return ys
+
+
+def element_chunks(count: int, dtype: str, nranks: int, nchannels: int,
+                   chunk_elems: int, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Chunk id (0..n-1) of every element under the oracle's partition."""
+    lib = lib or load()
+    out = np.empty(count, dtype=np.int32)
+    rc = lib.oracle_element_chunks(count, DTYPES[dtype][0], nranks, nchannels, chunk_elems,
+                                   _ptr(out) if count else None)
+    if rc != 0:
+        raise ValueError("oracle_element_chunks rejected its arguments")
+    return out
+
+
+def channel_range(count: int, dtype: str, nchannels: int, c: int) -> tuple[int, int]:
+    lib = load()
+    lo, hi = ctypes.c_size_t(), ctypes.c_size_t()
+    lib.oracle_channel_range(count, DTYPES[dtype][2], nchannels, c, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def loop_chunk(length: int, off: int, dtype: str, nranks: int, chunk_elems: int) -> int:
+    return load().oracle_loop_chunk(length, off, DTYPES[dtype][2], nranks, chunk_elems)
+
+
+def f16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.size, dtype=np.float32)
+    load().oracle_f16_decode_array(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def f16_encode(vals: np.ndarray) -> np.ndarray:
+    vals = np.ascontiguousarray(vals, dtype=np.float32)
+    out = np.empty(vals.size, dtype=np.uint16)
+    load().oracle_f16_encode_array(_ptr(vals), _ptr(out), vals.size)
+    return out
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.size, dtype=np.float32)
+    load().oracle_bf16_decode_array(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def bf16_encode(vals: np.ndarray) -> np.ndarray:
+    vals = np.ascontiguousarray(vals, dtype=np.float32)
+    out = np.empty(vals.size, dtype=np.uint16)
+    load().oracle_bf16_encode_array(_ptr(vals), _ptr(out), vals.size)
+    return out

@@ -1,0 +1,377 @@
+/*
+ * Ring AllReduce oracle: a plain, sequential, slow CPU model of the ring
+ * AllReduce that NCCL runs on the device (reduce-scatter, then all-gather,
+ * 2(n-1) ring steps per loop, each channel on its own contiguous range).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this file's library.  The product
+ * library neither links nor calls it, and the two share no code, headers or
+ * constants.
+ *
+ * Sources, cited by page title and section:
+ *   [ARCH]  arganzheng.life, "NCCL architecture: topology, channels,
+ *           algorithms and protocols" (Chinese; part 4 of the series).
+ *   [BOOK]  aireadcode.com, "NCCL Source Code Deep Dive: A GPU Journey of One
+ *           AllReduce" (English edition; the Japanese edition holds ch. 5-6).
+ *
+ * What is computed (plain reading of the pages, one decision per step):
+ *   1. Channel split: each channel owns one contiguous range of the buffer
+ *      ([BOOK] §2.2, channels split count/nChannels contiguously).  The pages
+ *      leave remainder and alignment open; this oracle rounds the per-channel
+ *      length up to whole 16-byte units, so trailing channels may be short or
+ *      empty.
+ *   2. Loops inside a channel: one loop covers nranks chunks of chunk_elems
+ *      elements; the last, partial loop uses chunks of
+ *      alignUp(ceil(rem / nranks), 16 B / elemSize) elements
+ *      ([BOOK] §2.3, RingARAlgorithm::getNextSendAddr).
+ *   3. Chunk visited at stage s by ring index i: (i + n - 1 - s) mod n
+ *      ([BOOK] §2.3, chunkId formula).
+ *   4. Primitive order per loop ([ARCH] §九.4, runRing): send;
+ *      (n-2) x recvReduceSend; recvReduceCopySend (the chunk is final here);
+ *      (n-2) x recvCopySend; recv.
+ *   5. Arithmetic: op(received, local) per hop.  Integers wrap (two's
+ *      complement).  fp16 and bf16 widen both operands exactly to fp32, apply
+ *      the op in fp32 and round back to 16 bits to nearest-even on every hop.
+ *      fp32 and fp64 use IEEE binary ops (no contraction; build with
+ *      -ffp-contract=off).  min keeps the received value unless the local one
+ *      is strictly smaller; max likewise with strictly larger.
+ *
+ * The stage simulation keeps one payload buffer per ring index: what that
+ * ring index put into its successor's FIFO at the previous stage.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Codes private to this file; the Python wrapper maps names onto them. */
+enum { OR_I8 = 0, OR_I32 = 1, OR_F16 = 2, OR_BF16 = 3, OR_F32 = 4, OR_F64 = 5 };
+enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3 };
+
+static size_t elem_size(int dtype) {
+  switch (dtype) {
+    case OR_I8: return 1;
+    case OR_I32: return 4;
+    case OR_F16: return 2;
+    case OR_BF16: return 2;
+    case OR_F32: return 4;
+    case OR_F64: return 8;
+    default: return 0;
+  }
+}
+
+static size_t div_up(size_t a, size_t b) { return (a + b - 1) / b; }
+static size_t align_up(size_t a, size_t b) { return div_up(a, b) * b; }
+static size_t min_sz(size_t a, size_t b) { return a < b ? a : b; }
+
+/* ---------------------------------------------------------------------
+ * 16-bit float formats, written from the IEEE-754 definitions.
+ * binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ * bfloat16: the upper half of binary32: 1 sign, 8 exponent (bias 127),
+ *           7 fraction bits.
+ * Decoding is exact.  Encoding rounds to nearest, ties to even: the value is
+ * divided by the spacing of the target format at its magnitude (a power of
+ * two, so the division is exact in double), rounded to an integer with rint()
+ * in the default rounding mode, and scaled back.
+ * --------------------------------------------------------------------- */
+static float f16_decode(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);            /* subnormal: m * 2^-24 */
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);       /* (1 + m/2^10) 2^(e-15) */
+  return (float)(s ? -v : v);
+}
+
+static uint16_t f16_encode_rne(float f) {
+  double v = f;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return sign | 0x7e00;
+  int e;
+  frexp(a, &e);                                     /* a in [2^(e-1), 2^e) */
+  int ex = e - 1;
+  double q = (a == 0.0 || ex < -14) ? ldexp(1.0, -24) : ldexp(1.0, ex - 10);
+  double r = rint(a / q) * q;
+  if (r >= 65536.0) return sign | 0x7c00;            /* beyond 65504 -> inf */
+  if (r < ldexp(1.0, -14)) return sign | (uint16_t)(r / ldexp(1.0, -24));
+  frexp(r, &e);
+  ex = e - 1;
+  uint16_t mant = (uint16_t)(r / ldexp(1.0, ex - 10) - 1024.0);
+  return sign | (uint16_t)((ex + 15) << 10) | mant;
+}
+
+static float bf16_decode(uint16_t h) {
+  int s = h >> 15, e = (h >> 7) & 0xff, m = h & 0x7f;
+  double v;
+  if (e == 0) v = ldexp((double)m, -133);           /* subnormal: m * 2^-133 */
+  else if (e == 255) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(128 + m), e - 134);       /* (1 + m/2^7) 2^(e-127) */
+  return (float)(s ? -v : v);
+}
+
+static uint16_t bf16_encode_rne(float f) {
+  double v = f;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return sign | 0x7fc0;
+  int e;
+  frexp(a, &e);
+  int ex = e - 1;
+  double q = (a == 0.0 || ex < -126) ? ldexp(1.0, -133) : ldexp(1.0, ex - 7);
+  double r = rint(a / q) * q;
+  if (r >= ldexp(1.0, 128)) return sign | 0x7f80;   /* beyond max -> inf */
+  if (r < ldexp(1.0, -126)) return sign | (uint16_t)(r / ldexp(1.0, -133));
+  frexp(r, &e);
+  ex = e - 1;
+  uint16_t mant = (uint16_t)(r / ldexp(1.0, ex - 7) - 128.0);
+  return sign | (uint16_t)((ex + 127) << 7) | mant;
+}
+
+/* Exposed so the tests can pin the codecs against library conversions. */
+float oracle_f16_to_f32(uint16_t h) { return f16_decode(h); }
+uint16_t oracle_f32_to_f16(float f) { return f16_encode_rne(f); }
+float oracle_bf16_to_f32(uint16_t h) { return bf16_decode(h); }
+uint16_t oracle_f32_to_bf16(float f) { return bf16_encode_rne(f); }
+
+/* ---------------------------------------------------------------------
+ * One hop of the reduction: out[e] = op(recv[e], local[e]).
+ * --------------------------------------------------------------------- */
+static float op_f32(int op, float a, float b) {
+  switch (op) {
+    case OR_SUM: return a + b;
+    case OR_PROD: return a * b;
+    case OR_MIN: return (b < a) ? b : a;
+    default: return (b > a) ? b : a;
+  }
+}
+
+static double op_f64(int op, double a, double b) {
+  switch (op) {
+    case OR_SUM: return a + b;
+    case OR_PROD: return a * b;
+    case OR_MIN: return (b < a) ? b : a;
+    default: return (b > a) ? b : a;
+  }
+}
+
+static void combine(int dtype, int op, const void* recv, const void* local,
+                    void* out, size_t len) {
+  size_t e;
+  switch (dtype) {
+    case OR_I8: {
+      const uint8_t* a = recv; const uint8_t* b = local; uint8_t* o = out;
+      for (e = 0; e < len; e++) {
+        int8_t sa = (int8_t)a[e], sb = (int8_t)b[e];
+        switch (op) {
+          case OR_SUM: o[e] = (uint8_t)(a[e] + b[e]); break;
+          case OR_PROD: o[e] = (uint8_t)((unsigned)a[e] * (unsigned)b[e]); break;
+          case OR_MIN: o[e] = (sb < sa) ? b[e] : a[e]; break;
+          default: o[e] = (sb > sa) ? b[e] : a[e]; break;
+        }
+      }
+      break;
+    }
+    case OR_I32: {
+      const uint32_t* a = recv; const uint32_t* b = local; uint32_t* o = out;
+      for (e = 0; e < len; e++) {
+        int32_t sa = (int32_t)a[e], sb = (int32_t)b[e];
+        switch (op) {
+          case OR_SUM: o[e] = a[e] + b[e]; break;
+          case OR_PROD: o[e] = a[e] * b[e]; break;
+          case OR_MIN: o[e] = (sb < sa) ? b[e] : a[e]; break;
+          default: o[e] = (sb > sa) ? b[e] : a[e]; break;
+        }
+      }
+      break;
+    }
+    case OR_F16: {
+      const uint16_t* a = recv; const uint16_t* b = local; uint16_t* o = out;
+      for (e = 0; e < len; e++)
+        o[e] = f16_encode_rne(op_f32(op, f16_decode(a[e]), f16_decode(b[e])));
+      break;
+    }
+    case OR_BF16: {
+      const uint16_t* a = recv; const uint16_t* b = local; uint16_t* o = out;
+      for (e = 0; e < len; e++)
+        o[e] = bf16_encode_rne(op_f32(op, bf16_decode(a[e]), bf16_decode(b[e])));
+      break;
+    }
+    case OR_F32: {
+      const float* a = recv; const float* b = local; float* o = out;
+      for (e = 0; e < len; e++) o[e] = op_f32(op, a[e], b[e]);
+      break;
+    }
+    default: {
+      const double* a = recv; const double* b = local; double* o = out;
+      for (e = 0; e < len; e++) o[e] = op_f64(op, a[e], b[e]);
+      break;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------
+ * Partition (steps 1-3 of the header).
+ * --------------------------------------------------------------------- */
+
+/* Channel c's element range [lo, hi). */
+void oracle_channel_range(size_t count, size_t esize, int nchannels, int c,
+                          size_t* lo, size_t* hi) {
+  size_t a = 16 / esize;
+  size_t per = align_up(div_up(count, (size_t)nchannels), a);
+  *lo = min_sz(count, (size_t)c * per);
+  *hi = min_sz(count, *lo + per);
+}
+
+/* Elements per chunk in the loop that starts at offset `off` of a channel of
+ * length `len`: the configured chunk for full loops, else the last-loop rule. */
+size_t oracle_loop_chunk(size_t len, size_t off, size_t esize, int nranks,
+                         size_t chunk_elems) {
+  size_t a = 16 / esize;
+  size_t loop = (size_t)nranks * chunk_elems;
+  size_t rem = len - off;
+  return rem < loop ? align_up(div_up(rem, (size_t)nranks), a) : chunk_elems;
+}
+
+/* Chunk k of a loop with `rem` elements left and chunk size `cur`:
+ * [k*cur, min(rem, (k+1)*cur)) relative to the loop start; may be empty. */
+static void chunk_span(size_t rem, size_t cur, int k, size_t* start, size_t* len) {
+  size_t s = (size_t)k * cur;
+  if (s >= rem) { *start = rem; *len = 0; return; }
+  *start = s;
+  *len = min_sz(cur, rem - s);
+}
+
+/* Chunk id of every element, for tests that need each element's fold order. */
+int oracle_element_chunks(size_t count, int dtype, int nranks, int nchannels,
+                          size_t chunk_elems, int32_t* chunk_of) {
+  size_t es = elem_size(dtype);
+  if (!es || nranks < 1 || nchannels < 1 || chunk_elems == 0) return -1;
+  if (chunk_elems % (16 / es)) return -1;
+  for (int c = 0; c < nchannels; c++) {
+    size_t lo, hi;
+    oracle_channel_range(count, es, nchannels, c, &lo, &hi);
+    size_t len = hi - lo;
+    for (size_t off = 0; off < len; off += (size_t)nranks * chunk_elems) {
+      size_t cur = oracle_loop_chunk(len, off, es, nranks, chunk_elems);
+      for (int k = 0; k < nranks; k++) {
+        size_t s, l;
+        chunk_span(len - off, cur, k, &s, &l);
+        for (size_t e = 0; e < l; e++) chunk_of[lo + off + s + e] = k;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------
+ * One loop of the ring schedule over all ring indices (step 4).
+ * base: first element of the loop; rem: elements left in the channel from
+ * base; cur: chunk size of this loop.  pay_old/pay_new: n payload buffers of
+ * cur elements each (what every ring index last sent).
+ * --------------------------------------------------------------------- */
+static void ring_loop(int n, int dtype, int op, size_t es, const int* ring,
+                      const void* const* x, void* const* y, size_t base,
+                      size_t rem, size_t cur, unsigned char** pay_old,
+                      unsigned char** pay_new) {
+  for (int s = 0; s <= 2 * n - 2; s++) {
+    for (int i = 0; i < n; i++) {
+      int prev = (i + n - 1) % n;                  /* ring predecessor */
+      int k = ((i + n - 1 - s) % n + n) % n;       /* chunk of this stage */
+      size_t st, len;
+      chunk_span(rem, cur, k, &st, &len);
+      const unsigned char* mine = (const unsigned char*)x[ring[i]] + (base + st) * es;
+      unsigned char* out = (unsigned char*)y[ring[i]] + (base + st) * es;
+      if (s == 0) {
+        /* send: own chunk straight into the successor's FIFO */
+        memcpy(pay_new[i], mine, len * es);
+      } else if (s <= n - 2) {
+        /* recvReduceSend: reduce the received chunk with our own, forward */
+        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);
+      } else if (s == n - 1) {
+        /* recvReduceCopySend: last reduction, the chunk is final: keep it
+         * in our output and forward it */
+        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);
+        memcpy(out, pay_new[i], len * es);
+      } else if (s <= 2 * n - 3) {
+        /* recvCopySend: all-gather hop: keep the final chunk and forward */
+        memcpy(pay_new[i], pay_old[prev], len * es);
+        memcpy(out, pay_new[i], len * es);
+      } else {
+        /* recv: the last final chunk arrives; nothing is forwarded */
+        memcpy(out, pay_old[prev], len * es);
+      }
+    }
+    unsigned char** t = pay_old; pay_old = pay_new; pay_new = t;
+  }
+}
+
+/*
+ * Ring AllReduce over n virtual ranks.
+ *   x[r], y[r]: rank r's input and output (count elements each; may alias).
+ *   ring[i]:    rank at ring index i (NULL = identity); i sends to i+1 mod n.
+ *   chunk_elems: per-rank, per-channel chunk of a full loop, a multiple of
+ *               16 bytes.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
+                          int nchannels, size_t chunk_elems, const int* ring,
+                          const void* const* x, void* const* y) {
+  size_t es = elem_size(dtype);
+  if (!es || op < OR_SUM || op > OR_MAX || nranks < 1 || nchannels < 1) return -1;
+  if (chunk_elems == 0 || chunk_elems % (16 / es)) return -1;
+  int* order = malloc(sizeof(int) * (size_t)nranks);
+  if (!order) return -1;
+  for (int i = 0; i < nranks; i++) order[i] = ring ? ring[i] : i;
+
+  if (nranks == 1) {                   /* a single rank only copies */
+    if (x[order[0]] != y[order[0]]) memcpy(y[order[0]], x[order[0]], count * es);
+    free(order);
+    return 0;
+  }
+
+  size_t maxcur = chunk_elems;
+  unsigned char** pa = calloc((size_t)nranks, sizeof(void*));
+  unsigned char** pb = calloc((size_t)nranks, sizeof(void*));
+  int rc = 0;
+  for (int i = 0; i < nranks && pa && pb; i++) {
+    pa[i] = malloc(maxcur * es);
+    pb[i] = malloc(maxcur * es);
+    if (!pa[i] || !pb[i]) rc = -1;
+  }
+  if (!pa || !pb) rc = -1;
+
+  for (int c = 0; c < nchannels && rc == 0; c++) {
+    size_t lo, hi;
+    oracle_channel_range(count, es, nchannels, c, &lo, &hi);
+    size_t len = hi - lo;
+    for (size_t off = 0; off < len; off += (size_t)nranks * chunk_elems) {
+      size_t cur = oracle_loop_chunk(len, off, es, nranks, chunk_elems);
+      ring_loop(nranks, dtype, op, es, order, x, y, lo + off, len - off, cur, pa, pb);
+    }
+  }
+
+  for (int i = 0; i < nranks; i++) {
+    if (pa) free(pa[i]);
+    if (pb) free(pb[i]);
+  }
+  free(pa);
+  free(pb);
+  free(order);
+  return rc;
+}
+
+/* Array forms of the 16-bit codecs, for the tests' exhaustive pins. */
+void oracle_f16_decode_array(const uint16_t* h, float* f, size_t len) {
+  for (size_t e = 0; e < len; e++) f[e] = f16_decode(h[e]);
+}
+void oracle_f16_encode_array(const float* f, uint16_t* h, size_t len) {
+  for (size_t e = 0; e < len; e++) h[e] = f16_encode_rne(f[e]);
+}
+void oracle_bf16_decode_array(const uint16_t* h, float* f, size_t len) {
+  for (size_t e = 0; e < len; e++) f[e] = bf16_decode(h[e]);
+}
+void oracle_bf16_encode_array(const float* f, uint16_t* h, size_t len) {
+  for (size_t e = 0; e < len; e++) h[e] = bf16_encode_rne(f[e]);
+}

@@ -1,0 +1,122 @@
+"""Planted mistakes: each mutation below is applied to a copy of the oracle's C
+source, compiled on the CPU, and run against a compact battery of the pins.
+Every mutation must make at least one pin fail, which shows the pins can see a
+dropped term, a wrong index or sign, a transposed operand or a wrong rounding
+anywhere in the oracle.  The real oracle must pass the same battery."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from bruteforce_ring import run as brute_run
+from refs import exact_reduce, fold_closed_form, hop
+from ring_allreduce_reduce_amd import workloads as W
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
+
+MUTATIONS = {
+    "chunk index off by one": ("int k = ((i + n - 1 - s) % n + n) % n;", "int k = ((i + n - s) % n + n) % n;"),
+    "reduce dropped (forward only)": (
+        "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);",
+        "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        memcpy(pay_new[i], pay_old[prev], len * es);"),
+    "final recv missing": ("for (int s = 0; s <= 2 * n - 2; s++)", "for (int s = 0; s < 2 * n - 2; s++)"),
+    "ring direction reversed": ("int prev = (i + n - 1) % n;", "int prev = (i + 1) % n;"),
+    "sum becomes difference": ("    case OR_SUM: return a + b;\n    case OR_PROD: return a * b;\n    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic double",
+                               "    case OR_SUM: return a - b;\n    case OR_PROD: return a * b;\n    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic double"),
+    "int8 min operands transposed": (
+        "(unsigned)b[e]); break;\n          case OR_MIN: o[e] = (sb < sa) ? b[e] : a[e]; break;",
+        "(unsigned)b[e]); break;\n          case OR_MIN: o[e] = (sb < sa) ? a[e] : b[e]; break;"),
+    "int32 product becomes sum": ("          case OR_PROD: o[e] = a[e] * b[e]; break;",
+                                  "          case OR_PROD: o[e] = a[e] + b[e]; break;"),
+    "bf16 truncates instead of rounding": (
+        "  double q = (a == 0.0 || ex < -126) ? ldexp(1.0, -133) : ldexp(1.0, ex - 7);\n  double r = rint(a / q) * q;",
+        "  double q = (a == 0.0 || ex < -126) ? ldexp(1.0, -133) : ldexp(1.0, ex - 7);\n  double r = floor(a / q) * q;"),
+    "f16 subnormal threshold wrong": ("ex < -14) ? ldexp(1.0, -24)", "ex < -15) ? ldexp(1.0, -24)"),
+    "last-loop chunk not 16-byte aligned": ("return rem < loop ? align_up(div_up(rem, (size_t)nranks), a) : chunk_elems;",
+                                            "return rem < loop ? div_up(rem, (size_t)nranks) : chunk_elems;"),
+    "channel length not rounded": ("size_t per = align_up(div_up(count, (size_t)nchannels), a);",
+                                   "size_t per = div_up(count, (size_t)nchannels);"),
+    "fp64 min uses max": ("    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void",
+                          "    case OR_MIN: return (b > a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void"),
+}
+
+
+def _battery(lib) -> list:
+    """Returns the names of the pins that fail for the oracle in `lib`."""
+    fails = []
+
+    def run(xs, dtype, op, nch, chunk, ring=None):
+        return oracle.ring_allreduce(xs, dtype, op, nch, chunk, ring=ring, lib=lib)
+
+    # closed form, integers and min/max (ragged, several channels)
+    for dtype in ("int8", "int32", "float64", "bfloat16"):
+        for op in ("sum", "prod", "min", "max"):
+            if dtype in W.FLOATS and op in ("sum", "prod"):
+                continue
+            xs = W.inputs(f"m-{dtype}-{op}", 5, 203, dtype, "uniform", -4, 4)
+            ys = run(xs, dtype, op, 3, 2 * (16 // W.ELEM_BYTES[dtype]))
+            ref = exact_reduce(xs, dtype, op)
+            if not all(np.array_equal(y.view(np.uint8), ref.view(np.uint8)) for y in ys):
+                fails.append(f"closed form {dtype} {op}")
+    # n = 2 single operation
+    for dtype in ("float16", "bfloat16", "float32"):
+        xs = W.inputs(f"m2-{dtype}", 2, 517, dtype, "normal")
+        ys = run(xs, dtype, "sum", 2, 16 // W.ELEM_BYTES[dtype])
+        ref = hop(dtype, "sum", xs[0], xs[1])
+        if not all(np.array_equal(y.view(np.uint8), ref.view(np.uint8)) for y in ys):
+            fails.append(f"two ranks {dtype}")
+    # fold order closed form (float sum, ragged)
+    for dtype in ("float32", "bfloat16", "float16"):
+        xs = W.inputs(f"mf-{dtype}", 4, 1001, dtype, "normal")
+        ch = oracle.element_chunks(1001, dtype, 4, 2, 3 * (16 // W.ELEM_BYTES[dtype]), lib=lib)
+        ys = run(xs, dtype, "sum", 2, 3 * (16 // W.ELEM_BYTES[dtype]))
+        ref = fold_closed_form(xs, dtype, "sum", ch)
+        if not all(np.array_equal(y.view(np.uint8), ref.view(np.uint8)) for y in ys):
+            fails.append(f"fold order {dtype}")
+    # brute force, a few tiny cases
+    for (n, count, nch, dtype) in [(3, 37, 2, "float32"), (4, 67, 3, "int32"), (2, 19, 1, "bfloat16")]:
+        chunk = 16 // W.ELEM_BYTES[dtype]
+        xs = W.inputs(f"mb-{n}-{count}", n, count, dtype, "normal" if dtype in W.FLOATS else "uniform", -4, 4)
+        want = brute_run(xs, dtype, "sum", nch, chunk)
+        got = run(xs, dtype, "sum", nch, chunk)
+        if not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
+            fails.append(f"brute force {n} {count} {dtype}")
+    # codecs against numpy / torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float32)
+    vals = vals[np.isfinite(vals)]
+    probe = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2, vals * np.float32(1.0009765625)])
+    probe = probe[np.isfinite(probe)].astype(np.float32)
+    lib.oracle_f16_encode_array.restype = None
+    out = np.empty(probe.size, dtype=np.uint16)
+    lib.oracle_f16_encode_array(probe.ctypes.data, out.ctypes.data, probe.size)
+    with np.errstate(over="ignore"):
+        if not np.array_equal(out, probe.astype(np.float16).view(np.uint16)):
+            fails.append("f16 codec")
+    import torch
+    out_b = np.empty(probe.size, dtype=np.uint16)
+    lib.oracle_bf16_encode_array(probe.ctypes.data, out_b.ctypes.data, probe.size)
+    ref_b = torch.from_numpy(probe).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if not np.array_equal(out_b, ref_b):
+        fails.append("bf16 codec")
+    return fails
+
+
+def test_real_oracle_passes_battery():
+    assert _battery(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path):
+    before, after = MUTATIONS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(before) == 1, f"mutation site for {name!r} not unique in the oracle"
+    mutated = tmp_path / "mutated.c"
+    mutated.write_text(src.replace(before, after))
+    so = tmp_path / "libmutated.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", str(so), str(mutated), "-lm"], check=True)
+    lib = oracle.load(str(so))
+    assert _battery(lib), f"no pin caught the planted mistake {name!r}"

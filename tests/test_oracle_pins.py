@@ -1,0 +1,256 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* 16-bit codecs: exhaustive against numpy (binary16) and torch (bfloat16).
+* Order-free cases (integers, min, max): numpy's reduction over ranks.
+* Float sum/prod with n = 2: one IEEE operation, computed by numpy/torch.
+* Float fold order: the closed form of a chunk's single trip round the ring,
+  and a threaded brute-force ring with real FIFOs on tiny inputs.
+* The pages' worked example; hand-written partition tables; error bounds;
+  invariants (all ranks equal, inputs untouched, in-place, ring order).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bruteforce_ring import run as brute_run
+from refs import all_equal, error_bound_ok, exact_reduce, fold_closed_form, hop
+from ring_allreduce_reduce_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DTYPES = list(W.STORAGE)
+OPS = ["sum", "prod", "min", "max"]
+
+
+def _gen(key, n, count, dtype, op):
+    if dtype in W.FLOATS and op == "prod":
+        return W.inputs(key, n, count, dtype, "uniform", 0.9, 1.1)
+    if dtype in W.FLOATS:
+        return W.inputs(key, n, count, dtype, "uniform", -4, 4)
+    return W.inputs(key, n, count, dtype, "uniform", -4, 4)
+
+
+def _a(dtype):
+    return 16 // W.ELEM_BYTES[dtype]
+
+
+# ---------------------------------------------------------------- codecs
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_decode(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_bf16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_decode(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _encode_probe_values():
+    rng = np.random.default_rng(7)
+    raw = rng.integers(0, 2 ** 32, size=400000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    # every binary16 / bfloat16 value, its neighbours and the exact halfway
+    # points between consecutive values (the ties)
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = h.view(np.float16).astype(np.float64)
+    b16 = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).double().numpy()
+    pts = []
+    for vals in (f16, b16):
+        v = vals[np.isfinite(vals)]
+        v = np.unique(v)
+        mids = (v[:-1] + v[1:]) / 2
+        pts += [v, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64),
+                np.nextafter(mids.astype(np.float32), np.float32(-np.inf)).astype(np.float64)]
+    extra = np.concatenate(pts).astype(np.float32)
+    allv = np.concatenate([raw, extra, np.array([65504, 65519.99, 65520, 65536, 1e-8, -0.0, 0.0,
+                                                  3.4e38, -3.4e38, np.inf, -np.inf], dtype=np.float32)])
+    return allv[~np.isnan(allv)]
+
+
+def test_f16_encode_rne_against_numpy():
+    v = _encode_probe_values()
+    got = oracle.f16_encode(v)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_encode_rne_against_torch():
+    v = _encode_probe_values()
+    got = oracle.bf16_encode(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- partition
+def _partition_cases():
+    with open(os.path.join(GOLDEN, "partition_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _partition_cases(), ids=lambda c: c["name"])
+def test_partition_matches_hand_tables(case):
+    for c, (lo, hi) in enumerate(case["channels"]):
+        assert oracle.channel_range(case["count"], case["dtype"], case["nchannels"], c) == (lo, hi)
+    want = np.full(case["count"], -1, dtype=np.int32)
+    for a, b, k in case["runs"]:
+        want[a:b] = k
+    got = oracle.element_chunks(case["count"], case["dtype"], case["nranks"],
+                                case["nchannels"], case["chunk_elems"])
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- closed forms
+SHAPES = [  # (n, count, nch, chunk in 16-byte units)
+    (1, 37, 1, 1), (2, 0, 1, 1), (2, 1, 1, 1), (2, 67, 2, 1), (3, 67, 3, 2), (4, 65536, 2, 256),
+    (5, 1000, 3, 3), (8, 4099, 4, 8), (8, 32768, 16, 16), (7, 513, 2, 5), (3, 16, 8, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["int8", "int32"])
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_integers_equal_numpy_reduction(dtype, op, shape):
+    n, count, nch, units = shape
+    xs = _gen(f"int-{dtype}-{op}-{shape}", n, count, dtype, op)
+    ys = oracle.ring_allreduce(xs, dtype, op, nch, units * _a(dtype))
+    ref = exact_reduce(xs, dtype, op)
+    for y in ys:
+        assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("dtype", list(W.FLOATS))
+@pytest.mark.parametrize("op", ["min", "max"])
+@pytest.mark.parametrize("shape", SHAPES[:8])
+def test_float_min_max_equal_library_reduction(dtype, op, shape):
+    n, count, nch, units = shape
+    xs = _gen(f"mm-{dtype}-{op}-{shape}", n, count, dtype, op)
+    ys = oracle.ring_allreduce(xs, dtype, op, nch, units * _a(dtype))
+    ref = exact_reduce(xs, dtype, op)
+    for y in ys:
+        assert np.array_equal(y.view(np.uint8), ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", list(W.FLOATS))
+@pytest.mark.parametrize("op", ["sum", "prod"])
+def test_two_ranks_is_one_ieee_operation(dtype, op):
+    xs = _gen(f"two-{dtype}-{op}", 2, 4133, dtype, op)
+    ys = oracle.ring_allreduce(xs, dtype, op, 3, 2 * _a(dtype))
+    ref = hop(dtype, op, xs[0], xs[1])          # commutative: order free for n = 2
+    for y in ys:
+        assert np.array_equal(y.view(np.uint8), ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", list(W.FLOATS))
+@pytest.mark.parametrize("op", ["sum", "prod"])
+@pytest.mark.parametrize("shape", [(3, 67, 3, 2), (4, 5000, 2, 8), (8, 32768, 16, 16), (5, 999, 4, 3)])
+def test_float_fold_order_closed_form(dtype, op, shape):
+    n, count, nch, units = shape
+    chunk = units * _a(dtype)
+    ring = list(np.random.default_rng(n * 31 + count).permutation(n))
+    xs = _gen(f"fold-{dtype}-{op}-{shape}", n, count, dtype, op)
+    ys = oracle.ring_allreduce(xs, dtype, op, nch, chunk, ring=ring)
+    ref = fold_closed_form(xs, dtype, op, oracle.element_chunks(count, dtype, n, nch, chunk), ring)
+    for y in ys:
+        assert np.array_equal(y.view(np.uint8), ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", list(W.FLOATS))
+@pytest.mark.parametrize("op", ["sum", "prod"])
+def test_float_error_bound(dtype, op):
+    n, count = 8, 3000
+    xs = W.inputs(f"bound-{dtype}-{op}", n, count, dtype, "normal") if op == "sum" else \
+        W.inputs(f"bound-{dtype}-{op}", n, count, dtype, "uniform", 0.9, 1.1)
+    ys = oracle.ring_allreduce(xs, dtype, op, 4, 4 * _a(dtype))
+    idx = np.random.default_rng(3).choice(count, size=300, replace=False)
+    assert error_bound_ok(ys[0], xs, dtype, op, idx)
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    for _ in range(160):
+        n = int(rng.integers(1, 6))
+        count = int(rng.integers(0, 68))
+        nch = int(rng.integers(1, 4))
+        units = int(rng.integers(1, 4))
+        dtype = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, 4))]
+        ring = [int(v) for v in rng.permutation(n)]
+        cases.append((n, count, nch, units, dtype, op, ring))
+    return cases
+
+
+@pytest.mark.parametrize("case", _brute_cases(), ids=lambda c: "-".join(map(str, c[:6])))
+def test_bruteforce_threaded_ring(case):
+    n, count, nch, units, dtype, op, ring = case
+    chunk = units * _a(dtype)
+    xs = _gen(f"brute-{case}", n, count, dtype, op)
+    want = brute_run(xs, dtype, op, nch, chunk, ring)
+    got = oracle.ring_allreduce(xs, dtype, op, nch, chunk, ring=ring)
+    for g, w in zip(got, want):
+        assert np.array_equal(g.view(np.uint8), w.view(np.uint8))
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_from_the_pages():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        n = case["nranks"]
+        count = g["count_float32"] if n == 8 else 1 << 16
+        xs = W.inputs("worked", n, count, "float32", "worked")
+        ys = oracle.ring_allreduce(xs, "float32", "sum", 16, 131072)
+        for y in ys:
+            assert y[0] == case["expected_element0"]
+            assert not np.any(y[1:])
+        del xs, ys
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_every_dtype(dtype):
+    for n in (2, 4, 8):
+        xs = W.inputs("worked", n, 1000, dtype, "worked")
+        ys = oracle.ring_allreduce(xs, dtype, "sum", 2, 4 * _a(dtype))
+        want = W.rank_input("x", n * (n - 1) // 2, 1000, dtype, "worked")   # element 0 = n(n-1)/2
+        for y in ys:
+            assert np.array_equal(y.view(np.uint8), want.view(np.uint8))
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_invariants(dtype):
+    n, count, nch, chunk = 6, 2051, 3, 3 * _a(dtype)
+    xs = _gen(f"inv-{dtype}", n, count, dtype, "sum")
+    keep = [x.copy() for x in xs]
+    ys = oracle.ring_allreduce(xs, dtype, "sum", nch, chunk)
+    assert all_equal(ys)
+    for x, k in zip(xs, keep):
+        assert np.array_equal(x.view(np.uint8), k.view(np.uint8))
+    inplace = [x.copy() for x in xs]
+    oracle.ring_allreduce(inplace, dtype, "sum", nch, chunk, out=inplace)
+    for a, b in zip(inplace, ys):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # a different ring order cannot change an order-free result
+    mm = oracle.ring_allreduce(xs, dtype, "max", nch, chunk)
+    mm2 = oracle.ring_allreduce(xs, dtype, "max", nch, chunk, ring=[3, 1, 5, 0, 2, 4])
+    for a, b in zip(mm, mm2):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_rejects_bad_arguments():
+    xs = W.inputs("bad", 2, 10, "int32", "uniform_int", -3, 3)
+    with pytest.raises(ValueError):
+        oracle.ring_allreduce(xs, "int32", "sum", 1, 3)       # chunk not 16-byte multiple
+    with pytest.raises(ValueError):
+        oracle.ring_allreduce(xs, "int32", "sum", 0, 4)       # no channel
