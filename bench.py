@@ -1,0 +1,190 @@
+"""Benchmark of the ring AllReduce hot path on one MI355X.
+
+Workload: n = 8 virtual ranks, fp32 sum, 16M elements (64 MiB) per rank drawn
+N(0, 1), Simple protocol, 16 channels, 512 KiB chunks, ring r -> r+1 mod 8.
+One step = one ring AllReduce over all 8 ranks with inputs resident in HBM.
+
+Prints one JSON line: busbw (value), algbw, the dominant kernel's roofline
+against MI355X's 8 TB/s HBM peak (algorithmic bytes per launch / average
+launch time measured with HIP events on the launch stream), and the CPU
+oracle timed on this host as a baseline.  The oracle's output also checks the
+last timed call bit for bit.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "busbw & achieved HBM GB/s (% of peak), fp32 sum, n=8 virtual ranks, 64 MiB"
+HBM_PEAK_GBS = 8000.0
+NRANKS = 8
+BYTES_PER_RANK = 64 << 20
+NCHANNELS = 16
+CHUNK_BYTES = 512 * 1024
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ring_simple_fp32_64MiB_n8_traffic.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "ring_allreduce_reduce_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def alg_bytes(n, s, e=1.0):
+    """Algorithmic bytes of one ring AllReduce of s bytes per rank: every rank
+    reads its send buffer once and writes its receive buffer once, and each of
+    the 2(n-1) steps writes and reads one chunk through a FIFO whose bytes are
+    e times the payload (Simple 1, LL 2, LL128 128/120)."""
+    return s * (2 * n + 4 * (n - 1) * e)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the {NRANKS} ranks are virtual ranks inside one MI355X; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ring_allreduce_reduce_amd as ra
+    from ring_allreduce_reduce_amd import workloads as W
+
+    count = BYTES_PER_RANK // 4
+    log("generating inputs")
+    xs = W.inputs("config2", NRANKS, count, "float32", "normal")
+    dev = torch.device("cuda:0")
+    sends = [W.to_torch(x, "float32", dev) for x in xs]
+    recvs = [torch.empty_like(s) for s in sends]
+    stream = torch.cuda.Stream()
+    plan = ra.ringar_plan(count, "float32", NRANKS, NCHANNELS, "Simple", ra.make_config(chunk_bytes=CHUNK_BYTES))
+    send_ptrs = [s.data_ptr() for s in sends]
+    recv_ptrs = [r.data_ptr() for r in recvs]
+    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES)
+
+    def step():
+        code = ra.ringar_allreduce_ex(send_ptrs, recv_ptrs, count, "float32", "sum", NRANKS, NCHANNELS,
+                                      "Simple", stream.cuda_stream, cfg)
+        if code != 0:
+            raise RuntimeError(f"ringar_allreduce_ex: {ra.ringar_result_string(code)}")
+
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if ra.ringar_get_async_error(stream.cuda_stream) != 0:
+        raise RuntimeError("warmup call reported an error")
+
+    log(f"timing {args.steps} steps")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    code = ra.ringar_get_async_error(stream.cuda_stream)
+    if code != 0:
+        raise RuntimeError(f"timed calls reported {ra.ringar_result_string(code)}")
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    log(f"ms/step {ms_per_step:.4f}  avg launch {avg_launch_ms:.4f} ms  min {min(per_launch_ms):.4f}")
+
+    s = BYTES_PER_RANK
+    algbw = s / (ms_per_step * 1e-3) / 1e9
+    busbw = algbw * 2 * (NRANKS - 1) / NRANKS
+    b_alg = alg_bytes(NRANKS, s)
+    achieved = b_alg / (avg_launch_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.load()
+        log("timing the CPU oracle on the full workload (one call)")
+        t0 = time.perf_counter()
+        want = oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+        dt = time.perf_counter() - t0
+        got = [r.cpu().numpy() for r in recvs]
+        same = all(np.array_equal(g.view(np.uint32), w.view(np.uint32)) for g, w in zip(got, want))
+        if not same:
+            raise RuntimeError("GPU result differs from the CPU oracle")
+        log(f"oracle {dt:.2f} s; GPU output matches bit for bit")
+        cpu_alg = s / dt / 1e9
+        cpu = {"value": round(cpu_alg * 2 * (NRANKS - 1) / NRANKS, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt, 3),
+               "sample": "the full workload (8 ranks x 64 MiB fp32), one call, single-threaded C oracle; "
+                         "value is busbw"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(busbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "ring AllReduce, 8 virtual ranks, fp32 sum, 64 MiB per rank, Simple, "
+                               "16 channels, 512 KiB chunks",
+                   "nranks": NRANKS, "bytes_per_rank": s, "proto": "Simple", "nchannels": NCHANNELS,
+                   "chunk_bytes": CHUNK_BYTES, "lanes": plan.lanes, "workgroups": plan.workgroups},
+        "algbw_gbs": round(algbw, 3),
+        "busbw_gbs": round(busbw, 3),
+        "hbm_alg_gbs": round(achieved, 1),
+        "hbm_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "alg_bytes_per_launch": b_alg, "avg_launch_ms": round(avg_launch_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * ringar: ring AllReduce over n virtual ranks that all live in one MI355X.
+ *
+ * The operation is the device-side ring AllReduce described on
+ *   [ARCH] arganzheng.life, "NCCL architecture: topology, channels, algorithms
+ *          and protocols": §九.4 (runRing: send, recvReduceSend x (n-2),
+ *          recvReduceCopySend, recvCopySend x (n-2), recv), §七.2 (the Simple,
+ *          LL and LL128 protocols), §六.5 (a FIFO of 8 steps per connection),
+ *          §八 (the alpha-beta tuning model), §九.1 (argument checks).
+ *   [BOOK] aireadcode.com, "NCCL Source Code Deep Dive: A GPU Journey of One
+ *          AllReduce": §1.3 (ncclAllReduce(sendbuff, recvbuff, count,
+ *          datatype, op, comm, stream) only enqueues; results are valid after
+ *          a stream synchronisation), §2.3 (chunk id and last-loop chunk size),
+ *          ch. 6 of the Japanese edition (count == 0 is a no-op; one rank is a
+ *          local copy; error classes).
+ *
+ * Every rank r contributes sendbuffs[r] (count elements) and receives in
+ * recvbuffs[r] the elementwise reduction over all ranks, identical on every
+ * rank.  All buffers, FIFO slots and step counters are in one GPU's HBM; a
+ * "rank" is a set of workgroups of one kernel launch.
+ *
+ * Threading: calls are host-thread safe.  Calls on one stream run in stream
+ * order and share that stream's FIFO memory; calls on different streams use
+ * different FIFO memory and may run concurrently if the GPU has room for both
+ * grids (the library checks only its own grid against the GPU's capacity).
+ */
+#ifndef RINGAR_H
+#define RINGAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (declared here so the header needs no HIP headers).
+ * NULL is the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* ringar_stream_t;
+
+typedef enum {
+  RINGAR_SUCCESS = 0,
+  RINGAR_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, enum, ring order, ... */
+  RINGAR_ERR_INVALID_USAGE = 2,    /* a valid request this GPU/config cannot run */
+  RINGAR_ERR_INTERNAL = 3,
+  RINGAR_ERR_DEVICE = 4,           /* a HIP call failed; see ringar_last_error() */
+  RINGAR_ERR_ABORTED = 5,          /* the abort word was set while the kernel waited */
+  RINGAR_ERR_TIMEOUT = 6           /* a wait exceeded the spin limit */
+} ringar_result_t;
+
+typedef enum {
+  RINGAR_INT8 = 0,
+  RINGAR_INT32 = 1,
+  RINGAR_FLOAT16 = 2,
+  RINGAR_BFLOAT16 = 3,
+  RINGAR_FLOAT32 = 4,
+  RINGAR_FLOAT64 = 5
+} ringar_dtype_t;
+
+/* sum and prod wrap for integers; fp16/bf16 apply the op in fp32 and round to
+ * nearest-even on every hop; min/max keep the received value on ties. */
+typedef enum { RINGAR_SUM = 0, RINGAR_PROD = 1, RINGAR_MIN = 2, RINGAR_MAX = 3 } ringar_op_t;
+
+/* Protocol codes follow the pages' protocol table order {LL, LL128, Simple}.
+ *   LL:     8-byte FIFO lines, 4 B data + 4 B flag, one 64-bit store each.
+ *   LL128:  128-byte FIFO lines, 120 B data + 8 B flag.
+ *   Simple: plain FIFO slots plus a tail counter (producer) and a head
+ *           counter (consumer), 8 slots per connection. */
+typedef enum {
+  RINGAR_PROTO_AUTO = -1,
+  RINGAR_PROTO_LL = 0,
+  RINGAR_PROTO_LL128 = 1,
+  RINGAR_PROTO_SIMPLE = 2
+} ringar_proto_t;
+
+/* Inputs of the alpha-beta model ([ARCH] §八.1-八.2), per protocol in the
+ * order LL, LL128, Simple.  Bandwidths GB/s, latencies microseconds.
+ *   bus bandwidth:  nch * bw_per_channel * eff[p], LL capped at ll_max_bw,
+ *                   LL128 capped at nch * ll128_per_channel_max_bw;
+ *   alg bandwidth:  bus * n / (2(n-1));
+ *   latency:        base_lat_us[p] + 2(n-1) * hw_lat_us[p];
+ *   time:           latency + bytes / (1000 * alg bandwidth).
+ * Channel auto rule ([ARCH] §六.4): start at min(max_channels,
+ * max_pairs / n) and drop one channel while
+ * bytes < nch * threads[p] * thread_threshold[p] (LL: times n). */
+typedef struct {
+  double bw_per_channel;
+  double ll_max_bw;
+  double ll128_per_channel_max_bw;
+  double eff[3];
+  double base_lat_us[3];
+  double hw_lat_us[3];
+  int max_channels;
+  int max_pairs;
+  int threads[3];
+  int thread_threshold[3];
+  size_t default_chunk_bytes[3];
+} ringar_model_t;
+
+/* Optional knobs of ringar_allreduce_ex.  Zero-initialise, then set fields.
+ *   chunk_bytes:     per-rank, per-channel chunk of one ring step; a multiple
+ *                    of 16 bytes; 0 = the protocol's default.
+ *   ring_order:      host array of nranks ints: rank at ring index i (ring
+ *                    index i sends to i+1 mod n); NULL = identity.  Must be a
+ *                    permutation of 0..n-1.
+ *   model:           model for AUTO choices; NULL = built-in MI355X model.
+ *   lanes:           wavefronts working in parallel on each (rank, channel),
+ *                    each with its own FIFO; 0 = chosen by size.  A power of
+ *                    two, at most 32.  Does not change any result.
+ *   spin_limit_ms:   a wait that lasts longer ends the kernel with
+ *                    RINGAR_ERR_TIMEOUT (reported by ringar_get_async_error);
+ *                    0 = default (env RINGAR_SPIN_LIMIT_MS, else 2000 ms).
+ *   abort_flag:      host-mapped (pinned) word, or NULL.  While nonzero, any
+ *                    waiting wavefront gives up with RINGAR_ERR_ABORTED.
+ *   skip_rank:       test hook, normally -1: every wavefront of this rank
+ *                    returns at once, so its peers must time out or abort. */
+typedef struct {
+  size_t chunk_bytes;
+  const int* ring_order;
+  const ringar_model_t* model;
+  int lanes;
+  uint32_t spin_limit_ms;
+  volatile uint32_t* abort_flag;
+  int skip_rank;
+} ringar_config_t;
+
+/* The resolved plan of a call (what ringar_allreduce would launch). */
+typedef struct {
+  ringar_proto_t proto;
+  int nchannels;
+  size_t chunk_bytes;
+  size_t chunk_elems;
+  size_t align_elems;      /* 16 B / element size */
+  size_t channel_elems;    /* per-channel length before clipping to count */
+  int lanes;               /* wavefronts per (rank, channel) */
+  int workgroups;          /* grid size */
+  int threads_per_group;
+  uint64_t max_steps;      /* upper bound on FIFO steps per connection */
+  double predicted_us[3];  /* model time per protocol (LL, LL128, Simple) */
+} ringar_plan_t;
+
+/*
+ * Ring AllReduce of n = nranks virtual ranks ([BOOK] §1.3 signature with a
+ * communicator replaced by the rank count).
+ *   sendbuffs, recvbuffs: host arrays of nranks DEVICE pointers; rank r reads
+ *       count elements at sendbuffs[r] and writes count elements at
+ *       recvbuffs[r].  sendbuffs[r] == recvbuffs[r] (in place) is allowed;
+ *       any other overlap between the 2n buffers is RINGAR_ERR_INVALID_USAGE.
+ *       Pointers must be aligned to the element size; 16-byte aligned
+ *       pointers take the vector path.  The caller owns all buffers; the
+ *       host arrays are read only during the call.
+ *   count: elements per rank.  0 is a successful no-op.
+ *   nchannels: 1..64, or 0 = chosen by the model's size rule.
+ *   proto: a protocol, or RINGAR_PROTO_AUTO = the model's fastest.
+ *   stream: the work is enqueued on this stream; results are valid after the
+ *       stream has been synchronised.  nranks == 1 enqueues a device copy.
+ * Errors are reported before anything is enqueued; a wait that times out or
+ * is aborted inside the kernel is reported by ringar_get_async_error.
+ */
+ringar_result_t ringar_allreduce(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                 ringar_dtype_t dtype, ringar_op_t op, int nranks,
+                                 int nchannels, ringar_proto_t proto, ringar_stream_t stream);
+
+/* As ringar_allreduce with the optional knobs of ringar_config_t (cfg may be
+ * NULL). */
+ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                    ringar_dtype_t dtype, ringar_op_t op, int nranks,
+                                    int nchannels, ringar_proto_t proto, ringar_stream_t stream,
+                                    const ringar_config_t* cfg);
+
+/* Host only, no GPU needed: the plan ringar_allreduce_ex would use for these
+ * arguments (cfg may be NULL).  Returns the same argument errors. */
+ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
+                            ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out);
+
+/* Host only: the model's fastest protocol for `bytes` per rank over nchannels
+ * channels (model NULL = built-in), ties going to Simple, then LL128
+ * ([BOOK] ch. 5 of the Japanese edition: the first strictly smaller time in a
+ * front-pushed candidate list wins).  predicted_us (may be NULL) receives the
+ * three times. */
+ringar_result_t ringar_select(size_t bytes, int nranks, int nchannels, const ringar_model_t* model,
+                              ringar_proto_t* out, double* predicted_us);
+
+/* Host only: the built-in MI355X model constants. */
+ringar_result_t ringar_default_model(ringar_model_t* out);
+
+/* Host only: element range [lo, hi) of channel c and, for the loop starting
+ * at element `loop_off` of that channel, chunk k's range [klo, khi)
+ * (absolute element indices; empty ranges have klo == khi). */
+ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
+                                   size_t chunk_elems, int c, size_t loop_off, int k,
+                                   size_t* lo, size_t* hi, size_t* klo, size_t* khi);
+
+/* Waits for `stream`, then returns (and clears) the first error a kernel on
+ * this stream recorded: RINGAR_ERR_TIMEOUT or RINGAR_ERR_ABORTED, else
+ * RINGAR_SUCCESS.  After such an error the library's FIFO state is still
+ * valid for later calls. */
+ringar_result_t ringar_get_async_error(ringar_stream_t stream);
+
+/* Synchronises the device and frees every FIFO, counter and scratch buffer
+ * the library holds (they are re-created on the next call). */
+ringar_result_t ringar_release(void);
+
+const char* ringar_result_string(ringar_result_t r);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char* ringar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGAR_H */

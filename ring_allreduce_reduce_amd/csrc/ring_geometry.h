@@ -1,0 +1,156 @@
+// Geometry of one ring AllReduce launch: how the buffer is cut into channels,
+// loops, chunks, lane parts and FIFO slices.  Used by the host (plan, step
+// bounds) and by the kernel (addressing), so both agree by construction.
+//
+// Page rules ([BOOK] = "NCCL Source Code Deep Dive", [ARCH] = "NCCL
+// architecture: topology, channels, algorithms and protocols"):
+//   * channels own contiguous ranges of the buffer ([BOOK] §2.2); the length
+//     per channel is rounded up to whole 16-byte units (the pages leave the
+//     remainder open);
+//   * a loop covers nranks chunks; the last partial loop uses chunks of
+//     alignUp(ceil(rem / nranks), 16 B / elemSize) elements ([BOOK] §2.3);
+//   * ring index i works on chunk (i + n - 1 - s) mod n at stage s ([BOOK] §2.3).
+// MI355X additions (they change no result): each (rank, channel) chunk is
+// split among `lanes` wavefronts in 1 KiB-aligned contiguous parts, each
+// lane with its own FIFO; a lane's part is sent in FIFO slices of one slot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define RA_HD __host__ __device__ __forceinline__
+
+namespace ringar {
+
+constexpr int kMaxRanks = 64;
+constexpr int kMaxChannels = 64;
+constexpr int kMaxLanes = 32;
+constexpr int kSteps = 8;                 // FIFO slots per connection (NCCL_STEPS)
+constexpr uint32_t kLaneGranBytes = 1024; // lane parts start on 1 KiB boundaries
+
+// FIFO slot geometry per protocol.
+constexpr uint32_t kSimpleSlotBytes = 32768;              // data bytes per slot
+constexpr uint32_t kLLSlotLines = 2048;                    // 8-byte lines per slot (8 KiB of data)
+constexpr uint32_t kLLSlotBytes = kLLSlotLines * 8;        // FIFO bytes per slot
+constexpr uint32_t kLL128SlotLines = 256;                  // 128-byte lines per slot (30 KiB of data)
+constexpr uint32_t kLL128SlotBytes = kLL128SlotLines * 128;// FIFO bytes per slot
+
+enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
+
+RA_HD uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+RA_HD uint64_t align_up(uint64_t a, uint64_t b) { return div_up(a, b) * b; }
+RA_HD uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Elements of one 16-byte unit.
+RA_HD uint64_t align_elems(uint32_t esize) { return 16 / esize; }
+
+// Per-channel length before clipping to the buffer.
+RA_HD uint64_t channel_len(uint64_t count, int nchannels, uint32_t esize) {
+  return align_up(div_up(count, (uint64_t)nchannels), align_elems(esize));
+}
+
+// Channel c's element range [lo, hi).
+RA_HD void channel_bounds(uint64_t count, uint64_t per_channel, int c, uint64_t* lo, uint64_t* hi) {
+  *lo = min_u64(count, (uint64_t)c * per_channel);
+  *hi = min_u64(count, *lo + per_channel);
+}
+
+// Chunk elements of the loop that starts `off` elements into a channel of
+// `len` elements.
+RA_HD uint64_t loop_chunk(uint64_t len, uint64_t off, int nranks, uint64_t chunk_elems,
+                          uint32_t esize) {
+  uint64_t loop = (uint64_t)nranks * chunk_elems;
+  uint64_t rem = len - off;
+  if (rem >= loop) return chunk_elems;
+  return align_up(div_up(rem, (uint64_t)nranks), align_elems(esize));
+}
+
+// Chunk k of a loop with `rem` elements left and chunk size `cur`: start and
+// length relative to the loop start (empty past the end).
+RA_HD void chunk_bounds(uint64_t rem, uint64_t cur, int k, uint64_t* start, uint64_t* len) {
+  uint64_t s = (uint64_t)k * cur;
+  if (s >= rem) {
+    *start = rem;
+    *len = 0;
+    return;
+  }
+  *start = s;
+  *len = min_u64(cur, rem - s);
+}
+
+// Chunk visited by ring index i at stage s (0 <= s <= 2n-2).
+RA_HD int stage_chunk(int i, int s, int nranks) { return (i - 1 - s + 2 * nranks) % nranks; }
+
+// Lane l's part of a chunk of `clen` elements: [start, start + len).
+RA_HD void lane_bounds(uint64_t clen, int lanes, uint32_t esize, int l, uint64_t* start,
+                       uint64_t* len) {
+  uint64_t gran = kLaneGranBytes / esize;
+  uint64_t part = align_up(div_up(clen, (uint64_t)lanes), gran);
+  uint64_t s = min_u64(clen, (uint64_t)l * part);
+  *start = s;
+  *len = min_u64(clen, s + part) - s;
+}
+
+// Elements one FIFO slot carries.
+RA_HD uint64_t slot_elems(int proto, uint32_t esize) {
+  if (proto == kSimple) return kSimpleSlotBytes / esize;
+  if (proto == kLL) return (kLLSlotLines * 4) / esize;
+  return (kLL128SlotLines * 120) / esize;
+}
+
+// FIFO bytes of one connection (kSteps slots).
+RA_HD uint64_t fifo_conn_bytes(int proto) {
+  if (proto == kSimple) return (uint64_t)kSteps * kSimpleSlotBytes;
+  if (proto == kLL) return (uint64_t)kSteps * kLLSlotBytes;
+  return (uint64_t)kSteps * kLL128SlotBytes;
+}
+
+// Counters of one connection: tail and head, each on its own 128-byte line.
+constexpr int kCounterWords = 32;   // uint64 words per connection (2 x 128 B)
+constexpr int kTailWord = 0;
+constexpr int kHeadWord = 16;
+
+// Connection feeding ring index i on channel c, lane l.
+RA_HD uint64_t conn_index(int c, int i, int l, int nranks, int lanes) {
+  return ((uint64_t)c * nranks + i) * lanes + l;
+}
+
+// Everything one launch needs, passed by value as kernel arguments.
+struct KernelArgs {
+  const char* send[kMaxRanks];   // by ring index
+  char* recv[kMaxRanks];         // by ring index
+  uint64_t count;
+  uint64_t per_channel;
+  uint64_t chunk_elems;
+  uint64_t base;                 // step base of this call (absolute counters)
+  char* fifo;                    // this protocol's FIFO region
+  uint64_t* counters;            // kCounterWords per connection
+  uint64_t* error;               // (call id << 8) | code of the first failure
+  const volatile uint32_t* abort_flag;
+  uint64_t spin_ticks;           // wall-clock ticks a wait may last
+  uint64_t call_id;
+  int nranks;
+  int nchannels;
+  int lanes;                     // wavefronts per (rank, channel)
+  int lanes_per_block;
+  int xcd_map;                   // 1: all ranks of a (channel, lane block) on one XCD
+  int skip_ring_index;           // -1: none
+  int vec_ok;                    // all user pointers 16-byte aligned
+};
+
+// Workgroup -> (ring index, channel, lane block).  With xcd_map the hardware's
+// round-robin dispatch of workgroup ids over the 8 XCDs puts the n workgroups
+// of one (channel, lane block) group on the same XCD, so a FIFO's producer and
+// consumer share that XCD's L2.  Without it groups are laid out linearly.
+RA_HD void decode_block(int block, int nranks, int xcd_map, int* ring_index, int* group) {
+  if (xcd_map) {
+    int xcd = block % 8, j = block / 8;
+    *group = xcd + 8 * (j / nranks);
+    *ring_index = j % nranks;
+  } else {
+    *group = block / nranks;
+    *ring_index = block % nranks;
+  }
+}
+
+}  // namespace ringar

@@ -1,0 +1,21 @@
+// Host-callable entry points of ring_kernel.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ring_geometry.h"
+
+namespace ringar {
+
+// Kernel instance for (dtype code, op code, protocol) of the public header.
+const void* kernel_for(int dtype, int op, int proto);
+
+hipError_t launch_ring(int dtype, int op, int proto, const KernelArgs& args, int grid, int block,
+                       hipStream_t stream);
+
+hipError_t max_active_blocks(int dtype, int op, int proto, int block, int* per_cu);
+
+// Stream-ordered fill of `words` 64-bit words.
+hipError_t launch_fill(uint64_t* p, uint64_t words, uint64_t value, hipStream_t stream);
+
+}  // namespace ringar

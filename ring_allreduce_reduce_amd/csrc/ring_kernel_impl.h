@@ -1,0 +1,596 @@
+// Ring AllReduce kernel for gfx950: n virtual ranks, all in one GPU.
+//
+// One launch runs every (ring index, channel, lane) as one wavefront.  Each
+// wavefront walks the runRing primitive sequence of
+// [ARCH] "NCCL architecture: topology, channels, algorithms and protocols",
+// §九.4: send; (n-2) x recvReduceSend; recvReduceCopySend; (n-2) x
+// recvCopySend; recv, once per loop of its channel.  A primitive moves the
+// wavefront's part of one chunk through the FIFO to the successor ring index
+// in slices of one FIFO slot, under one of the three protocols of §七.2:
+//
+//   Simple  data in the slot; the producer waits until its stores are
+//           complete, then publishes the tail counter; the consumer polls the
+//           tail, reads, then publishes the head counter that frees the slot.
+//   LL      8-byte lines of 4 data bytes + 4 flag bytes, each written with a
+//           single 64-bit store; the consumer re-reads a line until its flag
+//           equals the step's flag.  No counter round trip for data.
+//   LL128   128-byte lines of 120 data bytes + an 8-byte flag in bytes
+//           120..127.  gfx950 does not promise that a 128-byte line written
+//           by 8 lanes becomes visible at once (the pages rely on NVLink for
+//           that), so the producer publishes a batch of line flags only after
+//           its data stores have completed, and the consumer reads a line's
+//           data only after it has seen that line's flag.
+//
+// FIFO accesses use device-coherent (sc1) loads and stores, which write
+// through and read past the per-XCD L2 caches, so producer and consumer may
+// sit on different XCDs.  Counters and flags are relaxed agent-scope atomics;
+// ordering comes from waiting for the issuing wavefront's own outstanding
+// memory operations (s_waitcnt vmcnt(0)) before a counter or flag is stored.
+// Flags and counters hold absolute step numbers (call base + step + 1) that
+// only grow across calls, so nothing is ever cleared between calls (§七.2:
+// the LL flag is the step number, monotonic, never cleared by the receiver).
+//
+// Every wait is bounded: it gives up after spin_ticks of wall clock, when the
+// host-mapped abort word is set, or when another wavefront of the same call
+// has already given up; the first failure is recorded in the error word.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ring_geometry.h"
+
+namespace ringar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// ----------------------------------------------------------------- elements
+// op(received a, local b); integers wrap, 16-bit floats go through fp32 and
+// round to nearest-even, min/max keep the received value on ties.
+struct I8 {
+  using T = uint8_t;
+  template <int OP> __device__ static T op(T a, T b) {
+    if (OP == 0) return (T)(a + b);
+    if (OP == 1) return (T)((uint32_t)a * (uint32_t)b);
+    int8_t sa = (int8_t)a, sb = (int8_t)b;
+    if (OP == 2) return sb < sa ? b : a;
+    return sb > sa ? b : a;
+  }
+};
+struct I32 {
+  using T = uint32_t;
+  template <int OP> __device__ static T op(T a, T b) {
+    if (OP == 0) return a + b;
+    if (OP == 1) return a * b;
+    int32_t sa = (int32_t)a, sb = (int32_t)b;
+    if (OP == 2) return sb < sa ? b : a;
+    return sb > sa ? b : a;
+  }
+};
+template <int OP> __device__ __forceinline__ float fop(float a, float b) {
+  if (OP == 0) return a + b;
+  if (OP == 1) return a * b;
+  if (OP == 2) return b < a ? b : a;
+  return b > a ? b : a;
+}
+struct F16 {
+  using T = uint16_t;
+  template <int OP> __device__ static T op(T a, T b) {
+    float fa = (float)__builtin_bit_cast(_Float16, a);
+    float fb = (float)__builtin_bit_cast(_Float16, b);
+    return __builtin_bit_cast(uint16_t, (_Float16)fop<OP>(fa, fb));
+  }
+};
+struct BF16 {
+  using T = uint16_t;
+  __device__ static float widen(T h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+  __device__ static T narrow(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (T)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                       // nearest-even
+    return (T)(u >> 16);
+  }
+  template <int OP> __device__ static T op(T a, T b) { return narrow(fop<OP>(widen(a), widen(b))); }
+};
+struct F32 {
+  using T = float;
+  template <int OP> __device__ static T op(T a, T b) { return fop<OP>(a, b); }
+};
+struct F64 {
+  using T = double;
+  template <int OP> __device__ static T op(T a, T b) {
+    if (OP == 0) return a + b;
+    if (OP == 1) return a * b;
+    if (OP == 2) return b < a ? b : a;
+    return b > a ? b : a;
+  }
+};
+
+// Elementwise op over a 16-byte packet.
+template <class E, int OP> __device__ __forceinline__ u32x4 vop(u32x4 a, u32x4 b) {
+  using T = typename E::T;
+  constexpr int N = 16 / sizeof(T);
+  struct P { T v[N]; };
+  P pa = __builtin_bit_cast(P, a), pb = __builtin_bit_cast(P, b), pr;
+#pragma unroll
+  for (int e = 0; e < N; e++) pr.v[e] = E::template op<OP>(pa.v[e], pb.v[e]);
+  return __builtin_bit_cast(u32x4, pr);
+}
+
+// ----------------------------------------------------------------- memory
+constexpr int kSC1 = 16;   // device-coherent: write through / read past L2
+constexpr int kNT = 2;     // streaming hint for user buffers
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int AUX> __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+template <int AUX> __device__ __forceinline__ void st16(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
+}
+template <int AUX> __device__ __forceinline__ u32x4 ld8(rsrc_t r, uint32_t off) {
+  u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
+  return u32x4{v.x, v.y, 0u, 0u};
+}
+template <int AUX> __device__ __forceinline__ void st8(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, (int)off, 0, AUX);
+}
+
+// Element-wise access to the first `nb` bytes (a multiple of the element
+// size, < 16) of a packet at byte offset `off`: for ragged tails and for
+// buffers that are not 16-byte aligned.
+template <class E, int AUX> __device__ __forceinline__ u32x4 ld_part(rsrc_t r, uint32_t off, uint32_t nb) {
+  using T = typename E::T;
+  constexpr int N = 16 / sizeof(T);
+  struct P { T v[N]; };
+  P p;
+#pragma unroll
+  for (int e = 0; e < N; e++) {
+    T x = 0;
+    if ((uint32_t)(e * sizeof(T)) < nb) {
+      uint32_t o = off + e * sizeof(T);
+      if constexpr (sizeof(T) == 1) x = __builtin_amdgcn_raw_buffer_load_b8(r, (int)o, 0, AUX);
+      else if constexpr (sizeof(T) == 2) x = __builtin_amdgcn_raw_buffer_load_b16(r, (int)o, 0, AUX);
+      else if constexpr (sizeof(T) == 4) x = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, AUX));
+      else x = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)o, 0, AUX));
+    }
+    p.v[e] = x;
+  }
+  return __builtin_bit_cast(u32x4, p);
+}
+template <class E, int AUX> __device__ __forceinline__ void st_part(u32x4 v, rsrc_t r, uint32_t off, uint32_t nb) {
+  using T = typename E::T;
+  constexpr int N = 16 / sizeof(T);
+  struct P { T v[N]; };
+  P p = __builtin_bit_cast(P, v);
+#pragma unroll
+  for (int e = 0; e < N; e++) {
+    if ((uint32_t)(e * sizeof(T)) < nb) {
+      uint32_t o = off + e * sizeof(T);
+      if constexpr (sizeof(T) == 1) __builtin_amdgcn_raw_buffer_store_b8(p.v[e], r, (int)o, 0, AUX);
+      else if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(p.v[e], r, (int)o, 0, AUX);
+      else if constexpr (sizeof(T) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p.v[e]), r, (int)o, 0, AUX);
+      else __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, p.v[e]), r, (int)o, 0, AUX);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------- waiting
+enum { kErrAborted = 5, kErrTimeout = 6 };
+
+struct Waiter {
+  const KernelArgs* a;
+  uint64_t t0;
+  uint32_t spins;
+  __device__ void start() { t0 = 0; spins = 0; }
+  // One idle round of a wait loop; false when the wait must give up.
+  __device__ __forceinline__ bool idle() {
+    __builtin_amdgcn_s_sleep(1);
+    if ((++spins & 127u) != 0) return true;
+    uint64_t now = wall_clock64();
+    if (t0 == 0) t0 = now;
+    uint64_t err = ld_relaxed(a->error);
+    if ((err >> 8) == a->call_id) return false;                 // a peer gave up
+    int code = 0;
+    if (a->abort_flag && __hip_atomic_load(a->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+      code = kErrAborted;
+    else if (now - t0 > a->spin_ticks)
+      code = kErrTimeout;
+    if (code) {
+      uint64_t word = (a->call_id << 8) | (uint64_t)code;
+      __hip_atomic_fetch_max(a->error, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    return true;
+  }
+};
+
+// Waits until *p >= v (wavefront-uniform).
+__device__ __forceinline__ bool wait_ge(Waiter& w, const uint64_t* p, uint64_t v) {
+  w.start();
+  while (true) {
+    // every lane loads the same word; vote so the exit is uniform
+    if (__all(ld_relaxed(p) >= v)) break;
+    if (!w.idle()) return false;
+  }
+  compiler_fence();
+  return true;
+}
+
+// ----------------------------------------------------------------- one lane
+struct Conn {
+  char* fifo;          // kSteps slots
+  uint64_t* tail;      // written by the producer
+  uint64_t* head;      // written by the consumer
+};
+
+struct Lane {
+  const KernelArgs* a;
+  Conn in, out;
+  const char* src;     // own send buffer
+  char* dst;           // own receive buffer
+  uint64_t sstep, rstep;
+  int lane;            // lane within the wavefront
+  Waiter w;
+};
+
+enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8 };
+
+constexpr int kUnroll = 4;
+
+// Result of one packet: op(received, local), or whichever operand exists.
+template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 b) {
+  if ((F & kRecv) && (F & kSrc)) return vop<E, OP>(a, b);
+  if (F & kRecv) return a;
+  return b;
+}
+
+// --- Simple: one slice = one slot ------------------------------------------
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_simple(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if (F & kRecv) {
+    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1)) return false;
+  }
+  if (F & kSend) {
+    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+  }
+  rsrc_t rin = make_rsrc(L.in.fifo + (L.rstep % kSteps) * kSimpleSlotBytes, kSimpleSlotBytes);
+  rsrc_t rout = make_rsrc(L.out.fifo + (L.sstep % kSteps) * kSimpleSlotBytes, kSimpleSlotBytes);
+  const uint64_t boff = e0 * sizeof(typename E::T);
+  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
+  const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
+  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
+    u32x4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      const bool in = p < nfull;
+      if (F & kRecv) va[u] = in ? ld16<kSC1>(rin, p * 16) : u32x4{0u, 0u, 0u, 0u};
+      if (F & kSrc) vb[u] = in ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      if (p >= nfull) continue;
+      const u32x4 r = combine<E, OP, F>(va[u], vb[u]);
+      if (F & kSend) st16<kSC1>(r, rout, p * 16);
+      if (F & kDst) st16<kNT>(r, rdst, p * 16);
+    }
+  }
+  // The ragged last packet, or every packet when a user buffer is not
+  // 16-byte aligned: element-wise on the user side.
+#pragma unroll 1
+  for (uint32_t p = nfull + L.lane; p < npk; p += 64) {
+    const uint32_t off = p * 16, nb = min(16u, nbytes - off);
+    u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+    if (F & kRecv) x = ld16<kSC1>(rin, off);
+    if (F & kSrc) y = ld_part<E, kNT>(rsrc_, off, nb);
+    const u32x4 r = combine<E, OP, F>(x, y);
+    if (F & kSend) st16<kSC1>(r, rout, off);
+    if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
+  }
+  if (F & kSend) {
+    wait_mem();
+    st_relaxed(L.out.tail, a.base + L.sstep + 1);
+    L.sstep++;
+  }
+  if (F & kRecv) {
+    wait_mem();
+    st_relaxed(L.in.head, a.base + L.rstep + 1);
+    L.rstep++;
+  }
+  return true;
+}
+
+// --- LL: 8-byte lines, 4 data bytes + 4 flag bytes ------------------------
+__device__ __forceinline__ uint64_t ll_line(uint32_t data, uint32_t flag) {
+  return ((uint64_t)flag << 32) | data;
+}
+
+__device__ __forceinline__ bool ll_ready(uint64_t line, uint32_t flag) {
+  return (uint32_t)(line >> 32) == flag;
+}
+
+// Polls the 4 lines of packet p until all carry `flag`; wavefront-uniform
+// over the active lanes.
+__device__ __forceinline__ bool ll_recv4(Waiter& w, const uint64_t* lin, uint32_t p, bool active,
+                                         uint32_t flag, uint64_t (&ln)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) ln[q] = active ? ld_relaxed(lin + 4 * p + q) : ll_line(0, flag);
+  w.start();
+  while (true) {
+    bool ok = ll_ready(ln[0], flag) && ll_ready(ln[1], flag) && ll_ready(ln[2], flag) &&
+              ll_ready(ln[3], flag);
+    if (__all(ok)) return true;
+    if (!w.idle()) return false;
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      if (!ll_ready(ln[q], flag)) ln[q] = ld_relaxed(lin + 4 * p + q);
+  }
+}
+
+__device__ __forceinline__ void ll_send4(uint64_t* lout, uint32_t p, u32x4 r, uint32_t flag) {
+  st_relaxed(lout + 4 * p + 0, ll_line(r.x, flag));
+  st_relaxed(lout + 4 * p + 1, ll_line(r.y, flag));
+  st_relaxed(lout + 4 * p + 2, ll_line(r.z, flag));
+  st_relaxed(lout + 4 * p + 3, ll_line(r.w, flag));
+}
+
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if (F & kSend) {
+    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+  }
+  const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
+  const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
+  const uint64_t* lin = (const uint64_t*)(L.in.fifo + (L.rstep % kSteps) * kLLSlotBytes);
+  uint64_t* lout = (uint64_t*)(L.out.fifo + (L.sstep % kSteps) * kLLSlotBytes);
+  const uint64_t boff = e0 * sizeof(typename E::T);
+  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
+  const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
+  constexpr int U = 2;
+  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
+    u32x4 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      if (F & kSrc) vb[u] = (p < nfull) ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (F & kRecv) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t p = p0 + u * 64 + L.lane;
+        uint64_t ln[4];
+        if (!ll_recv4(L.w, lin, p, p < nfull, fin, ln)) return false;
+        va[u] = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      if (p >= nfull) continue;
+      const u32x4 r = combine<E, OP, F>(va[u], vb[u]);
+      if (F & kSend) ll_send4(lout, p, r, fout);
+      if (F & kDst) st16<kNT>(r, rdst, p * 16);
+    }
+  }
+  bool failed = false;
+#pragma unroll 1
+  for (uint32_t p = nfull + L.lane; p < npk; p += 64) {
+    const uint32_t off = p * 16, nb = min(16u, nbytes - off);
+    u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+    if (F & kSrc) y = ld_part<E, kNT>(rsrc_, off, nb);
+    if (F & kRecv) {
+      uint64_t ln[4];
+      if (!ll_recv4(L.w, lin, p, true, fin, ln)) { failed = true; break; }
+      x = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+    }
+    const u32x4 r = combine<E, OP, F>(x, y);
+    if (F & kSend) ll_send4(lout, p, r, fout);
+    if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
+  }
+  if (__any(failed)) return false;
+  if (F & kSend) L.sstep++;
+  if (F & kRecv) {
+    wait_mem();
+    st_relaxed(L.in.head, a.base + L.rstep + 1);
+    L.rstep++;
+  }
+  return true;
+}
+
+// --- LL128: 128-byte lines, 120 data bytes + 8-byte flag -------------------
+// A batch is 64 lines; packet u of a lane covers line b0 + 8u + lane/8,
+// 16-byte column lane%8 (column 7 carries 8 data bytes and the flag).
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if (F & kSend) {
+    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+  }
+  const uint64_t fin = a.base + L.rstep + 1;
+  const uint64_t fout = a.base + L.sstep + 1;
+  char* sin = L.in.fifo + (L.rstep % kSteps) * kLL128SlotBytes;
+  char* sout = L.out.fifo + (L.sstep % kSteps) * kLL128SlotBytes;
+  rsrc_t rin = make_rsrc(sin, kLL128SlotBytes);
+  rsrc_t rout = make_rsrc(sout, kLL128SlotBytes);
+  const uint64_t boff = e0 * sizeof(typename E::T);
+  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  const bool vec = a.vec_ok;
+  const uint32_t nlines = (nbytes + 119) / 120;
+  const int col = L.lane & 7;
+  const uint32_t psize = col == 7 ? 8u : 16u;
+  const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;   // data bytes of the column
+  for (uint32_t b0 = 0; b0 < nlines; b0 += 64) {
+    const uint32_t nl = min(64u, nlines - b0);
+    u32x4 va[8], vb[8];
+    uint32_t part = 0;   // packets (bit u) that end inside their column
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const uint32_t line = b0 + 8 * u + (L.lane >> 3);
+      const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + col * 16);
+      const bool live = line < b0 + nl && valid > 0;
+      const bool full = live && vec && (uint32_t)valid >= psize;
+      if (live && !full) part |= 1u << u;
+      if (F & kSrc) vb[u] = full ? (col == 7 ? ld8<kNT>(rsrc_, line * 120 + 112) : ld16<kNT>(rsrc_, line * 120 + col * 16))
+                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (F & kRecv) {
+      // flags first: lane t watches line b0 + t
+      const uint64_t* fl = (const uint64_t*)(sin + (size_t)(b0 + L.lane) * 128 + 120);
+      L.w.start();
+      uint64_t f = (L.lane < (int)nl) ? ld_relaxed(fl) : fin;
+      while (true) {
+        if (__all(f == fin)) break;
+        if (!L.w.idle()) return false;
+        if (f != fin) f = ld_relaxed(fl);
+      }
+      compiler_fence();
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
+        va[u] = (line < b0 + nl) ? ld16<kSC1>(rin, line * 128 + col * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) va[u] = combine<E, OP, F>(va[u], vb[u]);
+    // Packets that end inside their column: element-wise on the user side.
+#pragma unroll 1
+    for (uint32_t bits = part; bits; bits &= bits - 1) {
+      const int u = __builtin_ctz(bits);
+      const uint32_t line = b0 + 8 * u + (L.lane >> 3);
+      const uint32_t uoff = line * 120 + coff;
+      const uint32_t nb = min(psize, nbytes - uoff);
+      u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+      if (F & kRecv) x = ld16<kSC1>(rin, line * 128 + col * 16);
+      if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
+      const u32x4 r = combine<E, OP, F>(x, y);
+      if (F & kSend) {
+        if (col == 7) st8<kSC1>(r, rout, line * 128 + 112);
+        else st16<kSC1>(r, rout, line * 128 + col * 16);
+      }
+      if (F & kDst) st_part<E, kNT>(r, rdst, uoff, nb);
+    }
+    if (F & kSend) {
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
+        if (line >= b0 + nl || (part >> u) & 1u) continue;
+        if (col == 7) st8<kSC1>(va[u], rout, line * 128 + 112);
+        else st16<kSC1>(va[u], rout, line * 128 + col * 16);
+      }
+      wait_mem();   // all data of the batch is visible before any of its flags
+      if (L.lane < (int)nl) st_relaxed((uint64_t*)(sout + (size_t)(b0 + L.lane) * 128 + 120), fout);
+    }
+    if (F & kDst) {
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
+        const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + col * 16);
+        if (line >= b0 + nl || valid <= 0 || (part >> u) & 1u) continue;
+        if (col == 7) st8<kNT>(va[u], rdst, line * 120 + 112);
+        else st16<kNT>(va[u], rdst, line * 120 + col * 16);
+      }
+    }
+  }
+  if (F & kSend) L.sstep++;
+  if (F & kRecv) {
+    wait_mem();
+    st_relaxed(L.in.head, a.base + L.rstep + 1);
+    L.rstep++;
+  }
+  return true;
+}
+
+// --- a primitive over the lane's part of one chunk ------------------------
+template <class E, int OP, int PROTO, int F>
+__device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) {
+  const uint64_t cap = slot_elems(PROTO, sizeof(typename E::T));
+  for (uint64_t j = 0; j < nelem; j += cap) {
+    uint32_t m = (uint32_t)min_u64(cap, nelem - j);
+    bool ok;
+    if (PROTO == kSimple) ok = slice_simple<E, OP, F>(L, e0 + j, m);
+    else if (PROTO == kLL) ok = slice_ll<E, OP, F>(L, e0 + j, m);
+    else ok = slice_ll128<E, OP, F>(L, e0 + j, m);
+    if (!ok) return false;
+  }
+  return true;
+}
+
+template <class E, int OP, int PROTO>
+__global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a) {
+  const int wave = threadIdx.x >> 6;
+  int ri, group;
+  decode_block(blockIdx.x, a.nranks, a.xcd_map, &ri, &group);
+  const int lane_blocks = a.lanes / a.lanes_per_block;
+  const int c = group / lane_blocks;
+  const int l = (group % lane_blocks) * a.lanes_per_block + wave;
+  if (ri == a.skip_ring_index) return;
+  const int n = a.nranks;
+  const uint32_t es = sizeof(typename E::T);
+
+  Lane L;
+  L.a = &a;
+  L.w.a = &a;
+  L.lane = threadIdx.x & 63;
+  L.sstep = 0;
+  L.rstep = 0;
+  const uint64_t cin = conn_index(c, ri, l, n, a.lanes);
+  const uint64_t cout = conn_index(c, (ri + 1) % n, l, n, a.lanes);
+  const uint64_t conn_bytes = fifo_conn_bytes(PROTO);
+  L.in = Conn{a.fifo + cin * conn_bytes, a.counters + cin * kCounterWords + kTailWord,
+              a.counters + cin * kCounterWords + kHeadWord};
+  L.out = Conn{a.fifo + cout * conn_bytes, a.counters + cout * kCounterWords + kTailWord,
+               a.counters + cout * kCounterWords + kHeadWord};
+  L.src = a.send[ri];
+  L.dst = a.recv[ri];
+
+  uint64_t lo, hi;
+  channel_bounds(a.count, a.per_channel, c, &lo, &hi);
+  const uint64_t len = hi - lo;
+  const uint64_t loop = (uint64_t)n * a.chunk_elems;
+  for (uint64_t off = 0; off < len; off += loop) {
+    const uint64_t rem = len - off;
+    const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
+    for (int s = 0; s <= 2 * n - 2; s++) {
+      const int k = stage_chunk(ri, s, n);
+      uint64_t ks, kl, ls, ll;
+      chunk_bounds(rem, cur, k, &ks, &kl);
+      lane_bounds(kl, a.lanes, es, l, &ls, &ll);
+      const uint64_t e0 = lo + off + ks + ls;
+      bool ok;
+      if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend>(L, e0, ll);
+      else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend>(L, e0, ll);
+      else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst>(L, e0, ll);
+      else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst>(L, e0, ll);
+      else ok = primitive<E, OP, PROTO, kRecv | kDst>(L, e0, ll);
+      if (!ok) return;
+    }
+  }
+}
+
+}  // namespace ringar

@@ -1,0 +1,54 @@
+// Kernel dispatch by (dtype, op, protocol), occupancy query and the fill
+// kernel that clears FIFO memory and counters.
+#include <hip/hip_runtime.h>
+
+#include "ring_geometry.h"
+#include "ring_kernel.h"
+
+namespace ringar {
+
+const void* kernel_for_i8(int op, int proto);
+const void* kernel_for_i32(int op, int proto);
+const void* kernel_for_f16(int op, int proto);
+const void* kernel_for_bf16(int op, int proto);
+const void* kernel_for_f32(int op, int proto);
+const void* kernel_for_f64(int op, int proto);
+
+const void* kernel_for(int dtype, int op, int proto) {
+  switch (dtype) {
+    case 0: return kernel_for_i8(op, proto);
+    case 1: return kernel_for_i32(op, proto);
+    case 2: return kernel_for_f16(op, proto);
+    case 3: return kernel_for_bf16(op, proto);
+    case 4: return kernel_for_f32(op, proto);
+    default: return kernel_for_f64(op, proto);
+  }
+}
+
+hipError_t launch_ring(int dtype, int op, int proto, const KernelArgs& args, int grid, int block,
+                       hipStream_t stream) {
+  void* params[] = {const_cast<KernelArgs*>(&args)};
+  return hipLaunchKernel(kernel_for(dtype, op, proto), dim3(grid), dim3(block), params, 0, stream);
+}
+
+hipError_t max_active_blocks(int dtype, int op, int proto, int block, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel_for(dtype, op, proto), block, 0);
+}
+
+// Writes `value` into `words` 64-bit words (plain vector stores).  A kernel,
+// not a memset, so that a caller may capture it in a graph.
+__global__ void fill_u64_kernel(uint64_t* p, uint64_t words, uint64_t value) {
+  for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+hipError_t launch_fill(uint64_t* p, uint64_t words, uint64_t value, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  uint64_t blocks = div_up(words, 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, words, value);
+  return hipGetLastError();
+}
+
+}  // namespace ringar

@@ -1,0 +1,579 @@
+// C ABI of the ring AllReduce library: argument checks, the alpha-beta
+// protocol model, the launch plan, per-stream FIFO memory and the launch.
+//
+// Page sources: [ARCH] arganzheng.life, "NCCL architecture: topology,
+// channels, algorithms and protocols" (§六.4 channel count by size, §六.5 FIFO
+// of 8 steps, §七.2 protocols, §八 tuning model, §九.1 argument checks);
+// [BOOK] aireadcode.com, "NCCL Source Code Deep Dive" (§1.3 enqueue-only
+// semantics; Japanese edition ch. 5 selection rule and ch. 6 count == 0 and
+// one-rank early outs, error classes).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/ringar.h"
+#include "ring_geometry.h"
+#include "ring_kernel.h"
+
+using namespace ringar;
+
+namespace {
+
+thread_local std::string t_last_error;
+
+ringar_result_t hip_fail(hipError_t e, const char* what) {
+  t_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return RINGAR_ERR_DEVICE;
+}
+
+#define HIP_TRY(call)                                   \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);   \
+  } while (0)
+
+size_t elem_size(int dtype) {
+  static const size_t sz[] = {1, 4, 2, 2, 4, 8};
+  return (dtype >= 0 && dtype <= 5) ? sz[dtype] : 0;
+}
+
+const char* kProtoName[3] = {"LL", "LL128", "Simple"};
+const char* kDtypeName[6] = {"int8", "int32", "float16", "bfloat16", "float32", "float64"};
+const char* kOpName[4] = {"sum", "prod", "min", "max"};
+
+// ---------------------------------------------------------------- env
+// RINGAR_* variables, each read once ([BOOK] §3.5: a parameter is read from
+// the environment on first use and cached).
+struct Env {
+  int debug = 0;
+  int proto_mask = 7;          // protocols AUTO may pick (bit p = protocol p)
+  size_t chunk_bytes = 0;
+  int max_nchannels = 0;
+  uint32_t spin_limit_ms = 2000;
+  int lanes = 0;
+};
+
+// RINGAR_PROTO: comma-separated protocol names (case-insensitive); a leading
+// '^' excludes the listed ones instead ([ARCH] §八.5 NCCL_PROTO grammar,
+// reduced to one list without per-function groups).
+int parse_proto_list(const char* s) {
+  if (!s || !*s) return 7;
+  bool exclude = false;
+  if (*s == '^') { exclude = true; s++; }
+  int mask = 0;
+  std::string tok;
+  auto flush = [&]() {
+    std::string t;
+    for (char ch : tok) t += (char)tolower((unsigned char)ch);
+    if (t == "ll") mask |= 1;
+    else if (t == "ll128") mask |= 2;
+    else if (t == "simple") mask |= 4;
+    tok.clear();
+  };
+  for (; *s; s++) {
+    if (*s == ',') flush();
+    else if (!isspace((unsigned char)*s)) tok += *s;
+  }
+  flush();
+  int m = exclude ? (7 & ~mask) : mask;
+  return m ? m : 7;
+}
+
+const Env& env() {
+  static Env e;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    if (const char* v = getenv("RINGAR_DEBUG")) e.debug = atoi(v);
+    e.proto_mask = parse_proto_list(getenv("RINGAR_PROTO"));
+    if (const char* v = getenv("RINGAR_CHUNK_BYTES")) e.chunk_bytes = strtoull(v, nullptr, 0);
+    if (const char* v = getenv("RINGAR_MAX_NCHANNELS")) e.max_nchannels = atoi(v);
+    if (const char* v = getenv("RINGAR_SPIN_LIMIT_MS")) e.spin_limit_ms = (uint32_t)strtoul(v, nullptr, 0);
+    if (const char* v = getenv("RINGAR_LANES")) e.lanes = atoi(v);
+  });
+  return e;
+}
+
+// ---------------------------------------------------------------- model
+// Built-in MI355X model.  The protocol efficiencies are the values the
+// pages give (LL 0.5, LL128 about 0.94, Simple 1.0); latencies and bandwidths
+// are measured on MI355X with this library (one GPU, virtual ranks).
+ringar_model_t default_model() {
+  ringar_model_t m;
+  memset(&m, 0, sizeof(m));
+  m.bw_per_channel = 10.0;
+  m.ll_max_bw = 60.0;
+  m.ll128_per_channel_max_bw = 9.0;
+  m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
+  m.base_lat_us[0] = 5.0; m.base_lat_us[1] = 6.0; m.base_lat_us[2] = 6.0;
+  m.hw_lat_us[0] = 1.0; m.hw_lat_us[1] = 1.5; m.hw_lat_us[2] = 2.5;
+  m.max_channels = 32;
+  m.max_pairs = 256;
+  m.threads[0] = 512; m.threads[1] = 640; m.threads[2] = 512;
+  m.thread_threshold[0] = 8; m.thread_threshold[1] = 8; m.thread_threshold[2] = 64;
+  m.default_chunk_bytes[0] = 32768;
+  m.default_chunk_bytes[1] = 491520;
+  m.default_chunk_bytes[2] = 524288;
+  return m;
+}
+
+// Bus bandwidth of protocol p on nch channels ([ARCH] §八.1).
+double bus_bw(const ringar_model_t& m, int nch, int p) {
+  double bus = nch * m.bw_per_channel;
+  if (p == kLL) return std::min(m.ll_max_bw, bus * m.eff[0]);
+  if (p == kLL128) return std::min(bus * m.eff[1], nch * m.ll128_per_channel_max_bw);
+  return bus * m.eff[2];
+}
+
+// Predicted microseconds of one call ([ARCH] §八.1-八.2):
+// base + 2(n-1) step latencies + bytes / (1000 x bus bandwidth x n / (2(n-1))).
+double predict_us(const ringar_model_t& m, int n, int nch, int p, size_t bytes) {
+  double nsteps = 2.0 * (n - 1);
+  double alg = bus_bw(m, nch, p) * n / nsteps;
+  double lat = m.base_lat_us[p] + nsteps * m.hw_lat_us[p];
+  return lat + (double)bytes / (1000.0 * alg);
+}
+
+int model_max_channels(const ringar_model_t& m, int n) {
+  int c = std::min(m.max_channels, m.max_pairs / std::max(1, n));
+  return std::max(1, std::min(c, kMaxChannels));
+}
+
+// Fastest enabled protocol.  Candidates are visited Simple, LL128, LL (the
+// pages' list is built by pushing to the front) and replaced only on a
+// strictly smaller time, so ties go to Simple, then LL128.
+int select_proto(const ringar_model_t& m, int n, int nch, size_t bytes, int mask, double* times) {
+  int best = -1;
+  double best_t = INFINITY;
+  for (int p = 2; p >= 0; p--) {
+    double t = predict_us(m, n, nch, p, bytes);
+    if (times) times[p] = t;
+    if (!(mask & (1 << p))) continue;
+    if (t < best_t) { best = p; best_t = t; }
+  }
+  return best;
+}
+
+// Channel count by size ([ARCH] §六.4): drop channels while each thread would
+// get fewer than threshold bytes; LL's threshold is multiplied by n on a ring.
+int auto_channels(const ringar_model_t& m, int n, int p, size_t bytes, int start) {
+  int nc = start;
+  double thr = (double)m.thread_threshold[p] * (p == kLL ? n : 1);
+  while (nc > 1 && (double)bytes < (double)nc * m.threads[p] * thr) nc--;
+  return nc;
+}
+
+// ---------------------------------------------------------------- plan
+struct Plan {
+  int proto = kSimple;
+  int nch = 1;
+  size_t chunk_bytes = 0;
+  uint64_t chunk_elems = 0;
+  uint64_t per_channel = 0;
+  int lanes = 1;
+  int lanes_per_block = 1;
+  int grid = 0;
+  int block = 64;
+  int xcd_map = 0;
+  uint64_t max_steps = 0;
+  double times[3] = {0, 0, 0};
+};
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int proto,
+                          const ringar_config_t* cfg, Plan* out) {
+  const Env& E = env();
+  const size_t es = elem_size(dtype);
+  if (!es) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (n < 1 || n > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (nchannels < 0 || nchannels > kMaxChannels) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (proto < RINGAR_PROTO_AUTO || proto > RINGAR_PROTO_SIMPLE) return RINGAR_ERR_INVALID_ARGUMENT;
+  ringar_model_t dm = default_model();
+  const ringar_model_t& m = (cfg && cfg->model) ? *cfg->model : dm;
+  size_t chunk_bytes = (cfg && cfg->chunk_bytes) ? cfg->chunk_bytes : E.chunk_bytes;
+  if (chunk_bytes % 16 != 0) return RINGAR_ERR_INVALID_ARGUMENT;
+  int lanes = (cfg && cfg->lanes) ? cfg->lanes : E.lanes;
+  if (lanes && (!is_pow2(lanes) || lanes > kMaxLanes)) return RINGAR_ERR_INVALID_ARGUMENT;
+
+  Plan P;
+  const size_t bytes = count * es;
+  int maxc = model_max_channels(m, n);
+  if (E.max_nchannels > 0) maxc = std::min(maxc, E.max_nchannels);
+  const int model_nch = nchannels > 0 ? nchannels : maxc;
+  int best = select_proto(m, n, model_nch, bytes, E.proto_mask, P.times);
+  P.proto = proto >= 0 ? proto : (n == 1 ? (int)kSimple : best);
+  P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc));
+  P.chunk_bytes = chunk_bytes ? chunk_bytes : m.default_chunk_bytes[P.proto];
+  if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)
+    return RINGAR_ERR_INVALID_ARGUMENT;
+  P.chunk_elems = P.chunk_bytes / es;
+  P.per_channel = channel_len(count, P.nch, (uint32_t)es);
+
+  // Lanes: about one per 32 KiB of the chunk actually used, at most 16, and
+  // at most 4096 wavefronts in all.  Lanes change no result.
+  uint64_t eff_chunk = std::min<uint64_t>(P.chunk_elems, std::max<uint64_t>(1, div_up(P.per_channel, n)));
+  if (!lanes) {
+    uint64_t want = std::max<uint64_t>(1, eff_chunk * es / 32768);
+    lanes = 1;
+    while (lanes * 2 <= (int)std::min<uint64_t>(want, 16)) lanes *= 2;
+    while (lanes > 1 && (uint64_t)n * P.nch * lanes > 4096) lanes /= 2;
+  }
+  P.lanes = lanes;
+  P.lanes_per_block = std::min(lanes, 4);
+  P.block = 64 * P.lanes_per_block;
+  const int groups = P.nch * (lanes / P.lanes_per_block);
+  P.grid = n * groups;
+  P.xcd_map = (groups % 8 == 0) ? 1 : 0;
+
+  // Upper bound of FIFO steps any connection takes in this call.
+  const uint64_t loops = std::max<uint64_t>(1, div_up(P.per_channel, (uint64_t)n * P.chunk_elems));
+  const uint64_t gran = kLaneGranBytes / es;
+  const uint64_t part = align_up(div_up(P.chunk_elems, (uint64_t)lanes), gran);
+  const uint64_t slices = div_up(part, slot_elems(P.proto, (uint32_t)es)) + 1;
+  P.max_steps = loops * (uint64_t)(2 * n - 1) * slices;
+  *out = P;
+  return RINGAR_SUCCESS;
+}
+
+// ---------------------------------------------------------------- resources
+// FIFO memory, counters and the error word of one (device, stream).  All
+// counters and flags are absolute step numbers below `base`, so memory that
+// is reused by a later call (of any shape or protocol) can never look fresh.
+struct Resources {
+  int device = 0;
+  char* fifo[3] = {nullptr, nullptr, nullptr};
+  uint64_t fifo_conns[3] = {0, 0, 0};
+  uint64_t* counters = nullptr;
+  uint64_t counter_conns = 0;
+  uint64_t* error = nullptr;
+  uint64_t base = 0;
+  uint64_t call_id = 0;
+  uint64_t reported_call = 0;
+  int wall_khz = 100000;
+  int num_cus = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Resources> g_res;
+std::map<long long, int> g_occupancy;   // (kernel, block) -> blocks per CU
+
+ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t conns) {
+  if (R.fifo_conns[proto] < conns) {
+    HIP_TRY(hipStreamSynchronize(st));
+    if (R.fifo[proto]) HIP_TRY(hipFree(R.fifo[proto]));
+    R.fifo[proto] = nullptr;
+    R.fifo_conns[proto] = 0;
+    const uint64_t bytes = conns * fifo_conn_bytes(proto);
+    HIP_TRY(hipMalloc((void**)&R.fifo[proto], bytes));
+    HIP_TRY(launch_fill((uint64_t*)R.fifo[proto], bytes / 8, 0, st));
+    R.fifo_conns[proto] = conns;
+  }
+  if (R.counter_conns < conns) {
+    HIP_TRY(hipStreamSynchronize(st));
+    if (R.counters) HIP_TRY(hipFree(R.counters));
+    R.counters = nullptr;
+    R.counter_conns = 0;
+    HIP_TRY(hipMalloc((void**)&R.counters, conns * kCounterWords * 8));
+    HIP_TRY(launch_fill(R.counters, conns * kCounterWords, 0, st));
+    R.counter_conns = conns;
+  }
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t get_resources(hipStream_t st, Resources** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto key = std::make_pair(dev, st);
+  auto it = g_res.find(key);
+  if (it == g_res.end()) {
+    Resources R;
+    R.device = dev;
+    HIP_TRY(hipDeviceGetAttribute(&R.wall_khz, hipDeviceAttributeWallClockRate, dev));
+    HIP_TRY(hipDeviceGetAttribute(&R.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+    HIP_TRY(hipMalloc((void**)&R.error, 8));
+    HIP_TRY(launch_fill(R.error, 1, 0, st));
+    it = g_res.emplace(key, R).first;
+  }
+  *out = &it->second;
+  return RINGAR_SUCCESS;
+}
+
+// Restart all step numbers at zero: clear every flag and counter first.
+ringar_result_t reset_steps(Resources& R, hipStream_t st) {
+  for (int p = 0; p < 3; p++)
+    if (R.fifo[p]) HIP_TRY(launch_fill((uint64_t*)R.fifo[p], R.fifo_conns[p] * fifo_conn_bytes(p) / 8, 0, st));
+  if (R.counters) HIP_TRY(launch_fill(R.counters, R.counter_conns * kCounterWords, 0, st));
+  R.base = 0;
+  return RINGAR_SUCCESS;
+}
+
+bool overlaps(uintptr_t a, uintptr_t b, size_t len) { return a < b + len && b < a + len; }
+
+ringar_result_t check_buffers(void* const* sb, void* const* rb, size_t count, size_t es, int n) {
+  if (!sb || !rb) return RINGAR_ERR_INVALID_ARGUMENT;
+  for (int r = 0; r < n; r++) {
+    if (!sb[r] || !rb[r]) return RINGAR_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)sb[r] % es) || ((uintptr_t)rb[r] % es)) return RINGAR_ERR_INVALID_ARGUMENT;
+  }
+  const size_t len = count * es;
+  // A receive buffer may only coincide exactly with its own rank's send
+  // buffer (in place); send buffers may overlap each other (read only).
+  for (int r = 0; r < n; r++) {
+    uintptr_t rr = (uintptr_t)rb[r];
+    for (int q = 0; q < n; q++) {
+      if (q != r && overlaps(rr, (uintptr_t)rb[q], len)) return RINGAR_ERR_INVALID_USAGE;
+      uintptr_t sq = (uintptr_t)sb[q];
+      if (overlaps(rr, sq, len) && !(q == r && rr == sq)) return RINGAR_ERR_INVALID_USAGE;
+    }
+  }
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t check_ring(const int* ring, int n) {
+  if (!ring) return RINGAR_SUCCESS;
+  // Follow the ring from index 0: it must visit every rank once and close
+  // ([BOOK] §4, ncclBuildRings' check that a ring loops back and holds all
+  // ranks).
+  std::vector<char> seen(n, 0);
+  for (int i = 0; i < n; i++) {
+    int r = ring[i];
+    if (r < 0 || r >= n || seen[r]) return RINGAR_ERR_INVALID_ARGUMENT;
+    seen[r] = 1;
+  }
+  return RINGAR_SUCCESS;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+const char* ringar_result_string(ringar_result_t r) {
+  switch (r) {
+    case RINGAR_SUCCESS: return "success";
+    case RINGAR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RINGAR_ERR_INVALID_USAGE: return "invalid usage";
+    case RINGAR_ERR_INTERNAL: return "internal error";
+    case RINGAR_ERR_DEVICE: return "device error";
+    case RINGAR_ERR_ABORTED: return "aborted";
+    case RINGAR_ERR_TIMEOUT: return "timeout";
+  }
+  return "unknown result";
+}
+
+const char* ringar_last_error(void) { return t_last_error.c_str(); }
+
+ringar_result_t ringar_default_model(ringar_model_t* out) {
+  if (!out) return RINGAR_ERR_INVALID_ARGUMENT;
+  *out = default_model();
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_select(size_t bytes, int nranks, int nchannels, const ringar_model_t* model,
+                              ringar_proto_t* out, double* predicted_us) {
+  if (!out || nranks < 1 || nranks > kMaxRanks || nchannels < 0 || nchannels > kMaxChannels)
+    return RINGAR_ERR_INVALID_ARGUMENT;
+  ringar_model_t dm = default_model();
+  const ringar_model_t& m = model ? *model : dm;
+  if (nranks == 1) {
+    *out = RINGAR_PROTO_SIMPLE;
+    if (predicted_us) predicted_us[0] = predicted_us[1] = predicted_us[2] = 0.0;
+    return RINGAR_SUCCESS;
+  }
+  int nch = nchannels > 0 ? nchannels : model_max_channels(m, nranks);
+  double t[3];
+  int p = select_proto(m, nranks, nch, bytes, env().proto_mask, t);
+  if (p < 0) return RINGAR_ERR_INVALID_USAGE;
+  *out = (ringar_proto_t)p;
+  if (predicted_us) memcpy(predicted_us, t, sizeof(t));
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
+                            ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out) {
+  if (!out) return RINGAR_ERR_INVALID_ARGUMENT;
+  Plan P;
+  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, &P);
+  if (r != RINGAR_SUCCESS) return r;
+  const size_t es = elem_size(dtype);
+  out->proto = (ringar_proto_t)P.proto;
+  out->nchannels = P.nch;
+  out->chunk_bytes = P.chunk_bytes;
+  out->chunk_elems = P.chunk_elems;
+  out->align_elems = 16 / es;
+  out->channel_elems = P.per_channel;
+  out->lanes = P.lanes;
+  out->workgroups = P.grid;
+  out->threads_per_group = P.block;
+  out->max_steps = P.max_steps;
+  for (int p = 0; p < 3; p++) out->predicted_us[p] = P.times[p];
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
+                                   size_t chunk_elems, int c, size_t loop_off, int k, size_t* lo,
+                                   size_t* hi, size_t* klo, size_t* khi) {
+  const size_t es = elem_size(dtype);
+  if (!es || nranks < 1 || nchannels < 1 || c < 0 || c >= nchannels || k < 0 || k >= nranks ||
+      chunk_elems == 0 || chunk_elems % (16 / es) || !lo || !hi || !klo || !khi)
+    return RINGAR_ERR_INVALID_ARGUMENT;
+  uint64_t per = channel_len(count, nchannels, (uint32_t)es), l, h;
+  channel_bounds(count, per, c, &l, &h);
+  *lo = l;
+  *hi = h;
+  const uint64_t len = h - l;
+  if (loop_off >= len) {
+    *klo = *khi = h;
+    return RINGAR_SUCCESS;
+  }
+  uint64_t cur = loop_chunk(len, loop_off, nranks, chunk_elems, (uint32_t)es), s, n;
+  chunk_bounds(len - loop_off, cur, k, &s, &n);
+  *klo = l + loop_off + s;
+  *khi = *klo + n;
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                    ringar_dtype_t dtype, ringar_op_t op, int nranks,
+                                    int nchannels, ringar_proto_t proto, ringar_stream_t stream,
+                                    const ringar_config_t* cfg) {
+  const size_t es = elem_size(dtype);
+  if (!es || op < RINGAR_SUM || op > RINGAR_MAX) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
+  Plan P;
+  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, &P);
+  if (r != RINGAR_SUCCESS) return r;
+  if (cfg && (r = check_ring(cfg->ring_order, nranks)) != RINGAR_SUCCESS) return r;
+  if (count == 0) return RINGAR_SUCCESS;                      // no-op, nothing enqueued
+  if ((r = check_buffers(sendbuffs, recvbuffs, count, es, nranks)) != RINGAR_SUCCESS) return r;
+  hipStream_t st = (hipStream_t)stream;
+  if (nranks == 1) {                                          // one rank: a local copy
+    if (sendbuffs[0] != recvbuffs[0])
+      HIP_TRY(hipMemcpyAsync(recvbuffs[0], sendbuffs[0], count * es, hipMemcpyDeviceToDevice, st));
+    return RINGAR_SUCCESS;
+  }
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  Resources* R = nullptr;
+  if ((r = get_resources(st, &R)) != RINGAR_SUCCESS) return r;
+
+  // All (rank, channel, lane) wavefronts wait on each other, so the whole
+  // grid must be resident at once.
+  const long long okey = ((long long)(dtype * 4 + op) * 3 + P.proto) * 1024 + P.block;
+  auto oc = g_occupancy.find(okey);
+  if (oc == g_occupancy.end()) {
+    int per_cu = 0;
+    HIP_TRY(max_active_blocks(dtype, op, P.proto, P.block, &per_cu));
+    oc = g_occupancy.emplace(okey, per_cu).first;
+  }
+  if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
+
+  const uint64_t conns = (uint64_t)P.nch * nranks * P.lanes;
+  if ((r = ensure_conns(*R, st, P.proto, conns)) != RINGAR_SUCCESS) return r;
+  // LL flags are 32-bit step numbers: restart the numbering before it wraps.
+  if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
+    if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;
+
+  KernelArgs A;
+  memset(&A, 0, sizeof(A));
+  const int* ring = cfg ? cfg->ring_order : nullptr;
+  for (int i = 0; i < nranks; i++) {
+    int rank = ring ? ring[i] : i;
+    A.send[i] = (const char*)sendbuffs[rank];
+    A.recv[i] = (char*)recvbuffs[rank];
+  }
+  int vec = 1;
+  for (int q = 0; q < nranks; q++)
+    if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
+  A.count = count;
+  A.per_channel = P.per_channel;
+  A.chunk_elems = P.chunk_elems;
+  A.base = R->base;
+  A.fifo = R->fifo[P.proto];
+  A.counters = R->counters;
+  A.error = R->error;
+  A.abort_flag = cfg ? cfg->abort_flag : nullptr;
+  uint32_t spin_ms = (cfg && cfg->spin_limit_ms) ? cfg->spin_limit_ms : env().spin_limit_ms;
+  A.spin_ticks = (uint64_t)spin_ms * (uint64_t)R->wall_khz;
+  A.call_id = ++R->call_id;
+  A.nranks = nranks;
+  A.nchannels = P.nch;
+  A.lanes = P.lanes;
+  A.lanes_per_block = P.lanes_per_block;
+  A.xcd_map = P.xcd_map;
+  A.skip_ring_index = -1;
+  if (cfg && cfg->skip_rank >= 0 && cfg->skip_rank < nranks) {
+    for (int i = 0; i < nranks; i++)
+      if ((ring ? ring[i] : i) == cfg->skip_rank) A.skip_ring_index = i;
+  }
+  A.vec_ok = vec;
+
+  HIP_TRY(launch_ring(dtype, op, P.proto, A, P.grid, P.block, st));
+  R->base += P.max_steps + 1;
+
+  if (env().debug) {
+    fprintf(stderr,
+            "ringar: AllReduce %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
+            "grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
+            count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
+            P.chunk_bytes, P.lanes, P.grid, P.block, P.times[0], P.times[1], P.times[2]);
+  }
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_allreduce(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                 ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                 ringar_proto_t proto, ringar_stream_t stream) {
+  return ringar_allreduce_ex(sendbuffs, recvbuffs, count, dtype, op, nranks, nchannels, proto,
+                             stream, nullptr);
+}
+
+ringar_result_t ringar_get_async_error(ringar_stream_t stream) {
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(st));
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_res.find(std::make_pair(dev, st));
+  if (it == g_res.end()) return RINGAR_SUCCESS;
+  Resources& R = it->second;
+  uint64_t word = 0;
+  HIP_TRY(hipMemcpy(&word, R.error, 8, hipMemcpyDeviceToHost));
+  uint64_t call = word >> 8;
+  if (call > R.reported_call) {
+    R.reported_call = call;
+    int code = (int)(word & 0xff);
+    return code == 5 ? RINGAR_ERR_ABORTED : RINGAR_ERR_TIMEOUT;
+  }
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  HIP_TRY(hipGetDevice(&cur));
+  for (auto& kv : g_res) {
+    Resources& R = kv.second;
+    HIP_TRY(hipSetDevice(R.device));
+    HIP_TRY(hipDeviceSynchronize());
+    for (int p = 0; p < 3; p++)
+      if (R.fifo[p]) HIP_TRY(hipFree(R.fifo[p]));
+    if (R.counters) HIP_TRY(hipFree(R.counters));
+    if (R.error) HIP_TRY(hipFree(R.error));
+  }
+  g_res.clear();
+  HIP_TRY(hipSetDevice(cur));
+  return RINGAR_SUCCESS;
+}
+
+}  // extern "C"

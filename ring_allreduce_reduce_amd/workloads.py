@@ -113,3 +113,22 @@ def config5_case(dtype: str, op: str):
 CONFIG5_OPS = ("sum", "prod", "min", "max")
 CONFIG5_DTYPES = ("int8", "int32", "float16", "bfloat16", "float32", "float64")
 CONFIG5_SIZES = [1 << s for s in range(3, 31)]
+
+
+def to_torch(arr: np.ndarray, dtype: str, device=None):
+    """Tensor of `dtype` holding the stored values (bfloat16 from its bits)."""
+    import torch
+    if dtype == "bfloat16":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device) if device is not None else t
+
+
+def from_torch(t, dtype: str) -> np.ndarray:
+    """Stored values of a tensor as the numpy storage type of `dtype`."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if dtype == "bfloat16":
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()

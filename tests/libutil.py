@@ -1,0 +1,47 @@
+"""Shared helpers of the library tests: build-on-demand and model fixtures."""
+import json
+import os
+
+import ring_allreduce_reduce_amd as ra
+from oracle import select as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def lib():
+    if not os.path.exists(ra.LIB_PATH):
+        from ring_allreduce_reduce_amd import _build
+        _build.build()
+    return ra.load()
+
+
+def golden_model_dict():
+    with open(os.path.join(GOLDEN, "mi355x_model.json")) as f:
+        return {k: v for k, v in json.load(f).items() if not k.startswith("_")}
+
+
+def oracle_model(d=None) -> S.RingModel:
+    d = d or golden_model_dict()
+    return S.RingModel(bw_per_channel=d["bw_per_channel"], ll_max_bw=d["ll_max_bw"],
+                       ll128_per_channel_max_bw=d["ll128_per_channel_max_bw"], eff=tuple(d["eff"]),
+                       base_lat=tuple(d["base_lat_us"]), hw_lat=tuple(d["hw_lat_us"]),
+                       max_channels=d["max_channels"], max_pairs=d["max_pairs"],
+                       threads=tuple(d["threads"]), thread_threshold=tuple(d["thread_threshold"]),
+                       default_chunk_bytes=tuple(d["default_chunk_bytes"]))
+
+
+def lib_model(d) -> "ra.ringar_model_t":
+    m = ra.ringar_model_t()
+    m.bw_per_channel = d["bw_per_channel"]
+    m.ll_max_bw = d["ll_max_bw"]
+    m.ll128_per_channel_max_bw = d["ll128_per_channel_max_bw"]
+    for i in range(3):
+        m.eff[i] = d["eff"][i]
+        m.base_lat_us[i] = d["base_lat_us"][i]
+        m.hw_lat_us[i] = d["hw_lat_us"][i]
+        m.threads[i] = d["threads"][i]
+        m.thread_threshold[i] = d["thread_threshold"][i]
+        m.default_chunk_bytes[i] = d["default_chunk_bytes"][i]
+    m.max_channels = d["max_channels"]
+    m.max_pairs = d["max_pairs"]
+    return m

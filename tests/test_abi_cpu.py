@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: it loads, exports what include/ringar.h
+declares, and its host logic (plan, protocol model, partition, argument
+checks) agrees with the oracle.  No call here reaches the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import ring_allreduce_reduce_amd as ra
+from libutil import golden_model_dict, lib, lib_model, oracle_model
+from oracle import select as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    lib()
+    os.environ.pop("RINGAR_PROTO", None)
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "ringar.h")) as f:
+        text = f.read()
+    names = set(re.findall(r"^\s*(?:ringar_result_t|const char\*)\s+(ringar_\w+)\s*\(", text, re.M))
+    assert "ringar_allreduce" in names and len(names) >= 10
+    cdll = ctypes.CDLL(ra.LIB_PATH)
+    for name in sorted(names):
+        assert hasattr(cdll, name), name
+
+
+def test_default_model_is_the_documented_one():
+    m = ra.ringar_default_model()
+    d = golden_model_dict()
+    assert m.bw_per_channel == d["bw_per_channel"]
+    assert m.ll_max_bw == d["ll_max_bw"]
+    assert m.ll128_per_channel_max_bw == d["ll128_per_channel_max_bw"]
+    assert list(m.eff) == d["eff"]
+    assert list(m.base_lat_us) == d["base_lat_us"]
+    assert list(m.hw_lat_us) == d["hw_lat_us"]
+    assert (m.max_channels, m.max_pairs) == (d["max_channels"], d["max_pairs"])
+    assert list(m.threads) == d["threads"]
+    assert list(m.thread_threshold) == d["thread_threshold"]
+    assert list(m.default_chunk_bytes) == d["default_chunk_bytes"]
+
+
+def test_select_matches_oracle_model_and_pages_table():
+    # the pages' 8x A100 inputs through the library's selector
+    d = dict(golden_model_dict(), bw_per_channel=20.0, ll_max_bw=87.7, ll128_per_channel_max_bw=36.7,
+             eff=[0.5, 0.92, 1.0], base_lat_us=[6.6, 14.0, 8.4], hw_lat_us=[0.6, 1.9, 3.4])
+    m, om = lib_model(d), oracle_model(d)
+    for nbytes in [8, 1000, 1 << 16, 1 << 20, 3 << 22, 1 << 26, 1 << 30]:
+        p, t = ra.ringar_select(nbytes, 8, 24, m)
+        op, ot = S.select(om, 8, 24, nbytes)
+        assert p == op
+        assert np.allclose(t, ot, rtol=1e-12, atol=0)
+    _, t = ra.ringar_select(0, 8, 24, m)
+    assert t[2] == pytest.approx(56.0, abs=0.05) and t[1] == pytest.approx(40.6, abs=0.05)
+
+
+PLAN_CASES = [(b, n, nch, proto)
+              for b in [8, 64, 1000, 4096, 65536, 1 << 20, 5 << 20, 64 << 20, 1 << 30]
+              for n in [2, 3, 8]
+              for nch in [0, 1, 16]
+              for proto in ["auto", "LL", "LL128", "Simple"]]
+
+
+@pytest.mark.parametrize("dtype", ["int8", "float32", "float64"])
+def test_plan_matches_oracle_resolution(dtype):
+    om = oracle_model()
+    es = ra.ELEM_BYTES[dtype]
+    for nbytes, n, nch, proto in PLAN_CASES:
+        count = nbytes // es
+        plan = ra.ringar_plan(count, dtype, n, nch, proto)
+        want = S.resolve(om, n, count * es, nch, None if proto == "auto" else proto)
+        assert (ra.PROTO_NAMES[plan.proto], plan.nchannels, plan.chunk_bytes) == want, (nbytes, n, nch, proto)
+        assert plan.chunk_elems * es == plan.chunk_bytes
+        assert plan.channel_elems == oracle.channel_range(count, dtype, plan.nchannels, 0)[1] or count == 0 \
+            or plan.channel_elems >= count
+
+
+def test_partition_matches_oracle():
+    rng = np.random.default_rng(5)
+    for _ in range(60):
+        dtype = ["int8", "int32", "float16", "bfloat16", "float32", "float64"][int(rng.integers(0, 6))]
+        es = ra.ELEM_BYTES[dtype]
+        n = int(rng.integers(2, 9))
+        nch = int(rng.integers(1, 6))
+        chunk = int(rng.integers(1, 5)) * (16 // es)
+        count = int(rng.integers(0, 3000))
+        want = oracle.element_chunks(count, dtype, n, nch, chunk)
+        got = np.full(count, -1, dtype=np.int32)
+        for c in range(nch):
+            lo, hi, _, _ = ra.ringar_chunk_range(count, dtype, n, nch, chunk, c, 0, 0)
+            assert (lo, hi) == oracle.channel_range(count, dtype, nch, c)
+            off = 0
+            while off < hi - lo:
+                for k in range(n):
+                    _, _, klo, khi = ra.ringar_chunk_range(count, dtype, n, nch, chunk, c, off, k)
+                    got[klo:khi] = k
+                off += n * chunk
+        assert np.array_equal(got, want)
+
+
+def _fake(n, step=1 << 20, base=1 << 32):
+    return [base + i * step for i in range(n)]
+
+
+def test_argument_errors_before_any_device_call():
+    n, count = 4, 1000
+    s, r = _fake(n), _fake(n, base=1 << 40)
+    E = ra
+    assert ra.ringar_allreduce(s, r, count, 9, "sum", n, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", 7, n, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", "sum", n, 2, 5, 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", "sum", 0, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", "sum", 65, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", "sum", n, 65, "Simple", 0) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce(s, r, count, "float32", "sum", n, -1, "Simple", 0) == E.INVALID_ARGUMENT
+    bad_chunk = ra.make_config(chunk_bytes=24)
+    assert ra.ringar_allreduce_ex(s, r, count, "float32", "sum", n, 2, "Simple", 0, bad_chunk) == E.INVALID_ARGUMENT
+    bad_ring = ra.make_config(ring_order=[0, 1, 1, 3])
+    assert ra.ringar_allreduce_ex(s, r, count, "float32", "sum", n, 2, "Simple", 0, bad_ring) == E.INVALID_ARGUMENT
+    bad_lanes = ra.make_config(lanes=3)
+    assert ra.ringar_allreduce_ex(s, r, count, "float32", "sum", n, 2, "Simple", 0, bad_lanes) == E.INVALID_ARGUMENT
+    # misaligned pointer
+    s2 = list(s)
+    s2[1] += 2
+    assert ra.ringar_allreduce(s2, r, count, "float32", "sum", n, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    # null pointer with work to do
+    assert ra.ringar_allreduce([0] * n, r, count, "float32", "sum", n, 2, "Simple", 0) == E.INVALID_ARGUMENT
+    # overlaps: receive buffers of two ranks, receive with another rank's send
+    r2 = list(r)
+    r2[2] = r2[1] + 400
+    assert ra.ringar_allreduce(s, r2, count, "float32", "sum", n, 2, "Simple", 0) == E.INVALID_USAGE
+    r3 = list(r)
+    r3[0] = s[3]
+    assert ra.ringar_allreduce(s, r3, count, "float32", "sum", n, 2, "Simple", 0) == E.INVALID_USAGE
+    r4 = list(r)
+    r4[1] = s[1] + 4          # partial in-place overlap
+    assert ra.ringar_allreduce(s, r4, count, "float32", "sum", n, 2, "Simple", 0) == E.INVALID_USAGE
+    # count == 0 succeeds without touching anything
+    assert ra.ringar_allreduce(s, r, 0, "float32", "sum", n, 2, "Simple", 0) == E.SUCCESS
+
+
+def test_proto_env_grammar_subset():
+    # parsed in a child process because the library caches its environment
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r); import ring_allreduce_reduce_amd as ra;"
+        "print(ra.ringar_plan(1 << 30, 'float32', 8).proto, ra.ringar_plan(8, 'float32', 8).proto)" % ROOT)
+    out = {}
+    for v in ["LL", "^LL,LL128", "simple", "LL128"]:
+        env = dict(os.environ, RINGAR_PROTO=v)
+        out[v] = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                                check=True).stdout.split()
+    assert out["LL"] == ["0", "0"]
+    assert out["^LL,LL128"] == ["2", "2"]
+    assert out["simple"] == ["2", "2"]
+    assert out["LL128"] == ["1", "1"]
