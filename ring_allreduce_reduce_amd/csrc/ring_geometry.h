@@ -26,6 +26,7 @@ constexpr int kMaxRanks = 64;
 constexpr int kMaxChannels = 64;
 constexpr int kMaxLanes = 32;
 constexpr int kSteps = 8;                 // FIFO slots per connection (NCCL_STEPS)
+constexpr int kMaxSlicesPerPart = kSteps / 2;  // slots one primitive may fill
 constexpr uint32_t kLaneGranBytes = 1024; // lane parts start on 1 KiB boundaries
 
 // FIFO slot geometry per protocol.

@@ -190,7 +190,12 @@ __device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
 }
 
 // ----------------------------------------------------------------- waiting
-enum { kErrAborted = 5, kErrTimeout = 6 };
+enum { kErrInternal = 3, kErrAborted = 5, kErrTimeout = 6 };
+
+__device__ __forceinline__ void record_error(const KernelArgs& a, int code) {
+  __hip_atomic_fetch_max(a.error, (a.call_id << 8) | (uint64_t)code, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct Waiter {
   const KernelArgs* a;
@@ -211,8 +216,7 @@ struct Waiter {
     else if (now - t0 > a->spin_ticks)
       code = kErrTimeout;
     if (code) {
-      uint64_t word = (a->call_id << 8) | (uint64_t)code;
-      __hip_atomic_fetch_max(a->error, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      record_error(*a, code);
       return false;
     }
     return true;
@@ -530,6 +534,12 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
 template <class E, int OP, int PROTO, int F>
 __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) {
   const uint64_t cap = slot_elems(PROTO, sizeof(typename E::T));
+  // The host plans parts of at most half a FIFO; a larger one could deadlock
+  // the ring, so refuse it instead.
+  if (nelem > kMaxSlicesPerPart * cap) {
+    record_error(*L.a, kErrInternal);
+    return false;
+  }
   for (uint64_t j = 0; j < nelem; j += cap) {
     uint32_t m = (uint32_t)min_u64(cap, nelem - j);
     bool ok;

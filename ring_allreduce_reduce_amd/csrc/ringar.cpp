@@ -190,8 +190,10 @@ struct Plan {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// capacity_waves: wavefronts of this kernel the GPU holds at once (0 when no
+// GPU is visible: then 4096 is assumed).
 ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int proto,
-                          const ringar_config_t* cfg, Plan* out) {
+                          const ringar_config_t* cfg, uint64_t capacity_waves, Plan* out) {
   const Env& E = env();
   const size_t es = elem_size(dtype);
   if (!es) return RINGAR_ERR_INVALID_ARGUMENT;
@@ -219,15 +221,35 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   P.chunk_elems = P.chunk_bytes / es;
   P.per_channel = channel_len(count, P.nch, (uint32_t)es);
 
-  // Lanes: about one per 32 KiB of the chunk actually used, at most 16, and
-  // at most 4096 wavefronts in all.  Lanes change no result.
-  uint64_t eff_chunk = std::min<uint64_t>(P.chunk_elems, std::max<uint64_t>(1, div_up(P.per_channel, n)));
-  if (!lanes) {
-    uint64_t want = std::max<uint64_t>(1, eff_chunk * es / 32768);
+  // Lanes: wavefronts sharing each (rank, channel) chunk, each with its own
+  // FIFO.  A primitive's part of a chunk may fill at most half the FIFO
+  // (kMaxSlicesPerPart slots, like a chunk of NCCL_STEPS/2 steps): a
+  // receiver keeps its slot until its own send is done, so parts of a full
+  // FIFO's size would let every FIFO of the ring fill up and deadlock.
+  // Beyond that, about one lane per 16 KiB of chunk, and no more wavefronts
+  // than the GPU holds at once (all of them wait on each other).  Lanes
+  // change no result.
+  const uint64_t first_chunk =
+      P.per_channel >= (uint64_t)n * P.chunk_elems
+          ? P.chunk_elems
+          : align_up(div_up(std::max<uint64_t>(1, P.per_channel), (uint64_t)n), align_elems((uint32_t)es));
+  const uint64_t gran = kLaneGranBytes / es;
+  const uint64_t slot = slot_elems(P.proto, (uint32_t)es);
+  auto slices_for = [&](int L) {
+    return div_up(align_up(div_up(first_chunk, (uint64_t)L), gran), slot);
+  };
+  const bool forced_lanes = lanes != 0;
+  if (!forced_lanes) {
+    uint64_t want = std::max<uint64_t>(1, first_chunk * es / 16384);
     lanes = 1;
-    while (lanes * 2 <= (int)std::min<uint64_t>(want, 16)) lanes *= 2;
-    while (lanes > 1 && (uint64_t)n * P.nch * lanes > 4096) lanes /= 2;
+    while (lanes * 2 <= (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
+    const uint64_t cap = capacity_waves ? capacity_waves : 4096;
+    while (lanes > 1 && (uint64_t)n * P.nch * lanes > cap && slices_for(lanes / 2) <= kMaxSlicesPerPart)
+      lanes /= 2;
+    while (lanes < kMaxLanes && slices_for(lanes) > kMaxSlicesPerPart) lanes *= 2;
   }
+  if (slices_for(lanes) > kMaxSlicesPerPart)
+    return forced_lanes ? RINGAR_ERR_INVALID_USAGE : RINGAR_ERR_INVALID_ARGUMENT;
   P.lanes = lanes;
   P.lanes_per_block = std::min(lanes, 4);
   P.block = 64 * P.lanes_per_block;
@@ -237,10 +259,7 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
 
   // Upper bound of FIFO steps any connection takes in this call.
   const uint64_t loops = std::max<uint64_t>(1, div_up(P.per_channel, (uint64_t)n * P.chunk_elems));
-  const uint64_t gran = kLaneGranBytes / es;
-  const uint64_t part = align_up(div_up(P.chunk_elems, (uint64_t)lanes), gran);
-  const uint64_t slices = div_up(part, slot_elems(P.proto, (uint32_t)es)) + 1;
-  P.max_steps = loops * (uint64_t)(2 * n - 1) * slices;
+  P.max_steps = loops * (uint64_t)(2 * n - 1) * (slices_for(lanes) + 1);
   *out = P;
   return RINGAR_SUCCESS;
 }
@@ -315,6 +334,34 @@ ringar_result_t reset_steps(Resources& R, hipStream_t st) {
   if (R.counters) HIP_TRY(launch_fill(R.counters, R.counter_conns * kCounterWords, 0, st));
   R.base = 0;
   return RINGAR_SUCCESS;
+}
+
+// Resident wavefronts of the (dtype, op, proto) kernel on the current device,
+// or 0 when no device is visible.  Cached per device and kernel.
+uint64_t capacity_waves(int dtype, int op, int proto) {
+  static const int ndev = [] {
+    int c = 0;
+    if (hipGetDeviceCount(&c) != hipSuccess) {
+      (void)hipGetLastError();
+      c = 0;
+    }
+    return c;
+  }();
+  if (ndev == 0) return 0;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const long long key = (((long long)dev * 8 + dtype) * 4 + op) * 3 + proto;
+  static std::mutex mu;
+  static std::map<long long, uint64_t> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      max_active_blocks(dtype, op, proto, 256, &per_cu) != hipSuccess)
+    return 0;
+  uint64_t w = (uint64_t)cus * (uint64_t)per_cu * 4;   // 4 wavefronts per 256-thread block
+  cache.emplace(key, w);
+  return w;
 }
 
 bool overlaps(uintptr_t a, uintptr_t b, size_t len) { return a < b + len && b < a + len; }
@@ -403,7 +450,15 @@ ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int 
                             ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out) {
   if (!out) return RINGAR_ERR_INVALID_ARGUMENT;
   Plan P;
-  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, &P);
+  const int p_guess = proto >= 0 ? (int)proto : -1;
+  uint64_t cap = 0;
+  if ((int)dtype >= 0 && (int)dtype <= 5) {
+    // the protocol is needed for the capacity; resolve it first without one
+    Plan Q;
+    if (make_plan(count, dtype, nranks, nchannels, proto, cfg, 0, &Q) == RINGAR_SUCCESS)
+      cap = capacity_waves(dtype, 0, p_guess >= 0 ? p_guess : Q.proto);
+  }
+  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, cap, &P);
   if (r != RINGAR_SUCCESS) return r;
   const size_t es = elem_size(dtype);
   out->proto = (ringar_proto_t)P.proto;
@@ -451,8 +506,13 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
   if (!es || op < RINGAR_SUM || op > RINGAR_MAX) return RINGAR_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
   Plan P;
-  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, &P);
+  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, 0, &P);
   if (r != RINGAR_SUCCESS) return r;
+  if (count > 0 && nranks > 1) {
+    const uint64_t cap = capacity_waves(dtype, op, P.proto);
+    if (cap && (r = make_plan(count, dtype, nranks, nchannels, proto, cfg, cap, &P)) != RINGAR_SUCCESS)
+      return r;
+  }
   if (cfg && (r = check_ring(cfg->ring_order, nranks)) != RINGAR_SUCCESS) return r;
   if (count == 0) return RINGAR_SUCCESS;                      // no-op, nothing enqueued
   if ((r = check_buffers(sendbuffs, recvbuffs, count, es, nranks)) != RINGAR_SUCCESS) return r;
@@ -553,7 +613,9 @@ ringar_result_t ringar_get_async_error(ringar_stream_t stream) {
   if (call > R.reported_call) {
     R.reported_call = call;
     int code = (int)(word & 0xff);
-    return code == 5 ? RINGAR_ERR_ABORTED : RINGAR_ERR_TIMEOUT;
+    if (code == RINGAR_ERR_ABORTED || code == RINGAR_ERR_TIMEOUT || code == RINGAR_ERR_INTERNAL)
+      return (ringar_result_t)code;
+    return RINGAR_ERR_INTERNAL;
   }
   return RINGAR_SUCCESS;
 }

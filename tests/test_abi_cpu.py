@@ -162,3 +162,25 @@ def test_proto_env_grammar_subset():
     assert out["^LL,LL128"] == ["2", "2"]
     assert out["simple"] == ["2", "2"]
     assert out["LL128"] == ["1", "1"]
+
+
+def test_parts_never_exceed_half_the_fifo():
+    # a primitive's part must fit in half the 8-slot FIFO, else the ring could
+    # fill every FIFO at once and deadlock; the plan adds lanes to keep it so
+    for proto, slot in [("Simple", 32768), ("LL", 8192), ("LL128", 30720)]:
+        for chunk in [16, 4096, 65536, 1 << 19, 1 << 20]:
+            if proto != "Simple" and chunk > (1 << 20):
+                continue
+            plan = ra.ringar_plan(1 << 26, "float32", 8, 16, proto, ra.make_config(chunk_bytes=chunk))
+            part = -(-chunk // plan.lanes)
+            part = -(-part // 1024) * 1024
+            assert -(-part // slot) <= 4, (proto, chunk, plan.lanes)
+    # forcing too few lanes for the chunk is refused
+    cfg = ra.make_config(chunk_bytes=1 << 19, lanes=1)
+    with pytest.raises(ra.RingarError) as e:
+        ra.ringar_plan(1 << 26, "float32", 8, 16, "Simple", cfg)
+    assert e.value.code == ra.INVALID_USAGE
+    # a chunk no lane count can split small enough is an invalid argument
+    with pytest.raises(ra.RingarError) as e:
+        ra.ringar_plan(1 << 28, "float32", 8, 1, "LL", ra.make_config(chunk_bytes=8 << 20))
+    assert e.value.code == ra.INVALID_ARGUMENT
