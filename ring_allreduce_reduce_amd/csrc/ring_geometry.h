@@ -134,24 +134,8 @@ struct KernelArgs {
   int nchannels;
   int lanes;                     // wavefronts per (rank, channel)
   int lanes_per_block;
-  int xcd_map;                   // 1: all ranks of a (channel, lane block) on one XCD
   int skip_ring_index;           // -1: none
   int vec_ok;                    // all user pointers 16-byte aligned
 };
-
-// Workgroup -> (ring index, channel, lane block).  With xcd_map the hardware's
-// round-robin dispatch of workgroup ids over the 8 XCDs puts the n workgroups
-// of one (channel, lane block) group on the same XCD, so a FIFO's producer and
-// consumer share that XCD's L2.  Without it groups are laid out linearly.
-RA_HD void decode_block(int block, int nranks, int xcd_map, int* ring_index, int* group) {
-  if (xcd_map) {
-    int xcd = block % 8, j = block / 8;
-    *group = xcd + 8 * (j / nranks);
-    *ring_index = j % nranks;
-  } else {
-    *group = block / nranks;
-    *ring_index = block % nranks;
-  }
-}
 
 }  // namespace ringar

@@ -254,7 +254,7 @@ struct Lane {
 
 enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8 };
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;   // 16-byte packets per lane in flight per source
 
 // Result of one packet: op(received, local), or whichever operand exists.
 template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 b) {
@@ -554,8 +554,8 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) 
 template <class E, int OP, int PROTO>
 __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a) {
   const int wave = threadIdx.x >> 6;
-  int ri, group;
-  decode_block(blockIdx.x, a.nranks, a.xcd_map, &ri, &group);
+  const int group = blockIdx.x / a.nranks;     // (channel, lane block)
+  const int ri = blockIdx.x % a.nranks;        // ring index
   const int lane_blocks = a.lanes / a.lanes_per_block;
   const int c = group / lane_blocks;
   const int l = (group % lane_blocks) * a.lanes_per_block + wave;

@@ -21,7 +21,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/ringar.h"
+#include "ringar.h"
 #include "ring_geometry.h"
 #include "ring_kernel.h"
 
@@ -183,7 +183,6 @@ struct Plan {
   int lanes_per_block = 1;
   int grid = 0;
   int block = 64;
-  int xcd_map = 0;
   uint64_t max_steps = 0;
   double times[3] = {0, 0, 0};
 };
@@ -255,7 +254,6 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   P.block = 64 * P.lanes_per_block;
   const int groups = P.nch * (lanes / P.lanes_per_block);
   P.grid = n * groups;
-  P.xcd_map = (groups % 8 == 0) ? 1 : 0;
 
   // Upper bound of FIFO steps any connection takes in this call.
   const uint64_t loops = std::max<uint64_t>(1, div_up(P.per_channel, (uint64_t)n * P.chunk_elems));
@@ -570,7 +568,6 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
   A.nchannels = P.nch;
   A.lanes = P.lanes;
   A.lanes_per_block = P.lanes_per_block;
-  A.xcd_map = P.xcd_map;
   A.skip_ring_index = -1;
   if (cfg && cfg->skip_rank >= 0 && cfg->skip_rank < nranks) {
     for (int i = 0; i < nranks; i++)
