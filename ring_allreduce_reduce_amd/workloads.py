@@ -9,9 +9,9 @@ configurations describe):
   * ``normal``:      N(0, 1) drawn in fp32, then rounded to nearest-even into
                      the target float type (fp16/bf16/fp64 via fp32).
   * ``uniform_int``: integers uniform in [lo, hi] inclusive.
-  * ``uniform``:     reals uniform in [lo, hi) drawn in fp64, then rounded to
-                     the target float type; for integer types, integers in
-                     [lo, hi] inclusive.
+  * ``uniform``:     reals uniform in [lo, hi) drawn in fp64 (fp64) or fp32
+                     (narrower types), then rounded to the target type; for
+                     integer types, integers in [lo, hi] inclusive.
   * ``worked``:      the pages' worked example: rank r holds r in element 0
                      and zeros elsewhere.
 Each rank's generator is numpy PCG64 seeded from a stable hash of
@@ -69,9 +69,15 @@ def rank_input(key: str, rank: int, count: int, dtype: str, dist: str,
     if dist == "normal":
         return _cast_float(rng.standard_normal(count, dtype=np.float32), dtype)
     if dist == "uniform_int" or (dist == "uniform" and dtype not in FLOATS):
-        return rng.integers(int(lo), int(hi), size=count, endpoint=True).astype(STORAGE[dtype])
+        return rng.integers(int(lo), int(hi), size=count, endpoint=True, dtype=STORAGE[dtype])
     if dist == "uniform":
-        return _cast_float(rng.uniform(lo, hi, size=count), dtype)
+        # fp64 draws for fp64; every narrower type draws fp32 (no 8-byte temporary)
+        if dtype == "float64":
+            return rng.uniform(lo, hi, size=count)
+        u = rng.random(count, dtype=np.float32)
+        u *= np.float32(hi - lo)
+        u += np.float32(lo)
+        return _cast_float(u, dtype)
     raise ValueError(f"unknown distribution {dist!r}")
 
 

@@ -117,6 +117,47 @@ def test_config5_grid_up_to_1MiB(dtype, op):
         assert (ra.PROTO_NAMES[plan.proto], plan.nchannels, plan.chunk_bytes) == want
 
 
+BIG_SIZES = [1 << s for s in range(21, 30)]          # 2 MiB .. 512 MiB per rank
+FULL_GIB = {("sum", "float32"), ("min", "int8"), ("prod", "bfloat16"), ("max", "float64"),
+            ("sum", "int32"), ("sum", "float16")}
+GRID = [(op, dt) for op in W.CONFIG5_OPS for dt in W.CONFIG5_DTYPES]
+
+
+def _big_case_sizes(j, op, dtype):
+    sizes = [BIG_SIZES[j % 9], BIG_SIZES[(j + 4) % 9]]
+    if (op, dtype) in FULL_GIB:
+        sizes.append(1 << 30)
+    return sizes
+
+
+@pytest.mark.parametrize("j", range(len(GRID)), ids=[f"{o}-{d}" for o, d in GRID])
+def test_config5_grid_large_sizes(j):
+    """The op x dtype grid above 1 MiB per rank, up to 1 GiB, automatic
+    protocol and channels, compared element by element with the oracle."""
+    op, dtype = GRID[j]
+    om = oracle_model()
+    es = W.ELEM_BYTES[dtype]
+    for nbytes in _big_case_sizes(j, op, dtype):
+        count = nbytes // es
+        rng = W.config5_case(dtype, op)
+        print(f"case grid {op} {dtype} {nbytes} bytes per rank", flush=True)
+        xs = W.inputs(f"config5-{dtype}-{op}-{nbytes}", 8, count, dtype, rng["dist"], rng["lo"], rng["hi"])
+        sends = [W.to_torch(x, dtype, DEV) for x in xs]
+        recvs = [torch.empty_like(t) for t in sends]
+        ra.allreduce(sends, recvs, op=op)
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(torch.cuda.current_stream().cuda_stream) == 0
+        plan = ra.ringar_plan(count, dtype, 8)
+        assert (ra.PROTO_NAMES[plan.proto], plan.nchannels, plan.chunk_bytes) == S.resolve(om, 8, nbytes)
+        del sends
+        want = oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems)
+        for r in range(8):
+            got = W.from_torch(recvs[r], dtype)
+            assert np.array_equal(_bits(got), _bits(want[r])), (op, dtype, nbytes, r)
+        del recvs, want, xs
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ edge cases
 RAGGED = [  # (n, count, nch, chunk units of 16 B, lanes)
     (2, 1, 1, 1, 0), (3, 17, 2, 1, 0), (5, 1000, 3, 2, 0), (8, 4099, 4, 3, 0), (7, 65537, 2, 64, 0),
