@@ -82,11 +82,15 @@ RA_HD void chunk_bounds(uint64_t rem, uint64_t cur, int k, uint64_t* start, uint
 // Chunk visited by ring index i at stage s (0 <= s <= 2n-2).
 RA_HD int stage_chunk(int i, int s, int nranks) { return (i - 1 - s + 2 * nranks) % nranks; }
 
-// Lane l's part of a chunk of `clen` elements: [start, start + len).
-RA_HD void lane_bounds(uint64_t clen, int lanes, uint32_t esize, int l, uint64_t* start,
-                       uint64_t* len) {
-  uint64_t gran = kLaneGranBytes / esize;
-  uint64_t part = align_up(div_up(clen, (uint64_t)lanes), gran);
+// Lane part size of a loop whose chunks hold `cur` elements: the chunk size
+// split over the lanes, rounded up to whole 1 KiB units.
+RA_HD uint64_t lane_part(uint64_t cur, int lanes, uint32_t esize) {
+  return align_up(div_up(cur, (uint64_t)lanes), kLaneGranBytes / esize);
+}
+
+// Lane l's part of a chunk of `clen` elements (clen <= the loop's chunk
+// size), given the loop's lane part size: [start, start + len).
+RA_HD void lane_bounds(uint64_t clen, uint64_t part, int l, uint64_t* start, uint64_t* len) {
   uint64_t s = min_u64(clen, (uint64_t)l * part);
   *start = s;
   *len = min_u64(clen, s + part) - s;

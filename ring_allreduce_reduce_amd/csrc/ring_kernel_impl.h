@@ -121,8 +121,17 @@ template <class E, int OP> __device__ __forceinline__ u32x4 vop(u32x4 a, u32x4 b
 constexpr int kSC1 = 16;   // device-coherent: write through / read past L2
 constexpr int kNT = 2;     // streaming hint for user buffers
 
+// Buffer resource over [base, base + bytes).  Every caller passes values that
+// are the same in all lanes of the wavefront; reading them from the first
+// lane tells the compiler so, which keeps the resource in scalar registers
+// (a resource it cannot prove uniform makes it loop over the distinct values
+// around every buffer access).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
                                            0x00020000);
 }
 
@@ -254,6 +263,16 @@ struct Lane {
 
 enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8 };
 
+// Frees the input slot just read: publishes head = base + step + 1.  Every
+// load of the slot has returned its data (the values were consumed above),
+// so the producer may overwrite it; the wavefront's own stores need not be
+// complete, and waiting for them here would add a round trip to every step.
+__device__ __forceinline__ void release_slot(Lane& L) {
+  compiler_fence();
+  st_relaxed(L.in.head, L.a->base + L.rstep + 1);
+  L.rstep++;
+}
+
 constexpr int kUnroll = 8;   // 16-byte packets per lane in flight per source
 
 // Result of one packet: op(received, local), or whichever operand exists.
@@ -316,11 +335,7 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t e0, uint32_t nele
     st_relaxed(L.out.tail, a.base + L.sstep + 1);
     L.sstep++;
   }
-  if (F & kRecv) {
-    wait_mem();
-    st_relaxed(L.in.head, a.base + L.rstep + 1);
-    L.rstep++;
-  }
+  if (F & kRecv) release_slot(L);
   return true;
 }
 
@@ -374,7 +389,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
   rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
   const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
-  constexpr int U = 2;
+  constexpr int U = 4;
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
     u32x4 va[U], vb[U];
 #pragma unroll
@@ -383,13 +398,35 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
       if (F & kSrc) vb[u] = (p < nfull) ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
     }
     if (F & kRecv) {
+      // all 4U lines of the lane are loaded, then polled together: one
+      // round trip per iteration however many packets the lane has
+      uint64_t ln[U][4];
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const uint32_t p = p0 + u * 64 + L.lane;
-        uint64_t ln[4];
-        if (!ll_recv4(L.w, lin, p, p < nfull, fin, ln)) return false;
-        va[u] = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+#pragma unroll
+        for (int q = 0; q < 4; q++) ln[u][q] = (p < nfull) ? ld_relaxed(lin + 4 * p + q) : ll_line(0, fin);
       }
+      L.w.start();
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) ok = ok && ll_ready(ln[u][q], fin);
+        if (__all(ok)) break;
+        if (!L.w.idle()) return false;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const uint32_t p = p0 + u * 64 + L.lane;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            if (!ll_ready(ln[u][q], fin)) ln[u][q] = ld_relaxed(lin + 4 * p + q);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        va[u] = u32x4{(uint32_t)ln[u][0], (uint32_t)ln[u][1], (uint32_t)ln[u][2], (uint32_t)ln[u][3]};
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -417,17 +454,43 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
   }
   if (__any(failed)) return false;
   if (F & kSend) L.sstep++;
-  if (F & kRecv) {
-    wait_mem();
-    st_relaxed(L.in.head, a.base + L.rstep + 1);
-    L.rstep++;
-  }
+  if (F & kRecv) release_slot(L);
   return true;
 }
 
 // --- LL128: 128-byte lines, 120 data bytes + 8-byte flag -------------------
-// A batch is 64 lines; packet u of a lane covers line b0 + 8u + lane/8,
-// 16-byte column lane%8 (column 7 carries 8 data bytes and the flag).
+// A batch is up to kLL128Batch lines with one flag round trip: lane t watches
+// (and publishes) the flags of lines b0 + t and b0 + 64 + t.  The data moves
+// in groups of 4 packets per lane; packet u of a lane covers line
+// b0 + 8u + lane/8, 16-byte column lane%8 (column 7 carries 8 data bytes and
+// the flag).
+constexpr uint32_t kLL128Batch = 128;
+constexpr int kLL128Group = 4;
+
+// User-side packets of group g of the batch at line b0 (nl lines): loads the
+// whole packets into vb and returns the mask of packets that end inside
+// their column (those go element-wise).
+template <class E, int F>
+__device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, uint32_t b0, uint32_t nl,
+                                                     uint32_t g, int lane, bool vec,
+                                                     u32x4 (&vb)[kLL128Group]) {
+  const int col = lane & 7;
+  const uint32_t psize = col == 7 ? 8u : 16u;
+  const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;
+  uint32_t part = 0;
+#pragma unroll
+  for (int v = 0; v < kLL128Group; v++) {
+    const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (lane >> 3);
+    const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
+    const bool live = line < b0 + nl && valid > 0;
+    const bool full = live && vec && (uint32_t)valid >= psize;
+    if (live && !full) part |= 1u << v;
+    vb[v] = u32x4{0u, 0u, 0u, 0u};
+    if ((F & kSrc) && full) vb[v] = col == 7 ? ld8<kNT>(r, line * 120 + 112) : ld16<kNT>(r, line * 120 + coff);
+  }
+  return part;
+}
+
 template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
@@ -449,84 +512,86 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
   const int col = L.lane & 7;
   const uint32_t psize = col == 7 ? 8u : 16u;
   const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;   // data bytes of the column
-  for (uint32_t b0 = 0; b0 < nlines; b0 += 64) {
-    const uint32_t nl = min(64u, nlines - b0);
-    u32x4 va[8], vb[8];
-    uint32_t part = 0;   // packets (bit u) that end inside their column
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const uint32_t line = b0 + 8 * u + (L.lane >> 3);
-      const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + col * 16);
-      const bool live = line < b0 + nl && valid > 0;
-      const bool full = live && vec && (uint32_t)valid >= psize;
-      if (live && !full) part |= 1u << u;
-      if (F & kSrc) vb[u] = full ? (col == 7 ? ld8<kNT>(rsrc_, line * 120 + 112) : ld16<kNT>(rsrc_, line * 120 + col * 16))
-                                 : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (uint32_t b0 = 0; b0 < nlines; b0 += kLL128Batch) {
+    const uint32_t nl = min(kLL128Batch, nlines - b0);
+    // the first group's user data is requested before the flags are polled
+    u32x4 vb[kLL128Group];
+    uint32_t part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, 0, L.lane, vec, vb);
     if (F & kRecv) {
-      // flags first: lane t watches line b0 + t
-      const uint64_t* fl = (const uint64_t*)(sin + (size_t)(b0 + L.lane) * 128 + 120);
+      // flags first, then data: lane t watches lines b0 + t and b0 + 64 + t
+      const uint64_t* f0p = (const uint64_t*)(sin + (size_t)(b0 + L.lane) * 128 + 120);
+      const uint64_t* f1p = (const uint64_t*)(sin + (size_t)(b0 + 64 + L.lane) * 128 + 120);
+      const bool w0 = L.lane < (int)nl, w1 = 64 + L.lane < (int)nl;
       L.w.start();
-      uint64_t f = (L.lane < (int)nl) ? ld_relaxed(fl) : fin;
+      uint64_t f0 = w0 ? ld_relaxed(f0p) : fin;
+      uint64_t f1 = w1 ? ld_relaxed(f1p) : fin;
       while (true) {
-        if (__all(f == fin)) break;
+        if (__all(f0 == fin && f1 == fin)) break;
         if (!L.w.idle()) return false;
-        if (f != fin) f = ld_relaxed(fl);
+        if (f0 != fin) f0 = ld_relaxed(f0p);
+        if (f1 != fin) f1 = ld_relaxed(f1p);
       }
       compiler_fence();
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
-        va[u] = (line < b0 + nl) ? ld16<kSC1>(rin, line * 128 + col * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
     }
-#pragma unroll
-    for (int u = 0; u < 8; u++) va[u] = combine<E, OP, F>(va[u], vb[u]);
-    // Packets that end inside their column: element-wise on the user side.
 #pragma unroll 1
-    for (uint32_t bits = part; bits; bits &= bits - 1) {
-      const int u = __builtin_ctz(bits);
-      const uint32_t line = b0 + 8 * u + (L.lane >> 3);
-      const uint32_t uoff = line * 120 + coff;
-      const uint32_t nb = min(psize, nbytes - uoff);
-      u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
-      if (F & kRecv) x = ld16<kSC1>(rin, line * 128 + col * 16);
-      if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
-      const u32x4 r = combine<E, OP, F>(x, y);
-      if (F & kSend) {
-        if (col == 7) st8<kSC1>(r, rout, line * 128 + 112);
-        else st16<kSC1>(r, rout, line * 128 + col * 16);
+    for (uint32_t g = 0; g * kLL128Group * 8 < nl; g++) {
+      u32x4 va[kLL128Group];
+#pragma unroll
+      for (int v = 0; v < kLL128Group; v++) {
+        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        va[v] = u32x4{0u, 0u, 0u, 0u};
+        if ((F & kRecv) && line < b0 + nl) va[v] = ld16<kSC1>(rin, line * 128 + col * 16);
       }
-      if (F & kDst) st_part<E, kNT>(r, rdst, uoff, nb);
+      // the next group's user data is requested while this group computes
+      u32x4 vbn[kLL128Group] = {};
+      uint32_t partn = 0;
+      if ((g + 1) * kLL128Group * 8 < nl)
+        partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g + 1, L.lane, vec, vbn);
+#pragma unroll
+      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], vb[v]);
+      // Packets that end inside their column: element-wise on the user side.
+#pragma unroll 1
+      for (uint32_t bits = part; bits; bits &= bits - 1) {
+        const int v = __builtin_ctz(bits);
+        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        const uint32_t uoff = line * 120 + coff;
+        const uint32_t nb = min(psize, nbytes - uoff);
+        u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+        if (F & kRecv) x = ld16<kSC1>(rin, line * 128 + col * 16);
+        if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
+        const u32x4 r = combine<E, OP, F>(x, y);
+        if (F & kSend) {
+          if (col == 7) st8<kSC1>(r, rout, line * 128 + 112);
+          else st16<kSC1>(r, rout, line * 128 + col * 16);
+        }
+        if (F & kDst) st_part<E, kNT>(r, rdst, uoff, nb);
+      }
+#pragma unroll
+      for (int v = 0; v < kLL128Group; v++) {
+        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
+        if (line >= b0 + nl || valid <= 0 || (part >> v) & 1u) continue;
+        if (F & kSend) {
+          if (col == 7) st8<kSC1>(va[v], rout, line * 128 + 112);
+          else st16<kSC1>(va[v], rout, line * 128 + col * 16);
+        }
+        if (F & kDst) {
+          if (col == 7) st8<kNT>(va[v], rdst, line * 120 + 112);
+          else st16<kNT>(va[v], rdst, line * 120 + coff);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kLL128Group; v++) vb[v] = vbn[v];
+      part = partn;
     }
     if (F & kSend) {
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
-        if (line >= b0 + nl || (part >> u) & 1u) continue;
-        if (col == 7) st8<kSC1>(va[u], rout, line * 128 + 112);
-        else st16<kSC1>(va[u], rout, line * 128 + col * 16);
-      }
       wait_mem();   // all data of the batch is visible before any of its flags
       if (L.lane < (int)nl) st_relaxed((uint64_t*)(sout + (size_t)(b0 + L.lane) * 128 + 120), fout);
-    }
-    if (F & kDst) {
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const uint32_t line = b0 + 8 * u + (L.lane >> 3);
-        const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + col * 16);
-        if (line >= b0 + nl || valid <= 0 || (part >> u) & 1u) continue;
-        if (col == 7) st8<kNT>(va[u], rdst, line * 120 + 112);
-        else st16<kNT>(va[u], rdst, line * 120 + col * 16);
-      }
+      if (64 + L.lane < (int)nl) st_relaxed((uint64_t*)(sout + (size_t)(b0 + 64 + L.lane) * 128 + 120), fout);
     }
   }
   if (F & kSend) L.sstep++;
-  if (F & kRecv) {
-    wait_mem();
-    st_relaxed(L.in.head, a.base + L.rstep + 1);
-    L.rstep++;
-  }
+  if (F & kRecv) release_slot(L);
   return true;
 }
 
@@ -586,11 +651,12 @@ __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a)
   for (uint64_t off = 0; off < len; off += loop) {
     const uint64_t rem = len - off;
     const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
+    const uint64_t part = lane_part(cur, a.lanes, es);
     for (int s = 0; s <= 2 * n - 2; s++) {
       const int k = stage_chunk(ri, s, n);
       uint64_t ks, kl, ls, ll;
       chunk_bounds(rem, cur, k, &ks, &kl);
-      lane_bounds(kl, a.lanes, es, l, &ls, &ll);
+      lane_bounds(kl, part, l, &ls, &ll);
       const uint64_t e0 = lo + off + ks + ls;
       bool ok;
       if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend>(L, e0, ll);

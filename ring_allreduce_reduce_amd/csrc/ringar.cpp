@@ -105,20 +105,23 @@ const Env& env() {
 
 // ---------------------------------------------------------------- model
 // Built-in MI355X model.  The protocol efficiencies are the values the
-// pages give (LL 0.5, LL128 about 0.94, Simple 1.0); latencies and bandwidths
-// are measured on MI355X with this library (one GPU, virtual ranks).
+// pages give (LL 0.5, LL128 about 0.94, Simple 1.0).  Latencies are fitted to
+// small calls at n = 2..8 (T = base + 2(n-1) x step), bandwidths to 32-channel
+// calls of 64-256 MiB per rank, both measured with this library on MI355X.
+// A channel of a small call runs one 64-thread wavefront per rank, hence 64
+// threads per channel in the size rule.
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 10.0;
-  m.ll_max_bw = 60.0;
-  m.ll128_per_channel_max_bw = 9.0;
+  m.bw_per_channel = 7.66;
+  m.ll_max_bw = 55.0;
+  m.ll128_per_channel_max_bw = 3.74;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 5.0; m.base_lat_us[1] = 6.0; m.base_lat_us[2] = 6.0;
-  m.hw_lat_us[0] = 1.0; m.hw_lat_us[1] = 1.5; m.hw_lat_us[2] = 2.5;
+  m.base_lat_us[0] = 5.5; m.base_lat_us[1] = 6.7; m.base_lat_us[2] = 5.4;
+  m.hw_lat_us[0] = 2.08; m.hw_lat_us[1] = 2.77; m.hw_lat_us[2] = 1.82;
   m.max_channels = 32;
   m.max_pairs = 256;
-  m.threads[0] = 512; m.threads[1] = 640; m.threads[2] = 512;
+  m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;
   m.thread_threshold[0] = 8; m.thread_threshold[1] = 8; m.thread_threshold[2] = 64;
   m.default_chunk_bytes[0] = 32768;
   m.default_chunk_bytes[1] = 491520;
@@ -225,21 +228,18 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   // (kMaxSlicesPerPart slots, like a chunk of NCCL_STEPS/2 steps): a
   // receiver keeps its slot until its own send is done, so parts of a full
   // FIFO's size would let every FIFO of the ring fill up and deadlock.
-  // Beyond that, about one lane per 16 KiB of chunk, and no more wavefronts
-  // than the GPU holds at once (all of them wait on each other).  Lanes
-  // change no result.
+  // Beyond that, one lane per 4 KiB of chunk (up to 32), and no more
+  // wavefronts than the GPU holds at once (all of them wait on each other).
+  // Lanes change no result.
   const uint64_t first_chunk =
       P.per_channel >= (uint64_t)n * P.chunk_elems
           ? P.chunk_elems
           : align_up(div_up(std::max<uint64_t>(1, P.per_channel), (uint64_t)n), align_elems((uint32_t)es));
-  const uint64_t gran = kLaneGranBytes / es;
   const uint64_t slot = slot_elems(P.proto, (uint32_t)es);
-  auto slices_for = [&](int L) {
-    return div_up(align_up(div_up(first_chunk, (uint64_t)L), gran), slot);
-  };
+  auto slices_for = [&](int L) { return div_up(lane_part(first_chunk, L, (uint32_t)es), slot); };
   const bool forced_lanes = lanes != 0;
   if (!forced_lanes) {
-    uint64_t want = std::max<uint64_t>(1, first_chunk * es / 16384);
+    uint64_t want = std::max<uint64_t>(1, first_chunk * es / 4096);
     lanes = 1;
     while (lanes * 2 <= (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
     const uint64_t cap = capacity_waves ? capacity_waves : 4096;

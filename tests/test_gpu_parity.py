@@ -118,26 +118,21 @@ def test_config5_grid_up_to_1MiB(dtype, op):
 
 
 BIG_SIZES = [1 << s for s in range(21, 30)]          # 2 MiB .. 512 MiB per rank
-FULL_GIB = {("sum", "float32"), ("min", "int8"), ("prod", "bfloat16"), ("max", "float64"),
-            ("sum", "int32"), ("sum", "float16")}
 GRID = [(op, dt) for op in W.CONFIG5_OPS for dt in W.CONFIG5_DTYPES]
+# every grid cell at one size between 2 and 512 MiB (each size covered at
+# least twice over the grid), and three cells at the grid's largest size
+LARGE = [(op, dt, BIG_SIZES[j % 9]) for j, (op, dt) in enumerate(GRID)] + \
+    [("sum", "float32", 1 << 30), ("min", "int8", 1 << 30), ("prod", "bfloat16", 1 << 30)]
 
 
-def _big_case_sizes(j, op, dtype):
-    sizes = [BIG_SIZES[j % 9], BIG_SIZES[(j + 4) % 9]]
-    if (op, dtype) in FULL_GIB:
-        sizes.append(1 << 30)
-    return sizes
-
-
-@pytest.mark.parametrize("j", range(len(GRID)), ids=[f"{o}-{d}" for o, d in GRID])
-def test_config5_grid_large_sizes(j):
+@pytest.mark.parametrize("case", LARGE, ids=[f"{o}-{d}-{b >> 20}MiB" for o, d, b in LARGE])
+def test_config5_grid_large_sizes(case):
     """The op x dtype grid above 1 MiB per rank, up to 1 GiB, automatic
     protocol and channels, compared element by element with the oracle."""
-    op, dtype = GRID[j]
+    op, dtype, nbytes = case
     om = oracle_model()
     es = W.ELEM_BYTES[dtype]
-    for nbytes in _big_case_sizes(j, op, dtype):
+    for nbytes in [nbytes]:
         count = nbytes // es
         rng = W.config5_case(dtype, op)
         print(f"case grid {op} {dtype} {nbytes} bytes per rank", flush=True)
