@@ -186,7 +186,8 @@ def main():
         "config": {"workload": "ring AllReduce, 8 virtual ranks, fp32 sum, 64 MiB per rank, Simple, "
                                "16 channels, 512 KiB chunks",
                    "nranks": NRANKS, "bytes_per_rank": s, "proto": "Simple", "nchannels": NCHANNELS,
-                   "chunk_bytes": CHUNK_BYTES, "lanes": plan.lanes, "workgroups": plan.workgroups},
+                   "chunk_bytes": CHUNK_BYTES, "lanes": plan.lanes, "fifo_depth": plan.fifo_depth,
+                   "workgroups": plan.workgroups},
         "algbw_gbs": round(algbw, 3),
         "busbw_gbs": round(busbw, 3),
         "hbm_alg_gbs": round(achieved, 1),

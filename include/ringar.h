@@ -114,7 +114,12 @@ typedef struct {
  *   abort_flag:      host-mapped (pinned) word, or NULL.  While nonzero, any
  *                    waiting wavefront gives up with RINGAR_ERR_ABORTED.
  *   skip_rank:       test hook, normally -1: every wavefront of this rank
- *                    returns at once, so its peers must time out or abort. */
+ *                    returns at once, so its peers must time out or abort.
+ *   fifo_depth:      FIFO slots each connection cycles through: 2, 4 or 8
+ *                    (the pages' NCCL_STEPS is 8); 0 = chosen by size.  A
+ *                    lane's part of a chunk may fill at most half of them,
+ *                    else RINGAR_ERR_INVALID_USAGE.  Does not change any
+ *                    result. */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;
@@ -123,6 +128,7 @@ typedef struct {
   uint32_t spin_limit_ms;
   volatile uint32_t* abort_flag;
   int skip_rank;
+  int fifo_depth;
 } ringar_config_t;
 
 /* The resolved plan of a call (what ringar_allreduce would launch). */
@@ -134,6 +140,7 @@ typedef struct {
   size_t align_elems;      /* 16 B / element size */
   size_t channel_elems;    /* per-channel length before clipping to count */
   int lanes;               /* wavefronts per (rank, channel) */
+  int fifo_depth;          /* FIFO slots in use per connection */
   int workgroups;          /* grid size */
   int threads_per_group;
   uint64_t max_steps;      /* upper bound on FIFO steps per connection */

@@ -55,6 +55,7 @@ class ringar_config_t(ctypes.Structure):
         ("spin_limit_ms", ctypes.c_uint32),
         ("abort_flag", ctypes.c_void_p),
         ("skip_rank", ctypes.c_int),
+        ("fifo_depth", ctypes.c_int),
     ]
 
 
@@ -67,6 +68,7 @@ class ringar_plan_t(ctypes.Structure):
         ("align_elems", ctypes.c_size_t),
         ("channel_elems", ctypes.c_size_t),
         ("lanes", ctypes.c_int),
+        ("fifo_depth", ctypes.c_int),
         ("workgroups", ctypes.c_int),
         ("threads_per_group", ctypes.c_int),
         ("max_steps", ctypes.c_uint64),
@@ -120,7 +122,7 @@ def _enum(table, v):
 
 
 def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_ms=0,
-                abort_flag=0, skip_rank=-1):
+                abort_flag=0, skip_rank=-1, fifo_depth=0):
     """A ringar_config_t; keeps the ring-order array alive on the object."""
     cfg = ringar_config_t()
     cfg.chunk_bytes = chunk_bytes
@@ -135,6 +137,7 @@ def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_
     cfg.spin_limit_ms = spin_limit_ms
     cfg.abort_flag = abort_flag or None
     cfg.skip_rank = skip_rank
+    cfg.fifo_depth = fifo_depth
     return cfg
 
 

@@ -25,8 +25,12 @@ namespace ringar {
 constexpr int kMaxRanks = 64;
 constexpr int kMaxChannels = 64;
 constexpr int kMaxLanes = 32;
-constexpr int kSteps = 8;                 // FIFO slots per connection (NCCL_STEPS)
-constexpr int kMaxSlicesPerPart = kSteps / 2;  // slots one primitive may fill
+// FIFO slots allocated per connection (the pages' NCCL_STEPS).  A call may
+// cycle through fewer of them (its FIFO depth: 2, 4 or 8); a primitive may
+// fill at most half the depth.
+constexpr int kMaxSteps = 8;
+constexpr int kMinSteps = 2;
+constexpr int kMaxSlicesPerPart = kMaxSteps / 2;
 constexpr uint32_t kLaneGranBytes = 1024; // lane parts start on 1 KiB boundaries
 
 // FIFO slot geometry per protocol.
@@ -103,12 +107,13 @@ RA_HD uint64_t slot_elems(int proto, uint32_t esize) {
   return (kLL128SlotLines * 120) / esize;
 }
 
-// FIFO bytes of one connection (kSteps slots).
-RA_HD uint64_t fifo_conn_bytes(int proto) {
-  if (proto == kSimple) return (uint64_t)kSteps * kSimpleSlotBytes;
-  if (proto == kLL) return (uint64_t)kSteps * kLLSlotBytes;
-  return (uint64_t)kSteps * kLL128SlotBytes;
+// FIFO bytes of one slot and of one connection (kMaxSteps slots).
+RA_HD uint64_t slot_bytes(int proto) {
+  if (proto == kSimple) return kSimpleSlotBytes;
+  if (proto == kLL) return kLLSlotBytes;
+  return kLL128SlotBytes;
 }
+RA_HD uint64_t fifo_conn_bytes(int proto) { return (uint64_t)kMaxSteps * slot_bytes(proto); }
 
 // Counters of one connection: tail and head, each on its own 128-byte line.
 constexpr int kCounterWords = 32;   // uint64 words per connection (2 x 128 B)
@@ -137,6 +142,7 @@ struct KernelArgs {
   int nranks;
   int nchannels;
   int lanes;                     // wavefronts per (rank, channel)
+  int depth;                     // FIFO slots in use per connection (2, 4, 8)
   int lanes_per_block;
   int skip_ring_index;           // -1: none
   int vec_ok;                    // all user pointers 16-byte aligned

@@ -232,12 +232,20 @@ struct Waiter {
   }
 };
 
-// Waits until *p >= v (wavefront-uniform).
-__device__ __forceinline__ bool wait_ge(Waiter& w, const uint64_t* p, uint64_t v) {
+// Waits until *p >= v (wavefront-uniform).  `seen` is the largest value of
+// *p this wavefront has observed; counters only grow, so a wait it already
+// satisfies costs no memory round trip, and a poll records what it saw.
+__device__ __forceinline__ bool wait_ge(Waiter& w, const uint64_t* p, uint64_t v, uint64_t& seen) {
+  if (seen >= v) return true;
   w.start();
   while (true) {
+    const uint64_t x = ld_relaxed(p);
     // every lane loads the same word; vote so the exit is uniform
-    if (__all(ld_relaxed(p) >= v)) break;
+    if (__all(x >= v)) {
+      seen = __builtin_amdgcn_readfirstlane((uint32_t)x) |
+             ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
+      break;
+    }
     if (!w.idle()) return false;
   }
   compiler_fence();
@@ -246,7 +254,7 @@ __device__ __forceinline__ bool wait_ge(Waiter& w, const uint64_t* p, uint64_t v
 
 // ----------------------------------------------------------------- one lane
 struct Conn {
-  char* fifo;          // kSteps slots
+  char* fifo;          // kMaxSteps slots, the first depth of them in use
   uint64_t* tail;      // written by the producer
   uint64_t* head;      // written by the consumer
 };
@@ -257,6 +265,8 @@ struct Lane {
   const char* src;     // own send buffer
   char* dst;           // own receive buffer
   uint64_t sstep, rstep;
+  uint64_t tail_seen;  // largest tail of the input connection seen so far
+  uint64_t head_seen;  // largest head of the output connection seen so far
   int lane;            // lane within the wavefront
   Waiter w;
 };
@@ -288,13 +298,13 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t e0, uint32_t nele
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kRecv) {
-    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1)) return false;
+    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1, L.tail_seen)) return false;
   }
   if (F & kSend) {
-    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
   }
-  rsrc_t rin = make_rsrc(L.in.fifo + (L.rstep % kSteps) * kSimpleSlotBytes, kSimpleSlotBytes);
-  rsrc_t rout = make_rsrc(L.out.fifo + (L.sstep % kSteps) * kSimpleSlotBytes, kSimpleSlotBytes);
+  rsrc_t rin = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
+  rsrc_t rout = make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
   const uint64_t boff = e0 * sizeof(typename E::T);
   rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
   rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
@@ -378,12 +388,12 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kSend) {
-    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
   }
   const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
   const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
-  const uint64_t* lin = (const uint64_t*)(L.in.fifo + (L.rstep % kSteps) * kLLSlotBytes);
-  uint64_t* lout = (uint64_t*)(L.out.fifo + (L.sstep % kSteps) * kLLSlotBytes);
+  const uint64_t* lin = (const uint64_t*)(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes);
+  uint64_t* lout = (uint64_t*)(L.out.fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes);
   const uint64_t boff = e0 * sizeof(typename E::T);
   rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
   rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
@@ -496,12 +506,12 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kSend) {
-    if (L.sstep >= kSteps && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - kSteps)) return false;
+    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
   }
   const uint64_t fin = a.base + L.rstep + 1;
   const uint64_t fout = a.base + L.sstep + 1;
-  char* sin = L.in.fifo + (L.rstep % kSteps) * kLL128SlotBytes;
-  char* sout = L.out.fifo + (L.sstep % kSteps) * kLL128SlotBytes;
+  char* sin = L.in.fifo + (L.rstep & (a.depth - 1)) * kLL128SlotBytes;
+  char* sout = L.out.fifo + (L.sstep & (a.depth - 1)) * kLL128SlotBytes;
   rsrc_t rin = make_rsrc(sin, kLL128SlotBytes);
   rsrc_t rout = make_rsrc(sout, kLL128SlotBytes);
   const uint64_t boff = e0 * sizeof(typename E::T);
@@ -599,9 +609,9 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
 template <class E, int OP, int PROTO, int F>
 __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) {
   const uint64_t cap = slot_elems(PROTO, sizeof(typename E::T));
-  // The host plans parts of at most half a FIFO; a larger one could deadlock
-  // the ring, so refuse it instead.
-  if (nelem > kMaxSlicesPerPart * cap) {
+  // The host plans parts of at most half the FIFO depth; a larger one could
+  // deadlock the ring, so refuse it instead.
+  if (nelem > (uint64_t)(L.a->depth / 2) * cap) {
     record_error(*L.a, kErrInternal);
     return false;
   }
@@ -634,6 +644,8 @@ __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a)
   L.lane = threadIdx.x & 63;
   L.sstep = 0;
   L.rstep = 0;
+  L.tail_seen = 0;     // below any value a wait of this call asks for
+  L.head_seen = 0;
   const uint64_t cin = conn_index(c, ri, l, n, a.lanes);
   const uint64_t cout = conn_index(c, (ri + 1) % n, l, n, a.lanes);
   const uint64_t conn_bytes = fifo_conn_bytes(PROTO);

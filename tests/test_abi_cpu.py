@@ -164,17 +164,23 @@ def test_proto_env_grammar_subset():
     assert out["LL128"] == ["1", "1"]
 
 
+SLOT_DATA = {"Simple": 32768, "LL": 8192, "LL128": 30720}
+SLOT_FIFO = {"Simple": lambda b: b, "LL": lambda b: 2 * b, "LL128": lambda b: -(-b // 120) * 128}
+
+
 def test_parts_never_exceed_half_the_fifo():
-    # a primitive's part must fit in half the 8-slot FIFO, else the ring could
+    # a primitive's part must fit in half the FIFO depth, else the ring could
     # fill every FIFO at once and deadlock; the plan adds lanes to keep it so
-    for proto, slot in [("Simple", 32768), ("LL", 8192), ("LL128", 30720)]:
+    for proto, slot in SLOT_DATA.items():
         for chunk in [16, 4096, 65536, 1 << 19, 1 << 20]:
             if proto != "Simple" and chunk > (1 << 20):
                 continue
-            plan = ra.ringar_plan(1 << 26, "float32", 8, 16, proto, ra.make_config(chunk_bytes=chunk))
-            part = -(-chunk // plan.lanes)
-            part = -(-part // 1024) * 1024
-            assert -(-part // slot) <= 4, (proto, chunk, plan.lanes)
+            for count in [1 << 20, 1 << 26]:
+                plan = ra.ringar_plan(count, "float32", 8, 16, proto, ra.make_config(chunk_bytes=chunk))
+                part = -(-chunk // plan.lanes)
+                part = -(-part // 1024) * 1024
+                assert plan.fifo_depth in (2, 4, 8)
+                assert -(-part // slot) <= plan.fifo_depth // 2, (proto, chunk, plan.lanes, plan.fifo_depth)
     # forcing too few lanes for the chunk is refused
     cfg = ra.make_config(chunk_bytes=1 << 19, lanes=1)
     with pytest.raises(ra.RingarError) as e:
@@ -184,3 +190,51 @@ def test_parts_never_exceed_half_the_fifo():
     with pytest.raises(ra.RingarError) as e:
         ra.ringar_plan(1 << 28, "float32", 8, 1, "LL", ra.make_config(chunk_bytes=8 << 20))
     assert e.value.code == ra.INVALID_ARGUMENT
+
+
+def test_fifo_depth_follows_the_footprint_budget():
+    # the deepest of 8, 4, 2 slots whose in-flight footprint (wavefronts x
+    # depth x FIFO bytes of one step) stays within 128 MiB, unless the part
+    # needs more slots
+    budget = 128 << 20
+    seen = set()
+    for proto in SLOT_DATA:
+        for count in [1 << 12, 1 << 18, 1 << 22, 1 << 24, 1 << 26]:
+            for nch in [1, 8, 16, 32]:
+                for n in [2, 8]:
+                    plan = ra.ringar_plan(count, "float32", n, nch, proto)
+                    waves = n * plan.nchannels * plan.lanes
+                    per_ch = plan.channel_elems
+                    first = (plan.chunk_elems if per_ch >= n * plan.chunk_elems
+                             else -(-(-(-max(1, per_ch) // n)) // 4) * 4)
+                    part = -(-(first * 4) // plan.lanes)
+                    part = -(-part // 1024) * 1024
+                    slices = -(-part // SLOT_DATA[proto])
+                    step = SLOT_FIFO[proto](min(part, SLOT_DATA[proto]))
+                    d = plan.fifo_depth
+                    seen.add(d)
+                    assert slices <= d // 2
+                    if d < 8:   # it was halved: the deeper FIFO was over budget
+                        assert waves * 2 * d * step > budget, (proto, count, nch, n, d)
+                    if d > 2:   # it was kept: within budget, or the part needs it
+                        assert waves * d * step <= budget or slices > d // 4, (proto, count, nch, n, d)
+    assert seen == {2, 4, 8}
+    # the 64 MiB, 16-channel case: 4096 wavefronts x 16 KiB steps
+    plan = ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", ra.make_config(chunk_bytes=1 << 19))
+    assert (plan.lanes, plan.fifo_depth) == (32, 2)
+
+
+def test_fifo_depth_knob():
+    for bad in (1, 3, 16, -2):
+        with pytest.raises(ra.RingarError) as e:
+            ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple", ra.make_config(fifo_depth=bad))
+        assert e.value.code == ra.INVALID_ARGUMENT
+    for d in (2, 4, 8):
+        assert ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple", ra.make_config(fifo_depth=d)).fifo_depth == d
+    # a 64 KiB part (two slots) cannot run on a 2-slot FIFO
+    cfg = ra.make_config(chunk_bytes=1 << 16, lanes=1, fifo_depth=2)
+    with pytest.raises(ra.RingarError) as e:
+        ra.ringar_plan(1 << 24, "float32", 8, 1, "Simple", cfg)
+    assert e.value.code == ra.INVALID_USAGE
+    assert ra.ringar_plan(1 << 24, "float32", 8, 1, "Simple",
+                          ra.make_config(chunk_bytes=1 << 16, lanes=1, fifo_depth=4)).fifo_depth == 4

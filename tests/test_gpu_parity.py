@@ -46,10 +46,10 @@ def run_gpu(xs, dtype, op, proto="auto", nch=0, chunk_bytes=0, ring=None, inplac
     return outs, plan, code, ins_after
 
 
-def check(xs, dtype, op, proto="auto", nch=0, chunk_bytes=0, ring=None, inplace=False, lanes=0):
+def check(xs, dtype, op, proto="auto", nch=0, chunk_bytes=0, ring=None, inplace=False, lanes=0, **cfg):
     print(f"case n={len(xs)} count={xs[0].size} {dtype} {op} {proto} nch={nch} chunk={chunk_bytes} "
-          f"ring={ring} inplace={inplace} lanes={lanes}", flush=True)
-    outs, plan, code, after = run_gpu(xs, dtype, op, proto, nch, chunk_bytes, ring, inplace, lanes)
+          f"ring={ring} inplace={inplace} lanes={lanes} {cfg}", flush=True)
+    outs, plan, code, after = run_gpu(xs, dtype, op, proto, nch, chunk_bytes, ring, inplace, lanes, **cfg)
     assert code == ra.SUCCESS, ra.ringar_result_string(code)
     want = oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems, ring=ring)
     for r, (g, w) in enumerate(zip(outs, want)):
@@ -169,6 +169,22 @@ def test_ragged_shapes(proto, dtype):
         xs = W.inputs(f"ragged-{proto}-{dtype}-{i}", n, count, dtype, "uniform", -4, 4)
         ring = list(np.random.default_rng(i).permutation(n)) if i % 2 else None
         check(xs, dtype, "sum" if i % 3 else "max", proto, nch, units * 16, ring=ring, lanes=lanes)
+
+
+# a chunk of four slots per lane at depth 8, two at depth 4, one at depth 2
+SLOT_BYTES = {"LL": 8192, "LL128": 30720, "Simple": 32768}
+
+
+@pytest.mark.parametrize("depth", [2, 4, 8])
+@pytest.mark.parametrize("proto", ["LL", "LL128", "Simple"])
+def test_every_fifo_depth(proto, depth):
+    chunk = 4 * SLOT_BYTES[proto]
+    lanes = 8 // depth
+    n, nch = 5, 3
+    count = nch * n * (chunk // 4) * 2 + 777     # two loops per channel and a ragged tail
+    xs = W.inputs("depth", n, count, "float32", "normal")
+    outs, plan = check(xs, "float32", "sum", proto, nch, chunk, lanes=lanes, fifo_depth=depth)
+    assert (plan.lanes, plan.nchannels) == (lanes, nch)
 
 
 @pytest.mark.parametrize("proto", ["LL", "LL128", "Simple"])
