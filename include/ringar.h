@@ -119,7 +119,9 @@ typedef struct {
  *                    (the pages' NCCL_STEPS is 8); 0 = chosen by size.  A
  *                    lane's part of a chunk may fill at most half of them,
  *                    else RINGAR_ERR_INVALID_USAGE.  Does not change any
- *                    result. */
+ *                    result.
+ *   force_general:   test hook, normally 0: 1 = never use the straight-line
+ *                    form for small lane parts (see ringar_plan_t). */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;
@@ -129,6 +131,7 @@ typedef struct {
   volatile uint32_t* abort_flag;
   int skip_rank;
   int fifo_depth;
+  int force_general;
 } ringar_config_t;
 
 /* The resolved plan of a call (what ringar_allreduce would launch). */
@@ -141,6 +144,10 @@ typedef struct {
   size_t channel_elems;    /* per-channel length before clipping to count */
   int lanes;               /* wavefronts per (rank, channel) */
   int fifo_depth;          /* FIFO slots in use per connection */
+  int small_slices;        /* 1: every lane part is at most 1 KiB, and LL or
+                              Simple run their straight-line form (one 16-byte
+                              packet per lane and step) when all buffers are
+                              16-byte aligned */
   int workgroups;          /* grid size */
   int threads_per_group;
   uint64_t max_steps;      /* upper bound on FIFO steps per connection */

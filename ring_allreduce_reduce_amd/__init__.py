@@ -56,6 +56,7 @@ class ringar_config_t(ctypes.Structure):
         ("abort_flag", ctypes.c_void_p),
         ("skip_rank", ctypes.c_int),
         ("fifo_depth", ctypes.c_int),
+        ("force_general", ctypes.c_int),
     ]
 
 
@@ -69,6 +70,7 @@ class ringar_plan_t(ctypes.Structure):
         ("channel_elems", ctypes.c_size_t),
         ("lanes", ctypes.c_int),
         ("fifo_depth", ctypes.c_int),
+        ("small_slices", ctypes.c_int),
         ("workgroups", ctypes.c_int),
         ("threads_per_group", ctypes.c_int),
         ("max_steps", ctypes.c_uint64),
@@ -122,7 +124,7 @@ def _enum(table, v):
 
 
 def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_ms=0,
-                abort_flag=0, skip_rank=-1, fifo_depth=0):
+                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0):
     """A ringar_config_t; keeps the ring-order array alive on the object."""
     cfg = ringar_config_t()
     cfg.chunk_bytes = chunk_bytes
@@ -138,6 +140,7 @@ def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_
     cfg.abort_flag = abort_flag or None
     cfg.skip_rank = skip_rank
     cfg.fifo_depth = fifo_depth
+    cfg.force_general = force_general
     return cfg
 
 

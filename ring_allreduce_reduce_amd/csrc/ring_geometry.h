@@ -32,6 +32,7 @@ constexpr int kMaxSteps = 8;
 constexpr int kMinSteps = 2;
 constexpr int kMaxSlicesPerPart = kMaxSteps / 2;
 constexpr uint32_t kLaneGranBytes = 1024; // lane parts start on 1 KiB boundaries
+constexpr uint32_t kSmallSliceBytes = 1024; // lane parts of the small-slice form (64 x 16 B)
 
 // FIFO slot geometry per protocol.
 constexpr uint32_t kSimpleSlotBytes = 32768;              // data bytes per slot

@@ -5,18 +5,20 @@
 namespace ringar {
 
 template <int OP>
-static const void* by_proto_bf16(int proto) {
-  if (proto == kLL) return (const void*)&ring_allreduce_kernel<BF16, OP, kLL>;
-  if (proto == kLL128) return (const void*)&ring_allreduce_kernel<BF16, OP, kLL128>;
-  return (const void*)&ring_allreduce_kernel<BF16, OP, kSimple>;
+static const void* by_proto_bf16(int proto, bool small) {
+  if (proto == kLL) return small ? (const void*)&ring_allreduce_kernel<BF16, OP, kLL, true>
+                                 : (const void*)&ring_allreduce_kernel<BF16, OP, kLL, false>;
+  if (proto == kLL128) return (const void*)&ring_allreduce_kernel<BF16, OP, kLL128, false>;
+  return small ? (const void*)&ring_allreduce_kernel<BF16, OP, kSimple, true>
+               : (const void*)&ring_allreduce_kernel<BF16, OP, kSimple, false>;
 }
 
-const void* kernel_for_bf16(int op, int proto) {
+const void* kernel_for_bf16(int op, int proto, bool small) {
   switch (op) {
-    case 0: return by_proto_bf16<0>(proto);
-    case 1: return by_proto_bf16<1>(proto);
-    case 2: return by_proto_bf16<2>(proto);
-    default: return by_proto_bf16<3>(proto);
+    case 0: return by_proto_bf16<0>(proto, small);
+    case 1: return by_proto_bf16<1>(proto, small);
+    case 2: return by_proto_bf16<2>(proto, small);
+    default: return by_proto_bf16<3>(proto, small);
   }
 }
 

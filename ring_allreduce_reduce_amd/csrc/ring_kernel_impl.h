@@ -120,6 +120,7 @@ template <class E, int OP> __device__ __forceinline__ u32x4 vop(u32x4 a, u32x4 b
 // ----------------------------------------------------------------- memory
 constexpr int kSC1 = 16;   // device-coherent: write through / read past L2
 constexpr int kNT = 2;     // streaming hint for user buffers
+constexpr int kVolatile = (int)0x80000000u;   // re-read on every poll (compiler side)
 
 // Buffer resource over [base, base + bytes).  Every caller passes values that
 // are the same in all lanes of the wavefront; reading them from the first
@@ -376,6 +377,15 @@ __device__ __forceinline__ bool ll_recv4(Waiter& w, const uint64_t* lin, uint32_
   }
 }
 
+// One LL line through a buffer resource (8-byte, device-coherent).
+__device__ __forceinline__ uint64_t ll_load(rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kSC1 | kVolatile);
+  return ((uint64_t)v.y << 32) | v.x;
+}
+__device__ __forceinline__ void ll_store(rsrc_t r, uint32_t off, uint32_t data, uint32_t flag) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{data, flag}, r, (int)off, 0, kSC1);
+}
+
 __device__ __forceinline__ void ll_send4(uint64_t* lout, uint32_t p, u32x4 r, uint32_t flag) {
   st_relaxed(lout + 4 * p + 0, ll_line(r.x, flag));
   st_relaxed(lout + 4 * p + 1, ll_line(r.y, flag));
@@ -605,9 +615,118 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
   return true;
 }
 
+// --- small slices: at most one 16-byte packet per lane ---------------------
+// Used when every lane part of the call is at most 1 KiB and all user
+// buffers are 16-byte aligned: the sizes where a ring step's time is mostly
+// the instructions of the step itself, so the code is straight-line.  Lane p
+// handles packet p; a lane past the last packet points its accesses just past
+// the buffer resources, so its loads read zeros and its stores are dropped by
+// the range check.  The lane of a ragged last packet goes element-wise on the
+// user side.
+template <class E, int F>
+__device__ __forceinline__ u32x4 small_user_load(const Lane& L, uint64_t boff, uint32_t nbytes) {
+  const uint32_t nfull = nbytes / 16, p = (uint32_t)L.lane;
+  u32x4 v = ld16<kNT>(make_rsrc(L.src + boff, nfull * 16), p * 16);
+  if (nfull * 16 < nbytes && p == nfull)
+    v = ld_part<E, kNT>(make_rsrc(L.src + boff, nbytes), p * 16, nbytes - p * 16);
+  return v;
+}
+
+template <class E, int F>
+__device__ __forceinline__ void small_user_store(const Lane& L, uint64_t boff, uint32_t nbytes, u32x4 v) {
+  const uint32_t nfull = nbytes / 16, p = (uint32_t)L.lane;
+  st16<kNT>(v, make_rsrc(L.dst + boff, nfull * 16), p * 16);
+  if (nfull * 16 < nbytes && p == nfull)
+    st_part<E, kNT>(v, make_rsrc(L.dst + boff, nbytes), p * 16, nbytes - p * 16);
+}
+
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if (F & kSend) {
+    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
+  }
+  const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
+  const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
+  const uint64_t boff = e0 * sizeof(typename E::T);
+  const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
+  const bool act = p < npk;
+  u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
+  if (F & kSrc) vb = small_user_load<E, F>(L, boff, nbytes);
+  if (F & kRecv) {
+    const rsrc_t ri = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
+    uint64_t ln[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) ln[q] = ll_load(ri, p * 32 + q * 8);
+    L.w.start();
+    while (true) {
+      const bool ok = !act || (ll_ready(ln[0], fin) && ll_ready(ln[1], fin) && ll_ready(ln[2], fin) &&
+                               ll_ready(ln[3], fin));
+      if (__all(ok)) break;
+      if (!L.w.idle()) return false;
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        if (!ll_ready(ln[q], fin)) ln[q] = ll_load(ri, p * 32 + q * 8);
+    }
+    va = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+  }
+  const u32x4 r = combine<E, OP, F>(va, vb);
+  if (F & kSend) {
+    const rsrc_t ro = make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
+    ll_store(ro, p * 32 + 0, r.x, fout);
+    ll_store(ro, p * 32 + 8, r.y, fout);
+    ll_store(ro, p * 32 + 16, r.z, fout);
+    ll_store(ro, p * 32 + 24, r.w, fout);
+    L.sstep++;
+  }
+  if (F & kDst) small_user_store<E, F>(L, boff, nbytes, r);
+  if (F & kRecv) release_slot(L);
+  return true;
+}
+
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if (F & kRecv) {
+    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1, L.tail_seen)) return false;
+  }
+  if (F & kSend) {
+    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
+  }
+  const uint64_t boff = e0 * sizeof(typename E::T);
+  const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
+  u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
+  if (F & kRecv)
+    va = ld16<kSC1>(make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
+  if (F & kSrc) vb = small_user_load<E, F>(L, boff, nbytes);
+  const u32x4 r = combine<E, OP, F>(va, vb);
+  if (F & kSend)
+    st16<kSC1>(r, make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
+  if (F & kDst) small_user_store<E, F>(L, boff, nbytes, r);
+  if (F & kSend) {
+    wait_mem();
+    st_relaxed(L.out.tail, a.base + L.sstep + 1);
+    L.sstep++;
+  }
+  if (F & kRecv) release_slot(L);
+  return true;
+}
+
 // --- a primitive over the lane's part of one chunk ------------------------
-template <class E, int OP, int PROTO, int F>
+template <class E, int OP, int PROTO, int F, bool SMALL>
 __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) {
+  if constexpr (SMALL) {
+    // the host launches this form only for lane parts of at most 1 KiB
+    if (nelem * sizeof(typename E::T) > kSmallSliceBytes) {
+      record_error(*L.a, kErrInternal);
+      return false;
+    }
+    if (nelem == 0) return true;
+    if (PROTO == kLL) return slice_ll_small<E, OP, F>(L, e0, (uint32_t)nelem);
+    return slice_simple_small<E, OP, F>(L, e0, (uint32_t)nelem);
+  }
   const uint64_t cap = slot_elems(PROTO, sizeof(typename E::T));
   // The host plans parts of at most half the FIFO depth; a larger one could
   // deadlock the ring, so refuse it instead.
@@ -626,8 +745,9 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) 
   return true;
 }
 
-template <class E, int OP, int PROTO>
+template <class E, int OP, int PROTO, bool SMALL>
 __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a) {
+  static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const int wave = threadIdx.x >> 6;
   const int group = blockIdx.x / a.nranks;     // (channel, lane block)
   const int ri = blockIdx.x % a.nranks;        // ring index
@@ -671,11 +791,11 @@ __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a)
       lane_bounds(kl, part, l, &ls, &ll);
       const uint64_t e0 = lo + off + ks + ls;
       bool ok;
-      if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend>(L, e0, ll);
-      else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend>(L, e0, ll);
-      else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst>(L, e0, ll);
-      else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst>(L, e0, ll);
-      else ok = primitive<E, OP, PROTO, kRecv | kDst>(L, e0, ll);
+      if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, e0, ll);
+      else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, e0, ll);
+      else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst, SMALL>(L, e0, ll);
+      else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, e0, ll);
+      else ok = primitive<E, OP, PROTO, kRecv | kDst, SMALL>(L, e0, ll);
       if (!ok) return;
     }
   }

@@ -7,32 +7,33 @@
 
 namespace ringar {
 
-const void* kernel_for_i8(int op, int proto);
-const void* kernel_for_i32(int op, int proto);
-const void* kernel_for_f16(int op, int proto);
-const void* kernel_for_bf16(int op, int proto);
-const void* kernel_for_f32(int op, int proto);
-const void* kernel_for_f64(int op, int proto);
+const void* kernel_for_i8(int op, int proto, bool small);
+const void* kernel_for_i32(int op, int proto, bool small);
+const void* kernel_for_f16(int op, int proto, bool small);
+const void* kernel_for_bf16(int op, int proto, bool small);
+const void* kernel_for_f32(int op, int proto, bool small);
+const void* kernel_for_f64(int op, int proto, bool small);
 
-const void* kernel_for(int dtype, int op, int proto) {
+const void* kernel_for(int dtype, int op, int proto, bool small) {
+  small = small && proto != kLL128;
   switch (dtype) {
-    case 0: return kernel_for_i8(op, proto);
-    case 1: return kernel_for_i32(op, proto);
-    case 2: return kernel_for_f16(op, proto);
-    case 3: return kernel_for_bf16(op, proto);
-    case 4: return kernel_for_f32(op, proto);
-    default: return kernel_for_f64(op, proto);
+    case 0: return kernel_for_i8(op, proto, small);
+    case 1: return kernel_for_i32(op, proto, small);
+    case 2: return kernel_for_f16(op, proto, small);
+    case 3: return kernel_for_bf16(op, proto, small);
+    case 4: return kernel_for_f32(op, proto, small);
+    default: return kernel_for_f64(op, proto, small);
   }
 }
 
-hipError_t launch_ring(int dtype, int op, int proto, const KernelArgs& args, int grid, int block,
-                       hipStream_t stream) {
+hipError_t launch_ring(int dtype, int op, int proto, bool small, const KernelArgs& args, int grid,
+                       int block, hipStream_t stream) {
   void* params[] = {const_cast<KernelArgs*>(&args)};
-  return hipLaunchKernel(kernel_for(dtype, op, proto), dim3(grid), dim3(block), params, 0, stream);
+  return hipLaunchKernel(kernel_for(dtype, op, proto, small), dim3(grid), dim3(block), params, 0, stream);
 }
 
-hipError_t max_active_blocks(int dtype, int op, int proto, int block, int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel_for(dtype, op, proto), block, 0);
+hipError_t max_active_blocks(int dtype, int op, int proto, bool small, int block, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel_for(dtype, op, proto, small), block, 0);
 }
 
 // Writes `value` into `words` 64-bit words (plain vector stores).  A kernel,

@@ -186,6 +186,7 @@ struct Plan {
   uint64_t per_channel = 0;
   int lanes = 1;
   int depth = kMaxSteps;
+  bool small = false;      // every lane part fits the small-slice form
   int lanes_per_block = 1;
   int grid = 0;
   int block = 64;
@@ -250,7 +251,8 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   // (kMaxSlicesPerPart slots, like a chunk of NCCL_STEPS/2 steps): a
   // receiver keeps its slot until its own send is done, so parts of a full
   // FIFO's size would let every FIFO of the ring fill up and deadlock.
-  // Beyond that, one lane per 1 KiB of chunk (up to 32), and at most
+  // Beyond that, one lane per started KiB of chunk (a power of two, up to
+  // 32), and at most
   // kTargetWaves wavefronts in all (on MI355X, 64 MiB over 16 channels: 32
   // lanes, 4096 wavefronts, ran 11% faster than 16 lanes) and never more
   // than the GPU holds at once (all of them wait on each other).  Lanes
@@ -263,9 +265,9 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   auto slices_for = [&](int L) { return div_up(lane_part(first_chunk, L, (uint32_t)es), slot); };
   const bool forced_lanes = lanes != 0;
   if (!forced_lanes) {
-    uint64_t want = std::max<uint64_t>(1, first_chunk * es / kLaneGranBytes);
+    const uint64_t want = std::max<uint64_t>(1, div_up(first_chunk * es, kLaneGranBytes));
     lanes = 1;
-    while (lanes * 2 <= (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
+    while (lanes < (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
     const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
     while (lanes > 1 && (uint64_t)n * P.nch * lanes > cap && slices_for(lanes / 2) <= kMaxSlicesPerPart)
       lanes /= 2;
@@ -289,6 +291,10 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
            (uint64_t)slices_for(lanes) <= (uint64_t)P.depth / 4)
       P.depth /= 2;
   }
+  // Lane parts of at most 1 KiB (one 16-byte packet per lane and step) run
+  // the straight-line form of LL and Simple when the buffers are aligned.
+  P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es) * es <= kSmallSliceBytes &&
+            !(cfg && cfg->force_general);
   P.lanes_per_block = std::min(lanes, 4);
   P.block = 64 * P.lanes_per_block;
   const int groups = P.nch * (lanes / P.lanes_per_block);
@@ -388,13 +394,14 @@ uint64_t capacity_waves(int dtype, int op, int proto) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const long long key = (((long long)dev * 8 + dtype) * 4 + op) * 3 + proto;
+  // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      max_active_blocks(dtype, op, proto, 256, &per_cu) != hipSuccess)
+      max_active_blocks(dtype, op, proto, false, 256, &per_cu) != hipSuccess)
     return 0;
   uint64_t w = (uint64_t)cus * (uint64_t)per_cu * 4;   // 4 wavefronts per 256-thread block
   cache.emplace(key, w);
@@ -506,6 +513,7 @@ ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int 
   out->channel_elems = P.per_channel;
   out->lanes = P.lanes;
   out->fifo_depth = P.depth;
+  out->small_slices = P.small ? 1 : 0;
   out->workgroups = P.grid;
   out->threads_per_group = P.block;
   out->max_steps = P.max_steps;
@@ -567,11 +575,15 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
 
   // All (rank, channel, lane) wavefronts wait on each other, so the whole
   // grid must be resident at once.
-  const long long okey = ((long long)(dtype * 4 + op) * 3 + P.proto) * 1024 + P.block;
+  int vec = 1;
+  for (int q = 0; q < nranks; q++)
+    if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
+  const bool small = P.small && vec;
+  const long long okey = (((long long)(dtype * 4 + op) * 3 + P.proto) * 2 + small) * 1024 + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;
-    HIP_TRY(max_active_blocks(dtype, op, P.proto, P.block, &per_cu));
+    HIP_TRY(max_active_blocks(dtype, op, P.proto, small, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
   if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
@@ -590,9 +602,6 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
     A.send[i] = (const char*)sendbuffs[rank];
     A.recv[i] = (char*)recvbuffs[rank];
   }
-  int vec = 1;
-  for (int q = 0; q < nranks; q++)
-    if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   A.count = count;
   A.per_channel = P.per_channel;
   A.chunk_elems = P.chunk_elems;
@@ -616,15 +625,15 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
   }
   A.vec_ok = vec;
 
-  HIP_TRY(launch_ring(dtype, op, P.proto, A, P.grid, P.block, st));
+  HIP_TRY(launch_ring(dtype, op, P.proto, small, A, P.grid, P.block, st));
   R->base += P.max_steps + 1;
 
   if (env().debug) {
     fprintf(stderr,
             "ringar: AllReduce %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
-            "depth %d grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
+            "depth %d%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
             count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
-            P.chunk_bytes, P.lanes, P.depth, P.grid, P.block, P.times[0], P.times[1], P.times[2]);
+            P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", P.grid, P.block, P.times[0], P.times[1], P.times[2]);
   }
   return RINGAR_SUCCESS;
 }

@@ -238,3 +238,23 @@ def test_fifo_depth_knob():
     assert e.value.code == ra.INVALID_USAGE
     assert ra.ringar_plan(1 << 24, "float32", 8, 1, "Simple",
                           ra.make_config(chunk_bytes=1 << 16, lanes=1, fifo_depth=4)).fifo_depth == 4
+
+
+def test_small_form_rule():
+    # the straight-line form serves LL and Simple when every lane part is at
+    # most 1 KiB (one 16-byte packet per lane and step); the lane count rounds
+    # up so that chunks of a few KiB still split into 1 KiB parts
+    for proto in ("LL", "Simple", "LL128"):
+        for count in [1, 100, 2048, 4096, 12345, 1 << 16, 1 << 18, 1 << 22, 1 << 24]:
+            for nch in [1, 4, 16]:
+                plan = ra.ringar_plan(count, "float32", 8, nch, proto)
+                per_ch = plan.channel_elems
+                first = (plan.chunk_elems if per_ch >= 8 * plan.chunk_elems
+                         else -(-(-(-max(1, per_ch) // 8)) // 4) * 4)
+                part = -(-(first * 4) // plan.lanes)
+                part = -(-part // 1024) * 1024
+                assert plan.small_slices == int(proto != "LL128" and part <= 1024), (proto, count, nch)
+                if proto != "LL128" and first * 4 <= 32 * 1024:
+                    assert plan.small_slices == 1, (proto, count, nch, plan.lanes)
+    cfg = ra.make_config(force_general=1)
+    assert ra.ringar_plan(4096, "float32", 8, 1, "LL", cfg).small_slices == 0

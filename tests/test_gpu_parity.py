@@ -161,14 +161,32 @@ RAGGED = [  # (n, count, nch, chunk units of 16 B, lanes)
 ]
 
 
+@pytest.mark.parametrize("form", ["auto", "general"])
 @pytest.mark.parametrize("proto", ["LL", "LL128", "Simple"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_ragged_shapes(proto, dtype):
-    es = W.ELEM_BYTES[dtype]
+def test_ragged_shapes(proto, dtype, form):
+    # "auto" runs the straight-line form wherever the lane parts allow it,
+    # "general" forces the general form on the same shapes
     for i, (n, count, nch, units, lanes) in enumerate(RAGGED):
         xs = W.inputs(f"ragged-{proto}-{dtype}-{i}", n, count, dtype, "uniform", -4, 4)
         ring = list(np.random.default_rng(i).permutation(n)) if i % 2 else None
-        check(xs, dtype, "sum" if i % 3 else "max", proto, nch, units * 16, ring=ring, lanes=lanes)
+        check(xs, dtype, "sum" if i % 3 else "max", proto, nch, units * 16, ring=ring, lanes=lanes,
+              force_general=int(form == "general"))
+
+
+@pytest.mark.parametrize("proto", ["LL", "Simple"])
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_small_form_every_op_and_dtype(proto, n):
+    # one 16-byte packet per lane and step: counts with and without a ragged
+    # last packet, in place and out of place
+    for dtype in DTYPES:
+        es = W.ELEM_BYTES[dtype]
+        for j, op in enumerate(W.CONFIG5_OPS):
+            count = (n * 64 * 16 // es) * (j + 1) // 3 + (j % 2) * 3 + 1
+            dist = ("uniform", 0.9, 1.1) if op == "prod" and es > 1 and dtype != "int32" else ("uniform", -4, 4)
+            xs = W.inputs(f"small-{proto}-{dtype}-{op}-{n}", n, count, dtype, *dist)
+            outs, plan = check(xs, dtype, op, proto, 1, 0, inplace=bool(j % 2))
+            assert plan.small_slices == 1, (dtype, op, count, plan.lanes)
 
 
 # a chunk of four slots per lane at depth 8, two at depth 4, one at depth 2
