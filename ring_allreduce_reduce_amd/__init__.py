@@ -182,6 +182,29 @@ def ringar_default_model() -> ringar_model_t:
     return m
 
 
+_MODEL_SCALARS = ("bw_per_channel", "ll_max_bw", "ll128_per_channel_max_bw", "max_channels", "max_pairs")
+_MODEL_ARRAYS = ("eff", "base_lat_us", "hw_lat_us", "threads", "thread_threshold", "default_chunk_bytes")
+
+
+def model_dict(m: ringar_model_t) -> dict:
+    """A ringar_model_t as a plain dict (the JSON layout of the model)."""
+    d = {k: getattr(m, k) for k in _MODEL_SCALARS}
+    d.update({k: list(getattr(m, k)) for k in _MODEL_ARRAYS})
+    return d
+
+
+def model_from_dict(d: dict) -> ringar_model_t:
+    """The inverse of ``model_dict`` (keys starting with '_' are ignored)."""
+    m = ringar_model_t()
+    for k in _MODEL_SCALARS:
+        setattr(m, k, d[k])
+    for k in _MODEL_ARRAYS:
+        arr = getattr(m, k)
+        for i in range(3):
+            arr[i] = d[k][i]
+    return m
+
+
 def ringar_chunk_range(count, dtype, nranks, nchannels, chunk_elems, c, loop_off, k):
     v = [ctypes.c_size_t() for _ in range(4)]
     _check(load().ringar_chunk_range(count, _enum(DTYPES, dtype), nranks, nchannels, chunk_elems, c,

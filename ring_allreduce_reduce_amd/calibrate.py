@@ -1,0 +1,165 @@
+"""Measures this GPU and fits the alpha-beta model of the protocol selector.
+
+The model is the one the pages give for a ring AllReduce ([ARCH] §八.1-八.2):
+a call of `bytes` per rank over n ranks and nch channels takes
+
+    T = base + 2(n-1) * step  +  bytes / (1000 * busBw * n / (2(n-1)))   [us]
+
+with busBw = nch * bw * eff for Simple, min(llMax, nch * bw * 0.5) for LL and
+min(nch * bw * eff, nch * perChLL128) for LL128.  This tool fits, per
+protocol, `base` and `step` to small calls at n = 2..8 (least squares over
+2(n-1)), and the bandwidth terms to large calls at the model's largest
+channel count; it keeps the pages' efficiencies and the size rule for the
+channel count.  It prints the fitted model (the JSON layout of
+`ringar_model_t`) and a tuning table: for each size the model's time per
+protocol, the measured time, and which protocol each picks.
+
+    python -m ring_allreduce_reduce_amd.calibrate [--json out.json] [--table out.txt]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+
+PROTOS = ("LL", "LL128", "Simple")
+
+
+def _time_calls(ra, torch, sends, recvs, count, n, nch, proto, stream, iters, cfg=None):
+    sp = [s.data_ptr() for s in sends[:n]]
+    rp = [r.data_ptr() for r in recvs[:n]]
+
+    def call():
+        code = ra.ringar_allreduce_ex(sp, rp, count, "float32", "sum", n, nch, proto, stream.cuda_stream, cfg)
+        if code:
+            raise ra.RingarError(code, f"ringar_allreduce_ex: {ra.ringar_result_string(code)}")
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    code = ra.ringar_get_async_error(stream.cuda_stream)
+    if code:
+        raise ra.RingarError(code, f"asynchronous error: {ra.ringar_result_string(code)}")
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return ts[len(ts) // 2]
+
+
+def _fit_line(xs, ys):
+    """Least-squares y = a + b x."""
+    m = len(xs)
+    sx, sy = sum(xs), sum(ys)
+    sxx = sum(x * x for x in xs)
+    sxy = sum(x * y for x, y in zip(xs, ys))
+    b = (m * sxy - sx * sy) / (m * sxx - sx * sx)
+    return (sy - b * sx) / m, b
+
+
+def model_time(m, n, nch, p, nbytes):
+    """The model's microseconds for protocol index p (LL 0, LL128 1, Simple 2)."""
+    bus = nch * m["bw_per_channel"]
+    if p == 0:
+        bus = min(m["ll_max_bw"], bus * m["eff"][0])
+    elif p == 1:
+        bus = min(bus * m["eff"][1], nch * m["ll128_per_channel_max_bw"])
+    else:
+        bus = bus * m["eff"][2]
+    steps = 2.0 * (n - 1)
+    alg = bus * n / steps
+    return m["base_lat_us"][p] + steps * m["hw_lat_us"][p] + nbytes / (1000.0 * alg)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--json", help="write the fitted model here")
+    ap.add_argument("--table", help="write the tuning table here")
+    ap.add_argument("--nranks", type=int, default=8)
+    args = ap.parse_args(argv)
+
+    import torch
+    import ring_allreduce_reduce_amd as ra
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    n = args.nranks
+    big = 256 << 20
+    sends = [torch.randn(big // 4, device=dev) for _ in range(n)]
+    recvs = [torch.empty_like(s) for s in sends]
+    m = ra.model_dict(ra.ringar_default_model())
+    maxc = min(m["max_channels"], m["max_pairs"] // n)
+    log = lambda s: print(s, file=sys.stderr, flush=True)
+
+    # latency: smallest calls whose chunks all hold one packet, one channel
+    for p, proto in enumerate(PROTOS):
+        xs, ys = [], []
+        for nr in range(2, n + 1):
+            us = _time_calls(ra, torch, sends, recvs, 64 * nr, nr, 1, proto, stream, 200)
+            xs.append(2.0 * (nr - 1))
+            ys.append(us)
+        base, step = _fit_line(xs, ys)
+        m["base_lat_us"][p] = round(base, 2)
+        m["hw_lat_us"][p] = round(step, 3)
+        log(f"{proto}: base {base:.2f} us, step {step:.3f} us")
+
+    # bandwidth: the largest call at the largest channel count
+    def bus_at(proto, p, nbytes):
+        us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10)
+        lat = m["base_lat_us"][p] + 2.0 * (n - 1) * m["hw_lat_us"][p]
+        alg = nbytes / (1000.0 * max(us - lat, 1e-3))
+        return alg * 2.0 * (n - 1) / n
+    simple = bus_at("Simple", 2, big)
+    m["bw_per_channel"] = round(simple / (maxc * m["eff"][2]), 3)
+    ll = bus_at("LL", 0, 64 << 20)
+    m["ll_max_bw"] = round(ll, 2)
+    ll128 = bus_at("LL128", 1, big)
+    m["ll128_per_channel_max_bw"] = round(ll128 / maxc, 3)
+    log(f"bus bandwidth at {maxc} channels: Simple {simple:.1f}, LL {ll:.1f}, LL128 {ll128:.1f} GB/s")
+
+    # tuning table: model vs measurement, each protocol at its own channel count
+    ra_model = ra.model_from_dict(m)
+    cfg = ra.make_config(model=ra_model)
+    rows = []
+    for sh in range(3, 29, 2):
+        nbytes = 1 << sh
+        count = max(1, nbytes // 4)
+        line = {"bytes": nbytes}
+        for p, proto in enumerate(PROTOS):
+            plan = ra.ringar_plan(count, "float32", n, 0, proto, cfg)
+            pred = plan.predicted_us[p]
+            us = _time_calls(ra, torch, sends, recvs, count, n, 0, proto, stream,
+                             20 if nbytes >= (16 << 20) else 100, cfg)
+            line[proto] = (plan.nchannels, pred, us)
+        line["model_pick"] = min(PROTOS, key=lambda q: (line[q][1], -PROTOS.index(q)))
+        line["measured_pick"] = min(PROTOS, key=lambda q: line[q][2])
+        rows.append(line)
+        log(f"{nbytes:>10d} B: " + "  ".join(f"{q} {line[q][2]:.1f}/{line[q][1]:.1f}" for q in PROTOS))
+
+    out = [f"# ring AllReduce tuning table, n = {n}, fp32 sum, one MI355X ({time.strftime('%Y-%m-%d')})",
+           "# command: python -m ring_allreduce_reduce_amd.calibrate --json <model.json> --table <this file>",
+           "# per protocol: channels chosen by the size rule, model us, measured us (median, HIP events)",
+           "# fitted model: " + json.dumps(m), ""]
+    hdr = f"{'bytes/rank':>11s} | " + " | ".join(f"{q:>6s} ch  model  meas." for q in PROTOS) + " | model pick | fastest"
+    out.append(hdr)
+    for r in rows:
+        cells = " | ".join(f"{r[q][0]:>9d} {r[q][1]:6.1f} {r[q][2]:6.1f}" for q in PROTOS)
+        out.append(f"{r['bytes']:>11d} | {cells} | {r['model_pick']:>10s} | {r['measured_pick']}")
+    agree = sum(r["model_pick"] == r["measured_pick"] for r in rows)
+    out.append("")
+    out.append(f"model pick = fastest measured at {agree} of {len(rows)} sizes")
+    text = "\n".join(out) + "\n"
+    print(text)
+    if args.table:
+        open(args.table, "w").write(text)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(m, f, indent=2)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -109,18 +109,19 @@ const Env& env() {
 // Built-in MI355X model.  The protocol efficiencies are the values the
 // pages give (LL 0.5, LL128 about 0.94, Simple 1.0).  Latencies are fitted to
 // small calls at n = 2..8 (T = base + 2(n-1) x step), bandwidths to 32-channel
-// calls of 64-256 MiB per rank, both measured with this library on MI355X.
+// calls of 64-256 MiB per rank, both measured with this library on MI355X by
+// `python -m ring_allreduce_reduce_amd.calibrate`.
 // A channel of a small call runs one 64-thread wavefront per rank, hence 64
 // threads per channel in the size rule.
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 7.66;
-  m.ll_max_bw = 55.0;
-  m.ll128_per_channel_max_bw = 3.74;
+  m.bw_per_channel = 8.483;
+  m.ll_max_bw = 54.97;
+  m.ll128_per_channel_max_bw = 4.201;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 5.5; m.base_lat_us[1] = 6.7; m.base_lat_us[2] = 5.4;
-  m.hw_lat_us[0] = 2.08; m.hw_lat_us[1] = 2.77; m.hw_lat_us[2] = 1.82;
+  m.base_lat_us[0] = 4.97; m.base_lat_us[1] = 6.76; m.base_lat_us[2] = 5.06;
+  m.hw_lat_us[0] = 1.418; m.hw_lat_us[1] = 2.692; m.hw_lat_us[2] = 1.598;
   m.max_channels = 32;
   m.max_pairs = 256;
   m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;

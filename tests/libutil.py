@@ -31,17 +31,4 @@ def oracle_model(d=None) -> S.RingModel:
 
 
 def lib_model(d) -> "ra.ringar_model_t":
-    m = ra.ringar_model_t()
-    m.bw_per_channel = d["bw_per_channel"]
-    m.ll_max_bw = d["ll_max_bw"]
-    m.ll128_per_channel_max_bw = d["ll128_per_channel_max_bw"]
-    for i in range(3):
-        m.eff[i] = d["eff"][i]
-        m.base_lat_us[i] = d["base_lat_us"][i]
-        m.hw_lat_us[i] = d["hw_lat_us"][i]
-        m.threads[i] = d["threads"][i]
-        m.thread_threshold[i] = d["thread_threshold"][i]
-        m.default_chunk_bytes[i] = d["default_chunk_bytes"][i]
-    m.max_channels = d["max_channels"]
-    m.max_pairs = d["max_pairs"]
-    return m
+    return ra.model_from_dict(d)
