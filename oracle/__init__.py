@@ -1,4 +1,5 @@
-"""CPU oracle for the ring AllReduce: test infrastructure only.
+"""CPU oracle for the ring AllReduce and its two halves (ReduceScatter,
+AllGather): test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never imports,
@@ -60,6 +61,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_channel_range.restype = None
     lib.oracle_loop_chunk.argtypes = [sz, sz, sz, ctypes.c_int, sz]
     lib.oracle_loop_chunk.restype = sz
+    lib.oracle_ring_reduce_scatter.argtypes = [
+        ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+        ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.oracle_ring_reduce_scatter.restype = ctypes.c_int
+    lib.oracle_ring_all_gather.argtypes = [
+        ctypes.c_int, sz, sz, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.oracle_ring_all_gather.restype = ctypes.c_int
     for name in ("oracle_f16_decode_array", "oracle_bf16_decode_array",
                  "oracle_f16_encode_array", "oracle_bf16_encode_array"):
         getattr(lib, name).argtypes = [vp, vp, sz]
@@ -86,6 +94,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     return _lib
 
 
+def _sentinel(count: int, npt) -> np.ndarray:
+    """A fresh output filled with 0xA5 bytes, so an element the oracle never
+    writes cannot pass for a result."""
+    return np.full(count * np.dtype(npt).itemsize, 0xA5, dtype=np.uint8).view(npt)
+
+
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
@@ -105,7 +119,7 @@ def ring_allreduce(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
     xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
     count = xs[0].size if n else 0
     assert all(x.size == count for x in xs)
-    ys = out if out is not None else [np.empty(count, dtype=npt) for _ in range(n)]
+    ys = out if out is not None else [_sentinel(count, npt) for _ in range(n)]
     xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
     yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
     rp = None
@@ -114,6 +128,44 @@ def ring_allreduce(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
     rc = lib.oracle_ring_allreduce(n, count, code, OPS[op], nchannels, chunk_elems, rp, xp, yp)
     if rc != 0:
         raise ValueError("oracle_ring_allreduce rejected its arguments")
+    return ys
+
+
+def ring_reduce_scatter(xs, dtype: str, op: str, ring=None, lib: ctypes.CDLL | None = None, out=None):
+    """Ring ReduceScatter: ``xs[r]`` holds n blocks of ``count`` elements;
+    returns the n outputs of ``count`` elements (rank r: block r reduced over
+    all ranks, in the ring's fold order).  ``out`` may hold views of the
+    inputs' own blocks (the in-place form)."""
+    lib = lib or load()
+    code, npt, _ = DTYPES[dtype]
+    n = len(xs)
+    xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
+    assert all(x.size == xs[0].size for x in xs) and xs[0].size % n == 0
+    count = xs[0].size // n
+    ys = out if out is not None else [_sentinel(count, npt) for _ in range(n)]
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    rp = (ctypes.c_int * n)(*[int(r) for r in ring]) if ring is not None else None
+    if lib.oracle_ring_reduce_scatter(n, count, code, OPS[op], rp, xp, yp) != 0:
+        raise ValueError("oracle_ring_reduce_scatter rejected its arguments")
+    return ys
+
+
+def ring_all_gather(xs, dtype: str, ring=None, lib: ctypes.CDLL | None = None, out=None):
+    """Ring AllGather: returns the n outputs of n blocks each (block q = rank
+    q's input).  ``out`` may be the outputs whose block r is ``xs[r]``."""
+    lib = lib or load()
+    _, npt, esize = DTYPES[dtype]
+    n = len(xs)
+    xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
+    count = xs[0].size
+    assert all(x.size == count for x in xs)
+    ys = out if out is not None else [_sentinel(n * count, npt) for _ in range(n)]
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    rp = (ctypes.c_int * n)(*[int(r) for r in ring]) if ring is not None else None
+    if lib.oracle_ring_all_gather(n, count, esize, rp, xp, yp) != 0:
+        raise ValueError("oracle_ring_all_gather rejected its arguments")
     return ys
 
 

@@ -362,6 +362,126 @@ int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
   return rc;
 }
 
+/* ---------------------------------------------------------------------
+ * The two halves of the ring as calls of their own ([ARCH] §七.1: the ring
+ * runs reduce_scatter and all_gather as n-1 steps each, runRing).  The pages
+ * give no buffer layout for these calls; the plain one is taken: a
+ * ReduceScatter input holds n blocks of `count` elements and rank r's output
+ * is block r reduced over all ranks; an AllGather output holds n blocks and
+ * block q is rank q's input.  Ring index i finishes the block of rank
+ * ring[i], so each stage visits whole blocks: chunk k of a stage is the block
+ * of rank ring[k].  Channels and loops only cut every block into the same
+ * pieces and change no element's fold order, so each block runs as one
+ * chunk here.
+ * --------------------------------------------------------------------- */
+
+static int* ring_order_copy(int n, const int* ring) {
+  int* order = malloc(sizeof(int) * (size_t)n);
+  if (order)
+    for (int i = 0; i < n; i++) order[i] = ring ? ring[i] : i;
+  return order;
+}
+
+static unsigned char** payloads(int n, size_t bytes) {
+  unsigned char** p = calloc((size_t)n, sizeof(void*));
+  if (!p) return NULL;
+  for (int i = 0; i < n; i++)
+    if (!(p[i] = malloc(bytes ? bytes : 1))) {
+      for (int j = 0; j < i; j++) free(p[j]);
+      free(p);
+      return NULL;
+    }
+  return p;
+}
+
+static void free_payloads(int n, unsigned char** p) {
+  if (!p) return;
+  for (int i = 0; i < n; i++) free(p[i]);
+  free(p);
+}
+
+/*
+ * Ring ReduceScatter: x[r] holds n*count elements, y[r] count elements (y[r]
+ * may be x[r]'s block r).  Per stage s = 0..n-1, ring index i visits chunk
+ * (i + n - 1 - s) mod n: send at s = 0, recvReduceSend up to s = n-2, and at
+ * s = n-1 (its own chunk) the last reduction goes to its output and is not
+ * forwarded.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_ring_reduce_scatter(int nranks, size_t count, int dtype, int op, const int* ring,
+                               const void* const* x, void* const* y) {
+  size_t es = elem_size(dtype);
+  if (!es || op < OR_SUM || op > OR_MAX || nranks < 1) return -1;
+  int n = nranks;
+  int* order = ring_order_copy(n, ring);
+  if (!order) return -1;
+  if (n == 1) {
+    memmove(y[order[0]], x[order[0]], count * es);
+    free(order);
+    return 0;
+  }
+  unsigned char** pa = payloads(n, count * es);
+  unsigned char** pb = payloads(n, count * es);
+  int rc = (pa && pb) ? 0 : -1;
+  for (int s = 0; s <= n - 1 && rc == 0; s++) {
+    for (int i = 0; i < n; i++) {
+      int prev = (i + n - 1) % n;
+      int k = ((i + n - 1 - s) % n + n) % n;
+      const unsigned char* mine = (const unsigned char*)x[order[i]] + (size_t)order[k] * count * es;
+      if (s == 0)
+        memcpy(pb[i], mine, count * es);                       /* send */
+      else if (s <= n - 2)
+        combine(dtype, op, pa[prev], mine, pb[i], count);      /* recvReduceSend */
+      else
+        combine(dtype, op, pa[prev], mine, y[order[i]], count); /* recvReduceCopy */
+    }
+    unsigned char** t = pa; pa = pb; pb = t;
+  }
+  free_payloads(n, pa);
+  free_payloads(n, pb);
+  free(order);
+  return rc;
+}
+
+/*
+ * Ring AllGather of `count` elements of `esize` bytes per rank: y[r] holds n
+ * blocks (x[r] may be y[r]'s block r).  Per stage s = 0..n-1, ring index i
+ * handles the block of rank ring[(i - s) mod n]: at s = 0 it copies its own
+ * input to its output and sends it, then receives, keeps and forwards
+ * (recvCopySend) up to s = n-2, and at s = n-1 only receives.
+ */
+int oracle_ring_all_gather(int nranks, size_t count, size_t esize, const int* ring,
+                           const void* const* x, void* const* y) {
+  if (nranks < 1 || esize == 0) return -1;
+  int n = nranks;
+  size_t bytes = count * esize;
+  int* order = ring_order_copy(n, ring);
+  if (!order) return -1;
+  unsigned char** pa = payloads(n, bytes);
+  unsigned char** pb = payloads(n, bytes);
+  int rc = (pa && pb) ? 0 : -1;
+  for (int s = 0; s <= n - 1 && rc == 0; s++) {
+    for (int i = 0; i < n; i++) {
+      int prev = (i + n - 1) % n;
+      int k = ((i - s) % n + n) % n;
+      unsigned char* out = (unsigned char*)y[order[i]] + (size_t)order[k] * bytes;
+      if (s == 0) {
+        memcpy(pb[i], x[order[i]], bytes);                     /* copySend */
+        memmove(out, x[order[i]], bytes);
+      } else if (s <= n - 2) {
+        memcpy(pb[i], pa[prev], bytes);                        /* recvCopySend */
+        memcpy(out, pa[prev], bytes);
+      } else {
+        memcpy(out, pa[prev], bytes);                          /* recv */
+      }
+    }
+    unsigned char** t = pa; pa = pb; pb = t;
+  }
+  free_payloads(n, pa);
+  free_payloads(n, pb);
+  free(order);
+  return rc;
+}
+
 /* Array forms of the 16-bit codecs, for the tests' exhaustive pins. */
 void oracle_f16_decode_array(const uint16_t* h, float* f, size_t len) {
   for (size_t e = 0; e < len; e++) f[e] = f16_decode(h[e]);

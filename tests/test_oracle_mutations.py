@@ -11,18 +11,21 @@ import pytest
 
 import oracle
 from bruteforce_ring import run as brute_run
+from bruteforce_ring import run_reduce_scatter as brute_rs
 from refs import exact_reduce, fold_closed_form, hop
 from ring_allreduce_reduce_amd import workloads as W
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
 
 MUTATIONS = {
-    "chunk index off by one": ("int k = ((i + n - 1 - s) % n + n) % n;", "int k = ((i + n - s) % n + n) % n;"),
+    "chunk index off by one": ("int k = ((i + n - 1 - s) % n + n) % n;       /* chunk of this stage */",
+                               "int k = ((i + n - s) % n + n) % n;       /* chunk of this stage */"),
     "reduce dropped (forward only)": (
         "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);",
         "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        memcpy(pay_new[i], pay_old[prev], len * es);"),
     "final recv missing": ("for (int s = 0; s <= 2 * n - 2; s++)", "for (int s = 0; s < 2 * n - 2; s++)"),
-    "ring direction reversed": ("int prev = (i + n - 1) % n;", "int prev = (i + 1) % n;"),
+    "ring direction reversed": ("int prev = (i + n - 1) % n;                  /* ring predecessor */",
+                                "int prev = (i + 1) % n;                  /* ring predecessor */"),
     "sum becomes difference": ("    case OR_SUM: return a + b;\n    case OR_PROD: return a * b;\n    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic double",
                                "    case OR_SUM: return a - b;\n    case OR_PROD: return a * b;\n    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic double"),
     "int8 min operands transposed": (
@@ -38,6 +41,18 @@ MUTATIONS = {
                                             "return rem < loop ? div_up(rem, (size_t)nranks) : chunk_elems;"),
     "channel length not rounded": ("size_t per = align_up(div_up(count, (size_t)nchannels), a);",
                                    "size_t per = div_up(count, (size_t)nchannels);"),
+    "reduce-scatter visits the wrong chunk": (
+        "      int k = ((i + n - 1 - s) % n + n) % n;\n      const unsigned char* mine = (const unsigned char*)x[order[i]] + (size_t)order[k] * count * es;",
+        "      int k = ((i + n - s) % n + n) % n;\n      const unsigned char* mine = (const unsigned char*)x[order[i]] + (size_t)order[k] * count * es;"),
+    "reduce-scatter block indexed by ring index, not rank": (
+        "(const unsigned char*)x[order[i]] + (size_t)order[k] * count * es;",
+        "(const unsigned char*)x[order[i]] + (size_t)k * count * es;"),
+    "reduce-scatter drops its last reduction": (
+        "        combine(dtype, op, pa[prev], mine, y[order[i]], count); /* recvReduceCopy */",
+        "        memcpy(y[order[i]], pa[prev], count * es);              /* recvReduceCopy */"),
+    "all-gather block off by one": ("      int k = ((i - s) % n + n) % n;", "      int k = ((i - s + 1) % n + n) % n;"),
+    "all-gather skips its final recv": ("  for (int s = 0; s <= n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;",
+                                        "  for (int s = 0; s < n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;"),
     "fp64 min uses max": ("    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void",
                           "    case OR_MIN: return (b > a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void"),
 }
@@ -83,6 +98,24 @@ def _battery(lib) -> list:
         got = run(xs, dtype, "sum", nch, chunk)
         if not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
             fails.append(f"brute force {n} {count} {dtype}")
+    # reduce-scatter: order-free closed form and the brute-force ring
+    for (n, count, dtype, op, ring) in [(5, 21, "int32", "sum", [3, 0, 4, 1, 2]), (4, 9, "int8", "min", None),
+                                        (3, 13, "float32", "sum", [1, 2, 0])]:
+        xs = W.inputs(f"mrs-{n}-{dtype}", n, n * count, dtype, "uniform", -4, 4)
+        got = oracle.ring_reduce_scatter(xs, dtype, op, ring=ring, lib=lib)
+        if dtype in W.FLOATS:
+            want = brute_rs(xs, dtype, op, 2, 16 // W.ELEM_BYTES[dtype], ring)
+        else:
+            full = exact_reduce(xs, dtype, op)
+            want = [full[r * count:(r + 1) * count] for r in range(n)]
+        if not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
+            fails.append(f"reduce-scatter {n} {dtype} {op}")
+    # all-gather: concatenation
+    for n, ring in [(4, [2, 3, 0, 1]), (3, None)]:
+        xs = W.inputs(f"mag-{n}", n, 11, "int32", "uniform", -4, 4)
+        got = oracle.ring_all_gather(xs, "int32", ring=ring, lib=lib)
+        if not all(np.array_equal(g, np.concatenate(xs)) for g in got):
+            fails.append(f"all-gather {n}")
     # codecs against numpy / torch
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = bits.view(np.float16).astype(np.float32)
