@@ -9,6 +9,10 @@ against MI355X's 8 TB/s HBM peak (algorithmic bytes per launch / average
 launch time measured with HIP events on the launch stream), and the CPU
 oracle timed on this host as a baseline.  The oracle's output also checks the
 last timed call bit for bit.
+
+`--coll reduce_scatter` / `--coll all_gather` time the two halves of the
+ring on the same shape instead (8 ranks, 64 MiB n-block buffer per rank, 8 MiB
+blocks); their busbw is algbw x (n-1)/n.
 """
 import argparse
 import glob
@@ -56,12 +60,18 @@ def read_traffic():
     return float(m_bytes.group(1))
 
 
-def alg_bytes(n, s, e=1.0):
-    """Algorithmic bytes of one ring AllReduce of s bytes per rank: every rank
-    reads its send buffer once and writes its receive buffer once, and each of
-    the 2(n-1) steps writes and reads one chunk through a FIFO whose bytes are
-    e times the payload (Simple 1, LL 2, LL128 128/120)."""
-    return s * (2 * n + 4 * (n - 1) * e)
+def alg_bytes(n, s, e=1.0, coll="allreduce"):
+    """Algorithmic bytes of one ring call over n ranks.  AllReduce of s bytes
+    per rank: every rank reads its send buffer once and writes its receive
+    buffer once, and each of the 2(n-1) steps writes and reads one chunk
+    through a FIFO whose bytes are e times the payload (Simple 1, LL 2, LL128
+    128/120).  ReduceScatter / AllGather with s bytes in the n-block buffer of
+    each rank: every rank reads its input once (s, resp. s/n), writes its
+    output once (s/n, resp. s), and each of the n-1 steps writes and reads one
+    block through the FIFO."""
+    if coll == "allreduce":
+        return s * (2 * n + 4 * (n - 1) * e)
+    return n * s + s + 2 * (n - 1) * s * e
 
 
 def main():
@@ -72,6 +82,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling memory counters)")
+    ap.add_argument("--coll", default="allreduce", choices=["allreduce", "reduce_scatter", "all_gather"],
+                    help="the AllReduce (default) or one of its halves on the same 8 x 64 MiB shape")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the {NRANKS} ranks are virtual ranks inside one MI355X; "
@@ -82,25 +94,43 @@ def main():
     import torch
 
     import ring_allreduce_reduce_amd as ra
+    oracle = None
+    if not args.no_cpu_baseline:
+        import oracle
     from ring_allreduce_reduce_amd import workloads as W
 
-    count = BYTES_PER_RANK // 4
+    coll = args.coll
+    count = BYTES_PER_RANK // 4              # elements in the n-block buffer of a rank
+    block = count // NRANKS
     log("generating inputs")
-    xs = W.inputs("config2", NRANKS, count, "float32", "normal")
     dev = torch.device("cuda:0")
-    sends = [W.to_torch(x, "float32", dev) for x in xs]
-    recvs = [torch.empty_like(s) for s in sends]
+    if coll == "all_gather":
+        xs = W.inputs("config2-ag", NRANKS, block, "float32", "normal")
+        sends = [W.to_torch(x, "float32", dev) for x in xs]
+        recvs = [torch.empty(count, device=dev) for _ in sends]
+    else:
+        xs = W.inputs("config2", NRANKS, count, "float32", "normal")
+        sends = [W.to_torch(x, "float32", dev) for x in xs]
+        recvs = [torch.empty(count if coll == "allreduce" else block, device=dev) for _ in sends]
     stream = torch.cuda.Stream()
-    plan = ra.ringar_plan(count, "float32", NRANKS, NCHANNELS, "Simple", ra.make_config(chunk_bytes=CHUNK_BYTES))
+    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES)
+    plan = ra.ringar_plan_coll(coll, count if coll == "allreduce" else block, "float32", NRANKS, NCHANNELS,
+                               "Simple", cfg)
     send_ptrs = [s.data_ptr() for s in sends]
     recv_ptrs = [r.data_ptr() for r in recvs]
-    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES)
 
     def step():
-        code = ra.ringar_allreduce_ex(send_ptrs, recv_ptrs, count, "float32", "sum", NRANKS, NCHANNELS,
-                                      "Simple", stream.cuda_stream, cfg)
+        if coll == "allreduce":
+            code = ra.ringar_allreduce_ex(send_ptrs, recv_ptrs, count, "float32", "sum", NRANKS, NCHANNELS,
+                                          "Simple", stream.cuda_stream, cfg)
+        elif coll == "reduce_scatter":
+            code = ra.ringar_reduce_scatter_ex(send_ptrs, recv_ptrs, block, "float32", "sum", NRANKS,
+                                               NCHANNELS, "Simple", stream.cuda_stream, cfg)
+        else:
+            code = ra.ringar_all_gather_ex(send_ptrs, recv_ptrs, block, "float32", NRANKS, NCHANNELS,
+                                           "Simple", stream.cuda_stream, cfg)
         if code != 0:
-            raise RuntimeError(f"ringar_allreduce_ex: {ra.ringar_result_string(code)}")
+            raise RuntimeError(f"{coll}: {ra.ringar_result_string(code)}")
 
     torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
@@ -142,21 +172,28 @@ def main():
 
     s = BYTES_PER_RANK
     algbw = s / (ms_per_step * 1e-3) / 1e9
-    busbw = algbw * 2 * (NRANKS - 1) / NRANKS
-    b_alg = alg_bytes(NRANKS, s)
+    bus_factor = (2 if coll == "allreduce" else 1) * (NRANKS - 1) / NRANKS
+    busbw = algbw * bus_factor
+    b_alg = alg_bytes(NRANKS, s, coll=coll)
     achieved = b_alg / (avg_launch_ms * 1e-3) / 1e9
-    traffic = read_traffic()
+    traffic = read_traffic() if coll == "allreduce" else None
+
+    def run_oracle():
+        if coll == "allreduce":
+            return oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+        if coll == "reduce_scatter":
+            return oracle.ring_reduce_scatter(xs, "float32", "sum")
+        return oracle.ring_all_gather(xs, "float32")
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
         oracle.load()
         log("timing the CPU oracle on the full workload for about 10 s")
         t0 = time.perf_counter()
-        want = oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+        want = run_oracle()
         calls = 1
         while time.perf_counter() - t0 < 10.0 and calls < 500:
-            oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+            run_oracle()
             calls += 1
         dt = (time.perf_counter() - t0) / calls
         got = [r.cpu().numpy() for r in recvs]
@@ -165,13 +202,17 @@ def main():
             raise RuntimeError("GPU result differs from the CPU oracle")
         log(f"oracle {dt:.3f} s per call over {calls} calls; GPU output matches bit for bit")
         cpu_alg = s / dt / 1e9
-        cpu = {"value": round(cpu_alg * 2 * (NRANKS - 1) / NRANKS, 4), "unit": "GB/s", "cores": 1,
+        cpu = {"value": round(cpu_alg * bus_factor, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle", "seconds_per_call": round(dt, 4), "calls": calls,
                "sample": f"the full workload (8 ranks x 64 MiB fp32) repeated {calls} times (~10 s), "
                          "single-threaded C oracle; value is busbw"}
 
+    what = {"allreduce": ("ring AllReduce", "64 MiB per rank"),
+            "reduce_scatter": ("ring ReduceScatter", "64 MiB input per rank (8 blocks of 8 MiB)"),
+            "all_gather": ("ring AllGather", "8 MiB input, 64 MiB output per rank")}[coll]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if coll == "allreduce" else
+        METRIC.replace("fp32 sum", f"{what[0]}, fp32" + (" sum" if coll == "reduce_scatter" else "")),
         "value": round(busbw, 3),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -183,7 +224,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "ring AllReduce, 8 virtual ranks, fp32 sum, 64 MiB per rank, Simple, "
+        "config": {"workload": f"{what[0]}, 8 virtual ranks, fp32{' sum' if coll != 'all_gather' else ''}, "
+                               f"{what[1]}, Simple, "
                                "16 channels, 512 KiB chunks",
                    "nranks": NRANKS, "bytes_per_rank": s, "proto": "Simple", "nchannels": NCHANNELS,
                    "chunk_bytes": CHUNK_BYTES, "lanes": plan.lanes, "fifo_depth": plan.fifo_depth,

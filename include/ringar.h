@@ -1,5 +1,6 @@
 /*
- * ringar: ring AllReduce over n virtual ranks that all live in one MI355X.
+ * ringar: ring AllReduce (and its two halves, ReduceScatter and AllGather)
+ * over n virtual ranks that all live in one MI355X.
  *
  * The operation is the device-side ring AllReduce described on
  *   [ARCH] arganzheng.life, "NCCL architecture: topology, channels, algorithms
@@ -73,6 +74,15 @@ typedef enum {
   RINGAR_PROTO_LL128 = 1,
   RINGAR_PROTO_SIMPLE = 2
 } ringar_proto_t;
+
+/* Collectives of ringar_plan_coll: the AllReduce and its two halves, which
+ * the ring also runs as calls of their own ([ARCH] §七.1: reduce_scatter and
+ * all_gather take n-1 ring steps each). */
+typedef enum {
+  RINGAR_ALLREDUCE = 0,
+  RINGAR_REDUCE_SCATTER = 1,
+  RINGAR_ALL_GATHER = 2
+} ringar_coll_t;
 
 /* Inputs of the alpha-beta model ([ARCH] §八.1-八.2), per protocol in the
  * order LL, LL128, Simple.  Bandwidths GB/s, latencies microseconds.
@@ -183,10 +193,57 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
                                     int nchannels, ringar_proto_t proto, ringar_stream_t stream,
                                     const ringar_config_t* cfg);
 
+/*
+ * Ring ReduceScatter, the first half of the ring AllReduce as a call of its
+ * own ([ARCH] §七.1; the pages give no buffer layout, the plain one is
+ * taken): sendbuffs[r] holds nranks blocks of recvcount elements, and
+ * recvbuffs[r] receives block r reduced over all ranks.  Ring index i
+ * finishes the block of rank ring_order[i]; float results follow that ring's
+ * fold order (the block starts at ring index i+1 and ring index i folds in
+ * last).  In place: recvbuffs[r] == sendbuffs[r] + r * recvcount elements;
+ * any other overlap with a receive buffer is RINGAR_ERR_INVALID_USAGE.
+ * Alignment, streams, errors, nranks == 1 and count == 0 as in
+ * ringar_allreduce; the vector path also needs recvcount * element size to
+ * be a multiple of 16 bytes.
+ */
+ringar_result_t ringar_reduce_scatter(void* const* sendbuffs, void* const* recvbuffs, size_t recvcount,
+                                      ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                      ringar_proto_t proto, ringar_stream_t stream);
+ringar_result_t ringar_reduce_scatter_ex(void* const* sendbuffs, void* const* recvbuffs, size_t recvcount,
+                                         ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                         ringar_proto_t proto, ringar_stream_t stream,
+                                         const ringar_config_t* cfg);
+
+/*
+ * Ring AllGather, the second half as a call of its own ([ARCH] §七.1; plain
+ * layout): sendbuffs[r] holds sendcount elements, and every recvbuffs[q]
+ * receives nranks blocks of sendcount elements, block r being rank r's
+ * input, bit for bit (a byte copy: the dtype only sets the element size).
+ * In place: sendbuffs[r] == recvbuffs[r] + r * sendcount elements.
+ * Otherwise as ringar_reduce_scatter.
+ */
+ringar_result_t ringar_all_gather(void* const* sendbuffs, void* const* recvbuffs, size_t sendcount,
+                                  ringar_dtype_t dtype, int nranks, int nchannels, ringar_proto_t proto,
+                                  ringar_stream_t stream);
+ringar_result_t ringar_all_gather_ex(void* const* sendbuffs, void* const* recvbuffs, size_t sendcount,
+                                     ringar_dtype_t dtype, int nranks, int nchannels, ringar_proto_t proto,
+                                     ringar_stream_t stream, const ringar_config_t* cfg);
+
 /* Host only, no GPU needed: the plan ringar_allreduce_ex would use for these
  * arguments (cfg may be NULL).  Returns the same argument errors. */
 ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
                             ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out);
+
+/* Host only: the plan of any of the three collectives; count as in its call
+ * (elements per rank, or per block for the halves).  The halves' model takes
+ * n-1 ring steps and counts all n blocks as the call's size (the pages'
+ * tuning rule for AllGather / ReduceScatter); their channel split applies to
+ * one block, and a loop takes up to one chunk of every block.  AllGather
+ * plans a byte copy: its chunk_elems, align_elems and channel_elems count
+ * bytes. */
+ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_t dtype, int nranks,
+                                 int nchannels, ringar_proto_t proto, const ringar_config_t* cfg,
+                                 ringar_plan_t* out);
 
 /* Host only: the model's fastest protocol for `bytes` per rank over nchannels
  * channels (model NULL = built-in), ties going to Simple, then LL128

@@ -93,6 +93,11 @@ def load() -> ctypes.CDLL:
     lib.ringar_allreduce.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i, i, i, i, i, vp]
     lib.ringar_allreduce_ex.argtypes = lib.ringar_allreduce.argtypes + [ctypes.POINTER(ringar_config_t)]
     lib.ringar_plan.argtypes = [sz, i, i, i, i, ctypes.POINTER(ringar_config_t), ctypes.POINTER(ringar_plan_t)]
+    lib.ringar_plan_coll.argtypes = [i] + lib.ringar_plan.argtypes
+    lib.ringar_reduce_scatter.argtypes = lib.ringar_allreduce.argtypes
+    lib.ringar_reduce_scatter_ex.argtypes = lib.ringar_allreduce_ex.argtypes
+    lib.ringar_all_gather.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i, i, i, i, vp]
+    lib.ringar_all_gather_ex.argtypes = lib.ringar_all_gather.argtypes + [ctypes.POINTER(ringar_config_t)]
     lib.ringar_select.argtypes = [sz, i, i, ctypes.POINTER(ringar_model_t), ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_double)]
     lib.ringar_default_model.argtypes = [ctypes.POINTER(ringar_model_t)]
@@ -103,7 +108,8 @@ def load() -> ctypes.CDLL:
     lib.ringar_result_string.restype = ctypes.c_char_p
     lib.ringar_last_error.argtypes = []
     lib.ringar_last_error.restype = ctypes.c_char_p
-    for name in ("ringar_allreduce", "ringar_allreduce_ex", "ringar_plan", "ringar_select",
+    for name in ("ringar_allreduce", "ringar_allreduce_ex", "ringar_plan", "ringar_select", "ringar_plan_coll",
+                 "ringar_reduce_scatter", "ringar_reduce_scatter_ex", "ringar_all_gather", "ringar_all_gather_ex",
                  "ringar_default_model", "ringar_chunk_range", "ringar_get_async_error", "ringar_release"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -157,6 +163,32 @@ def ringar_allreduce_ex(sendbuffs, recvbuffs, count, dtype, op, nranks, nchannel
                                       _enum(OPS, op), nranks, nchannels, _enum(PROTOS, proto),
                                       ctypes.c_void_p(stream or 0),
                                       ctypes.byref(cfg) if cfg is not None else None)
+
+
+COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+
+
+def ringar_reduce_scatter_ex(sendbuffs, recvbuffs, recvcount, dtype, op, nranks, nchannels, proto, stream,
+                             cfg=None) -> int:
+    return load().ringar_reduce_scatter_ex(_ptrs(sendbuffs), _ptrs(recvbuffs), recvcount, _enum(DTYPES, dtype),
+                                           _enum(OPS, op), nranks, nchannels, _enum(PROTOS, proto),
+                                           ctypes.c_void_p(stream or 0),
+                                           ctypes.byref(cfg) if cfg is not None else None)
+
+
+def ringar_all_gather_ex(sendbuffs, recvbuffs, sendcount, dtype, nranks, nchannels, proto, stream,
+                         cfg=None) -> int:
+    return load().ringar_all_gather_ex(_ptrs(sendbuffs), _ptrs(recvbuffs), sendcount, _enum(DTYPES, dtype),
+                                       nranks, nchannels, _enum(PROTOS, proto), ctypes.c_void_p(stream or 0),
+                                       ctypes.byref(cfg) if cfg is not None else None)
+
+
+def ringar_plan_coll(coll, count, dtype, nranks, nchannels=0, proto="auto", cfg=None) -> ringar_plan_t:
+    out = ringar_plan_t()
+    _check(load().ringar_plan_coll(_enum(COLLS, coll), count, _enum(DTYPES, dtype), nranks, nchannels,
+                                   _enum(PROTOS, proto), ctypes.byref(cfg) if cfg is not None else None,
+                                   ctypes.byref(out)), "ringar_plan_coll")
+    return out
 
 
 def ringar_plan(count, dtype, nranks, nchannels=0, proto="auto", cfg=None) -> ringar_plan_t:
@@ -265,3 +297,40 @@ def allreduce(sends, recvs, op="sum", nchannels=0, proto="auto", stream=None, **
     code = ringar_allreduce_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count,
                                dtype, op, n, nchannels, proto, st.cuda_stream, cfg)
     _check(code, "ringar_allreduce")
+
+
+def _tensors(sends, recvs, what, send_numel, recv_numel):
+    n = len(sends)
+    if n == 0 or len(recvs) != n:
+        raise RingarError(INVALID_ARGUMENT, f"{what} needs one send and one receive tensor per rank")
+    for t in list(sends) + list(recvs):
+        if t.dtype != sends[0].dtype or not t.is_contiguous() or not t.is_cuda:
+            raise RingarError(INVALID_ARGUMENT, "tensors must be contiguous CUDA tensors of one dtype")
+    if any(t.numel() != send_numel for t in sends) or any(t.numel() != recv_numel for t in recvs):
+        raise RingarError(INVALID_ARGUMENT, f"{what}: wrong tensor sizes")
+    return n, _torch_dtype_name(sends[0])
+
+
+def reduce_scatter(sends, recvs, op="sum", nchannels=0, proto="auto", stream=None, **cfg_kwargs) -> None:
+    """ReduceScatter over len(sends) virtual ranks: ``sends[r]`` holds n blocks
+    of ``recvs[r].numel()`` elements; ``recvs[r]`` receives block r reduced
+    over all ranks.  Enqueues on ``stream`` and returns at once."""
+    import torch
+    count = recvs[0].numel() if len(recvs) else 0
+    n, dtype = _tensors(sends, recvs, "reduce_scatter", len(sends) * count, count)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    cfg = make_config(**cfg_kwargs) if cfg_kwargs else None
+    _check(ringar_reduce_scatter_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count,
+                                    dtype, op, n, nchannels, proto, st.cuda_stream, cfg), "ringar_reduce_scatter")
+
+
+def all_gather(sends, recvs, nchannels=0, proto="auto", stream=None, **cfg_kwargs) -> None:
+    """AllGather over len(sends) virtual ranks: every ``recvs[q]`` receives n
+    blocks, block r being ``sends[r]``.  Enqueues on ``stream``."""
+    import torch
+    count = sends[0].numel() if len(sends) else 0
+    n, dtype = _tensors(sends, recvs, "all_gather", count, len(sends) * count)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    cfg = make_config(**cfg_kwargs) if cfg_kwargs else None
+    _check(ringar_all_gather_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count,
+                                dtype, n, nchannels, proto, st.cuda_stream, cfg), "ringar_all_gather")

@@ -14,9 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libringar.so")
-SOURCES = ["ring_kernel_i8.hip", "ring_kernel_i32.hip", "ring_kernel_f16.hip",
-           "ring_kernel_bf16.hip", "ring_kernel_f32.hip", "ring_kernel_f64.hip",
-           "ring_launch.hip", "ringar.cpp"]
+_TYPES = ("i8", "i32", "f16", "bf16", "f32", "f64")
+SOURCES = ([f"ring_kernel_{t}.hip" for t in _TYPES] + [f"ring_rs_{t}.hip" for t in _TYPES] +
+           ["ring_ag.hip", "ring_launch.hip", "ringar.cpp"])
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

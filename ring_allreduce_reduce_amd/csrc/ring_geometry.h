@@ -42,6 +42,7 @@ constexpr uint32_t kLL128SlotLines = 256;                  // 128-byte lines per
 constexpr uint32_t kLL128SlotBytes = kLL128SlotLines * 128;// FIFO bytes per slot
 
 enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
+enum Coll { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
 RA_HD uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 RA_HD uint64_t align_up(uint64_t a, uint64_t b) { return div_up(a, b) * b; }
@@ -130,7 +131,8 @@ RA_HD uint64_t conn_index(int c, int i, int l, int nranks, int lanes) {
 struct KernelArgs {
   const char* send[kMaxRanks];   // by ring index
   char* recv[kMaxRanks];         // by ring index
-  uint64_t count;
+  int rank_of[kMaxRanks];        // rank at ring index (blocks of the halves)
+  uint64_t count;                // elements per rank (per block in the halves)
   uint64_t per_channel;
   uint64_t chunk_elems;
   uint64_t base;                 // step base of this call (absolute counters)

@@ -5,20 +5,20 @@
 namespace ringar {
 
 template <int OP>
-static const void* by_proto_i32(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_allreduce_kernel<I32, OP, kLL, true>
-                                 : (const void*)&ring_allreduce_kernel<I32, OP, kLL, false>;
-  if (proto == kLL128) return (const void*)&ring_allreduce_kernel<I32, OP, kLL128, false>;
-  return small ? (const void*)&ring_allreduce_kernel<I32, OP, kSimple, true>
-               : (const void*)&ring_allreduce_kernel<I32, OP, kSimple, false>;
+static const void* by_proto_kernel_i32(int proto, bool small) {
+  if (proto == kLL) return small ? (const void*)&ring_kernel<I32, OP, kLL, true, kAllReduce>
+                                 : (const void*)&ring_kernel<I32, OP, kLL, false, kAllReduce>;
+  if (proto == kLL128) return (const void*)&ring_kernel<I32, OP, kLL128, false, kAllReduce>;
+  return small ? (const void*)&ring_kernel<I32, OP, kSimple, true, kAllReduce>
+               : (const void*)&ring_kernel<I32, OP, kSimple, false, kAllReduce>;
 }
 
 const void* kernel_for_i32(int op, int proto, bool small) {
   switch (op) {
-    case 0: return by_proto_i32<0>(proto, small);
-    case 1: return by_proto_i32<1>(proto, small);
-    case 2: return by_proto_i32<2>(proto, small);
-    default: return by_proto_i32<3>(proto, small);
+    case 0: return by_proto_kernel_i32<0>(proto, small);
+    case 1: return by_proto_kernel_i32<1>(proto, small);
+    case 2: return by_proto_kernel_i32<2>(proto, small);
+    default: return by_proto_kernel_i32<3>(proto, small);
   }
 }
 

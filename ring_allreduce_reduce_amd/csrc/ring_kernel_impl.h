@@ -295,7 +295,7 @@ template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4
 
 // --- Simple: one slice = one slot ------------------------------------------
 template <class E, int OP, int F>
-__device__ __forceinline__ bool slice_simple(Lane& L, uint64_t e0, uint32_t nelem) {
+__device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kRecv) {
@@ -306,9 +306,8 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t e0, uint32_t nele
   }
   rsrc_t rin = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
   rsrc_t rout = make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
-  const uint64_t boff = e0 * sizeof(typename E::T);
-  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
-  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
@@ -394,7 +393,7 @@ __device__ __forceinline__ void ll_send4(uint64_t* lout, uint32_t p, u32x4 r, ui
 }
 
 template <class E, int OP, int F>
-__device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
+__device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kSend) {
@@ -404,9 +403,8 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t e0, uint32_t nelem) {
   const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
   const uint64_t* lin = (const uint64_t*)(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes);
   uint64_t* lout = (uint64_t*)(L.out.fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes);
-  const uint64_t boff = e0 * sizeof(typename E::T);
-  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
-  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
   constexpr int U = 4;
@@ -512,7 +510,7 @@ __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, 
 }
 
 template <class E, int OP, int F>
-__device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem) {
+__device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kSend) {
@@ -524,9 +522,8 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
   char* sout = L.out.fifo + (L.sstep & (a.depth - 1)) * kLL128SlotBytes;
   rsrc_t rin = make_rsrc(sin, kLL128SlotBytes);
   rsrc_t rout = make_rsrc(sout, kLL128SlotBytes);
-  const uint64_t boff = e0 * sizeof(typename E::T);
-  rsrc_t rsrc_ = make_rsrc(L.src + boff, nbytes);
-  rsrc_t rdst = make_rsrc(L.dst + boff, nbytes);
+  rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
+  rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const bool vec = a.vec_ok;
   const uint32_t nlines = (nbytes + 119) / 120;
   const int col = L.lane & 7;
@@ -623,25 +620,25 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t e0, uint32_t nelem
 // the buffer resources, so its loads read zeros and its stores are dropped by
 // the range check.  The lane of a ragged last packet goes element-wise on the
 // user side.
-template <class E, int F>
-__device__ __forceinline__ u32x4 small_user_load(const Lane& L, uint64_t boff, uint32_t nbytes) {
+template <class E>
+__device__ __forceinline__ u32x4 small_user_load(const Lane& L, uint64_t soff, uint32_t nbytes) {
   const uint32_t nfull = nbytes / 16, p = (uint32_t)L.lane;
-  u32x4 v = ld16<kNT>(make_rsrc(L.src + boff, nfull * 16), p * 16);
+  u32x4 v = ld16<kNT>(make_rsrc(L.src + soff, nfull * 16), p * 16);
   if (nfull * 16 < nbytes && p == nfull)
-    v = ld_part<E, kNT>(make_rsrc(L.src + boff, nbytes), p * 16, nbytes - p * 16);
+    v = ld_part<E, kNT>(make_rsrc(L.src + soff, nbytes), p * 16, nbytes - p * 16);
   return v;
 }
 
-template <class E, int F>
-__device__ __forceinline__ void small_user_store(const Lane& L, uint64_t boff, uint32_t nbytes, u32x4 v) {
+template <class E>
+__device__ __forceinline__ void small_user_store(const Lane& L, uint64_t doff, uint32_t nbytes, u32x4 v) {
   const uint32_t nfull = nbytes / 16, p = (uint32_t)L.lane;
-  st16<kNT>(v, make_rsrc(L.dst + boff, nfull * 16), p * 16);
+  st16<kNT>(v, make_rsrc(L.dst + doff, nfull * 16), p * 16);
   if (nfull * 16 < nbytes && p == nfull)
-    st_part<E, kNT>(v, make_rsrc(L.dst + boff, nbytes), p * 16, nbytes - p * 16);
+    st_part<E, kNT>(v, make_rsrc(L.dst + doff, nbytes), p * 16, nbytes - p * 16);
 }
 
 template <class E, int OP, int F>
-__device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t e0, uint32_t nelem) {
+__device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kSend) {
@@ -649,11 +646,11 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t e0, uint32_t ne
   }
   const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
   const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
-  const uint64_t boff = e0 * sizeof(typename E::T);
+  const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   const bool act = p < npk;
   u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
-  if (F & kSrc) vb = small_user_load<E, F>(L, boff, nbytes);
+  if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
   if (F & kRecv) {
     const rsrc_t ri = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
     uint64_t ln[4];
@@ -680,13 +677,13 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t e0, uint32_t ne
     ll_store(ro, p * 32 + 24, r.w, fout);
     L.sstep++;
   }
-  if (F & kDst) small_user_store<E, F>(L, boff, nbytes, r);
+  if (F & kDst) small_user_store<E>(L, doff, nbytes, r);
   if (F & kRecv) release_slot(L);
   return true;
 }
 
 template <class E, int OP, int F>
-__device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t e0, uint32_t nelem) {
+__device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
   if (F & kRecv) {
@@ -695,16 +692,16 @@ __device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t e0, uint32_
   if (F & kSend) {
     if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
   }
-  const uint64_t boff = e0 * sizeof(typename E::T);
+  const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
   if (F & kRecv)
     va = ld16<kSC1>(make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
-  if (F & kSrc) vb = small_user_load<E, F>(L, boff, nbytes);
+  if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
   const u32x4 r = combine<E, OP, F>(va, vb);
   if (F & kSend)
     st16<kSC1>(r, make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
-  if (F & kDst) small_user_store<E, F>(L, boff, nbytes, r);
+  if (F & kDst) small_user_store<E>(L, doff, nbytes, r);
   if (F & kSend) {
     wait_mem();
     st_relaxed(L.out.tail, a.base + L.sstep + 1);
@@ -715,8 +712,10 @@ __device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t e0, uint32_
 }
 
 // --- a primitive over the lane's part of one chunk ------------------------
+// es0 / ed0: element offsets of the part in the source and destination user
+// buffers (equal in the AllReduce; block-relative in its two halves).
 template <class E, int OP, int PROTO, int F, bool SMALL>
-__device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) {
+__device__ __forceinline__ bool primitive(Lane& L, uint64_t es0, uint64_t ed0, uint64_t nelem) {
   if constexpr (SMALL) {
     // the host launches this form only for lane parts of at most 1 KiB
     if (nelem * sizeof(typename E::T) > kSmallSliceBytes) {
@@ -724,8 +723,8 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) 
       return false;
     }
     if (nelem == 0) return true;
-    if (PROTO == kLL) return slice_ll_small<E, OP, F>(L, e0, (uint32_t)nelem);
-    return slice_simple_small<E, OP, F>(L, e0, (uint32_t)nelem);
+    if (PROTO == kLL) return slice_ll_small<E, OP, F>(L, es0, ed0, (uint32_t)nelem);
+    return slice_simple_small<E, OP, F>(L, es0, ed0, (uint32_t)nelem);
   }
   const uint64_t cap = slot_elems(PROTO, sizeof(typename E::T));
   // The host plans parts of at most half the FIFO depth; a larger one could
@@ -737,16 +736,19 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t e0, uint64_t nelem) 
   for (uint64_t j = 0; j < nelem; j += cap) {
     uint32_t m = (uint32_t)min_u64(cap, nelem - j);
     bool ok;
-    if (PROTO == kSimple) ok = slice_simple<E, OP, F>(L, e0 + j, m);
-    else if (PROTO == kLL) ok = slice_ll<E, OP, F>(L, e0 + j, m);
-    else ok = slice_ll128<E, OP, F>(L, e0 + j, m);
+    if (PROTO == kSimple) ok = slice_simple<E, OP, F>(L, es0 + j, ed0 + j, m);
+    else if (PROTO == kLL) ok = slice_ll<E, OP, F>(L, es0 + j, ed0 + j, m);
+    else ok = slice_ll128<E, OP, F>(L, es0 + j, ed0 + j, m);
     if (!ok) return false;
   }
   return true;
 }
 
-template <class E, int OP, int PROTO, bool SMALL>
-__global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a) {
+// One launch of a ring collective: every (ring index, channel, lane)
+// wavefront of every virtual rank.  COLL: kAllReduce (2n-1 stages per loop),
+// kReduceScatter or kAllGather (n stages per loop, whole blocks by rank).
+template <class E, int OP, int PROTO, bool SMALL, int COLL>
+__global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const int wave = threadIdx.x >> 6;
   const int group = blockIdx.x / a.nranks;     // (channel, lane block)
@@ -779,24 +781,51 @@ __global__ void __launch_bounds__(256) ring_allreduce_kernel(const KernelArgs a)
   uint64_t lo, hi;
   channel_bounds(a.count, a.per_channel, c, &lo, &hi);
   const uint64_t len = hi - lo;
-  const uint64_t loop = (uint64_t)n * a.chunk_elems;
-  for (uint64_t off = 0; off < len; off += loop) {
-    const uint64_t rem = len - off;
-    const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
-    const uint64_t part = lane_part(cur, a.lanes, es);
-    for (int s = 0; s <= 2 * n - 2; s++) {
-      const int k = stage_chunk(ri, s, n);
-      uint64_t ks, kl, ls, ll;
-      chunk_bounds(rem, cur, k, &ks, &kl);
-      lane_bounds(kl, part, l, &ls, &ll);
-      const uint64_t e0 = lo + off + ks + ls;
-      bool ok;
-      if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, e0, ll);
-      else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, e0, ll);
-      else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst, SMALL>(L, e0, ll);
-      else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, e0, ll);
-      else ok = primitive<E, OP, PROTO, kRecv | kDst, SMALL>(L, e0, ll);
-      if (!ok) return;
+  if constexpr (COLL == kAllReduce) {
+    const uint64_t loop = (uint64_t)n * a.chunk_elems;
+    for (uint64_t off = 0; off < len; off += loop) {
+      const uint64_t rem = len - off;
+      const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
+      const uint64_t part = lane_part(cur, a.lanes, es);
+      for (int s = 0; s <= 2 * n - 2; s++) {
+        const int k = stage_chunk(ri, s, n);
+        uint64_t ks, kl, ls, ll;
+        chunk_bounds(rem, cur, k, &ks, &kl);
+        lane_bounds(kl, part, l, &ls, &ll);
+        const uint64_t e0 = lo + off + ks + ls;
+        bool ok;
+        if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, e0, e0, ll);
+        else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, e0, e0, ll);
+        else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst, SMALL>(L, e0, e0, ll);
+        else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, e0, e0, ll);
+        else ok = primitive<E, OP, PROTO, kRecv | kDst, SMALL>(L, e0, e0, ll);
+        if (!ok) return;
+      }
+    }
+  } else {
+    // The halves: a.count is the block length; a loop takes up to one chunk
+    // of every block, and the block of rank q starts at q * a.count.
+    for (uint64_t off = 0; off < len; off += a.chunk_elems) {
+      const uint64_t cur = min_u64(a.chunk_elems, len - off);
+      const uint64_t part = lane_part(cur, a.lanes, es);
+      uint64_t ls, ll;
+      lane_bounds(cur, part, l, &ls, &ll);
+      const uint64_t pos = lo + off + ls;           // element offset inside a block
+      for (int s = 0; s <= n - 1; s++) {
+        const int k = COLL == kReduceScatter ? stage_chunk(ri, s, n) : (ri - s + n) % n;
+        const uint64_t blk = (uint64_t)a.rank_of[k] * a.count + pos;
+        bool ok;
+        if (COLL == kReduceScatter) {
+          if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, blk, 0, ll);
+          else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, blk, 0, ll);
+          else ok = primitive<E, OP, PROTO, kRecv | kSrc | kDst, SMALL>(L, blk, pos, ll);
+        } else {
+          if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend | kDst, SMALL>(L, pos, blk, ll);
+          else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, 0, blk, ll);
+          else ok = primitive<E, OP, PROTO, kRecv | kDst, SMALL>(L, 0, blk, ll);
+        }
+        if (!ok) return;
+      }
     }
   }
 }

@@ -1,4 +1,4 @@
-// Kernel dispatch by (dtype, op, protocol), occupancy query and the fill
+// Kernel dispatch by (collective, dtype, op, protocol, form), occupancy query and the fill
 // kernel that clears FIFO memory and counters.
 #include <hip/hip_runtime.h>
 
@@ -13,9 +13,27 @@ const void* kernel_for_f16(int op, int proto, bool small);
 const void* kernel_for_bf16(int op, int proto, bool small);
 const void* kernel_for_f32(int op, int proto, bool small);
 const void* kernel_for_f64(int op, int proto, bool small);
+const void* kernel_rs_for_i8(int op, int proto, bool small);
+const void* kernel_rs_for_i32(int op, int proto, bool small);
+const void* kernel_rs_for_f16(int op, int proto, bool small);
+const void* kernel_rs_for_bf16(int op, int proto, bool small);
+const void* kernel_rs_for_f32(int op, int proto, bool small);
+const void* kernel_rs_for_f64(int op, int proto, bool small);
+const void* kernel_ag_for(int proto, bool small);
 
-const void* kernel_for(int dtype, int op, int proto, bool small) {
+const void* kernel_for(int coll, int dtype, int op, int proto, bool small) {
   small = small && proto != kLL128;
+  if (coll == kAllGather) return kernel_ag_for(proto, small);
+  if (coll == kReduceScatter) {
+    switch (dtype) {
+      case 0: return kernel_rs_for_i8(op, proto, small);
+      case 1: return kernel_rs_for_i32(op, proto, small);
+      case 2: return kernel_rs_for_f16(op, proto, small);
+      case 3: return kernel_rs_for_bf16(op, proto, small);
+      case 4: return kernel_rs_for_f32(op, proto, small);
+      default: return kernel_rs_for_f64(op, proto, small);
+    }
+  }
   switch (dtype) {
     case 0: return kernel_for_i8(op, proto, small);
     case 1: return kernel_for_i32(op, proto, small);
@@ -26,14 +44,16 @@ const void* kernel_for(int dtype, int op, int proto, bool small) {
   }
 }
 
-hipError_t launch_ring(int dtype, int op, int proto, bool small, const KernelArgs& args, int grid,
-                       int block, hipStream_t stream) {
+hipError_t launch_ring(int coll, int dtype, int op, int proto, bool small, const KernelArgs& args,
+                       int grid, int block, hipStream_t stream) {
   void* params[] = {const_cast<KernelArgs*>(&args)};
-  return hipLaunchKernel(kernel_for(dtype, op, proto, small), dim3(grid), dim3(block), params, 0, stream);
+  return hipLaunchKernel(kernel_for(coll, dtype, op, proto, small), dim3(grid), dim3(block), params, 0,
+                         stream);
 }
 
-hipError_t max_active_blocks(int dtype, int op, int proto, bool small, int block, int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel_for(dtype, op, proto, small), block, 0);
+hipError_t max_active_blocks(int coll, int dtype, int op, int proto, bool small, int block, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel_for(coll, dtype, op, proto, small),
+                                                      block, 0);
 }
 
 // Writes `value` into `words` 64-bit words (plain vector stores).  A kernel,

@@ -50,6 +50,7 @@ size_t elem_size(int dtype) {
 const char* kProtoName[3] = {"LL", "LL128", "Simple"};
 const char* kDtypeName[6] = {"int8", "int32", "float16", "bfloat16", "float32", "float64"};
 const char* kOpName[4] = {"sum", "prod", "min", "max"};
+const char* kCollName[3] = {"AllReduce", "ReduceScatter", "AllGather"};
 
 // ---------------------------------------------------------------- env
 // RINGAR_* variables, each read once ([BOOK] §3.5: a parameter is read from
@@ -141,9 +142,11 @@ double bus_bw(const ringar_model_t& m, int nch, int p) {
 }
 
 // Predicted microseconds of one call ([ARCH] §八.1-八.2):
-// base + 2(n-1) step latencies + bytes / (1000 x bus bandwidth x n / (2(n-1))).
-double predict_us(const ringar_model_t& m, int n, int nch, int p, size_t bytes) {
-  double nsteps = 2.0 * (n - 1);
+// base + nsteps step latencies + bytes / (1000 x bus bandwidth x n / nsteps),
+// with nsteps = 2(n-1) for the AllReduce and n-1 for its halves, whose
+// `bytes` count the whole n-block buffer (the tuning model's rule).
+double predict_us(const ringar_model_t& m, int n, int nch, int p, size_t bytes, int coll = kAllReduce) {
+  double nsteps = (coll == kAllReduce ? 2.0 : 1.0) * (n - 1);
   double alg = bus_bw(m, nch, p) * n / nsteps;
   double lat = m.base_lat_us[p] + nsteps * m.hw_lat_us[p];
   return lat + (double)bytes / (1000.0 * alg);
@@ -157,11 +160,12 @@ int model_max_channels(const ringar_model_t& m, int n) {
 // Fastest enabled protocol.  Candidates are visited Simple, LL128, LL (the
 // pages' list is built by pushing to the front) and replaced only on a
 // strictly smaller time, so ties go to Simple, then LL128.
-int select_proto(const ringar_model_t& m, int n, int nch, size_t bytes, int mask, double* times) {
+int select_proto(const ringar_model_t& m, int n, int nch, size_t bytes, int mask, double* times,
+                 int coll = kAllReduce) {
   int best = -1;
   double best_t = INFINITY;
   for (int p = 2; p >= 0; p--) {
-    double t = predict_us(m, n, nch, p, bytes);
+    double t = predict_us(m, n, nch, p, bytes, coll);
     if (times) times[p] = t;
     if (!(mask & (1 << p))) continue;
     if (t < best_t) { best = p; best_t = t; }
@@ -216,7 +220,9 @@ uint64_t fifo_bytes_for(int proto, uint64_t bytes) {
 
 // capacity_waves: wavefronts of this kernel the GPU holds at once (0 when no
 // GPU is visible: then 4096 is assumed).
-ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int proto,
+// coll: kAllReduce (count = elements per rank) or one of its halves (count =
+// elements per block; AllGather plans bytes, dtype int8).
+ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannels, int proto,
                           const ringar_config_t* cfg, uint64_t capacity_waves, Plan* out) {
   const Env& E = env();
   const size_t es = elem_size(dtype);
@@ -234,11 +240,12 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   if (depth && (!is_pow2(depth) || depth < kMinSteps || depth > kMaxSteps)) return RINGAR_ERR_INVALID_ARGUMENT;
 
   Plan P;
-  const size_t bytes = count * es;
+  const bool halves = coll != kAllReduce;
+  const size_t bytes = count * es * (halves ? (size_t)n : 1);
   int maxc = model_max_channels(m, n);
   if (E.max_nchannels > 0) maxc = std::min(maxc, E.max_nchannels);
   const int model_nch = nchannels > 0 ? nchannels : maxc;
-  int best = select_proto(m, n, model_nch, bytes, E.proto_mask, P.times);
+  int best = select_proto(m, n, model_nch, bytes, E.proto_mask, P.times, coll);
   P.proto = proto >= 0 ? proto : (n == 1 ? (int)kSimple : best);
   P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc));
   P.chunk_bytes = chunk_bytes ? chunk_bytes : m.default_chunk_bytes[P.proto];
@@ -258,8 +265,10 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   // lanes, 4096 wavefronts, ran 11% faster than 16 lanes) and never more
   // than the GPU holds at once (all of them wait on each other).  Lanes
   // change no result.
+  // (The halves' loops take up to one chunk of every block.)
   const uint64_t first_chunk =
-      P.per_channel >= (uint64_t)n * P.chunk_elems
+      halves ? std::max<uint64_t>(1, std::min<uint64_t>(P.chunk_elems, P.per_channel))
+      : P.per_channel >= (uint64_t)n * P.chunk_elems
           ? P.chunk_elems
           : align_up(div_up(std::max<uint64_t>(1, P.per_channel), (uint64_t)n), align_elems((uint32_t)es));
   const uint64_t slot = slot_elems(P.proto, (uint32_t)es);
@@ -302,8 +311,9 @@ ringar_result_t make_plan(size_t count, int dtype, int n, int nchannels, int pro
   P.grid = n * groups;
 
   // Upper bound of FIFO steps any connection takes in this call.
-  const uint64_t loops = std::max<uint64_t>(1, div_up(P.per_channel, (uint64_t)n * P.chunk_elems));
-  P.max_steps = loops * (uint64_t)(2 * n - 1) * (slices_for(lanes) + 1);
+  const uint64_t loops =
+      std::max<uint64_t>(1, div_up(P.per_channel, (halves ? 1 : (uint64_t)n) * P.chunk_elems));
+  P.max_steps = loops * (uint64_t)(halves ? n : 2 * n - 1) * (slices_for(lanes) + 1);
   *out = P;
   return RINGAR_SUCCESS;
 }
@@ -382,7 +392,7 @@ ringar_result_t reset_steps(Resources& R, hipStream_t st) {
 
 // Resident wavefronts of the (dtype, op, proto) kernel on the current device,
 // or 0 when no device is visible.  Cached per device and kernel.
-uint64_t capacity_waves(int dtype, int op, int proto) {
+uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   static const int ndev = [] {
     int c = 0;
     if (hipGetDeviceCount(&c) != hipSuccess) {
@@ -394,7 +404,7 @@ uint64_t capacity_waves(int dtype, int op, int proto) {
   if (ndev == 0) return 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const long long key = (((long long)dev * 8 + dtype) * 4 + op) * 3 + proto;
+  const long long key = ((((long long)dev * 3 + coll) * 8 + dtype) * 4 + op) * 3 + proto;
   // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
@@ -402,7 +412,7 @@ uint64_t capacity_waves(int dtype, int op, int proto) {
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      max_active_blocks(dtype, op, proto, false, 256, &per_cu) != hipSuccess)
+      max_active_blocks(coll, dtype, op, proto, false, 256, &per_cu) != hipSuccess)
     return 0;
   uint64_t w = (uint64_t)cus * (uint64_t)per_cu * 4;   // 4 wavefronts per 256-thread block
   cache.emplace(key, w);
@@ -411,21 +421,34 @@ uint64_t capacity_waves(int dtype, int op, int proto) {
 
 bool overlaps(uintptr_t a, uintptr_t b, size_t len) { return a < b + len && b < a + len; }
 
-ringar_result_t check_buffers(void* const* sb, void* const* rb, size_t count, size_t es, int n) {
+// Buffers of rank r: send [sb[r], + slen), receive [rb[r], + rlen), both
+// aligned to the element size.  Receive buffers must not overlap each other
+// or any send buffer, except that a rank's buffers may share its own block
+// in the collective's in-place form: receive == send for the AllReduce,
+// receive == send + r * rlen for ReduceScatter, send == receive + r * slen
+// for AllGather.  Send buffers may overlap each other (they are only read).
+ringar_result_t check_buffers(int coll, void* const* sb, void* const* rb, size_t count, size_t es, int n) {
   if (!sb || !rb) return RINGAR_ERR_INVALID_ARGUMENT;
   for (int r = 0; r < n; r++) {
     if (!sb[r] || !rb[r]) return RINGAR_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)sb[r] % es) || ((uintptr_t)rb[r] % es)) return RINGAR_ERR_INVALID_ARGUMENT;
   }
   const size_t len = count * es;
-  // A receive buffer may only coincide exactly with its own rank's send
-  // buffer (in place); send buffers may overlap each other (read only).
+  const size_t slen = coll == kReduceScatter ? (size_t)n * len : len;
+  const size_t rlen = coll == kAllGather ? (size_t)n * len : len;
   for (int r = 0; r < n; r++) {
-    uintptr_t rr = (uintptr_t)rb[r];
+    const uintptr_t rr = (uintptr_t)rb[r];
     for (int q = 0; q < n; q++) {
-      if (q != r && overlaps(rr, (uintptr_t)rb[q], len)) return RINGAR_ERR_INVALID_USAGE;
-      uintptr_t sq = (uintptr_t)sb[q];
-      if (overlaps(rr, sq, len) && !(q == r && rr == sq)) return RINGAR_ERR_INVALID_USAGE;
+      const uintptr_t rq = (uintptr_t)rb[q], sq = (uintptr_t)sb[q];
+      if (q != r && rr < rq + rlen && rq < rr + rlen) return RINGAR_ERR_INVALID_USAGE;
+      if (!(rr < sq + slen && sq < rr + rlen)) continue;
+      bool in_place = false;
+      if (q == r) {
+        if (coll == kAllReduce) in_place = rr == sq;
+        else if (coll == kReduceScatter) in_place = rr == sq + (uintptr_t)r * len;
+        else in_place = sq == rr + (uintptr_t)r * len;
+      }
+      if (!in_place) return RINGAR_ERR_INVALID_USAGE;
     }
   }
   return RINGAR_SUCCESS;
@@ -491,21 +514,38 @@ ringar_result_t ringar_select(size_t bytes, int nranks, int nchannels, const rin
   return RINGAR_SUCCESS;
 }
 
-ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
-                            ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out) {
-  if (!out) return RINGAR_ERR_INVALID_ARGUMENT;
-  Plan P;
-  const int p_guess = proto >= 0 ? (int)proto : -1;
-  uint64_t cap = 0;
-  if ((int)dtype >= 0 && (int)dtype <= 5) {
-    // the protocol is needed for the capacity; resolve it first without one
-    Plan Q;
-    if (make_plan(count, dtype, nranks, nchannels, proto, cfg, 0, &Q) == RINGAR_SUCCESS)
-      cap = capacity_waves(dtype, 0, p_guess >= 0 ? p_guess : Q.proto);
-  }
-  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, cap, &P);
-  if (r != RINGAR_SUCCESS) return r;
+// The (count, dtype) a collective's kernels work on: AllGather is a byte copy.
+static void kernel_shape(int coll, size_t count, int dtype, size_t* kcount, int* kdtype) {
   const size_t es = elem_size(dtype);
+  *kcount = coll == kAllGather ? count * es : count;
+  *kdtype = coll == kAllGather ? (int)RINGAR_INT8 : dtype;
+}
+
+// The plan a launch uses: first without, then with the kernel's residency.
+static ringar_result_t plan_for_launch(int coll, size_t count, int dtype, int op, int nranks, int nchannels,
+                                int proto, const ringar_config_t* cfg, Plan* P) {
+  ringar_result_t r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, 0, P);
+  if (r != RINGAR_SUCCESS) return r;
+  if (count > 0 && nranks > 1) {
+    const uint64_t cap = capacity_waves(coll, dtype, op, P->proto);
+    if (cap && (r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, cap, P)) != RINGAR_SUCCESS)
+      return r;
+  }
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_t dtype, int nranks,
+                                 int nchannels, ringar_proto_t proto, const ringar_config_t* cfg,
+                                 ringar_plan_t* out) {
+  if (!out || coll < RINGAR_ALLREDUCE || coll > RINGAR_ALL_GATHER) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (!elem_size(dtype)) return RINGAR_ERR_INVALID_ARGUMENT;
+  size_t kcount;
+  int kdtype;
+  kernel_shape(coll, count, dtype, &kcount, &kdtype);
+  Plan P;
+  ringar_result_t r = plan_for_launch(coll, kcount, kdtype, 0, nranks, nchannels, proto, cfg, &P);
+  if (r != RINGAR_SUCCESS) return r;
+  const size_t es = elem_size(kdtype);
   out->proto = (ringar_proto_t)P.proto;
   out->nchannels = P.nch;
   out->chunk_bytes = P.chunk_bytes;
@@ -520,6 +560,11 @@ ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int 
   out->max_steps = P.max_steps;
   for (int p = 0; p < 3; p++) out->predicted_us[p] = P.times[p];
   return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
+                            ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out) {
+  return ringar_plan_coll(RINGAR_ALLREDUCE, count, dtype, nranks, nchannels, proto, cfg, out);
 }
 
 ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
@@ -545,30 +590,31 @@ ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nrank
   return RINGAR_SUCCESS;
 }
 
-ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuffs, size_t count,
-                                    ringar_dtype_t dtype, ringar_op_t op, int nranks,
-                                    int nchannels, ringar_proto_t proto, ringar_stream_t stream,
-                                    const ringar_config_t* cfg) {
-  const size_t es = elem_size(dtype);
-  if (!es || op < RINGAR_SUM || op > RINGAR_MAX) return RINGAR_ERR_INVALID_ARGUMENT;
+// One ring collective.  count: elements per rank for the AllReduce, per
+// block for ReduceScatter (recvcount) and AllGather (sendcount).
+static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                               int udtype, int op, int nranks, int nchannels, int proto,
+                               ringar_stream_t stream, const ringar_config_t* cfg) {
+  const size_t ues = elem_size(udtype);
+  if (!ues || op < RINGAR_SUM || op > RINGAR_MAX) return RINGAR_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
+  size_t kcount;
+  int dtype;
+  kernel_shape(coll, count, udtype, &kcount, &dtype);
+  const size_t es = elem_size(dtype);
   Plan P;
-  ringar_result_t r = make_plan(count, dtype, nranks, nchannels, proto, cfg, 0, &P);
+  ringar_result_t r = plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, cfg, &P);
   if (r != RINGAR_SUCCESS) return r;
-  if (count > 0 && nranks > 1) {
-    const uint64_t cap = capacity_waves(dtype, op, P.proto);
-    if (cap && (r = make_plan(count, dtype, nranks, nchannels, proto, cfg, cap, &P)) != RINGAR_SUCCESS)
-      return r;
-  }
   if (cfg && (r = check_ring(cfg->ring_order, nranks)) != RINGAR_SUCCESS) return r;
   if (count == 0) return RINGAR_SUCCESS;                      // no-op, nothing enqueued
-  if ((r = check_buffers(sendbuffs, recvbuffs, count, es, nranks)) != RINGAR_SUCCESS) return r;
+  if ((r = check_buffers(coll, sendbuffs, recvbuffs, count, ues, nranks)) != RINGAR_SUCCESS) return r;
   hipStream_t st = (hipStream_t)stream;
   if (nranks == 1) {                                          // one rank: a local copy
     if (sendbuffs[0] != recvbuffs[0])
-      HIP_TRY(hipMemcpyAsync(recvbuffs[0], sendbuffs[0], count * es, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpyAsync(recvbuffs[0], sendbuffs[0], count * ues, hipMemcpyDeviceToDevice, st));
     return RINGAR_SUCCESS;
   }
+  count = kcount;
 
   std::lock_guard<std::mutex> lock(g_mu);
   Resources* R = nullptr;
@@ -576,15 +622,18 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
 
   // All (rank, channel, lane) wavefronts wait on each other, so the whole
   // grid must be resident at once.
-  int vec = 1;
+  // The vector path needs every user address 16-byte aligned, including the
+  // block starts of the halves.
+  int vec = (coll == kAllReduce || (count * es) % 16 == 0) ? 1 : 0;
   for (int q = 0; q < nranks; q++)
     if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   const bool small = P.small && vec;
-  const long long okey = (((long long)(dtype * 4 + op) * 3 + P.proto) * 2 + small) * 1024 + P.block;
+  const long long okey =
+      ((((long long)coll * 8 + dtype) * 4 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;
-    HIP_TRY(max_active_blocks(dtype, op, P.proto, small, P.block, &per_cu));
+    HIP_TRY(max_active_blocks(coll, dtype, op, P.proto, small, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
   if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
@@ -602,6 +651,7 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
     int rank = ring ? ring[i] : i;
     A.send[i] = (const char*)sendbuffs[rank];
     A.recv[i] = (char*)recvbuffs[rank];
+    A.rank_of[i] = rank;
   }
   A.count = count;
   A.per_channel = P.per_channel;
@@ -626,17 +676,54 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
   }
   A.vec_ok = vec;
 
-  HIP_TRY(launch_ring(dtype, op, P.proto, small, A, P.grid, P.block, st));
+  HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, A, P.grid, P.block, st));
   R->base += P.max_steps + 1;
 
   if (env().debug) {
     fprintf(stderr,
-            "ringar: AllReduce %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
+            "ringar: %s %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
             "depth %d%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
-            count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
+            kCollName[coll], count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
             P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", P.grid, P.block, P.times[0], P.times[1], P.times[2]);
   }
   return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                    ringar_dtype_t dtype, ringar_op_t op, int nranks,
+                                    int nchannels, ringar_proto_t proto, ringar_stream_t stream,
+                                    const ringar_config_t* cfg) {
+  return run_collective(kAllReduce, sendbuffs, recvbuffs, count, dtype, op, nranks, nchannels, proto,
+                        stream, cfg);
+}
+
+ringar_result_t ringar_reduce_scatter_ex(void* const* sendbuffs, void* const* recvbuffs, size_t recvcount,
+                                         ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                         ringar_proto_t proto, ringar_stream_t stream,
+                                         const ringar_config_t* cfg) {
+  return run_collective(kReduceScatter, sendbuffs, recvbuffs, recvcount, dtype, op, nranks, nchannels,
+                        proto, stream, cfg);
+}
+
+ringar_result_t ringar_reduce_scatter(void* const* sendbuffs, void* const* recvbuffs, size_t recvcount,
+                                      ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                      ringar_proto_t proto, ringar_stream_t stream) {
+  return ringar_reduce_scatter_ex(sendbuffs, recvbuffs, recvcount, dtype, op, nranks, nchannels, proto,
+                                  stream, nullptr);
+}
+
+ringar_result_t ringar_all_gather_ex(void* const* sendbuffs, void* const* recvbuffs, size_t sendcount,
+                                     ringar_dtype_t dtype, int nranks, int nchannels, ringar_proto_t proto,
+                                     ringar_stream_t stream, const ringar_config_t* cfg) {
+  return run_collective(kAllGather, sendbuffs, recvbuffs, sendcount, dtype, RINGAR_SUM, nranks, nchannels,
+                        proto, stream, cfg);
+}
+
+ringar_result_t ringar_all_gather(void* const* sendbuffs, void* const* recvbuffs, size_t sendcount,
+                                  ringar_dtype_t dtype, int nranks, int nchannels, ringar_proto_t proto,
+                                  ringar_stream_t stream) {
+  return ringar_all_gather_ex(sendbuffs, recvbuffs, sendcount, dtype, nranks, nchannels, proto, stream,
+                              nullptr);
 }
 
 ringar_result_t ringar_allreduce(void* const* sendbuffs, void* const* recvbuffs, size_t count,

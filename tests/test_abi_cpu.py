@@ -258,3 +258,80 @@ def test_small_form_rule():
                     assert plan.small_slices == 1, (proto, count, nch, plan.lanes)
     cfg = ra.make_config(force_general=1)
     assert ra.ringar_plan(4096, "float32", 8, 1, "LL", cfg).small_slices == 0
+
+
+def test_halves_buffer_rules_before_any_device_call():
+    n, count = 4, 1000
+    E = ra
+    blk = count * 4
+    # ReduceScatter: sends hold n blocks, receives one
+    s = _fake(n, step=1 << 24)
+    r = _fake(n, base=1 << 40, step=1 << 24)
+    rs = lambda s_, r_, c=count: ra.ringar_reduce_scatter_ex(s_, r_, c, "float32", "sum", n, 2, "Simple", 0)
+    assert rs(s, [0] * n) == E.INVALID_ARGUMENT
+    assert rs(s, r, 0) == E.SUCCESS
+    r_ip = [s[q] + q * blk for q in range(n)]            # in place: own block of own input
+    assert ra.ringar_plan_coll("reduce_scatter", count, "float32", n, 2, "Simple").nchannels == 2
+    r_bad = list(r_ip)
+    r_bad[1] = s[1]                                      # rank 1's output on block 0 of its input
+    assert rs(s, r_bad) == E.INVALID_USAGE
+    r_bad = list(r)
+    r_bad[2] = s[0] + 3 * blk                            # inside another rank's input
+    assert rs(s, r_bad) == E.INVALID_USAGE
+    r_bad = list(r)
+    r_bad[3] = r[0] + 8                                  # two outputs overlap
+    assert rs(s, r_bad) == E.INVALID_USAGE
+    # AllGather: sends hold one block, receives n
+    ag = lambda s_, r_: ra.ringar_all_gather_ex(s_, r_, count, "float32", n, 2, "Simple", 0)
+    s_ip = [r[q] + q * blk for q in range(n)]            # in place: own block of own output
+    s_bad = list(s_ip)
+    s_bad[2] = r[2]
+    assert ag(s_bad, r) == E.INVALID_USAGE
+    s_bad = list(s)
+    s_bad[0] = r[1] + 4 * blk - 16                       # inside another rank's output
+    assert ag(s_bad, r) == E.INVALID_USAGE
+    r_bad = list(r)
+    r_bad[1] = r[0] + blk                                # outputs of n blocks overlap
+    assert ag(s, r_bad) == E.INVALID_USAGE
+    s_mis = list(s)
+    s_mis[0] += 2
+    assert ag(s_mis, r) == E.INVALID_ARGUMENT
+    assert ra.ringar_all_gather_ex(s, r, count, "float32", 0, 2, "Simple", 0) == E.INVALID_ARGUMENT
+
+
+def test_halves_plan_rule():
+    # n-1 ring steps and all n blocks counted as the call's size; the channel
+    # split applies to one block; AllGather plans bytes
+    m = golden_model_dict()
+    for coll in ("reduce_scatter", "all_gather"):
+        for count in [1, 1000, 1 << 16, 1 << 20, 1 << 24]:
+            for n in (2, 8):
+                plan = ra.ringar_plan_coll(coll, count, "float32", n)
+                total = n * count * 4
+                maxc = min(m["max_channels"], m["max_pairs"] // n)
+                times = [_halves_time(m, n, maxc, p, total) for p in range(3)]
+                assert plan.predicted_us[:] == pytest.approx(times, rel=1e-12)
+                best = min(range(3), key=lambda p: (times[p], -p))
+                assert plan.proto == best, (coll, count, n)
+                es = 1 if coll == "all_gather" else 4
+                per = -(-(count * 4 // es) // plan.nchannels)
+                per = -(-per // (16 // es)) * (16 // es)
+                assert plan.channel_elems == per
+                loops = max(1, -(-per // plan.chunk_elems))
+                assert plan.max_steps % (loops * n) == 0
+    # the AllReduce plan is unchanged by the new entry point
+    a = ra.ringar_plan(1 << 20, "float32", 8)
+    b = ra.ringar_plan_coll("allreduce", 1 << 20, "float32", 8)
+    assert (a.proto, a.nchannels, a.lanes, a.max_steps) == (b.proto, b.nchannels, b.lanes, b.max_steps)
+
+
+def _halves_time(m, n, nch, p, nbytes):
+    bus = nch * m["bw_per_channel"]
+    if p == 0:
+        bus = min(m["ll_max_bw"], bus * m["eff"][0])
+    elif p == 1:
+        bus = min(bus * m["eff"][1], nch * m["ll128_per_channel_max_bw"])
+    else:
+        bus *= m["eff"][2]
+    steps = n - 1
+    return m["base_lat_us"][p] + steps * m["hw_lat_us"][p] + nbytes / (1000.0 * bus * n / steps)
