@@ -1,12 +1,13 @@
-"""CPU oracle for the ring AllReduce and its two halves (ReduceScatter,
-AllGather): test infrastructure only.
+"""CPU oracle for the ring AllReduce, its two halves (ReduceScatter,
+AllGather) and the double-binary-tree AllReduce: test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never imports,
 links or calls it, and it imports nothing from the product.
 
 ``ring_oracle.c`` is the reduction itself (a sequential simulation of the ring
-schedule, see its header for the passages it follows); ``select.py`` is the
+schedule, and of the tree's reduce-up / broadcast-down passes; see its
+comments for the passages they follow); ``select.py`` is the
 alpha-beta protocol model.  This module builds the C file with gcc and wraps it
 with ctypes over numpy arrays.  bfloat16 arrays are carried as raw ``uint16``
 bit patterns, since numpy has no bfloat16 type.
@@ -68,6 +69,15 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_ring_all_gather.argtypes = [
         ctypes.c_int, sz, sz, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.oracle_ring_all_gather.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_btree.argtypes = [ctypes.c_int, ctypes.c_int, ip, ip, ip]
+    lib.oracle_btree.restype = None
+    lib.oracle_dtree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ip, ip, ip]
+    lib.oracle_dtree.restype = None
+    lib.oracle_tree_allreduce.argtypes = [
+        ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz,
+        ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.oracle_tree_allreduce.restype = ctypes.c_int
     for name in ("oracle_f16_decode_array", "oracle_bf16_decode_array",
                  "oracle_f16_encode_array", "oracle_bf16_encode_array"):
         getattr(lib, name).argtypes = [vp, vp, sz]
@@ -166,6 +176,43 @@ def ring_all_gather(xs, dtype: str, ring=None, lib: ctypes.CDLL | None = None, o
     rp = (ctypes.c_int * n)(*[int(r) for r in ring]) if ring is not None else None
     if lib.oracle_ring_all_gather(n, count, esize, rp, xp, yp) != 0:
         raise ValueError("oracle_ring_all_gather rejected its arguments")
+    return ys
+
+
+def btree(n: int, rank: int, lib: ctypes.CDLL | None = None) -> tuple[int, int, int]:
+    """(parent, child slot 0, child slot 1) of ``rank`` in the binary tree
+    over n ranks; -1 = none."""
+    lib = lib or load()
+    u, a, b = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.oracle_btree(n, rank, ctypes.byref(u), ctypes.byref(a), ctypes.byref(b))
+    return u.value, a.value, b.value
+
+
+def dtree(n: int, rank: int, tree: int, lib: ctypes.CDLL | None = None) -> tuple[int, int, int]:
+    """(parent, child slot 0, child slot 1) of ``rank`` in tree 0 or 1 of the
+    double binary tree over n ranks; -1 = none."""
+    lib = lib or load()
+    u, a, b = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.oracle_dtree(n, rank, tree, ctypes.byref(u), ctypes.byref(a), ctypes.byref(b))
+    return u.value, a.value, b.value
+
+
+def tree_allreduce(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
+                   lib: ctypes.CDLL | None = None, out=None):
+    """Tree AllReduce of the n input arrays ``xs`` over the double binary tree
+    (channel c on tree c mod 2).  Returns the n outputs (fresh ones unless
+    ``out`` is given; ``out`` may be ``xs`` for the in-place form)."""
+    lib = lib or load()
+    code, npt, _ = DTYPES[dtype]
+    n = len(xs)
+    xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
+    count = xs[0].size if n else 0
+    assert all(x.size == count for x in xs)
+    ys = out if out is not None else [_sentinel(count, npt) for _ in range(n)]
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    if lib.oracle_tree_allreduce(n, count, code, OPS[op], nchannels, chunk_elems, xp, yp) != 0:
+        raise ValueError("oracle_tree_allreduce rejected its arguments")
     return ys
 
 

@@ -482,6 +482,143 @@ int oracle_ring_all_gather(int nranks, size_t count, size_t esize, const int* ri
   return rc;
 }
 
+/* ---------------------------------------------------------------------
+ * Tree AllReduce over a double binary tree ([ARCH] §五.4 "double binary
+ * tree", §九.1 and §九.4: Tree all_reduce first reduces up the tree to the
+ * root, then the root broadcasts the result back down; [BOOK] ch. 4 of the
+ * Japanese edition, ncclGetBtree / ncclGetDtree).  Every virtual rank is one
+ * vertex of the tree (one rank per node, so there is no intra-node chain).
+ *
+ * Readings where the pages are silent:
+ *   - the two trees each carry half of the data: channel c runs on tree
+ *     c mod 2 (with one channel, tree 0 carries everything);
+ *   - a vertex folds its own input first and then its children in child-slot
+ *     order: acc = x; acc = op(P(child 0), acc); acc = op(P(child 1), acc),
+ *     with op(received, local) as on the ring;
+ *   - the odd-n second tree shifts every rank by one: it is the binary tree
+ *     of rank (r - 1) mod n with every rank it names moved back by +1 mod n;
+ *   - channels split the buffer as on the ring, and each channel's range is
+ *     cut into chunks of chunk_elems elements (the last one shorter); a
+ *     chunk goes all the way up and down before the next one.
+ * --------------------------------------------------------------------- */
+
+/*
+ * Binary tree over ranks 0..n-1 (the pages' bit construction).  For a rank
+ * r > 0 let b be its lowest set bit.  The parent clears b and sets the next
+ * higher bit; if that is not a rank, it only clears b.  Children are r - b/2
+ * (slot 0) and r + h (slot 1) for the largest h in b/2, b/4, ..., 1 with
+ * r + h < n; a rank with b == 1 is a leaf.  Rank 0 is the root: its only
+ * child (slot 1) is B/2, B the smallest power of two >= n.  -1 = none.
+ */
+void oracle_btree(int n, int r, int* up, int* down0, int* down1) {
+  int b = 1;
+  while (b < n && (r & b) == 0) b <<= 1;   /* r's lowest set bit (r = 0: B) */
+  if (r == 0) {
+    *up = -1;
+    *down0 = -1;
+    *down1 = n > 1 ? b / 2 : -1;
+    return;
+  }
+  int parent = (r & ~b) | (b << 1);
+  if (parent >= n) parent = r & ~b;
+  *up = parent;
+  int h = b / 2;
+  *down0 = h > 0 ? r - h : -1;
+  while (h > 0 && r + h >= n) h /= 2;
+  *down1 = h > 0 ? r + h : -1;
+}
+
+/* Tree t (0 or 1) of the double binary tree: tree 0 is the binary tree;
+ * tree 1 is its mirror image (rank r plays rank n-1-r) when n is even, and
+ * the binary tree shifted by one rank when n is odd. */
+void oracle_dtree(int n, int r, int t, int* up, int* down0, int* down1) {
+  if (t == 0) {
+    oracle_btree(n, r, up, down0, down1);
+    return;
+  }
+  int u, d0, d1;
+  if (n % 2 == 0) {
+    oracle_btree(n, n - 1 - r, &u, &d0, &d1);
+    *up = u < 0 ? -1 : n - 1 - u;
+    *down0 = d0 < 0 ? -1 : n - 1 - d0;
+    *down1 = d1 < 0 ? -1 : n - 1 - d1;
+  } else {
+    oracle_btree(n, (r - 1 + n) % n, &u, &d0, &d1);
+    *up = u < 0 ? -1 : (u + 1) % n;
+    *down0 = d0 < 0 ? -1 : (d0 + 1) % n;
+    *down1 = d1 < 0 ? -1 : (d1 + 1) % n;
+  }
+}
+
+/*
+ * Tree AllReduce of n virtual ranks (x[r], y[r]: count elements each; they
+ * may alias for the in-place form).  Per channel, per chunk: the reduce
+ * phase visits vertices deepest first, so every child's partial result P
+ * exists before its parent folds it in; the root's P is the result; the
+ * broadcast phase then visits vertices shallowest first, each taking the
+ * result from its parent and storing it in its output.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_tree_allreduce(int nranks, size_t count, int dtype, int op, int nchannels,
+                          size_t chunk_elems, const void* const* x, void* const* y) {
+  size_t es = elem_size(dtype);
+  int n = nranks;
+  if (!es || op < OR_SUM || op > OR_MAX || n < 1 || nchannels < 1 || chunk_elems == 0) return -1;
+  if (n == 1) {
+    memmove(y[0], x[0], count * es);
+    return 0;
+  }
+  int* up = malloc(sizeof(int) * (size_t)n);
+  int* dn = malloc(sizeof(int) * 2 * (size_t)n);
+  int* depth = malloc(sizeof(int) * (size_t)n);
+  int* order = malloc(sizeof(int) * (size_t)n);   /* vertices, deepest first */
+  unsigned char** P = payloads(n, chunk_elems * es);
+  int rc = (up && dn && depth && order && P) ? 0 : -1;
+  for (int c = 0; c < nchannels && rc == 0; c++) {
+    int t = c % 2, root = -1;
+    for (int r = 0; r < n; r++) {
+      oracle_dtree(n, r, t, &up[r], &dn[2 * r], &dn[2 * r + 1]);
+      if (up[r] < 0) root = r;
+    }
+    for (int r = 0; r < n; r++) {
+      depth[r] = 0;
+      for (int v = r; up[v] >= 0 && depth[r] <= n; v = up[v]) depth[r]++;
+    }
+    int k = 0;
+    for (int d = n; d >= 0; d--)
+      for (int r = 0; r < n; r++)
+        if (depth[r] == d) order[k++] = r;
+    if (root < 0 || k != n) { rc = -1; break; }
+
+    size_t lo, hi;
+    oracle_channel_range(count, es, nchannels, c, &lo, &hi);
+    for (size_t off = lo; off < hi; off += chunk_elems) {
+      size_t len = min_sz(chunk_elems, hi - off);
+      /* reduce: up the tree */
+      for (int j = 0; j < n; j++) {
+        int v = order[j];
+        memcpy(P[v], (const unsigned char*)x[v] + off * es, len * es);
+        for (int s = 0; s < 2; s++) {
+          int ch = dn[2 * v + s];
+          if (ch >= 0) combine(dtype, op, P[ch], P[v], P[v], len);
+        }
+      }
+      /* broadcast: down the tree */
+      for (int j = n - 1; j >= 0; j--) {
+        int v = order[j];
+        if (v != root) memcpy(P[v], P[up[v]], len * es);
+        memcpy((unsigned char*)y[v] + off * es, P[v], len * es);
+      }
+    }
+  }
+  free(up);
+  free(dn);
+  free(depth);
+  free(order);
+  free_payloads(n, P);
+  return rc;
+}
+
 /* Array forms of the 16-bit codecs, for the tests' exhaustive pins. */
 void oracle_f16_decode_array(const uint16_t* h, float* f, size_t len) {
   for (size_t e = 0; e < len; e++) f[e] = f16_decode(h[e]);

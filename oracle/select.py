@@ -1,7 +1,8 @@
-"""Alpha-beta protocol model of the ring AllReduce: test infrastructure only.
+"""Alpha-beta protocol model of the ring and tree AllReduce: test
+infrastructure only.
 
 A plain transcription of the tuning model on the pages, restricted to the Ring
-algorithm and its three protocols:
+and Tree algorithms and their three protocols:
 
   [ARCH] arganzheng.life, "NCCL architecture: topology, channels, algorithms
          and protocols": §八.1 (ncclTopoTuneModel: per-protocol bus bandwidth,
@@ -14,6 +15,18 @@ algorithm and its three protocols:
          ch. 5 §一): candidates are pushed to the front of a list in id order
          and the first strictly smaller time wins, so on a tie the candidate
          enumerated last wins: Simple, then LL128, then LL.
+
+  [BOOK] Japanese edition, ch. 5 §四 (tree.cc): the Tree rows only serve
+         AllReduce; bus bandwidth = min(channels x bw x 0.92, channels x
+         per-channel tree cap), LL divided by 3.8 and capped at the LL
+         maximum, LL128 times 7/9 on one node (120/128 across nodes) and
+         capped per channel; latency = base + 2 x ((ranks per node - 1) x
+         intra-node step + log2(nodes) x inter-node step); the Tree
+         correction table scales the bandwidth by message size; [ARCH] §八.1
+         adds the x0.85 of the TREE pattern and the algorithm bandwidth =
+         bus bandwidth x 0.5.  The candidate ids run Tree LL, Tree LL128,
+         Tree Simple, Ring LL, Ring LL128, Ring Simple (the model map), so on
+         a tie Ring Simple wins first and Tree LL last.
 
 Protocol order everywhere is the pages' protocol table order: LL, LL128,
 Simple.  Bandwidths are GB/s, times microseconds, sizes bytes.
@@ -125,3 +138,95 @@ def resolve(m: RingModel, nranks: int, nbytes: int, nchannels: int = 0,
 def crossover_bytes(lat1: float, bw1: float, lat2: float, bw2: float) -> float:
     """Message size where lat1 + S/(1000 bw1) == lat2 + S/(1000 bw2)."""
     return 1000.0 * (lat2 - lat1) / (1.0 / bw1 - 1.0 / bw2)
+
+
+# ---------------------------------------------------------------- Tree rows
+ALGOS = ("Tree", "Ring")
+
+# Bandwidth correction of the Tree AllReduce by message size, per protocol
+# (LL, LL128, Simple), indexed by log2(bytes / 64) ([BOOK] Japanese edition,
+# ch. 5 §四, cost_model.cc table; the pages' measured "tree efficiency curve").
+TREE_CORRECTION = (
+    (1.0, 1.0, 1.0, 1.0, .9, .8, .7, .7, .7, .7, .6, .5, .4, .4, .5, .6, .7, .8, .9, 1.0, 1.0, 1.0, 1.0, 1.0),
+    (1.0, 1.0, 1.0, 1.0, 1.0, .9, .8, .8, .8, .7, .6, .6, .6, .6, .6, .6, .8, .9, .9, .9, .9, 1.0, 1.0, 1.0),
+    (.9, .9, .9, .9, .9, .9, .9, .8, .7, .6, .6, .5, .5, .5, .5, .6, .7, .8, .7, .7, .8, .9, .9, .9),
+)
+
+
+@dataclass
+class TreeModel:
+    """Inputs of the Tree rows of the tuning model."""
+    bw_per_channel: float                  # per-channel bandwidth of the tree graph
+    per_channel_max_bw: float              # perChMaxTreeBw
+    ll_max_bw: float                       # absolute cap on LL bus bandwidth
+    per_channel_max_ll128_bw: float = 1e30 # perChMaxTreeLL128Bw (no cap when unknown)
+    allreduce_eff: float = 0.92
+    ll_divisor: float = 3.8
+    n_nodes: int = 1
+    ranks_per_node: int = 8
+    tree_pattern: bool = False             # the TREE pattern's extra x0.85
+    base_lat: tuple = (6.8, 14.0, 8.4)     # per-call latency per protocol
+    intra_lat: tuple = (0.6, 1.25, 4.0)    # per step inside a node (NVLink table)
+    inter_lat: tuple = (5.0, 8.5, 14.0)    # per step between nodes (network table)
+    correction: bool = True                # apply TREE_CORRECTION
+
+
+def log2i(x: int) -> int:
+    """Floor of log2 for x >= 1; -1 for x < 1."""
+    return x.bit_length() - 1 if x >= 1 else -1
+
+
+def tree_bus_bw(m: TreeModel, nchannels: int, proto: str) -> float:
+    """Bus bandwidth of the Tree AllReduce under `proto`."""
+    bus = nchannels * m.bw_per_channel
+    bus = min(bus * m.allreduce_eff, nchannels * m.per_channel_max_bw)
+    if proto == "LL":
+        bus = min(bus / m.ll_divisor, m.ll_max_bw)
+    elif proto == "LL128":
+        f = 7.0 / 9.0 if m.n_nodes == 1 else 120.0 / 128.0
+        bus = min(bus * f, nchannels * m.per_channel_max_ll128_bw)
+    if m.tree_pattern:
+        bus *= 0.85
+    return bus
+
+
+def tree_alg_bw(m: TreeModel, nchannels: int, proto: str) -> float:
+    """Algorithm bandwidth of the Tree AllReduce: bus bandwidth x 0.5."""
+    return tree_bus_bw(m, nchannels, proto) * 0.5
+
+
+def tree_latency(m: TreeModel, proto: str) -> float:
+    """base + 2 x ((ranks per node - 1) x intra step + log2(nodes) x inter step)."""
+    p = PROTOS.index(proto)
+    return m.base_lat[p] + 2 * ((m.ranks_per_node - 1) * m.intra_lat[p] + log2i(m.n_nodes) * m.inter_lat[p])
+
+
+def tree_time_us(m: TreeModel, nchannels: int, proto: str, nbytes: int) -> float:
+    """Predicted time of one Tree AllReduce of nbytes per rank, with the size
+    correction of the bandwidth when enabled."""
+    bw = tree_alg_bw(m, nchannels, proto)
+    ls = log2i(nbytes >> 6)
+    if m.correction and 0 <= ls < 23:
+        bw *= TREE_CORRECTION[PROTOS.index(proto)][ls]
+    return tree_latency(m, proto) + nbytes / (1000.0 * bw)
+
+
+def select_algo(ring: RingModel, tree: TreeModel, nranks: int, nchannels: int, nbytes: int,
+                enabled=(("Tree", "LL"), ("Tree", "LL128"), ("Tree", "Simple"),
+                         ("Ring", "LL"), ("Ring", "LL128"), ("Ring", "Simple"))):
+    """Fastest enabled (algorithm, protocol) and the six predicted times in
+    id order (Tree LL, LL128, Simple, Ring LL, LL128, Simple).  Candidates are
+    visited in reverse id order and replaced only on a strictly smaller
+    time."""
+    times = [tree_time_us(tree, nchannels, p, nbytes) for p in PROTOS] + \
+            [ring_time_us(ring, nranks, nchannels, p, nbytes) for p in PROTOS]
+    ids = [(a, p) for a in ALGOS for p in PROTOS]
+    best, best_t = None, float("inf")
+    for i in reversed(range(len(ids))):
+        if ids[i] not in enabled:
+            continue
+        if times[i] < best_t:
+            best, best_t = ids[i], times[i]
+    if best is None:
+        raise ValueError("no algorithm/protocol enabled")
+    return best, times

@@ -12,6 +12,7 @@ import pytest
 import oracle
 from bruteforce_ring import run as brute_run
 from bruteforce_ring import run_reduce_scatter as brute_rs
+from bruteforce_tree import run as brute_tree
 from refs import exact_reduce, fold_closed_form, hop
 from ring_allreduce_reduce_amd import workloads as W
 
@@ -53,6 +54,16 @@ MUTATIONS = {
     "all-gather block off by one": ("      int k = ((i - s) % n + n) % n;", "      int k = ((i - s + 1) % n + n) % n;"),
     "all-gather skips its final recv": ("  for (int s = 0; s <= n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;",
                                         "  for (int s = 0; s < n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;"),
+    "tree children folded right to left": ("        for (int s = 0; s < 2; s++) {\n          int ch = dn[2 * v + s];",
+                                           "        for (int s = 1; s >= 0; s--) {\n          int ch = dn[2 * v + s];"),
+    "second tree mirrored for odd counts too": ("  if (n % 2 == 0) {\n    oracle_btree(n, n - 1 - r, &u, &d0, &d1);",
+                                                "  if (1) {\n    oracle_btree(n, n - 1 - r, &u, &d0, &d1);"),
+    "channel runs on the other tree": ("    int t = c % 2, root = -1;", "    int t = (c + 1) % 2, root = -1;"),
+    "second child without the range search": ("  while (h > 0 && r + h >= n) h /= 2;", "  if (r + h >= n) h = 0;"),
+    "tree root keeps no output": ("        memcpy((unsigned char*)y[v] + off * es, P[v], len * es);",
+                                  "        if (v != root) memcpy((unsigned char*)y[v] + off * es, P[v], len * es);"),
+    "tree vertex drops its own input": ("        memcpy(P[v], (const unsigned char*)x[v] + off * es, len * es);",
+                                        "        memset(P[v], 0, len * es);"),
     "fp64 min uses max": ("    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void",
                           "    case OR_MIN: return (b > a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void"),
 }
@@ -116,6 +127,29 @@ def _battery(lib) -> list:
         got = oracle.ring_all_gather(xs, "int32", ring=ring, lib=lib)
         if not all(np.array_equal(g, np.concatenate(xs)) for g in got):
             fails.append(f"all-gather {n}")
+    # tree: order-free closed form, one operation at n = 2, the recursive
+    # brute force (n = 3, 6, 8 with two channels: both trees, odd and even)
+    def tree(xs, dtype, op, nch, chunk):
+        try:
+            return oracle.tree_allreduce(xs, dtype, op, nch, chunk, lib=lib)
+        except ValueError:
+            return None
+    for (n, dtype, op) in [(6, "int32", "sum"), (5, "int8", "max")]:
+        xs = W.inputs(f"mt-{n}-{dtype}", n, 83, dtype, "uniform", -4, 4)
+        got = tree(xs, dtype, op, 3, 16)
+        ref = exact_reduce(xs, dtype, op)
+        if got is None or not all(np.array_equal(g.view(np.uint8), ref.view(np.uint8)) for g in got):
+            fails.append(f"tree closed form {n} {dtype}")
+    xs = W.inputs("mt2", 2, 99, "float32", "normal")
+    got = tree(xs, "float32", "sum", 2, 16)
+    if got is None or not all(np.array_equal(g, hop("float32", "sum", xs[0], xs[1])) for g in got):
+        fails.append("tree two ranks")
+    for n in (3, 6, 8):
+        xs = W.inputs(f"mtb-{n}", n, 131, "float32", "normal")
+        got = tree(xs, "float32", "sum", 2, 8)
+        want = brute_tree(xs, "float32", "sum", 2)
+        if got is None or not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
+            fails.append(f"tree brute force {n}")
     # codecs against numpy / torch
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = bits.view(np.float16).astype(np.float32)
