@@ -1,6 +1,7 @@
 /*
  * ringar: ring AllReduce (and its two halves, ReduceScatter and AllGather)
- * over n virtual ranks that all live in one MI355X.
+ * over n virtual ranks that all live in one MI355X, and the tree AllReduce
+ * over the pages' double binary tree.
  *
  * The operation is the device-side ring AllReduce described on
  *   [ARCH] arganzheng.life, "NCCL architecture: topology, channels, algorithms
@@ -84,6 +85,24 @@ typedef enum {
   RINGAR_ALL_GATHER = 2
 } ringar_coll_t;
 
+/* AllReduce algorithms ([ARCH] §七.1: Ring, and Tree = reduce up a double
+ * binary tree to its root, then broadcast back down; the tuning model runs
+ * Tree for AllReduce only).
+ *   RING: the ring of the pages' runRing (the default: 0 in a zeroed config).
+ *   TREE: the double binary tree of [ARCH] §五.4 over the n virtual ranks,
+ *         each rank one tree vertex; channel c runs on tree c % 2.  A vertex
+ *         folds its own input, then child 0's and child 1's partial results,
+ *         each hop as op(received, local); every rank receives the root's
+ *         result.
+ *   AUTO: the model's fastest (algorithm, protocol) pair among those the
+ *         environment allows (RINGAR_ALGO: "ring", "tree", a list, or '^' to
+ *         exclude, like RINGAR_PROTO). */
+typedef enum {
+  RINGAR_ALGO_RING = 0,
+  RINGAR_ALGO_TREE = 1,
+  RINGAR_ALGO_AUTO = 2
+} ringar_algo_t;
+
 /* Inputs of the alpha-beta model ([ARCH] §八.1-八.2), per protocol in the
  * order LL, LL128, Simple.  Bandwidths GB/s, latencies microseconds.
  *   bus bandwidth:  nch * bw_per_channel * eff[p], LL capped at ll_max_bw,
@@ -106,6 +125,24 @@ typedef struct {
   int threads[3];
   int thread_threshold[3];
   size_t default_chunk_bytes[3];
+  /* Tree rows ([BOOK] Japanese edition ch. 5 §四; [ARCH] §八.1), with every
+   * virtual rank one tree vertex (one rank per node):
+   *   bus bandwidth: min(nch * bw_per_channel * tree_allreduce_eff,
+   *                      nch * tree_per_channel_max_bw);
+   *                  LL: that / tree_ll_divisor, capped at ll_max_bw;
+   *                  LL128: that * tree_ll128_factor, capped at
+   *                  nch * tree_ll128_per_channel_max_bw;
+   *   alg bandwidth: bus * 0.5, times the pages' size correction table when
+   *                  tree_correction is 1;
+   *   latency:       tree_base_lat_us[p] + 2 * floor(log2 n) * tree_hw_lat_us[p]. */
+  double tree_allreduce_eff;
+  double tree_per_channel_max_bw;
+  double tree_ll_divisor;
+  double tree_ll128_factor;
+  double tree_ll128_per_channel_max_bw;
+  double tree_base_lat_us[3];
+  double tree_hw_lat_us[3];
+  int tree_correction;
 } ringar_model_t;
 
 /* Optional knobs of ringar_allreduce_ex.  Zero-initialise, then set fields.
@@ -131,7 +168,9 @@ typedef struct {
  *                    else RINGAR_ERR_INVALID_USAGE.  Does not change any
  *                    result.
  *   force_general:   test hook, normally 0: 1 = never use the straight-line
- *                    form for small lane parts (see ringar_plan_t). */
+ *                    form for small lane parts (see ringar_plan_t).
+ *   algo:            a ringar_algo_t (AllReduce only; the halves run the
+ *                    ring).  Zero = RINGAR_ALGO_RING. */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;
@@ -142,6 +181,7 @@ typedef struct {
   int skip_rank;
   int fifo_depth;
   int force_general;
+  int algo;
 } ringar_config_t;
 
 /* The resolved plan of a call (what ringar_allreduce would launch). */
@@ -161,7 +201,11 @@ typedef struct {
   int workgroups;          /* grid size */
   int threads_per_group;
   uint64_t max_steps;      /* upper bound on FIFO steps per connection */
-  double predicted_us[3];  /* model time per protocol (LL, LL128, Simple) */
+  double predicted_us[3];  /* model time per protocol (LL, LL128, Simple) of
+                              the plan's algorithm */
+  ringar_algo_t algo;      /* RING or TREE */
+  double predicted_tree_us[3];  /* Tree AllReduce model times (AllReduce) */
+  double predicted_ring_us[3];  /* Ring model times */
 } ringar_plan_t;
 
 /*
@@ -192,6 +236,11 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
                                     ringar_dtype_t dtype, ringar_op_t op, int nranks,
                                     int nchannels, ringar_proto_t proto, ringar_stream_t stream,
                                     const ringar_config_t* cfg);
+/* With cfg->algo = RINGAR_ALGO_TREE (or AUTO choosing it) the same call runs
+ * the tree AllReduce: buffers, in place, alignment, streams, errors, count ==
+ * 0 and nranks == 1 as above.  The chunk is per channel (the tree moves a
+ * whole chunk up and down, not one chunk per rank as the ring's loop), and
+ * float results follow the tree's fold order, not the ring's. */
 
 /*
  * Ring ReduceScatter, the first half of the ring AllReduce as a call of its
@@ -252,6 +301,21 @@ ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_
  * three times. */
 ringar_result_t ringar_select(size_t bytes, int nranks, int nchannels, const ringar_model_t* model,
                               ringar_proto_t* out, double* predicted_us);
+
+/* Host only: the model's fastest (algorithm, protocol) pair for an
+ * AllReduce of `bytes` per rank over nchannels channels (0 = the model's
+ * maximum), among the pairs RINGAR_ALGO and RINGAR_PROTO allow.  The
+ * candidates are numbered Tree LL, Tree LL128, Tree Simple, Ring LL, Ring
+ * LL128, Ring Simple (the pages' model map) and visited in reverse, the
+ * first strictly smaller time winning, so ties go to Ring Simple first.
+ * predicted_us (may be NULL) receives the six times in that order. */
+ringar_result_t ringar_select_algo(size_t bytes, int nranks, int nchannels, const ringar_model_t* model,
+                                   ringar_algo_t* algo, ringar_proto_t* proto, double* predicted_us);
+
+/* Host only: vertex `rank` of tree `tree` (0 or 1) of the double binary tree
+ * the tree AllReduce uses over nranks ranks ([ARCH] §五.4): its parent and
+ * its children in child-slot order, -1 = none. */
+ringar_result_t ringar_tree(int nranks, int tree, int rank, int* parent, int* child0, int* child1);
 
 /* Host only: the built-in MI355X model constants. */
 ringar_result_t ringar_default_model(ringar_model_t* out);

@@ -169,6 +169,7 @@ class TreeModel:
     intra_lat: tuple = (0.6, 1.25, 4.0)    # per step inside a node (NVLink table)
     inter_lat: tuple = (5.0, 8.5, 14.0)    # per step between nodes (network table)
     correction: bool = True                # apply TREE_CORRECTION
+    ll128_factor: float | None = None      # None: the pages' 7/9 (one node) or 120/128
 
 
 def log2i(x: int) -> int:
@@ -183,7 +184,7 @@ def tree_bus_bw(m: TreeModel, nchannels: int, proto: str) -> float:
     if proto == "LL":
         bus = min(bus / m.ll_divisor, m.ll_max_bw)
     elif proto == "LL128":
-        f = 7.0 / 9.0 if m.n_nodes == 1 else 120.0 / 128.0
+        f = m.ll128_factor if m.ll128_factor is not None else (7.0 / 9.0 if m.n_nodes == 1 else 120.0 / 128.0)
         bus = min(bus * f, nchannels * m.per_channel_max_ll128_bw)
     if m.tree_pattern:
         bus *= 0.85

@@ -1,4 +1,4 @@
-"""Python binding of libringar.so, the MI355X ring AllReduce library.
+"""Python binding of libringar.so, the MI355X ring (and tree) AllReduce library.
 
 Argument marshalling only: every step of the AllReduce runs in the library's
 HIP kernels.  The functions carry the C names declared in include/ringar.h;
@@ -21,6 +21,8 @@ DTYPES = {"int8": 0, "int32": 1, "float16": 2, "bfloat16": 3, "float32": 4, "flo
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
 PROTOS = {"auto": -1, "LL": 0, "LL128": 1, "Simple": 2}
 PROTO_NAMES = {v: k for k, v in PROTOS.items()}
+ALGOS = {"ring": 0, "tree": 1, "auto": 2}
+ALGO_NAMES = {0: "ring", 1: "tree"}
 ELEM_BYTES = {"int8": 1, "int32": 4, "float16": 2, "bfloat16": 2, "float32": 4, "float64": 8}
 
 
@@ -43,6 +45,14 @@ class ringar_model_t(ctypes.Structure):
         ("threads", ctypes.c_int * 3),
         ("thread_threshold", ctypes.c_int * 3),
         ("default_chunk_bytes", ctypes.c_size_t * 3),
+        ("tree_allreduce_eff", ctypes.c_double),
+        ("tree_per_channel_max_bw", ctypes.c_double),
+        ("tree_ll_divisor", ctypes.c_double),
+        ("tree_ll128_factor", ctypes.c_double),
+        ("tree_ll128_per_channel_max_bw", ctypes.c_double),
+        ("tree_base_lat_us", ctypes.c_double * 3),
+        ("tree_hw_lat_us", ctypes.c_double * 3),
+        ("tree_correction", ctypes.c_int),
     ]
 
 
@@ -57,6 +67,7 @@ class ringar_config_t(ctypes.Structure):
         ("skip_rank", ctypes.c_int),
         ("fifo_depth", ctypes.c_int),
         ("force_general", ctypes.c_int),
+        ("algo", ctypes.c_int),
     ]
 
 
@@ -75,6 +86,9 @@ class ringar_plan_t(ctypes.Structure):
         ("threads_per_group", ctypes.c_int),
         ("max_steps", ctypes.c_uint64),
         ("predicted_us", ctypes.c_double * 3),
+        ("algo", ctypes.c_int),
+        ("predicted_tree_us", ctypes.c_double * 3),
+        ("predicted_ring_us", ctypes.c_double * 3),
     ]
 
 
@@ -100,6 +114,9 @@ def load() -> ctypes.CDLL:
     lib.ringar_all_gather_ex.argtypes = lib.ringar_all_gather.argtypes + [ctypes.POINTER(ringar_config_t)]
     lib.ringar_select.argtypes = [sz, i, i, ctypes.POINTER(ringar_model_t), ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_double)]
+    lib.ringar_select_algo.argtypes = [sz, i, i, ctypes.POINTER(ringar_model_t), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
+    lib.ringar_tree.argtypes = [i, i, i] + [ctypes.POINTER(ctypes.c_int)] * 3
     lib.ringar_default_model.argtypes = [ctypes.POINTER(ringar_model_t)]
     lib.ringar_chunk_range.argtypes = [sz, i, i, i, sz, i, sz, i] + [ctypes.POINTER(sz)] * 4
     lib.ringar_get_async_error.argtypes = [vp]
@@ -109,6 +126,7 @@ def load() -> ctypes.CDLL:
     lib.ringar_last_error.argtypes = []
     lib.ringar_last_error.restype = ctypes.c_char_p
     for name in ("ringar_allreduce", "ringar_allreduce_ex", "ringar_plan", "ringar_select", "ringar_plan_coll",
+                 "ringar_select_algo", "ringar_tree",
                  "ringar_reduce_scatter", "ringar_reduce_scatter_ex", "ringar_all_gather", "ringar_all_gather_ex",
                  "ringar_default_model", "ringar_chunk_range", "ringar_get_async_error", "ringar_release"):
         getattr(lib, name).restype = ctypes.c_int
@@ -130,7 +148,7 @@ def _enum(table, v):
 
 
 def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_ms=0,
-                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0):
+                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0, algo="ring"):
     """A ringar_config_t; keeps the ring-order array alive on the object."""
     cfg = ringar_config_t()
     cfg.chunk_bytes = chunk_bytes
@@ -147,6 +165,7 @@ def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_
     cfg.skip_rank = skip_rank
     cfg.fifo_depth = fifo_depth
     cfg.force_general = force_general
+    cfg.algo = _enum(ALGOS, algo)
     return cfg
 
 
@@ -208,14 +227,35 @@ def ringar_select(nbytes, nranks, nchannels=0, model=None):
     return PROTO_NAMES[p.value], list(t)
 
 
+def ringar_select_algo(nbytes, nranks, nchannels=0, model=None):
+    """(algorithm name, protocol name, [predicted us: Tree LL, LL128, Simple,
+    Ring LL, LL128, Simple])."""
+    a, p = ctypes.c_int(), ctypes.c_int()
+    t = (ctypes.c_double * 6)()
+    _check(load().ringar_select_algo(nbytes, nranks, nchannels,
+                                     ctypes.byref(model) if model is not None else None,
+                                     ctypes.byref(a), ctypes.byref(p), t), "ringar_select_algo")
+    return ALGO_NAMES[a.value], PROTO_NAMES[p.value], list(t)
+
+
+def ringar_tree(nranks, tree, rank):
+    """(parent, child slot 0, child slot 1) of ``rank`` in tree 0 or 1."""
+    v = [ctypes.c_int() for _ in range(3)]
+    _check(load().ringar_tree(nranks, tree, rank, *[ctypes.byref(x) for x in v]), "ringar_tree")
+    return tuple(x.value for x in v)
+
+
 def ringar_default_model() -> ringar_model_t:
     m = ringar_model_t()
     _check(load().ringar_default_model(ctypes.byref(m)), "ringar_default_model")
     return m
 
 
-_MODEL_SCALARS = ("bw_per_channel", "ll_max_bw", "ll128_per_channel_max_bw", "max_channels", "max_pairs")
-_MODEL_ARRAYS = ("eff", "base_lat_us", "hw_lat_us", "threads", "thread_threshold", "default_chunk_bytes")
+_MODEL_SCALARS = ("bw_per_channel", "ll_max_bw", "ll128_per_channel_max_bw", "max_channels", "max_pairs",
+                  "tree_allreduce_eff", "tree_per_channel_max_bw", "tree_ll_divisor", "tree_ll128_factor",
+                  "tree_ll128_per_channel_max_bw", "tree_correction")
+_MODEL_ARRAYS = ("eff", "base_lat_us", "hw_lat_us", "threads", "thread_threshold", "default_chunk_bytes",
+                 "tree_base_lat_us", "tree_hw_lat_us")
 
 
 def model_dict(m: ringar_model_t) -> dict:
@@ -229,11 +269,11 @@ def model_from_dict(d: dict) -> ringar_model_t:
     """The inverse of ``model_dict`` (keys starting with '_' are ignored)."""
     m = ringar_model_t()
     for k in _MODEL_SCALARS:
-        setattr(m, k, d[k])
+        setattr(m, k, d.get(k, 0))
     for k in _MODEL_ARRAYS:
         arr = getattr(m, k)
         for i in range(3):
-            arr[i] = d[k][i]
+            arr[i] = d.get(k, [0, 0, 0])[i]
     return m
 
 
@@ -281,7 +321,8 @@ def allreduce(sends, recvs, op="sum", nchannels=0, proto="auto", stream=None, **
     ``sends[r]`` / ``recvs[r]``: contiguous tensors of equal size and dtype
     (``recvs`` may be ``sends`` for the in-place form).  Enqueues on ``stream``
     (a torch stream; default: the current stream) and returns at once.
-    Extra keyword arguments go to ``make_config``.
+    Extra keyword arguments go to ``make_config`` (``algo="tree"`` runs the
+    double-binary-tree AllReduce).
     """
     import torch
     n = len(sends)

@@ -42,7 +42,9 @@ constexpr uint32_t kLL128SlotLines = 256;                  // 128-byte lines per
 constexpr uint32_t kLL128SlotBytes = kLL128SlotLines * 128;// FIFO bytes per slot
 
 enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
-enum Coll { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+// Launch kinds: the ring AllReduce and its halves (the public collective
+// codes), and the tree AllReduce.
+enum Coll { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kTreeAllReduce = 3 };
 
 RA_HD uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 RA_HD uint64_t align_up(uint64_t a, uint64_t b) { return div_up(a, b) * b; }
@@ -127,6 +129,18 @@ RA_HD uint64_t conn_index(int c, int i, int l, int nranks, int lanes) {
   return ((uint64_t)c * nranks + i) * lanes + l;
 }
 
+// Tree AllReduce connections: vertex v of channel c, lane l has an up
+// connection (v -> its parent) and a down connection (its parent -> v).
+enum TreeDir { kUp = 0, kDown = 1 };
+RA_HD uint64_t tree_conn_index(int c, int v, int dir, int l, int nranks, int lanes) {
+  return (((uint64_t)c * nranks + v) * 2 + dir) * lanes + l;
+}
+
+// Wavefront roles per (channel, lane) of the tree AllReduce: role v < n
+// reduces vertex v into its parent (the root's role also starts the
+// broadcast); role n + j broadcasts into the j-th vertex other than the root.
+RA_HD int tree_roles(int nranks) { return 2 * nranks - 1; }
+
 // Everything one launch needs, passed by value as kernel arguments.
 struct KernelArgs {
   const char* send[kMaxRanks];   // by ring index
@@ -149,6 +163,16 @@ struct KernelArgs {
   int lanes_per_block;
   int skip_ring_index;           // -1: none
   int vec_ok;                    // all user pointers 16-byte aligned
+};
+
+// Arguments of a tree AllReduce launch: the ring's, plus the two trees
+// (channel c runs on tree c % 2), by rank: parent and children in child-slot
+// order, -1 = none.
+struct TreeArgs {
+  KernelArgs k;
+  int8_t parent[2][kMaxRanks];
+  int8_t child[2][2][kMaxRanks];
+  int root[2];
 };
 
 }  // namespace ringar

@@ -7,7 +7,7 @@
 
 namespace ringar {
 
-// Kernel instance for (collective, dtype code, op code, protocol) of the
+// Kernel instance for (launch kind, dtype code, op code, protocol) of the
 // public header (AllGather: a byte copy, dtype and op ignored); `small`: the
 // form for lane parts of at most 1 KiB in 16-byte aligned buffers (LL and
 // Simple only; ignored for LL128).
@@ -15,6 +15,10 @@ const void* kernel_for(int coll, int dtype, int op, int proto, bool small);
 
 hipError_t launch_ring(int coll, int dtype, int op, int proto, bool small, const KernelArgs& args,
                        int grid, int block, hipStream_t stream);
+
+// Tree AllReduce launch (kernel_for(kTreeAllReduce, ...)).
+hipError_t launch_tree(int dtype, int op, int proto, bool small, const TreeArgs& args, int grid, int block,
+                       hipStream_t stream);
 
 hipError_t max_active_blocks(int coll, int dtype, int op, int proto, bool small, int block, int* per_cu);
 

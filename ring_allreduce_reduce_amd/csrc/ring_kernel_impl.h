@@ -260,37 +260,85 @@ struct Conn {
   uint64_t* head;      // written by the consumer
 };
 
+template <int PROTO> __device__ __forceinline__ Conn conn_at(const KernelArgs& a, uint64_t idx) {
+  return Conn{a.fifo + idx * fifo_conn_bytes(PROTO), a.counters + idx * kCounterWords + kTailWord,
+              a.counters + idx * kCounterWords + kHeadWord};
+}
+
+// A wavefront's connections: one input and one output on the ring; a tree
+// vertex receives from up to two children and sends to up to two.  All
+// connections of a wavefront move in lockstep (one slice is one step on
+// each), so they share the step numbers.
 struct Lane {
   const KernelArgs* a;
-  Conn in, out;
+  Conn in[2], out[2];
   const char* src;     // own send buffer
   char* dst;           // own receive buffer
   uint64_t sstep, rstep;
-  uint64_t tail_seen;  // largest tail of the input connection seen so far
-  uint64_t head_seen;  // largest head of the output connection seen so far
+  uint64_t tail_seen[2];  // largest tail of each input connection seen so far
+  uint64_t head_seen[2];  // largest head of each output connection seen so far
   int lane;            // lane within the wavefront
   Waiter w;
 };
 
-enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8 };
+// Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
+// output 0, and output 1 with kSend2), read the own send buffer, write the
+// own receive buffer.
+enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8, kRecv2 = 16, kSend2 = 32 };
 
-// Frees the input slot just read: publishes head = base + step + 1.  Every
-// load of the slot has returned its data (the values were consumed above),
+// Frees the input slots just read: publishes head = base + step + 1.  Every
+// load of a slot has returned its data (the values were consumed above),
 // so the producer may overwrite it; the wavefront's own stores need not be
 // complete, and waiting for them here would add a round trip to every step.
-__device__ __forceinline__ void release_slot(Lane& L) {
+template <int F> __device__ __forceinline__ void release_slot(Lane& L) {
   compiler_fence();
-  st_relaxed(L.in.head, L.a->base + L.rstep + 1);
+  st_relaxed(L.in[0].head, L.a->base + L.rstep + 1);
+  if (F & kRecv2) st_relaxed(L.in[1].head, L.a->base + L.rstep + 1);
   L.rstep++;
+}
+
+// Waits for the tails of the inputs and for free slots on the outputs of
+// the next step.
+template <int F> __device__ __forceinline__ bool wait_inputs(Lane& L) {
+  const KernelArgs& a = *L.a;
+  if ((F & kRecv) && !wait_ge(L.w, L.in[0].tail, a.base + L.rstep + 1, L.tail_seen[0])) return false;
+  if ((F & kRecv2) && !wait_ge(L.w, L.in[1].tail, a.base + L.rstep + 1, L.tail_seen[1])) return false;
+  return true;
+}
+template <int F> __device__ __forceinline__ bool wait_outputs(Lane& L) {
+  const KernelArgs& a = *L.a;
+  if (L.sstep < (uint64_t)a.depth) return true;
+  const uint64_t need = a.base + L.sstep + 1 - a.depth;
+  if ((F & kSend) && !wait_ge(L.w, L.out[0].head, need, L.head_seen[0])) return false;
+  if ((F & kSend2) && !wait_ge(L.w, L.out[1].head, need, L.head_seen[1])) return false;
+  return true;
+}
+
+// Publishes the tails of the outputs after the step's data stores.
+template <int F> __device__ __forceinline__ void publish_tails(Lane& L) {
+  wait_mem();
+  st_relaxed(L.out[0].tail, L.a->base + L.sstep + 1);
+  if (F & kSend2) st_relaxed(L.out[1].tail, L.a->base + L.sstep + 1);
+  L.sstep++;
 }
 
 constexpr int kUnroll = 8;   // 16-byte packets per lane in flight per source
 
-// Result of one packet: op(received, local), or whichever operand exists.
-template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 b) {
-  if ((F & kRecv) && (F & kSrc)) return vop<E, OP>(a, b);
-  if (F & kRecv) return a;
-  return b;
+// Result of one packet: the local operand b folded with what was received
+// from input 0 (a) and then input 1 (a2), each hop as op(received, local);
+// or the received packet alone when there is no local operand.
+template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 a2, u32x4 b) {
+  static_assert(!(F & kRecv2) || ((F & kRecv) && (F & kSrc)), "a second input is folded into a local operand");
+  static_assert(!(F & kSend2) || (F & kSend), "a second output needs the first");
+  if constexpr ((F & kRecv) && (F & kSrc)) {
+    u32x4 r = vop<E, OP>(a, b);
+    if constexpr (F & kRecv2) r = vop<E, OP>(a2, r);
+    return r;
+  } else if constexpr (F & kRecv) {
+    return a;
+  } else {
+    return b;
+  }
 }
 
 // --- Simple: one slice = one slot ------------------------------------------
@@ -298,33 +346,34 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
-  if (F & kRecv) {
-    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1, L.tail_seen)) return false;
-  }
-  if (F & kSend) {
-    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
-  }
-  rsrc_t rin = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
-  rsrc_t rout = make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, kSimpleSlotBytes);
+  if (!wait_inputs<F>(L) || !wait_outputs<F>(L)) return false;
+  const uint32_t rslot = (uint32_t)(L.rstep & (a.depth - 1)) * kSimpleSlotBytes;
+  const uint32_t sslot = (uint32_t)(L.sstep & (a.depth - 1)) * kSimpleSlotBytes;
+  rsrc_t rin = make_rsrc(L.in[0].fifo + rslot, kSimpleSlotBytes);
+  rsrc_t rin2 = make_rsrc(L.in[(F & kRecv2) ? 1 : 0].fifo + rslot, kSimpleSlotBytes);
+  rsrc_t rout = make_rsrc(L.out[0].fifo + sslot, kSimpleSlotBytes);
+  rsrc_t rout2 = make_rsrc(L.out[(F & kSend2) ? 1 : 0].fifo + sslot, kSimpleSlotBytes);
   rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
-    u32x4 va[kUnroll], vb[kUnroll];
+    u32x4 va[kUnroll], va2[kUnroll], vb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       const bool in = p < nfull;
       if (F & kRecv) va[u] = in ? ld16<kSC1>(rin, p * 16) : u32x4{0u, 0u, 0u, 0u};
+      if (F & kRecv2) va2[u] = in ? ld16<kSC1>(rin2, p * 16) : u32x4{0u, 0u, 0u, 0u};
       if (F & kSrc) vb[u] = in ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
-      const u32x4 r = combine<E, OP, F>(va[u], vb[u]);
+      const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u]);
       if (F & kSend) st16<kSC1>(r, rout, p * 16);
+      if (F & kSend2) st16<kSC1>(r, rout2, p * 16);
       if (F & kDst) st16<kNT>(r, rdst, p * 16);
     }
   }
@@ -333,19 +382,17 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
 #pragma unroll 1
   for (uint32_t p = nfull + L.lane; p < npk; p += 64) {
     const uint32_t off = p * 16, nb = min(16u, nbytes - off);
-    u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+    u32x4 x = u32x4{0u, 0u, 0u, 0u}, x2 = x, y = x;
     if (F & kRecv) x = ld16<kSC1>(rin, off);
+    if (F & kRecv2) x2 = ld16<kSC1>(rin2, off);
     if (F & kSrc) y = ld_part<E, kNT>(rsrc_, off, nb);
-    const u32x4 r = combine<E, OP, F>(x, y);
+    const u32x4 r = combine<E, OP, F>(x, x2, y);
     if (F & kSend) st16<kSC1>(r, rout, off);
+    if (F & kSend2) st16<kSC1>(r, rout2, off);
     if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
   }
-  if (F & kSend) {
-    wait_mem();
-    st_relaxed(L.out.tail, a.base + L.sstep + 1);
-    L.sstep++;
-  }
-  if (F & kRecv) release_slot(L);
+  if (F & kSend) publish_tails<F>(L);
+  if (F & kRecv) release_slot<F>(L);
   return true;
 }
 
@@ -396,62 +443,74 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
-  if (F & kSend) {
-    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
-  }
+  if (!wait_outputs<F>(L)) return false;
+  constexpr int NI = (F & kRecv2) ? 2 : 1;   // inputs
   const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
   const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
-  const uint64_t* lin = (const uint64_t*)(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes);
-  uint64_t* lout = (uint64_t*)(L.out.fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes);
+  const uint64_t rslot = (L.rstep & (a.depth - 1)) * kLLSlotBytes;
+  const uint64_t sslot = (L.sstep & (a.depth - 1)) * kLLSlotBytes;
+  const uint64_t* lin[2] = {(const uint64_t*)(L.in[0].fifo + rslot),
+                            (const uint64_t*)(L.in[NI - 1].fifo + rslot)};
+  uint64_t* lout = (uint64_t*)(L.out[0].fifo + sslot);
+  uint64_t* lout2 = (uint64_t*)(L.out[(F & kSend2) ? 1 : 0].fifo + sslot);
   rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
-  constexpr int U = 4;
+  constexpr int U = NI == 2 ? 2 : 4;   // packets per lane per poll (registers)
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
-    u32x4 va[U], vb[U];
+    u32x4 va[NI][U], vb[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (F & kSrc) vb[u] = (p < nfull) ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
     }
     if (F & kRecv) {
-      // all 4U lines of the lane are loaded, then polled together: one
-      // round trip per iteration however many packets the lane has
-      uint64_t ln[U][4];
+      // all 4U lines of the lane (of every input) are loaded, then polled
+      // together: one round trip per iteration however many packets
+      uint64_t ln[NI][U][4];
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const uint32_t p = p0 + u * 64 + L.lane;
-#pragma unroll
-        for (int q = 0; q < 4; q++) ln[u][q] = (p < nfull) ? ld_relaxed(lin + 4 * p + q) : ll_line(0, fin);
-      }
-      L.w.start();
-      while (true) {
-        bool ok = true;
-#pragma unroll
-        for (int u = 0; u < U; u++)
-#pragma unroll
-          for (int q = 0; q < 4; q++) ok = ok && ll_ready(ln[u][q], fin);
-        if (__all(ok)) break;
-        if (!L.w.idle()) return false;
+      for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int u = 0; u < U; u++) {
           const uint32_t p = p0 + u * 64 + L.lane;
 #pragma unroll
-          for (int q = 0; q < 4; q++)
-            if (!ll_ready(ln[u][q], fin)) ln[u][q] = ld_relaxed(lin + 4 * p + q);
+          for (int q = 0; q < 4; q++) ln[i][u][q] = (p < nfull) ? ld_relaxed(lin[i] + 4 * p + q) : ll_line(0, fin);
         }
+      L.w.start();
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+          for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) ok = ok && ll_ready(ln[i][u][q], fin);
+        if (__all(ok)) break;
+        if (!L.w.idle()) return false;
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+          for (int u = 0; u < U; u++) {
+            const uint32_t p = p0 + u * 64 + L.lane;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+              if (!ll_ready(ln[i][u][q], fin)) ln[i][u][q] = ld_relaxed(lin[i] + 4 * p + q);
+          }
       }
 #pragma unroll
-      for (int u = 0; u < U; u++)
-        va[u] = u32x4{(uint32_t)ln[u][0], (uint32_t)ln[u][1], (uint32_t)ln[u][2], (uint32_t)ln[u][3]};
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int u = 0; u < U; u++)
+          va[i][u] = u32x4{(uint32_t)ln[i][u][0], (uint32_t)ln[i][u][1], (uint32_t)ln[i][u][2], (uint32_t)ln[i][u][3]};
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
-      const u32x4 r = combine<E, OP, F>(va[u], vb[u]);
+      const u32x4 r = combine<E, OP, F>(va[0][u], va[NI - 1][u], vb[u]);
       if (F & kSend) ll_send4(lout, p, r, fout);
+      if (F & kSend2) ll_send4(lout2, p, r, fout);
       if (F & kDst) st16<kNT>(r, rdst, p * 16);
     }
   }
@@ -459,20 +518,27 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
 #pragma unroll 1
   for (uint32_t p = nfull + L.lane; p < npk; p += 64) {
     const uint32_t off = p * 16, nb = min(16u, nbytes - off);
-    u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
+    u32x4 x[NI], y = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NI; i++) x[i] = y;
     if (F & kSrc) y = ld_part<E, kNT>(rsrc_, off, nb);
     if (F & kRecv) {
-      uint64_t ln[4];
-      if (!ll_recv4(L.w, lin, p, true, fin, ln)) { failed = true; break; }
-      x = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+#pragma unroll
+      for (int i = 0; i < NI; i++) {
+        uint64_t ln[4];
+        if (!ll_recv4(L.w, lin[i], p, true, fin, ln)) { failed = true; break; }
+        x[i] = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+      }
+      if (failed) break;
     }
-    const u32x4 r = combine<E, OP, F>(x, y);
+    const u32x4 r = combine<E, OP, F>(x[0], x[NI - 1], y);
     if (F & kSend) ll_send4(lout, p, r, fout);
+    if (F & kSend2) ll_send4(lout2, p, r, fout);
     if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
   }
   if (__any(failed)) return false;
   if (F & kSend) L.sstep++;
-  if (F & kRecv) release_slot(L);
+  if (F & kRecv) release_slot<F>(L);
   return true;
 }
 
@@ -513,15 +579,17 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
-  if (F & kSend) {
-    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
-  }
+  if (!wait_outputs<F>(L)) return false;
+  constexpr int NI = (F & kRecv2) ? 2 : 1;   // inputs
+  constexpr int NO = (F & kSend2) ? 2 : 1;   // outputs
   const uint64_t fin = a.base + L.rstep + 1;
   const uint64_t fout = a.base + L.sstep + 1;
-  char* sin = L.in.fifo + (L.rstep & (a.depth - 1)) * kLL128SlotBytes;
-  char* sout = L.out.fifo + (L.sstep & (a.depth - 1)) * kLL128SlotBytes;
-  rsrc_t rin = make_rsrc(sin, kLL128SlotBytes);
-  rsrc_t rout = make_rsrc(sout, kLL128SlotBytes);
+  const uint64_t rslot = (L.rstep & (a.depth - 1)) * kLL128SlotBytes;
+  const uint64_t sslot = (L.sstep & (a.depth - 1)) * kLL128SlotBytes;
+  char* sin[2] = {L.in[0].fifo + rslot, L.in[NI - 1].fifo + rslot};
+  char* sout[2] = {L.out[0].fifo + sslot, L.out[NO - 1].fifo + sslot};
+  rsrc_t rin[2] = {make_rsrc(sin[0], kLL128SlotBytes), make_rsrc(sin[1], kLL128SlotBytes)};
+  rsrc_t rout[2] = {make_rsrc(sout[0], kLL128SlotBytes), make_rsrc(sout[1], kLL128SlotBytes)};
   rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const bool vec = a.vec_ok;
@@ -536,28 +604,42 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
     uint32_t part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, 0, L.lane, vec, vb);
     if (F & kRecv) {
       // flags first, then data: lane t watches lines b0 + t and b0 + 64 + t
-      const uint64_t* f0p = (const uint64_t*)(sin + (size_t)(b0 + L.lane) * 128 + 120);
-      const uint64_t* f1p = (const uint64_t*)(sin + (size_t)(b0 + 64 + L.lane) * 128 + 120);
+      // of every input
       const bool w0 = L.lane < (int)nl, w1 = 64 + L.lane < (int)nl;
+      const uint64_t* fp[NI][2];
+      uint64_t f[NI][2];
+#pragma unroll
+      for (int i = 0; i < NI; i++) {
+        fp[i][0] = (const uint64_t*)(sin[i] + (size_t)(b0 + L.lane) * 128 + 120);
+        fp[i][1] = (const uint64_t*)(sin[i] + (size_t)(b0 + 64 + L.lane) * 128 + 120);
+        f[i][0] = w0 ? ld_relaxed(fp[i][0]) : fin;
+        f[i][1] = w1 ? ld_relaxed(fp[i][1]) : fin;
+      }
       L.w.start();
-      uint64_t f0 = w0 ? ld_relaxed(f0p) : fin;
-      uint64_t f1 = w1 ? ld_relaxed(f1p) : fin;
       while (true) {
-        if (__all(f0 == fin && f1 == fin)) break;
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NI; i++) ok = ok && f[i][0] == fin && f[i][1] == fin;
+        if (__all(ok)) break;
         if (!L.w.idle()) return false;
-        if (f0 != fin) f0 = ld_relaxed(f0p);
-        if (f1 != fin) f1 = ld_relaxed(f1p);
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+          if (f[i][0] != fin) f[i][0] = ld_relaxed(fp[i][0]);
+          if (f[i][1] != fin) f[i][1] = ld_relaxed(fp[i][1]);
+        }
       }
       compiler_fence();
     }
 #pragma unroll 1
     for (uint32_t g = 0; g * kLL128Group * 8 < nl; g++) {
-      u32x4 va[kLL128Group];
+      u32x4 va[kLL128Group], va2[kLL128Group];
 #pragma unroll
       for (int v = 0; v < kLL128Group; v++) {
         const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
         va[v] = u32x4{0u, 0u, 0u, 0u};
-        if ((F & kRecv) && line < b0 + nl) va[v] = ld16<kSC1>(rin, line * 128 + col * 16);
+        va2[v] = va[v];
+        if ((F & kRecv) && line < b0 + nl) va[v] = ld16<kSC1>(rin[0], line * 128 + col * 16);
+        if ((F & kRecv2) && line < b0 + nl) va2[v] = ld16<kSC1>(rin[1], line * 128 + col * 16);
       }
       // the next group's user data is requested while this group computes
       u32x4 vbn[kLL128Group] = {};
@@ -565,7 +647,7 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       if ((g + 1) * kLL128Group * 8 < nl)
         partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g + 1, L.lane, vec, vbn);
 #pragma unroll
-      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], vb[v]);
+      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], va2[v], vb[v]);
       // Packets that end inside their column: element-wise on the user side.
 #pragma unroll 1
       for (uint32_t bits = part; bits; bits &= bits - 1) {
@@ -573,13 +655,17 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
         const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
         const uint32_t uoff = line * 120 + coff;
         const uint32_t nb = min(psize, nbytes - uoff);
-        u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = u32x4{0u, 0u, 0u, 0u};
-        if (F & kRecv) x = ld16<kSC1>(rin, line * 128 + col * 16);
+        u32x4 x = u32x4{0u, 0u, 0u, 0u}, x2 = x, y = x;
+        if (F & kRecv) x = ld16<kSC1>(rin[0], line * 128 + col * 16);
+        if (F & kRecv2) x2 = ld16<kSC1>(rin[1], line * 128 + col * 16);
         if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
-        const u32x4 r = combine<E, OP, F>(x, y);
+        const u32x4 r = combine<E, OP, F>(x, x2, y);
         if (F & kSend) {
-          if (col == 7) st8<kSC1>(r, rout, line * 128 + 112);
-          else st16<kSC1>(r, rout, line * 128 + col * 16);
+#pragma unroll
+          for (int o = 0; o < NO; o++) {
+            if (col == 7) st8<kSC1>(r, rout[o], line * 128 + 112);
+            else st16<kSC1>(r, rout[o], line * 128 + col * 16);
+          }
         }
         if (F & kDst) st_part<E, kNT>(r, rdst, uoff, nb);
       }
@@ -589,8 +675,11 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
         const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
         if (line >= b0 + nl || valid <= 0 || (part >> v) & 1u) continue;
         if (F & kSend) {
-          if (col == 7) st8<kSC1>(va[v], rout, line * 128 + 112);
-          else st16<kSC1>(va[v], rout, line * 128 + col * 16);
+#pragma unroll
+          for (int o = 0; o < NO; o++) {
+            if (col == 7) st8<kSC1>(va[v], rout[o], line * 128 + 112);
+            else st16<kSC1>(va[v], rout[o], line * 128 + col * 16);
+          }
         }
         if (F & kDst) {
           if (col == 7) st8<kNT>(va[v], rdst, line * 120 + 112);
@@ -603,12 +692,15 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
     }
     if (F & kSend) {
       wait_mem();   // all data of the batch is visible before any of its flags
-      if (L.lane < (int)nl) st_relaxed((uint64_t*)(sout + (size_t)(b0 + L.lane) * 128 + 120), fout);
-      if (64 + L.lane < (int)nl) st_relaxed((uint64_t*)(sout + (size_t)(b0 + 64 + L.lane) * 128 + 120), fout);
+#pragma unroll
+      for (int o = 0; o < NO; o++) {
+        if (L.lane < (int)nl) st_relaxed((uint64_t*)(sout[o] + (size_t)(b0 + L.lane) * 128 + 120), fout);
+        if (64 + L.lane < (int)nl) st_relaxed((uint64_t*)(sout[o] + (size_t)(b0 + 64 + L.lane) * 128 + 120), fout);
+      }
     }
   }
   if (F & kSend) L.sstep++;
-  if (F & kRecv) release_slot(L);
+  if (F & kRecv) release_slot<F>(L);
   return true;
 }
 
@@ -641,44 +733,60 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
-  if (F & kSend) {
-    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
-  }
+  if (!wait_outputs<F>(L)) return false;
+  constexpr int NI = (F & kRecv2) ? 2 : 1;   // inputs
+  constexpr int NO = (F & kSend2) ? 2 : 1;   // outputs
   const uint32_t fin = (uint32_t)(a.base + L.rstep + 1);
   const uint32_t fout = (uint32_t)(a.base + L.sstep + 1);
   const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   const bool act = p < npk;
-  u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
+  u32x4 va[NI], vb = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < NI; i++) va[i] = vb;
   if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
   if (F & kRecv) {
-    const rsrc_t ri = make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
-    uint64_t ln[4];
+    rsrc_t ri[NI];
+    uint64_t ln[NI][4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) ln[q] = ll_load(ri, p * 32 + q * 8);
+    for (int i = 0; i < NI; i++) {
+      ri[i] = make_rsrc(L.in[i].fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
+#pragma unroll
+      for (int q = 0; q < 4; q++) ln[i][q] = ll_load(ri[i], p * 32 + q * 8);
+    }
     L.w.start();
     while (true) {
-      const bool ok = !act || (ll_ready(ln[0], fin) && ll_ready(ln[1], fin) && ll_ready(ln[2], fin) &&
-                               ll_ready(ln[3], fin));
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+        ok = ok && (!act || (ll_ready(ln[i][0], fin) && ll_ready(ln[i][1], fin) && ll_ready(ln[i][2], fin) &&
+                             ll_ready(ln[i][3], fin)));
       if (__all(ok)) break;
       if (!L.w.idle()) return false;
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-        if (!ll_ready(ln[q], fin)) ln[q] = ll_load(ri, p * 32 + q * 8);
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (!ll_ready(ln[i][q], fin)) ln[i][q] = ll_load(ri[i], p * 32 + q * 8);
     }
-    va = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+#pragma unroll
+    for (int i = 0; i < NI; i++)
+      va[i] = u32x4{(uint32_t)ln[i][0], (uint32_t)ln[i][1], (uint32_t)ln[i][2], (uint32_t)ln[i][3]};
   }
-  const u32x4 r = combine<E, OP, F>(va, vb);
+  const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb);
   if (F & kSend) {
-    const rsrc_t ro = make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
-    ll_store(ro, p * 32 + 0, r.x, fout);
-    ll_store(ro, p * 32 + 8, r.y, fout);
-    ll_store(ro, p * 32 + 16, r.z, fout);
-    ll_store(ro, p * 32 + 24, r.w, fout);
+#pragma unroll
+    for (int o = 0; o < NO; o++) {
+      const rsrc_t ro = make_rsrc(L.out[o].fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
+      ll_store(ro, p * 32 + 0, r.x, fout);
+      ll_store(ro, p * 32 + 8, r.y, fout);
+      ll_store(ro, p * 32 + 16, r.z, fout);
+      ll_store(ro, p * 32 + 24, r.w, fout);
+    }
     L.sstep++;
   }
   if (F & kDst) small_user_store<E>(L, doff, nbytes, r);
-  if (F & kRecv) release_slot(L);
+  if (F & kRecv) release_slot<F>(L);
   return true;
 }
 
@@ -686,28 +794,21 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
-  if (F & kRecv) {
-    if (!wait_ge(L.w, L.in.tail, a.base + L.rstep + 1, L.tail_seen)) return false;
-  }
-  if (F & kSend) {
-    if (L.sstep >= (uint64_t)a.depth && !wait_ge(L.w, L.out.head, a.base + L.sstep + 1 - a.depth, L.head_seen)) return false;
-  }
+  if (!wait_inputs<F>(L) || !wait_outputs<F>(L)) return false;
   const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
-  u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
-  if (F & kRecv)
-    va = ld16<kSC1>(make_rsrc(L.in.fifo + (L.rstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
+  const uint64_t rslot = (L.rstep & (a.depth - 1)) * kSimpleSlotBytes;
+  const uint64_t sslot = (L.sstep & (a.depth - 1)) * kSimpleSlotBytes;
+  u32x4 va = u32x4{0u, 0u, 0u, 0u}, va2 = va, vb = va;
+  if (F & kRecv) va = ld16<kSC1>(make_rsrc(L.in[0].fifo + rslot, npk * 16), p * 16);
+  if (F & kRecv2) va2 = ld16<kSC1>(make_rsrc(L.in[1].fifo + rslot, npk * 16), p * 16);
   if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
-  const u32x4 r = combine<E, OP, F>(va, vb);
-  if (F & kSend)
-    st16<kSC1>(r, make_rsrc(L.out.fifo + (L.sstep & (a.depth - 1)) * kSimpleSlotBytes, npk * 16), p * 16);
+  const u32x4 r = combine<E, OP, F>(va, va2, vb);
+  if (F & kSend) st16<kSC1>(r, make_rsrc(L.out[0].fifo + sslot, npk * 16), p * 16);
+  if (F & kSend2) st16<kSC1>(r, make_rsrc(L.out[1].fifo + sslot, npk * 16), p * 16);
   if (F & kDst) small_user_store<E>(L, doff, nbytes, r);
-  if (F & kSend) {
-    wait_mem();
-    st_relaxed(L.out.tail, a.base + L.sstep + 1);
-    L.sstep++;
-  }
-  if (F & kRecv) release_slot(L);
+  if (F & kSend) publish_tails<F>(L);
+  if (F & kRecv) release_slot<F>(L);
   return true;
 }
 
@@ -766,15 +867,10 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
   L.lane = threadIdx.x & 63;
   L.sstep = 0;
   L.rstep = 0;
-  L.tail_seen = 0;     // below any value a wait of this call asks for
-  L.head_seen = 0;
-  const uint64_t cin = conn_index(c, ri, l, n, a.lanes);
-  const uint64_t cout = conn_index(c, (ri + 1) % n, l, n, a.lanes);
-  const uint64_t conn_bytes = fifo_conn_bytes(PROTO);
-  L.in = Conn{a.fifo + cin * conn_bytes, a.counters + cin * kCounterWords + kTailWord,
-              a.counters + cin * kCounterWords + kHeadWord};
-  L.out = Conn{a.fifo + cout * conn_bytes, a.counters + cout * kCounterWords + kTailWord,
-               a.counters + cout * kCounterWords + kHeadWord};
+  L.tail_seen[0] = L.tail_seen[1] = 0;   // below any value a wait of this call asks for
+  L.head_seen[0] = L.head_seen[1] = 0;
+  L.in[0] = conn_at<PROTO>(a, conn_index(c, ri, l, n, a.lanes));
+  L.out[0] = conn_at<PROTO>(a, conn_index(c, (ri + 1) % n, l, n, a.lanes));
   L.src = a.send[ri];
   L.dst = a.recv[ri];
 
@@ -827,6 +923,112 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
         if (!ok) return;
       }
     }
+  }
+}
+
+// ----------------------------------------------------------------- tree
+// One launch of the tree AllReduce over the double binary tree of
+// [ARCH] §五.4 (channel c runs on tree c % 2): the reduce runs up the tree
+// and the root's result is broadcast back down ([ARCH] §七.1 and §九.4,
+// runTreeUpDown / runTreeSplit), with the up and down directions on separate
+// wavefronts so that each chunk starts down as soon as the root has it.
+// Per chunk of the channel, in lane parts as on the ring:
+//   reduce role of v:    own input folded with child 0's, then child 1's
+//                        partial result (each hop op(received, local)),
+//                        sent to the parent (leaves: send only);
+//   root:                the same fold, written to its output and sent to
+//                        its children;
+//   broadcast role of v: receives the result from the parent, writes its
+//                        output and forwards it to its children.
+// Every connection carries the same sequence of slices, so producer and
+// consumer agree on step numbers as on the ring.
+template <class E, int OP, int PROTO, bool SMALL, int F>
+__device__ __forceinline__ bool tree_chunks(Lane& L, uint64_t lo, uint64_t len, int l, uint32_t es) {
+  const KernelArgs& a = *L.a;
+  for (uint64_t off = 0; off < len; off += a.chunk_elems) {
+    const uint64_t cur = min_u64(a.chunk_elems, len - off);
+    const uint64_t part = lane_part(cur, a.lanes, es);
+    uint64_t ls, ll;
+    lane_bounds(cur, part, l, &ls, &ll);
+    const uint64_t e0 = lo + off + ls;
+    if (!primitive<E, OP, PROTO, F, SMALL>(L, e0, e0, ll)) return false;
+  }
+  return true;
+}
+
+template <class E, int OP, int PROTO, bool SMALL>
+__global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
+  static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
+  const KernelArgs& a = ta.k;
+  const int n = a.nranks;
+  const int R = tree_roles(n);
+  const int wave = threadIdx.x >> 6;
+  const int role = blockIdx.x % R;
+  const int group = blockIdx.x / R;
+  const int lane_blocks = a.lanes / a.lanes_per_block;
+  const int c = group / lane_blocks;
+  const int l = (group % lane_blocks) * a.lanes_per_block + wave;
+  const int t = c & 1;
+  const int root = ta.root[t];
+  const bool bcast = role >= n;
+  int v = role;
+  if (bcast) {
+    v = role - n;
+    if (v >= root) v++;
+  }
+  if (v == a.skip_ring_index) return;
+  const uint32_t es = sizeof(typename E::T);
+
+  Lane L;
+  L.a = &a;
+  L.w.a = &a;
+  L.lane = threadIdx.x & 63;
+  L.sstep = 0;
+  L.rstep = 0;
+  L.tail_seen[0] = L.tail_seen[1] = 0;
+  L.head_seen[0] = L.head_seen[1] = 0;
+  L.src = a.send[v];
+  L.dst = a.recv[v];
+  // present children in child-slot order: k0 first, then k1 (-1 = none);
+  // an unused connection points at k0's so that it is still a valid address
+  const int s0 = ta.child[t][0][v], s1 = ta.child[t][1][v];
+  const int k0 = s0 >= 0 ? s0 : s1;
+  const int k1 = s0 >= 0 ? s1 : -1;
+  const int nk = (k0 >= 0 ? 1 : 0) + (k1 >= 0 ? 1 : 0);
+  const int k0c = k0 >= 0 ? k0 : v, k1c = k1 >= 0 ? k1 : k0c;
+  if (!bcast) {
+    // inputs: the children's up connections
+    L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kUp, l, n, a.lanes));
+    L.in[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kUp, l, n, a.lanes));
+    if (v == root) {
+      L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
+      L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
+    } else {
+      L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kUp, l, n, a.lanes));
+      L.out[1] = L.out[0];
+    }
+  } else {
+    L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kDown, l, n, a.lanes));
+    L.in[1] = L.in[0];
+    L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
+    L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
+  }
+
+  uint64_t lo, hi;
+  channel_bounds(a.count, a.per_channel, c, &lo, &hi);
+  const uint64_t len = hi - lo;
+  if (!bcast && v == root) {
+    // (n >= 2, so the root has at least one child)
+    if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kDst | kSend>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kRecv2 | kDst | kSend | kSend2>(L, lo, len, l, es);
+  } else if (!bcast) {
+    if (nk == 0) tree_chunks<E, OP, PROTO, SMALL, kSrc | kSend>(L, lo, len, l, es);
+    else if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kSend>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kRecv2 | kSend>(L, lo, len, l, es);
+  } else {
+    if (nk == 0) tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst>(L, lo, len, l, es);
+    else if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst | kSend>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst | kSend | kSend2>(L, lo, len, l, es);
   }
 }
 

@@ -1,4 +1,4 @@
-// Kernel dispatch by (collective, dtype, op, protocol, form), occupancy query and the fill
+// Kernel dispatch by (launch kind, dtype, op, protocol, form), occupancy query and the fill
 // kernel that clears FIFO memory and counters.
 #include <hip/hip_runtime.h>
 
@@ -20,10 +20,26 @@ const void* kernel_rs_for_bf16(int op, int proto, bool small);
 const void* kernel_rs_for_f32(int op, int proto, bool small);
 const void* kernel_rs_for_f64(int op, int proto, bool small);
 const void* kernel_ag_for(int proto, bool small);
+const void* kernel_tree_for_i8(int op, int proto, bool small);
+const void* kernel_tree_for_i32(int op, int proto, bool small);
+const void* kernel_tree_for_f16(int op, int proto, bool small);
+const void* kernel_tree_for_bf16(int op, int proto, bool small);
+const void* kernel_tree_for_f32(int op, int proto, bool small);
+const void* kernel_tree_for_f64(int op, int proto, bool small);
 
 const void* kernel_for(int coll, int dtype, int op, int proto, bool small) {
   small = small && proto != kLL128;
   if (coll == kAllGather) return kernel_ag_for(proto, small);
+  if (coll == kTreeAllReduce) {
+    switch (dtype) {
+      case 0: return kernel_tree_for_i8(op, proto, small);
+      case 1: return kernel_tree_for_i32(op, proto, small);
+      case 2: return kernel_tree_for_f16(op, proto, small);
+      case 3: return kernel_tree_for_bf16(op, proto, small);
+      case 4: return kernel_tree_for_f32(op, proto, small);
+      default: return kernel_tree_for_f64(op, proto, small);
+    }
+  }
   if (coll == kReduceScatter) {
     switch (dtype) {
       case 0: return kernel_rs_for_i8(op, proto, small);
@@ -49,6 +65,13 @@ hipError_t launch_ring(int coll, int dtype, int op, int proto, bool small, const
   void* params[] = {const_cast<KernelArgs*>(&args)};
   return hipLaunchKernel(kernel_for(coll, dtype, op, proto, small), dim3(grid), dim3(block), params, 0,
                          stream);
+}
+
+hipError_t launch_tree(int dtype, int op, int proto, bool small, const TreeArgs& args, int grid, int block,
+                       hipStream_t stream) {
+  void* params[] = {const_cast<TreeArgs*>(&args)};
+  return hipLaunchKernel(kernel_for(kTreeAllReduce, dtype, op, proto, small), dim3(grid), dim3(block), params,
+                         0, stream);
 }
 
 hipError_t max_active_blocks(int coll, int dtype, int op, int proto, bool small, int block, int* per_cu) {

@@ -50,7 +50,7 @@ size_t elem_size(int dtype) {
 const char* kProtoName[3] = {"LL", "LL128", "Simple"};
 const char* kDtypeName[6] = {"int8", "int32", "float16", "bfloat16", "float32", "float64"};
 const char* kOpName[4] = {"sum", "prod", "min", "max"};
-const char* kCollName[3] = {"AllReduce", "ReduceScatter", "AllGather"};
+const char* kCollName[4] = {"AllReduce", "ReduceScatter", "AllGather", "Tree AllReduce"};
 
 // ---------------------------------------------------------------- env
 // RINGAR_* variables, each read once ([BOOK] §3.5: a parameter is read from
@@ -58,6 +58,7 @@ const char* kCollName[3] = {"AllReduce", "ReduceScatter", "AllGather"};
 struct Env {
   int debug = 0;
   int proto_mask = 7;          // protocols AUTO may pick (bit p = protocol p)
+  int algo_mask = 3;           // algorithms AUTO may pick (bit a = ringar_algo_t a)
   size_t chunk_bytes = 0;
   int max_nchannels = 0;
   uint32_t spin_limit_ms = 2000;
@@ -65,11 +66,13 @@ struct Env {
   int fifo_depth = 0;
 };
 
-// RINGAR_PROTO: comma-separated protocol names (case-insensitive); a leading
-// '^' excludes the listed ones instead ([ARCH] §八.5 NCCL_PROTO grammar,
-// reduced to one list without per-function groups).
-int parse_proto_list(const char* s) {
-  if (!s || !*s) return 7;
+// RINGAR_PROTO / RINGAR_ALGO: comma-separated names (case-insensitive); a
+// leading '^' excludes the listed ones instead ([ARCH] §八.5 NCCL_PROTO /
+// NCCL_ALGO grammar, reduced to one list without per-function groups).
+// names[i] sets bit i; an empty result means all.
+int parse_name_list(const char* s, const char* const* names, int count) {
+  const int all = (1 << count) - 1;
+  if (!s || !*s) return all;
   bool exclude = false;
   if (*s == '^') { exclude = true; s++; }
   int mask = 0;
@@ -77,9 +80,8 @@ int parse_proto_list(const char* s) {
   auto flush = [&]() {
     std::string t;
     for (char ch : tok) t += (char)tolower((unsigned char)ch);
-    if (t == "ll") mask |= 1;
-    else if (t == "ll128") mask |= 2;
-    else if (t == "simple") mask |= 4;
+    for (int i = 0; i < count; i++)
+      if (t == names[i]) mask |= 1 << i;
     tok.clear();
   };
   for (; *s; s++) {
@@ -87,16 +89,20 @@ int parse_proto_list(const char* s) {
     else if (!isspace((unsigned char)*s)) tok += *s;
   }
   flush();
-  int m = exclude ? (7 & ~mask) : mask;
-  return m ? m : 7;
+  int m = exclude ? (all & ~mask) : mask;
+  return m ? m : all;
 }
+
+const char* const kProtoKeys[3] = {"ll", "ll128", "simple"};
+const char* const kAlgoKeys[2] = {"ring", "tree"};
 
 const Env& env() {
   static Env e;
   static std::once_flag once;
   std::call_once(once, [] {
     if (const char* v = getenv("RINGAR_DEBUG")) e.debug = atoi(v);
-    e.proto_mask = parse_proto_list(getenv("RINGAR_PROTO"));
+    e.proto_mask = parse_name_list(getenv("RINGAR_PROTO"), kProtoKeys, 3);
+    e.algo_mask = parse_name_list(getenv("RINGAR_ALGO"), kAlgoKeys, 2);
     if (const char* v = getenv("RINGAR_CHUNK_BYTES")) e.chunk_bytes = strtoull(v, nullptr, 0);
     if (const char* v = getenv("RINGAR_MAX_NCHANNELS")) e.max_nchannels = atoi(v);
     if (const char* v = getenv("RINGAR_SPIN_LIMIT_MS")) e.spin_limit_ms = (uint32_t)strtoul(v, nullptr, 0);
@@ -130,7 +136,31 @@ ringar_model_t default_model() {
   m.default_chunk_bytes[0] = 32768;
   m.default_chunk_bytes[1] = 491520;
   m.default_chunk_bytes[2] = 524288;
+  // Tree rows: the pages' form with MI355X constants (see the ring's note).
+  m.tree_allreduce_eff = 0.92;
+  m.tree_per_channel_max_bw = 1e9;
+  m.tree_ll_divisor = 2.0;
+  m.tree_ll128_factor = 0.94;
+  m.tree_ll128_per_channel_max_bw = 1e9;
+  m.tree_base_lat_us[0] = 4.97; m.tree_base_lat_us[1] = 6.76; m.tree_base_lat_us[2] = 5.06;
+  m.tree_hw_lat_us[0] = 1.418; m.tree_hw_lat_us[1] = 2.692; m.tree_hw_lat_us[2] = 1.598;
+  m.tree_correction = 0;
   return m;
+}
+
+// Bandwidth correction of the Tree AllReduce by message size, per protocol,
+// indexed by floor(log2(bytes / 64)) ([BOOK] Japanese edition ch. 5 §四: the
+// pages' table, measured on NVIDIA systems; used only when a model sets
+// tree_correction).
+const float kTreeCorrection[3][24] = {
+    {1.0f, 1.0f, 1.0f, 1.0f, .9f, .8f, .7f, .7f, .7f, .7f, .6f, .5f, .4f, .4f, .5f, .6f, .7f, .8f, .9f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f},
+    {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, .9f, .8f, .8f, .8f, .7f, .6f, .6f, .6f, .6f, .6f, .6f, .8f, .9f, .9f, .9f, .9f, 1.0f, 1.0f, 1.0f},
+    {.9f, .9f, .9f, .9f, .9f, .9f, .9f, .8f, .7f, .6f, .6f, .5f, .5f, .5f, .5f, .6f, .7f, .8f, .7f, .7f, .8f, .9f, .9f, .9f}};
+
+int floor_log2(uint64_t x) {
+  int r = -1;
+  while (x) { x >>= 1; r++; }
+  return r;
 }
 
 // Bus bandwidth of protocol p on nch channels ([ARCH] §八.1).
@@ -150,6 +180,88 @@ double predict_us(const ringar_model_t& m, int n, int nch, int p, size_t bytes, 
   double alg = bus_bw(m, nch, p) * n / nsteps;
   double lat = m.base_lat_us[p] + nsteps * m.hw_lat_us[p];
   return lat + (double)bytes / (1000.0 * alg);
+}
+
+// Tree AllReduce bus bandwidth of protocol p on nch channels ([BOOK]
+// Japanese edition ch. 5 §四).
+double tree_bus_bw(const ringar_model_t& m, int nch, int p) {
+  double bus = std::min(nch * m.bw_per_channel * m.tree_allreduce_eff, nch * m.tree_per_channel_max_bw);
+  if (p == kLL) bus = std::min(bus / m.tree_ll_divisor, m.ll_max_bw);
+  else if (p == kLL128) bus = std::min(bus * m.tree_ll128_factor, nch * m.tree_ll128_per_channel_max_bw);
+  return bus;
+}
+
+// Predicted microseconds of one tree AllReduce: every rank is one vertex, so
+// the tree's depth term is 2 x floor(log2 n) steps; algorithm bandwidth =
+// bus bandwidth x 0.5, corrected by size when the model asks for it.
+double predict_tree_us(const ringar_model_t& m, int n, int nch, int p, size_t bytes) {
+  double alg = tree_bus_bw(m, nch, p) * 0.5;
+  const int ls = floor_log2((uint64_t)bytes >> 6);
+  if (m.tree_correction && ls >= 0 && ls < 23) alg *= kTreeCorrection[p][ls];
+  double lat = m.tree_base_lat_us[p] + 2.0 * floor_log2((uint64_t)n) * m.tree_hw_lat_us[p];
+  return lat + (double)bytes / (1000.0 * alg);
+}
+
+// Fastest enabled (algorithm, protocol) of an AllReduce.  Candidates are
+// numbered Tree LL, LL128, Simple, Ring LL, LL128, Simple (the pages' model
+// map) and visited from the last, replaced only on a strictly smaller time.
+// times6 receives the six times in that order.  Returns false when nothing
+// is enabled.
+bool select_algo_proto(const ringar_model_t& m, int n, int nch, size_t bytes, int algo_mask, int proto_mask,
+                       int* algo, int* proto, double* times6) {
+  double t[6];
+  for (int p = 0; p < 3; p++) {
+    t[p] = predict_tree_us(m, n, nch, p, bytes);
+    t[3 + p] = predict_us(m, n, nch, p, bytes);
+  }
+  if (times6) memcpy(times6, t, sizeof(t));
+  double best_t = INFINITY;
+  bool found = false;
+  for (int id = 5; id >= 0; id--) {
+    const int a = id >= 3 ? RINGAR_ALGO_RING : RINGAR_ALGO_TREE, p = id % 3;
+    if (!(algo_mask & (1 << a)) || !(proto_mask & (1 << p))) continue;
+    if (t[id] < best_t) {
+      best_t = t[id];
+      *algo = a;
+      *proto = p;
+      found = true;
+    }
+  }
+  return found;
+}
+
+// The binary tree of [ARCH] §五.4 over ranks 0..n-1: a rank's lowest set bit
+// b decides its level; its parent clears b and sets the bit above (or only
+// clears b when that rank does not exist); its children are rank - b/2 and
+// the largest rank + b/2^k (k >= 1) that exists.  Rank 0 is the root with the
+// single child B/2, B = the smallest power of two >= n.  The second tree
+// mirrors ranks (r -> n-1-r) for even n and shifts them by one for odd n.
+// Child slots keep their order through the renaming.
+void tree_links(int n, int t, int rank, int* up, int* c0, int* c1) {
+  int r = rank;
+  if (t == 1) r = (n % 2 == 0) ? n - 1 - rank : (rank + n - 1) % n;
+  int b = 1;
+  while (b < n && !(r & b)) b <<= 1;
+  int u, d0, d1;
+  if (r == 0) {
+    u = -1;
+    d0 = -1;
+    d1 = n > 1 ? b >> 1 : -1;
+  } else {
+    u = (r ^ b) | (b << 1);
+    if (u >= n) u = r ^ b;
+    d0 = (b >> 1) ? r - (b >> 1) : -1;
+    d1 = -1;
+    for (int h = b >> 1; h > 0; h >>= 1)
+      if (r + h < n) { d1 = r + h; break; }
+  }
+  auto back = [&](int x) {
+    if (x < 0 || t == 0) return x;
+    return (n % 2 == 0) ? n - 1 - x : (x + 1) % n;
+  };
+  *up = back(u);
+  *c0 = back(d0);
+  *c1 = back(d1);
 }
 
 int model_max_channels(const ringar_model_t& m, int n) {
@@ -173,17 +285,28 @@ int select_proto(const ringar_model_t& m, int n, int nch, size_t bytes, int mask
   return best;
 }
 
+// Fastest enabled protocol of three model times (the tie rule of
+// select_proto); -1 when none is enabled.
+int select_proto_of(const double* times, int mask) {
+  int best = -1;
+  double best_t = INFINITY;
+  for (int p = 2; p >= 0; p--)
+    if ((mask & (1 << p)) && times[p] < best_t) { best = p; best_t = times[p]; }
+  return best;
+}
+
 // Channel count by size ([ARCH] §六.4): drop channels while each thread would
 // get fewer than threshold bytes; LL's threshold is multiplied by n on a ring.
-int auto_channels(const ringar_model_t& m, int n, int p, size_t bytes, int start) {
+int auto_channels(const ringar_model_t& m, int n, int p, size_t bytes, int start, bool ring = true) {
   int nc = start;
-  double thr = (double)m.thread_threshold[p] * (p == kLL ? n : 1);
+  double thr = (double)m.thread_threshold[p] * (p == kLL && ring ? n : 1);
   while (nc > 1 && (double)bytes < (double)nc * m.threads[p] * thr) nc--;
   return nc;
 }
 
 // ---------------------------------------------------------------- plan
 struct Plan {
+  int kind = kAllReduce;   // launch kind (kTreeAllReduce for the tree)
   int proto = kSimple;
   int nch = 1;
   size_t chunk_bytes = 0;
@@ -196,7 +319,10 @@ struct Plan {
   int grid = 0;
   int block = 64;
   uint64_t max_steps = 0;
+  uint64_t conns = 0;      // FIFO connections of the launch
   double times[3] = {0, 0, 0};
+  double tree_times[3] = {0, 0, 0};
+  double ring_times[3] = {0, 0, 0};
 };
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -220,8 +346,9 @@ uint64_t fifo_bytes_for(int proto, uint64_t bytes) {
 
 // capacity_waves: wavefronts of this kernel the GPU holds at once (0 when no
 // GPU is visible: then 4096 is assumed).
-// coll: kAllReduce (count = elements per rank) or one of its halves (count =
-// elements per block; AllGather plans bytes, dtype int8).
+// coll: kAllReduce (count = elements per rank; the algorithm comes from the
+// config) or one of its halves (count = elements per block; AllGather plans
+// bytes, dtype int8).
 ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannels, int proto,
                           const ringar_config_t* cfg, uint64_t capacity_waves, Plan* out) {
   const Env& E = env();
@@ -230,6 +357,9 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   if (n < 1 || n > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
   if (nchannels < 0 || nchannels > kMaxChannels) return RINGAR_ERR_INVALID_ARGUMENT;
   if (proto < RINGAR_PROTO_AUTO || proto > RINGAR_PROTO_SIMPLE) return RINGAR_ERR_INVALID_ARGUMENT;
+  const int algo_req = cfg ? cfg->algo : RINGAR_ALGO_RING;
+  if (algo_req < RINGAR_ALGO_RING || algo_req > RINGAR_ALGO_AUTO) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (coll != kAllReduce && algo_req == RINGAR_ALGO_TREE) return RINGAR_ERR_INVALID_ARGUMENT;
   ringar_model_t dm = default_model();
   const ringar_model_t& m = (cfg && cfg->model) ? *cfg->model : dm;
   size_t chunk_bytes = (cfg && cfg->chunk_bytes) ? cfg->chunk_bytes : E.chunk_bytes;
@@ -245,9 +375,29 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   int maxc = model_max_channels(m, n);
   if (E.max_nchannels > 0) maxc = std::min(maxc, E.max_nchannels);
   const int model_nch = nchannels > 0 ? nchannels : maxc;
-  int best = select_proto(m, n, model_nch, bytes, E.proto_mask, P.times, coll);
+  int best = select_proto(m, n, model_nch, bytes, E.proto_mask, P.ring_times, coll);
+  // Algorithm: the ring unless the config asks for the tree, or for the
+  // model's choice (AllReduce only, more than one rank).
+  bool tree = false;
+  if (!halves && n > 1) {
+    for (int p = 0; p < 3; p++) P.tree_times[p] = predict_tree_us(m, n, model_nch, p, bytes);
+    if (algo_req == RINGAR_ALGO_TREE) {
+      tree = true;
+      best = select_proto_of(P.tree_times, E.proto_mask);
+    } else if (algo_req == RINGAR_ALGO_AUTO) {
+      int a = RINGAR_ALGO_RING, p = best;
+      const int pmask = proto >= 0 ? (1 << proto) : E.proto_mask;
+      if (select_algo_proto(m, n, model_nch, bytes, E.algo_mask, pmask, &a, &p, nullptr)) {
+        tree = a == RINGAR_ALGO_TREE;
+        best = p;
+      }
+    }
+  }
+  if (proto < 0 && best < 0 && n > 1) return RINGAR_ERR_INVALID_USAGE;
+  P.kind = tree ? kTreeAllReduce : coll;
+  memcpy(P.times, tree ? P.tree_times : P.ring_times, sizeof(P.times));
   P.proto = proto >= 0 ? proto : (n == 1 ? (int)kSimple : best);
-  P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc));
+  P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc, !tree));
   P.chunk_bytes = chunk_bytes ? chunk_bytes : m.default_chunk_bytes[P.proto];
   if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)
     return RINGAR_ERR_INVALID_ARGUMENT;
@@ -265,21 +415,24 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // lanes, 4096 wavefronts, ran 11% faster than 16 lanes) and never more
   // than the GPU holds at once (all of them wait on each other).  Lanes
   // change no result.
-  // (The halves' loops take up to one chunk of every block.)
+  // (The halves' loops take up to one chunk of every block, the tree's one
+  // chunk of the channel.)
   const uint64_t first_chunk =
-      halves ? std::max<uint64_t>(1, std::min<uint64_t>(P.chunk_elems, P.per_channel))
+      (halves || tree) ? std::max<uint64_t>(1, std::min<uint64_t>(P.chunk_elems, P.per_channel))
       : P.per_channel >= (uint64_t)n * P.chunk_elems
           ? P.chunk_elems
           : align_up(div_up(std::max<uint64_t>(1, P.per_channel), (uint64_t)n), align_elems((uint32_t)es));
   const uint64_t slot = slot_elems(P.proto, (uint32_t)es);
   auto slices_for = [&](int L) { return div_up(lane_part(first_chunk, L, (uint32_t)es), slot); };
+  // wavefronts per lane: one per rank on the ring, 2n - 1 roles on the tree
+  const uint64_t waves_per_lane = (uint64_t)(tree ? tree_roles(n) : n) * P.nch;
   const bool forced_lanes = lanes != 0;
   if (!forced_lanes) {
     const uint64_t want = std::max<uint64_t>(1, div_up(first_chunk * es, kLaneGranBytes));
     lanes = 1;
     while (lanes < (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
     const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
-    while (lanes > 1 && (uint64_t)n * P.nch * lanes > cap && slices_for(lanes / 2) <= kMaxSlicesPerPart)
+    while (lanes > 1 && waves_per_lane * lanes > cap && slices_for(lanes / 2) <= kMaxSlicesPerPart)
       lanes /= 2;
     while (lanes < kMaxLanes && slices_for(lanes) > kMaxSlicesPerPart) lanes *= 2;
   }
@@ -289,7 +442,7 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
 
   // FIFO depth: the deepest of 8, 4, 2 slots whose footprint fits
   // kFifoBudgetBytes, but always at least twice the slots of a part.
-  const uint64_t waves = (uint64_t)n * P.nch * lanes;
+  const uint64_t waves = waves_per_lane * lanes;
   const uint64_t step_bytes =
       fifo_bytes_for(P.proto, std::min<uint64_t>(lane_part(first_chunk, lanes, (uint32_t)es), slot) * es);
   if (depth) {
@@ -308,12 +461,14 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   P.lanes_per_block = std::min(lanes, 4);
   P.block = 64 * P.lanes_per_block;
   const int groups = P.nch * (lanes / P.lanes_per_block);
-  P.grid = n * groups;
+  P.grid = (tree ? tree_roles(n) : n) * groups;
+  P.conns = (uint64_t)P.nch * n * lanes * (tree ? 2 : 1);
 
   // Upper bound of FIFO steps any connection takes in this call.
   const uint64_t loops =
-      std::max<uint64_t>(1, div_up(P.per_channel, (halves ? 1 : (uint64_t)n) * P.chunk_elems));
-  P.max_steps = loops * (uint64_t)(halves ? n : 2 * n - 1) * (slices_for(lanes) + 1);
+      std::max<uint64_t>(1, div_up(P.per_channel, ((halves || tree) ? 1 : (uint64_t)n) * P.chunk_elems));
+  const uint64_t prims = tree ? 1 : (uint64_t)(halves ? n : 2 * n - 1);   // primitives per loop
+  P.max_steps = loops * prims * (slices_for(lanes) + 1);
   *out = P;
   return RINGAR_SUCCESS;
 }
@@ -404,7 +559,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   if (ndev == 0) return 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const long long key = ((((long long)dev * 3 + coll) * 8 + dtype) * 4 + op) * 3 + proto;
+  const long long key = ((((long long)dev * 4 + coll) * 8 + dtype) * 4 + op) * 3 + proto;
   // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
@@ -514,6 +669,36 @@ ringar_result_t ringar_select(size_t bytes, int nranks, int nchannels, const rin
   return RINGAR_SUCCESS;
 }
 
+ringar_result_t ringar_tree(int nranks, int tree, int rank, int* parent, int* child0, int* child1) {
+  if (nranks < 1 || nranks > kMaxRanks || tree < 0 || tree > 1 || rank < 0 || rank >= nranks || !parent ||
+      !child0 || !child1)
+    return RINGAR_ERR_INVALID_ARGUMENT;
+  tree_links(nranks, tree, rank, parent, child0, child1);
+  return RINGAR_SUCCESS;
+}
+
+ringar_result_t ringar_select_algo(size_t bytes, int nranks, int nchannels, const ringar_model_t* model,
+                                   ringar_algo_t* algo, ringar_proto_t* proto, double* predicted_us) {
+  if (!algo || !proto || nranks < 1 || nranks > kMaxRanks || nchannels < 0 || nchannels > kMaxChannels)
+    return RINGAR_ERR_INVALID_ARGUMENT;
+  ringar_model_t dm = default_model();
+  const ringar_model_t& m = model ? *model : dm;
+  if (nranks == 1) {
+    *algo = RINGAR_ALGO_RING;
+    *proto = RINGAR_PROTO_SIMPLE;
+    if (predicted_us)
+      for (int i = 0; i < 6; i++) predicted_us[i] = 0.0;
+    return RINGAR_SUCCESS;
+  }
+  const int nch = nchannels > 0 ? nchannels : model_max_channels(m, nranks);
+  int a = 0, p = 0;
+  if (!select_algo_proto(m, nranks, nch, bytes, env().algo_mask, env().proto_mask, &a, &p, predicted_us))
+    return RINGAR_ERR_INVALID_USAGE;
+  *algo = (ringar_algo_t)a;
+  *proto = (ringar_proto_t)p;
+  return RINGAR_SUCCESS;
+}
+
 // The (count, dtype) a collective's kernels work on: AllGather is a byte copy.
 static void kernel_shape(int coll, size_t count, int dtype, size_t* kcount, int* kdtype) {
   const size_t es = elem_size(dtype);
@@ -527,7 +712,7 @@ static ringar_result_t plan_for_launch(int coll, size_t count, int dtype, int op
   ringar_result_t r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, 0, P);
   if (r != RINGAR_SUCCESS) return r;
   if (count > 0 && nranks > 1) {
-    const uint64_t cap = capacity_waves(coll, dtype, op, P->proto);
+    const uint64_t cap = capacity_waves(P->kind, dtype, op, P->proto);
     if (cap && (r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, cap, P)) != RINGAR_SUCCESS)
       return r;
   }
@@ -558,7 +743,12 @@ ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_
   out->workgroups = P.grid;
   out->threads_per_group = P.block;
   out->max_steps = P.max_steps;
-  for (int p = 0; p < 3; p++) out->predicted_us[p] = P.times[p];
+  for (int p = 0; p < 3; p++) {
+    out->predicted_us[p] = P.times[p];
+    out->predicted_tree_us[p] = P.tree_times[p];
+    out->predicted_ring_us[p] = P.ring_times[p];
+  }
+  out->algo = P.kind == kTreeAllReduce ? RINGAR_ALGO_TREE : RINGAR_ALGO_RING;
   return RINGAR_SUCCESS;
 }
 
@@ -629,17 +819,16 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   const bool small = P.small && vec;
   const long long okey =
-      ((((long long)coll * 8 + dtype) * 4 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
+      ((((long long)P.kind * 8 + dtype) * 4 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;
-    HIP_TRY(max_active_blocks(coll, dtype, op, P.proto, small, P.block, &per_cu));
+    HIP_TRY(max_active_blocks(P.kind, dtype, op, P.proto, small, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
   if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
 
-  const uint64_t conns = (uint64_t)P.nch * nranks * P.lanes;
-  if ((r = ensure_conns(*R, st, P.proto, conns)) != RINGAR_SUCCESS) return r;
+  if ((r = ensure_conns(*R, st, P.proto, P.conns)) != RINGAR_SUCCESS) return r;
   // LL flags are 32-bit step numbers: restart the numbering before it wraps.
   if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
     if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;
@@ -676,14 +865,37 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   }
   A.vec_ok = vec;
 
-  HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, A, P.grid, P.block, st));
+  if (P.kind == kTreeAllReduce) {
+    // the tree runs over ranks 0..n-1 (a ring order does not apply)
+    TreeArgs T;
+    memset(&T, 0, sizeof(T));
+    T.k = A;
+    for (int i = 0; i < nranks; i++) {
+      T.k.send[i] = (const char*)sendbuffs[i];
+      T.k.recv[i] = (char*)recvbuffs[i];
+      T.k.rank_of[i] = i;
+    }
+    T.k.skip_ring_index = (cfg && cfg->skip_rank >= 0 && cfg->skip_rank < nranks) ? cfg->skip_rank : -1;
+    for (int t = 0; t < 2; t++)
+      for (int v = 0; v < nranks; v++) {
+        int u, c0, c1;
+        tree_links(nranks, t, v, &u, &c0, &c1);
+        T.parent[t][v] = (int8_t)u;
+        T.child[t][0][v] = (int8_t)c0;
+        T.child[t][1][v] = (int8_t)c1;
+        if (u < 0) T.root[t] = v;
+      }
+    HIP_TRY(launch_tree(dtype, op, P.proto, small, T, P.grid, P.block, st));
+  } else {
+    HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, A, P.grid, P.block, st));
+  }
   R->base += P.max_steps + 1;
 
   if (env().debug) {
     fprintf(stderr,
             "ringar: %s %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
             "depth %d%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
-            kCollName[coll], count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
+            kCollName[P.kind], count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
             P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", P.grid, P.block, P.times[0], P.times[1], P.times[2]);
   }
   return RINGAR_SUCCESS;

@@ -32,3 +32,15 @@ def oracle_model(d=None) -> S.RingModel:
 
 def lib_model(d) -> "ra.ringar_model_t":
     return ra.model_from_dict(d)
+
+
+def oracle_tree_model(d, nranks) -> S.TreeModel:
+    """The library's Tree rows as the oracle's model: every virtual rank one
+    vertex (n_nodes = n, one rank per node), the per-level latency as the
+    inter-node step."""
+    return S.TreeModel(bw_per_channel=d["bw_per_channel"], per_channel_max_bw=d["tree_per_channel_max_bw"],
+                       ll_max_bw=d["ll_max_bw"], per_channel_max_ll128_bw=d["tree_ll128_per_channel_max_bw"],
+                       allreduce_eff=d["tree_allreduce_eff"], ll_divisor=d["tree_ll_divisor"],
+                       n_nodes=nranks, ranks_per_node=1, base_lat=tuple(d["tree_base_lat_us"]),
+                       intra_lat=(0.0, 0.0, 0.0), inter_lat=tuple(d["tree_hw_lat_us"]),
+                       correction=bool(d["tree_correction"]), ll128_factor=d["tree_ll128_factor"])

@@ -1,0 +1,145 @@
+"""Host logic of the tree AllReduce in the C-ABI library, on the CPU: the
+library's tree builder equals the oracle's, its plan has the tree's geometry,
+its (algorithm, protocol) choice equals the oracle model's for the same
+constants, and bad requests fail before anything reaches a GPU."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import ring_allreduce_reduce_amd as ra
+from libutil import golden_model_dict, lib, lib_model, oracle_model, oracle_tree_model
+from oracle import select as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+E = ra
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    lib()
+
+
+@pytest.mark.parametrize("n", list(range(1, 65)))
+def test_library_tree_equals_oracle_tree(n):
+    for t in (0, 1):
+        for r in range(n):
+            assert ra.ringar_tree(n, t, r) == oracle.dtree(n, r, t), (n, t, r)
+
+
+def test_tree_query_errors():
+    for args in [(0, 0, 0), (65, 0, 0), (8, 2, 0), (8, 0, 8), (8, -1, 0)]:
+        with pytest.raises(ra.RingarError):
+            ra.ringar_tree(*args)
+
+
+@pytest.mark.parametrize("n,count,nch,proto", [(8, 1 << 24, 16, "Simple"), (8, 1 << 15, 8, "LL"),
+                                               (5, 1000, 3, "LL128"), (2, 17, 1, "Simple")])
+def test_tree_plan_geometry(n, count, nch, proto):
+    cfg = ra.make_config(algo="tree")
+    p = ra.ringar_plan(count, "float32", n, nch, proto, cfg)
+    assert p.algo == 1
+    assert p.nchannels == nch
+    lanes_per_block = min(p.lanes, 4)
+    assert p.threads_per_group == 64 * lanes_per_block
+    assert p.workgroups == (2 * n - 1) * nch * (p.lanes // lanes_per_block)
+    # the tree moves one chunk of the channel per step: a lane part is at
+    # most half the FIFO
+    slot = {"Simple": 32768, "LL": 8192, "LL128": 30720}[proto] // 4
+    part = -(-min(p.chunk_elems, p.channel_elems) // p.lanes)
+    part = -(-part // 256) * 256
+    assert -(-part // slot) <= p.fifo_depth // 2
+    assert list(p.predicted_us) == list(p.predicted_tree_us)
+    ring = ra.ringar_plan(count, "float32", n, nch, proto)
+    assert ring.algo == 0 and list(ring.predicted_us) == list(ring.predicted_ring_us)
+
+
+def test_tree_is_allreduce_only():
+    cfg = ra.make_config(algo="tree")
+    for coll in ("reduce_scatter", "all_gather"):
+        with pytest.raises(ra.RingarError) as e:
+            ra.ringar_plan_coll(coll, 1024, "float32", 8, 0, "auto", cfg)
+        assert e.value.code == E.INVALID_ARGUMENT
+    # AUTO picks the ring for the halves
+    p = ra.ringar_plan_coll("reduce_scatter", 1024, "float32", 8, 0, "auto", ra.make_config(algo="auto"))
+    assert p.algo == 0
+    cfg = ra.make_config()
+    cfg.algo = 7
+    with pytest.raises(ra.RingarError):
+        ra.ringar_plan(1024, "float32", 8, 0, "auto", cfg)
+
+
+def _perturbed(d, k):
+    """The golden model with tree constants spread out so that every
+    candidate wins somewhere in a size sweep."""
+    d = dict(d)
+    d.update(tree_allreduce_eff=[0.92, 0.8, 1.1][k], tree_ll_divisor=[2.0, 3.8, 1.5][k],
+             tree_ll128_factor=[0.94, 7 / 9, 0.5][k], tree_per_channel_max_bw=[1e9, 6.0, 9.0][k],
+             tree_ll128_per_channel_max_bw=[1e9, 4.0, 2.0][k],
+             tree_base_lat_us=[[3.0, 5.0, 4.0], [6.8, 14.0, 8.4], [2.0, 9.0, 3.0]][k],
+             tree_hw_lat_us=[[1.0, 2.0, 1.2], [0.6, 1.25, 4.0], [3.0, 1.0, 2.0]][k],
+             tree_correction=[0, 1, 1][k])
+    return d
+
+
+@pytest.mark.parametrize("k", [0, 1, 2])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_select_algo_matches_oracle_model(k, n):
+    d = _perturbed(golden_model_dict(), k)
+    m = lib_model(d)
+    ring, tree = oracle_model(d), oracle_tree_model(d, n)
+    for nch in (1, 4, 16):
+        for nbytes in [0, 8, 1000, 1 << 12, 1 << 16, 1 << 20, 3 << 22, 1 << 26, 1 << 30]:
+            a, p, t = ra.ringar_select_algo(nbytes, n, nch, m)
+            (oa, op), ot = S.select_algo(ring, tree, n, nch, nbytes)
+            assert (a, p) == (oa.lower(), op), (nch, nbytes)
+            assert np.allclose(t, ot, rtol=1e-6, atol=0)
+
+
+def test_auto_plan_follows_the_model():
+    d = _perturbed(golden_model_dict(), 2)
+    m = lib_model(d)
+    seen = set()
+    for nbytes in [8, 1 << 12, 1 << 16, 1 << 20, 1 << 24, 1 << 28]:
+        a, p, _ = ra.ringar_select_algo(nbytes, 8, 0, m)
+        plan = ra.ringar_plan(nbytes // 4, "float32", 8, 0, "auto", ra.make_config(algo="auto", model=m))
+        assert (ra.ALGO_NAMES[plan.algo], ra.PROTO_NAMES[plan.proto]) == (a, p)
+        seen.add(a)
+        # a forced protocol keeps the faster algorithm for that protocol
+        for fp in ("LL", "Simple"):
+            plan = ra.ringar_plan(nbytes // 4, "float32", 8, 0, fp, ra.make_config(algo="auto", model=m))
+            times = [plan.predicted_tree_us[ra.PROTOS[fp]], plan.predicted_ring_us[ra.PROTOS[fp]]]
+            want = "tree" if times[0] < times[1] else "ring"
+            assert ra.ALGO_NAMES[plan.algo] == want
+    assert seen == {"ring", "tree"}
+
+
+def test_algo_env_grammar():
+    code = (
+        "import sys; sys.path.insert(0, %r); import ring_allreduce_reduce_amd as ra;"
+        "a = [ra.ringar_select_algo(b, 8)[0] for b in (8, 1 << 30)]; print(*a)" % ROOT)
+    out = {}
+    for v in ["tree", "^tree", "ring", "Tree,Ring"]:
+        env = dict(os.environ, RINGAR_ALGO=v)
+        out[v] = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                                check=True).stdout.split()
+    assert out["tree"] == ["tree", "tree"]
+    assert out["^tree"] == ["ring", "ring"]
+    assert out["ring"] == ["ring", "ring"]
+
+
+def test_tree_buffer_errors_before_any_device_call():
+    n, count = 4, 256
+    s = [0x10000 * (i + 1) for i in range(n)]
+    r = [0x100000 * (i + 1) for i in range(n)]
+    cfg = ra.make_config(algo="tree")
+    r2 = list(r)
+    r2[2] = r2[1]
+    assert ra.ringar_allreduce_ex(s, r2, count, "float32", "sum", n, 2, "Simple", 0, cfg) == E.INVALID_USAGE
+    r3 = list(r)
+    r3[0] = 0
+    assert ra.ringar_allreduce_ex(s, r3, count, "float32", "sum", n, 2, "Simple", 0, cfg) == E.INVALID_ARGUMENT
+    assert ra.ringar_allreduce_ex(s, r, 0, "float32", "sum", n, 2, "Simple", 0, cfg) == E.SUCCESS
