@@ -12,7 +12,9 @@ last timed call bit for bit.
 
 `--coll reduce_scatter` / `--coll all_gather` time the two halves of the
 ring on the same shape instead (8 ranks, 64 MiB n-block buffer per rank, 8 MiB
-blocks); their busbw is algbw x (n-1)/n.
+blocks); their busbw is algbw x (n-1)/n.  `--algo tree` times the tree
+AllReduce (double binary tree, channel c on tree c % 2) on the AllReduce
+workload; its busbw keeps the AllReduce convention algbw x 2(n-1)/n.
 """
 import argparse
 import glob
@@ -65,7 +67,9 @@ def alg_bytes(n, s, e=1.0, coll="allreduce"):
     per rank: every rank reads its send buffer once and writes its receive
     buffer once, and each of the 2(n-1) steps writes and reads one chunk
     through a FIFO whose bytes are e times the payload (Simple 1, LL 2, LL128
-    128/120).  ReduceScatter / AllGather with s bytes in the n-block buffer of
+    128/120).  The tree AllReduce moves the same bytes: each of the n-1
+    non-root vertices sends the whole buffer up once and receives it down
+    once through a FIFO, 4(n-1) e s in all, plus the 2n s of user buffers.  ReduceScatter / AllGather with s bytes in the n-block buffer of
     each rank: every rank reads its input once (s, resp. s/n), writes its
     output once (s/n, resp. s), and each of the n-1 steps writes and reads one
     block through the FIFO."""
@@ -84,6 +88,8 @@ def main():
                     help="also run a plain 256 MiB device copy (for scaling memory counters)")
     ap.add_argument("--coll", default="allreduce", choices=["allreduce", "reduce_scatter", "all_gather"],
                     help="the AllReduce (default) or one of its halves on the same 8 x 64 MiB shape")
+    ap.add_argument("--algo", default="ring", choices=["ring", "tree"],
+                    help="AllReduce algorithm: the ring (default) or the double binary tree")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the {NRANKS} ranks are virtual ranks inside one MI355X; "
@@ -100,6 +106,7 @@ def main():
     from ring_allreduce_reduce_amd import workloads as W
 
     coll = args.coll
+    algo = args.algo if coll == "allreduce" else "ring"
     count = BYTES_PER_RANK // 4              # elements in the n-block buffer of a rank
     block = count // NRANKS
     log("generating inputs")
@@ -113,7 +120,7 @@ def main():
         sends = [W.to_torch(x, "float32", dev) for x in xs]
         recvs = [torch.empty(count if coll == "allreduce" else block, device=dev) for _ in sends]
     stream = torch.cuda.Stream()
-    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES)
+    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES, algo=algo)
     plan = ra.ringar_plan_coll(coll, count if coll == "allreduce" else block, "float32", NRANKS, NCHANNELS,
                                "Simple", cfg)
     send_ptrs = [s.data_ptr() for s in sends]
@@ -176,9 +183,11 @@ def main():
     busbw = algbw * bus_factor
     b_alg = alg_bytes(NRANKS, s, coll=coll)
     achieved = b_alg / (avg_launch_ms * 1e-3) / 1e9
-    traffic = read_traffic() if coll == "allreduce" else None
+    traffic = read_traffic() if coll == "allreduce" and algo == "ring" else None
 
     def run_oracle():
+        if coll == "allreduce" and algo == "tree":
+            return oracle.tree_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
         if coll == "allreduce":
             return oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
         if coll == "reduce_scatter":
@@ -207,11 +216,12 @@ def main():
                "sample": f"the full workload (8 ranks x 64 MiB fp32) repeated {calls} times (~10 s), "
                          "single-threaded C oracle; value is busbw"}
 
-    what = {"allreduce": ("ring AllReduce", "64 MiB per rank"),
+    what = {"allreduce": (f"{algo} AllReduce", "64 MiB per rank"),
             "reduce_scatter": ("ring ReduceScatter", "64 MiB input per rank (8 blocks of 8 MiB)"),
             "all_gather": ("ring AllGather", "8 MiB input, 64 MiB output per rank")}[coll]
     out = {
-        "metric": METRIC if coll == "allreduce" else
+        "metric": METRIC if coll == "allreduce" and algo == "ring" else
+        METRIC.replace("fp32 sum", "tree AllReduce, fp32 sum") if coll == "allreduce" else
         METRIC.replace("fp32 sum", f"{what[0]}, fp32" + (" sum" if coll == "reduce_scatter" else "")),
         "value": round(busbw, 3),
         "unit": "GB/s",

@@ -10,9 +10,17 @@ min(nch * bw * eff, nch * perChLL128) for LL128.  This tool fits, per
 protocol, `base` and `step` to small calls at n = 2..8 (least squares over
 2(n-1)), and the bandwidth terms to large calls at the model's largest
 channel count; it keeps the pages' efficiencies and the size rule for the
-channel count.  It prints the fitted model (the JSON layout of
-`ringar_model_t`) and a tuning table: for each size the model's time per
-protocol, the measured time, and which protocol each picks.
+channel count.  The tree AllReduce rows take the pages' Tree form with every
+virtual rank one vertex ([BOOK] Japanese edition ch. 5 §四):
+
+    T = tbase + 2 floor(log2 n) * tstep  +  bytes / (1000 * busBw * 0.5)
+
+with busBw = nch * bw * treeEff for Simple, that / llDiv (capped at llMax)
+for LL and that * ll128Factor for LL128; tbase and tstep are fitted to small
+calls at n = 2..16, treeEff, llDiv and ll128Factor to large calls.  It prints
+the fitted model (the JSON layout of `ringar_model_t`) and a tuning table: for
+each size the model's time per (algorithm, protocol), the measured time, and
+which pair each picks.
 
     python -m ring_allreduce_reduce_amd.calibrate [--json out.json] [--table out.txt]
 """
@@ -26,7 +34,9 @@ import time
 PROTOS = ("LL", "LL128", "Simple")
 
 
-def _time_calls(ra, torch, sends, recvs, count, n, nch, proto, stream, iters, cfg=None):
+def _time_calls(ra, torch, sends, recvs, count, n, nch, proto, stream, iters, cfg=None, algo=None):
+    if algo is not None:
+        cfg = ra.make_config(algo=algo, model=cfg._model_keep if cfg is not None and cfg.model else None)
     sp = [s.data_ptr() for s in sends[:n]]
     rp = [r.data_ptr() for r in recvs[:n]]
 
@@ -58,6 +68,21 @@ def _fit_line(xs, ys):
     sxy = sum(x * y for x, y in zip(xs, ys))
     b = (m * sxy - sx * sy) / (m * sxx - sx * sx)
     return (sy - b * sx) / m, b
+
+
+def _flog2(x: int) -> int:
+    return x.bit_length() - 1
+
+
+def tree_model_time(m, n, nch, p, nbytes):
+    """The model's microseconds of a tree AllReduce for protocol index p."""
+    bus = min(nch * m["bw_per_channel"] * m["tree_allreduce_eff"], nch * m["tree_per_channel_max_bw"])
+    if p == 0:
+        bus = min(bus / m["tree_ll_divisor"], m["ll_max_bw"])
+    elif p == 1:
+        bus = min(bus * m["tree_ll128_factor"], nch * m["tree_ll128_per_channel_max_bw"])
+    lat = m["tree_base_lat_us"][p] + 2.0 * _flog2(n) * m["tree_hw_lat_us"][p]
+    return lat + nbytes / (1000.0 * bus * 0.5)
 
 
 def model_time(m, n, nch, p, nbytes):
@@ -120,34 +145,76 @@ def main(argv=None):
     m["ll128_per_channel_max_bw"] = round(ll128 / maxc, 3)
     log(f"bus bandwidth at {maxc} channels: Simple {simple:.1f}, LL {ll:.1f}, LL128 {ll128:.1f} GB/s")
 
+    # tree latency: one packet per lane, one channel, n = 2..16 (floor(log2 n) levels)
+    small = [torch.randn(64 * 16, device=dev) for _ in range(16)]
+    small_out = [torch.empty_like(t) for t in small]
+    for p, proto in enumerate(PROTOS):
+        xs, ys = [], []
+        for nr in range(2, 17):
+            us = _time_calls(ra, torch, small, small_out, 64 * nr, nr, 1, proto, stream, 200, algo="tree")
+            xs.append(2.0 * _flog2(nr))
+            ys.append(us)
+        base, step = _fit_line(xs, ys)
+        m["tree_base_lat_us"][p] = round(base, 2)
+        m["tree_hw_lat_us"][p] = round(step, 3)
+        log(f"tree {proto}: base {base:.2f} us, step per level {step:.3f} us")
+
+    # tree bandwidth at the largest channel count
+    def tree_bus_at(proto, p, nbytes):
+        us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10, algo="tree")
+        lat = m["tree_base_lat_us"][p] + 2.0 * _flog2(n) * m["tree_hw_lat_us"][p]
+        return 2.0 * nbytes / (1000.0 * max(us - lat, 1e-3))
+    tsimple = tree_bus_at("Simple", 2, big)
+    m["tree_allreduce_eff"] = round(tsimple / (maxc * m["bw_per_channel"]), 4)
+    m["tree_per_channel_max_bw"] = 1e9
+    tll = tree_bus_at("LL", 0, 64 << 20)
+    m["tree_ll_divisor"] = round(tsimple / tll, 4) if tll < m["ll_max_bw"] else 1.0
+    tll128 = tree_bus_at("LL128", 1, big)
+    m["tree_ll128_factor"] = round(tll128 / tsimple, 4)
+    m["tree_ll128_per_channel_max_bw"] = 1e9
+    m["tree_correction"] = 0
+    log(f"tree bus bandwidth at {maxc} channels: Simple {tsimple:.1f}, LL {tll:.1f}, LL128 {tll128:.1f} GB/s")
+
     # tuning table: model vs measurement, each protocol at its own channel count
     ra_model = ra.model_from_dict(m)
     cfg = ra.make_config(model=ra_model)
     rows = []
+    pairs = [("Tree", q) for q in PROTOS] + [("Ring", q) for q in PROTOS]
     for sh in range(3, 29, 2):
         nbytes = 1 << sh
         count = max(1, nbytes // 4)
         line = {"bytes": nbytes}
-        for p, proto in enumerate(PROTOS):
-            plan = ra.ringar_plan(count, "float32", n, 0, proto, cfg)
+        for a, proto in pairs:
+            p = PROTOS.index(proto)
+            pcfg = ra.make_config(model=ra_model, algo=a.lower())
+            plan = ra.ringar_plan(count, "float32", n, 0, proto, pcfg)
             pred = plan.predicted_us[p]
             us = _time_calls(ra, torch, sends, recvs, count, n, 0, proto, stream,
-                             20 if nbytes >= (16 << 20) else 100, cfg)
-            line[proto] = (plan.nchannels, pred, us)
-        line["model_pick"] = min(PROTOS, key=lambda q: (line[q][1], -PROTOS.index(q)))
-        line["measured_pick"] = min(PROTOS, key=lambda q: line[q][2])
+                             20 if nbytes >= (16 << 20) else 100, pcfg)
+            line[(a, proto)] = (plan.nchannels, pred, us)
+        # the model's pick: reverse id order, strictly smaller wins (ties to Ring Simple)
+        best = None
+        for pair in reversed(pairs):
+            if best is None or line[pair][1] < line[best][1]:
+                best = pair
+        line["model_pick"] = best
+        line["measured_pick"] = min(pairs, key=lambda q: line[q][2])
         rows.append(line)
-        log(f"{nbytes:>10d} B: " + "  ".join(f"{q} {line[q][2]:.1f}/{line[q][1]:.1f}" for q in PROTOS))
+        log(f"{nbytes:>10d} B: " + "  ".join(f"{a[0]}{q} {line[(a, q)][2]:.1f}/{line[(a, q)][1]:.1f}"
+                                            for a, q in pairs))
 
-    out = [f"# ring AllReduce tuning table, n = {n}, fp32 sum, one MI355X ({time.strftime('%Y-%m-%d')})",
+    out = [f"# ring and tree AllReduce tuning table, n = {n}, fp32 sum, one MI355X ({time.strftime('%Y-%m-%d')})",
            "# command: python -m ring_allreduce_reduce_amd.calibrate --json <model.json> --table <this file>",
-           "# per protocol: channels chosen by the size rule, model us, measured us (median, HIP events)",
+           "# per (algorithm, protocol): channels chosen by the size rule, model us, measured us (median,",
+           "# HIP events)",
            "# fitted model: " + json.dumps(m), ""]
-    hdr = f"{'bytes/rank':>11s} | " + " | ".join(f"{q:>6s} ch  model  meas." for q in PROTOS) + " | model pick | fastest"
+    name = lambda pr: f"{pr[0]} {pr[1]}"
+    hdr = f"{'bytes/rank':>11s} | " + " | ".join(f"{name(pr):>12s} ch model  meas." for pr in pairs) + \
+        " |     model pick |   fastest"
     out.append(hdr)
     for r in rows:
-        cells = " | ".join(f"{r[q][0]:>9d} {r[q][1]:6.1f} {r[q][2]:6.1f}" for q in PROTOS)
-        out.append(f"{r['bytes']:>11d} | {cells} | {r['model_pick']:>10s} | {r['measured_pick']}")
+        cells = " | ".join(f"{r[pr][0]:>15d} {r[pr][1]:6.1f} {r[pr][2]:6.1f}" for pr in pairs)
+        out.append(f"{r['bytes']:>11d} | {cells} | {name(r['model_pick']):>14s} | {name(r['measured_pick'])}")
     agree = sum(r["model_pick"] == r["measured_pick"] for r in rows)
     out.append("")
     out.append(f"model pick = fastest measured at {agree} of {len(rows)} sizes")

@@ -357,10 +357,13 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
-  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
-    u32x4 va[kUnroll], va2[kUnroll], vb[kUnroll];
+  // three sources in flight (a tree vertex with two children) take half the
+  // unroll, so that the kernel keeps the ring's register budget
+  constexpr int U = (F & kRecv2) ? kUnroll / 2 : kUnroll;
+  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
+    u32x4 va[U], va2[U], vb[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       const bool in = p < nfull;
       if (F & kRecv) va[u] = in ? ld16<kSC1>(rin, p * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -368,7 +371,7 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
       if (F & kSrc) vb[u] = in ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
       const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u]);

@@ -117,18 +117,19 @@ const Env& env() {
 // pages give (LL 0.5, LL128 about 0.94, Simple 1.0).  Latencies are fitted to
 // small calls at n = 2..8 (T = base + 2(n-1) x step), bandwidths to 32-channel
 // calls of 64-256 MiB per rank, both measured with this library on MI355X by
-// `python -m ring_allreduce_reduce_amd.calibrate`.
+// `python -m ring_allreduce_reduce_amd.calibrate` (which also fits the Tree
+// rows below).
 // A channel of a small call runs one 64-thread wavefront per rank, hence 64
 // threads per channel in the size rule.
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 8.483;
-  m.ll_max_bw = 54.97;
-  m.ll128_per_channel_max_bw = 4.201;
+  m.bw_per_channel = 8.469;
+  m.ll_max_bw = 55.1;
+  m.ll128_per_channel_max_bw = 4.132;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 4.97; m.base_lat_us[1] = 6.76; m.base_lat_us[2] = 5.06;
-  m.hw_lat_us[0] = 1.418; m.hw_lat_us[1] = 2.692; m.hw_lat_us[2] = 1.598;
+  m.base_lat_us[0] = 4.87; m.base_lat_us[1] = 6.33; m.base_lat_us[2] = 5.38;
+  m.hw_lat_us[0] = 1.431; m.hw_lat_us[1] = 2.414; m.hw_lat_us[2] = 1.566;
   m.max_channels = 32;
   m.max_pairs = 256;
   m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;
@@ -136,14 +137,15 @@ ringar_model_t default_model() {
   m.default_chunk_bytes[0] = 32768;
   m.default_chunk_bytes[1] = 491520;
   m.default_chunk_bytes[2] = 524288;
-  // Tree rows: the pages' form with MI355X constants (see the ring's note).
-  m.tree_allreduce_eff = 0.92;
+  // Tree rows: the pages' form with MI355X constants fitted the same way
+  // (latency over n = 2..16 as base + 2 floor(log2 n) x step per level).
+  m.tree_allreduce_eff = 0.915;
   m.tree_per_channel_max_bw = 1e9;
-  m.tree_ll_divisor = 2.0;
-  m.tree_ll128_factor = 0.94;
+  m.tree_ll_divisor = 5.3379;
+  m.tree_ll128_factor = 0.3388;
   m.tree_ll128_per_channel_max_bw = 1e9;
-  m.tree_base_lat_us[0] = 4.97; m.tree_base_lat_us[1] = 6.76; m.tree_base_lat_us[2] = 5.06;
-  m.tree_hw_lat_us[0] = 1.418; m.tree_hw_lat_us[1] = 2.692; m.tree_hw_lat_us[2] = 1.598;
+  m.tree_base_lat_us[0] = 4.59; m.tree_base_lat_us[1] = 7.71; m.tree_base_lat_us[2] = 6.82;
+  m.tree_hw_lat_us[0] = 1.695; m.tree_hw_lat_us[1] = 2.168; m.tree_hw_lat_us[2] = 1.742;
   m.tree_correction = 0;
   return m;
 }

@@ -143,3 +143,11 @@ def test_tree_buffer_errors_before_any_device_call():
     r3[0] = 0
     assert ra.ringar_allreduce_ex(s, r3, count, "float32", "sum", n, 2, "Simple", 0, cfg) == E.INVALID_ARGUMENT
     assert ra.ringar_allreduce_ex(s, r, 0, "float32", "sum", n, 2, "Simple", 0, cfg) == E.SUCCESS
+
+
+def test_default_tree_model_is_the_documented_one():
+    m = ra.model_dict(ra.ringar_default_model())
+    d = golden_model_dict()
+    for k in ("tree_allreduce_eff", "tree_per_channel_max_bw", "tree_ll_divisor", "tree_ll128_factor",
+              "tree_ll128_per_channel_max_bw", "tree_base_lat_us", "tree_hw_lat_us", "tree_correction"):
+        assert m[k] == d[k], k
