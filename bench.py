@@ -15,6 +15,8 @@ ring on the same shape instead (8 ranks, 64 MiB n-block buffer per rank, 8 MiB
 blocks); their busbw is algbw x (n-1)/n.  `--algo tree` times the tree
 AllReduce (double binary tree, channel c on tree c % 2) on the AllReduce
 workload; its busbw keeps the AllReduce convention algbw x 2(n-1)/n.
+`--direct` times the direct form of the ring AllReduce (Simple, each slice
+written straight into the successor's receive buffer, no FIFO).
 """
 import argparse
 import glob
@@ -75,6 +77,11 @@ def alg_bytes(n, s, e=1.0, coll="allreduce"):
     block through the FIFO."""
     if coll == "allreduce":
         return s * (2 * n + 4 * (n - 1) * e)
+    if coll == "direct":
+        # per ring index and chunk C: send 2C, n-2 x recvReduceSend 3C,
+        # recvReduceCopySend 4C, n-2 x recvCopySend 2C, recv 0 (the data is
+        # already in place): C (5n - 4); over the n ring indices s (5n - 4)
+        return s * (5 * n - 4)
     return n * s + s + 2 * (n - 1) * s * e
 
 
@@ -90,6 +97,8 @@ def main():
                     help="the AllReduce (default) or one of its halves on the same 8 x 64 MiB shape")
     ap.add_argument("--algo", default="ring", choices=["ring", "tree"],
                     help="AllReduce algorithm: the ring (default) or the double binary tree")
+    ap.add_argument("--direct", action="store_true",
+                    help="the ring AllReduce's direct form (no FIFO: the successor's receive buffer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the {NRANKS} ranks are virtual ranks inside one MI355X; "
@@ -107,6 +116,7 @@ def main():
 
     coll = args.coll
     algo = args.algo if coll == "allreduce" else "ring"
+    direct = bool(args.direct) and coll == "allreduce" and algo == "ring"
     count = BYTES_PER_RANK // 4              # elements in the n-block buffer of a rank
     block = count // NRANKS
     log("generating inputs")
@@ -120,7 +130,7 @@ def main():
         sends = [W.to_torch(x, "float32", dev) for x in xs]
         recvs = [torch.empty(count if coll == "allreduce" else block, device=dev) for _ in sends]
     stream = torch.cuda.Stream()
-    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES, algo=algo)
+    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES, algo=algo, direct=int(direct))
     plan = ra.ringar_plan_coll(coll, count if coll == "allreduce" else block, "float32", NRANKS, NCHANNELS,
                                "Simple", cfg)
     send_ptrs = [s.data_ptr() for s in sends]
@@ -181,9 +191,9 @@ def main():
     algbw = s / (ms_per_step * 1e-3) / 1e9
     bus_factor = (2 if coll == "allreduce" else 1) * (NRANKS - 1) / NRANKS
     busbw = algbw * bus_factor
-    b_alg = alg_bytes(NRANKS, s, coll=coll)
+    b_alg = alg_bytes(NRANKS, s, coll="direct" if direct else coll)
     achieved = b_alg / (avg_launch_ms * 1e-3) / 1e9
-    traffic = read_traffic() if coll == "allreduce" and algo == "ring" else None
+    traffic = read_traffic() if coll == "allreduce" and algo == "ring" and not direct else None
 
     def run_oracle():
         if coll == "allreduce" and algo == "tree":
@@ -216,11 +226,12 @@ def main():
                "sample": f"the full workload (8 ranks x 64 MiB fp32) repeated {calls} times (~10 s), "
                          "single-threaded C oracle; value is busbw"}
 
-    what = {"allreduce": (f"{algo} AllReduce", "64 MiB per rank"),
+    what = {"allreduce": (f"{algo} AllReduce" + (" (direct form)" if direct else ""), "64 MiB per rank"),
             "reduce_scatter": ("ring ReduceScatter", "64 MiB input per rank (8 blocks of 8 MiB)"),
             "all_gather": ("ring AllGather", "8 MiB input, 64 MiB output per rank")}[coll]
     out = {
-        "metric": METRIC if coll == "allreduce" and algo == "ring" else
+        "metric": METRIC if coll == "allreduce" and algo == "ring" and not direct else
+        METRIC.replace("fp32 sum", "direct ring AllReduce, fp32 sum") if direct else
         METRIC.replace("fp32 sum", "tree AllReduce, fp32 sum") if coll == "allreduce" else
         METRIC.replace("fp32 sum", f"{what[0]}, fp32" + (" sum" if coll == "reduce_scatter" else "")),
         "value": round(busbw, 3),

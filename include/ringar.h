@@ -170,7 +170,14 @@ typedef struct {
  *   force_general:   test hook, normally 0: 1 = never use the straight-line
  *                    form for small lane parts (see ringar_plan_t).
  *   algo:            a ringar_algo_t (AllReduce only; the halves run the
- *                    ring).  Zero = RINGAR_ALGO_RING. */
+ *                    ring).  Zero = RINGAR_ALGO_RING.
+ *   direct:          1 = the ring AllReduce under Simple writes each
+ *                    outgoing slice straight into the successor's receive
+ *                    buffer instead of a FIFO slot (the pages' direct
+ *                    primitives, [ARCH] §九.4): fewer bytes moved, same
+ *                    results.  Used when the call is a ring AllReduce with
+ *                    the Simple protocol and every rank is out of place;
+ *                    otherwise the call runs with FIFOs as usual. */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;
@@ -182,6 +189,7 @@ typedef struct {
   int fifo_depth;
   int force_general;
   int algo;
+  int direct;
 } ringar_config_t;
 
 /* The resolved plan of a call (what ringar_allreduce would launch). */
@@ -206,6 +214,8 @@ typedef struct {
   ringar_algo_t algo;      /* RING or TREE */
   double predicted_tree_us[3];  /* Tree AllReduce model times (AllReduce) */
   double predicted_ring_us[3];  /* Ring model times */
+  int direct;              /* 1: runs the direct form when every rank is out
+                              of place */
 } ringar_plan_t;
 
 /*

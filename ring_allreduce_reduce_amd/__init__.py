@@ -68,6 +68,7 @@ class ringar_config_t(ctypes.Structure):
         ("fifo_depth", ctypes.c_int),
         ("force_general", ctypes.c_int),
         ("algo", ctypes.c_int),
+        ("direct", ctypes.c_int),
     ]
 
 
@@ -89,6 +90,7 @@ class ringar_plan_t(ctypes.Structure):
         ("algo", ctypes.c_int),
         ("predicted_tree_us", ctypes.c_double * 3),
         ("predicted_ring_us", ctypes.c_double * 3),
+        ("direct", ctypes.c_int),
     ]
 
 
@@ -148,7 +150,7 @@ def _enum(table, v):
 
 
 def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_ms=0,
-                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0, algo="ring"):
+                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0, algo="ring", direct=0):
     """A ringar_config_t; keeps the ring-order array alive on the object."""
     cfg = ringar_config_t()
     cfg.chunk_bytes = chunk_bytes
@@ -166,6 +168,7 @@ def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_
     cfg.fifo_depth = fifo_depth
     cfg.force_general = force_general
     cfg.algo = _enum(ALGOS, algo)
+    cfg.direct = int(direct)
     return cfg
 
 

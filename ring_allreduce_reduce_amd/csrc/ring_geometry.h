@@ -163,6 +163,7 @@ struct KernelArgs {
   int lanes_per_block;
   int skip_ring_index;           // -1: none
   int vec_ok;                    // all user pointers 16-byte aligned
+  int direct;                    // Simple AllReduce writing the successor's receive buffer
 };
 
 // Arguments of a tree AllReduce launch: the ring's, plus the two trees

@@ -274,6 +274,7 @@ struct Lane {
   Conn in[2], out[2];
   const char* src;     // own send buffer
   char* dst;           // own receive buffer
+  char* peer;          // the successor's receive buffer (direct form)
   uint64_t sstep, rstep;
   uint64_t tail_seen[2];  // largest tail of each input connection seen so far
   uint64_t head_seen[2];  // largest head of each output connection seen so far
@@ -815,6 +816,81 @@ __device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t es0, uint64
   return true;
 }
 
+// --- direct: the successor's receive buffer instead of a FIFO -------------
+// The pages' "direct" primitives read and write the peer's user buffer
+// without a staging FIFO ([ARCH] §九.4).  Here ring index i writes each
+// outgoing slice into its successor's receive buffer at the slice's own
+// element offset and publishes the tail; the successor reads it there (kRecv
+// = read own receive buffer), folds in its own input and writes the result
+// on into its successor's buffer (kSend), or keeps it (kDst).  Every slice
+// has its own place, so no slot is reused and no head counter is needed: a
+// partial result in a receive buffer is overwritten only by the final value
+// of the same chunk, which can only arrive after the owner has read the
+// partial and passed it on.  Only valid out of place (a partial result would
+// otherwise overwrite the receiver's own input).
+template <class E, int OP, int F>
+__device__ __forceinline__ bool slice_direct(Lane& L, uint64_t e0, uint32_t nelem) {
+  const KernelArgs& a = *L.a;
+  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  if ((F & kRecv) && !wait_ge(L.w, L.in[0].tail, a.base + L.rstep + 1, L.tail_seen[0])) return false;
+  const uint64_t off = e0 * sizeof(typename E::T);
+  rsrc_t rin = make_rsrc(L.dst + off, nbytes);     // own receive buffer, written by the predecessor
+  rsrc_t rpeer = make_rsrc(L.peer + off, nbytes);  // the successor's receive buffer
+  rsrc_t rsrc_ = make_rsrc(L.src + off, nbytes);
+  rsrc_t rdst = rin;
+  const uint32_t npk = (nbytes + 15) / 16;
+  const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
+  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
+    u32x4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      const bool in = p < nfull;
+      if (F & kRecv) va[u] = in ? ld16<kSC1>(rin, p * 16) : u32x4{0u, 0u, 0u, 0u};
+      if (F & kSrc) vb[u] = in ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t p = p0 + u * 64 + L.lane;
+      if (p >= nfull) continue;
+      const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u]);
+      if (F & kSend) st16<kSC1>(r, rpeer, p * 16);
+      if (F & kDst) st16<kNT>(r, rdst, p * 16);
+    }
+  }
+#pragma unroll 1
+  for (uint32_t p = nfull + L.lane; p < npk; p += 64) {
+    const uint32_t o = p * 16, nb = min(16u, nbytes - o);
+    u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
+    if (F & kRecv) x = ld_part<E, kSC1>(rin, o, nb);
+    if (F & kSrc) y = ld_part<E, kNT>(rsrc_, o, nb);
+    const u32x4 r = combine<E, OP, F>(x, x, y);
+    if (F & kSend) st_part<E, kSC1>(r, rpeer, o, nb);
+    if (F & kDst) st_part<E, kNT>(r, rdst, o, nb);
+  }
+  if (F & kSend) publish_tails<F>(L);
+  if (F & kRecv) L.rstep++;
+  return true;
+}
+
+// A primitive of the direct form over the lane's part of one chunk, in
+// slices of one Simple slot (the tail's granularity).  A part the receiver
+// does not need to read (the last stage: the data is already in its buffer)
+// only advances its step count.
+template <class E, int OP, int F>
+__device__ __forceinline__ bool primitive_direct(Lane& L, uint64_t e0, uint64_t nelem) {
+  const uint64_t cap = slot_elems(kSimple, sizeof(typename E::T));
+  for (uint64_t j = 0; j < nelem; j += cap) {
+    const uint32_t m = (uint32_t)min_u64(cap, nelem - j);
+    if (F == kRecv) {
+      L.rstep++;
+      continue;
+    }
+    if (!slice_direct<E, OP, F>(L, e0 + j, m)) return false;
+  }
+  return true;
+}
+
 // --- a primitive over the lane's part of one chunk ------------------------
 // es0 / ed0: element offsets of the part in the source and destination user
 // buffers (equal in the AllReduce; block-relative in its two halves).
@@ -876,10 +952,36 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
   L.out[0] = conn_at<PROTO>(a, conn_index(c, (ri + 1) % n, l, n, a.lanes));
   L.src = a.send[ri];
   L.dst = a.recv[ri];
+  L.peer = a.recv[(ri + 1) % n];
 
   uint64_t lo, hi;
   channel_bounds(a.count, a.per_channel, c, &lo, &hi);
   const uint64_t len = hi - lo;
+  if constexpr (COLL == kAllReduce && PROTO == kSimple && !SMALL) {
+    if (a.direct) {
+      const uint64_t loop = (uint64_t)n * a.chunk_elems;
+      for (uint64_t off = 0; off < len; off += loop) {
+        const uint64_t rem = len - off;
+        const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
+        const uint64_t part = lane_part(cur, a.lanes, es);
+        for (int s = 0; s <= 2 * n - 2; s++) {
+          const int k = stage_chunk(ri, s, n);
+          uint64_t ks, kl, ls, ll;
+          chunk_bounds(rem, cur, k, &ks, &kl);
+          lane_bounds(kl, part, l, &ls, &ll);
+          const uint64_t e0 = lo + off + ks + ls;
+          bool ok;
+          if (s == 0) ok = primitive_direct<E, OP, kSrc | kSend>(L, e0, ll);
+          else if (s <= n - 2) ok = primitive_direct<E, OP, kRecv | kSrc | kSend>(L, e0, ll);
+          else if (s == n - 1) ok = primitive_direct<E, OP, kRecv | kSrc | kSend | kDst>(L, e0, ll);
+          else if (s <= 2 * n - 3) ok = primitive_direct<E, OP, kRecv | kSend>(L, e0, ll);
+          else ok = primitive_direct<E, OP, kRecv>(L, e0, ll);
+          if (!ok) return;
+        }
+      }
+      return;
+    }
+  }
   if constexpr (COLL == kAllReduce) {
     const uint64_t loop = (uint64_t)n * a.chunk_elems;
     for (uint64_t off = 0; off < len; off += loop) {

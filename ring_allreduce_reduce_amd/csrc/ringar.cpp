@@ -317,6 +317,7 @@ struct Plan {
   int lanes = 1;
   int depth = kMaxSteps;
   bool small = false;      // every lane part fits the small-slice form
+  bool direct = false;     // direct form requested and possible (if out of place)
   int lanes_per_block = 1;
   int grid = 0;
   int block = 64;
@@ -458,8 +459,9 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   }
   // Lane parts of at most 1 KiB (one 16-byte packet per lane and step) run
   // the straight-line form of LL and Simple when the buffers are aligned.
+  P.direct = cfg && cfg->direct && P.kind == kAllReduce && P.proto == kSimple && n > 1;
   P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es) * es <= kSmallSliceBytes &&
-            !(cfg && cfg->force_general);
+            !(cfg && cfg->force_general) && !P.direct;
   P.lanes_per_block = std::min(lanes, 4);
   P.block = 64 * P.lanes_per_block;
   const int groups = P.nch * (lanes / P.lanes_per_block);
@@ -497,8 +499,9 @@ std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Resources> g_res;
 std::map<long long, int> g_occupancy;   // (kernel, block) -> blocks per CU
 
-ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t conns) {
-  if (R.fifo_conns[proto] < conns) {
+// FIFO slots (unless `counters_only`) and counters for `conns` connections.
+ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t conns, bool counters_only) {
+  if (!counters_only && R.fifo_conns[proto] < conns) {
     HIP_TRY(hipStreamSynchronize(st));
     if (R.fifo[proto]) HIP_TRY(hipFree(R.fifo[proto]));
     R.fifo[proto] = nullptr;
@@ -751,6 +754,7 @@ ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_
     out->predicted_ring_us[p] = P.ring_times[p];
   }
   out->algo = P.kind == kTreeAllReduce ? RINGAR_ALGO_TREE : RINGAR_ALGO_RING;
+  out->direct = P.direct ? 1 : 0;
   return RINGAR_SUCCESS;
 }
 
@@ -830,7 +834,11 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   }
   if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
 
-  if ((r = ensure_conns(*R, st, P.proto, P.conns)) != RINGAR_SUCCESS) return r;
+  // the direct form needs every rank out of place
+  bool direct = P.direct;
+  for (int q = 0; q < nranks && direct; q++)
+    if (sendbuffs[q] == recvbuffs[q]) direct = false;
+  if ((r = ensure_conns(*R, st, P.proto, P.conns, direct)) != RINGAR_SUCCESS) return r;
   // LL flags are 32-bit step numbers: restart the numbering before it wraps.
   if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
     if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;
@@ -848,7 +856,6 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   A.per_channel = P.per_channel;
   A.chunk_elems = P.chunk_elems;
   A.base = R->base;
-  A.fifo = R->fifo[P.proto];
   A.counters = R->counters;
   A.error = R->error;
   A.abort_flag = cfg ? cfg->abort_flag : nullptr;
@@ -866,6 +873,8 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
       if ((ring ? ring[i] : i) == cfg->skip_rank) A.skip_ring_index = i;
   }
   A.vec_ok = vec;
+  A.direct = direct ? 1 : 0;
+  A.fifo = direct ? nullptr : R->fifo[P.proto];
 
   if (P.kind == kTreeAllReduce) {
     // the tree runs over ranks 0..n-1 (a ring order does not apply)
@@ -896,9 +905,10 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   if (env().debug) {
     fprintf(stderr,
             "ringar: %s %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
-            "depth %d%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
+            "depth %d%s%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
             kCollName[P.kind], count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
-            P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", P.grid, P.block, P.times[0], P.times[1], P.times[2]);
+            P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", direct ? " direct" : "", P.grid, P.block,
+            P.times[0], P.times[1], P.times[2]);
   }
   return RINGAR_SUCCESS;
 }

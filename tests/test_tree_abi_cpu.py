@@ -151,3 +151,18 @@ def test_default_tree_model_is_the_documented_one():
     for k in ("tree_allreduce_eff", "tree_per_channel_max_bw", "tree_ll_divisor", "tree_ll128_factor",
               "tree_ll128_per_channel_max_bw", "tree_base_lat_us", "tree_hw_lat_us", "tree_correction"):
         assert m[k] == d[k], k
+
+
+def test_direct_form_is_planned_only_where_it_applies():
+    d = ra.make_config(direct=1)
+    p = ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple", d)
+    assert p.direct == 1 and p.small_slices == 0
+    assert ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple").direct == 0
+    for proto in ("LL", "LL128"):
+        assert ra.ringar_plan(1 << 20, "float32", 8, 4, proto, d).direct == 0
+    assert ra.ringar_plan(1 << 20, "float32", 1, 4, "Simple", d).direct == 0
+    assert ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple", ra.make_config(direct=1, algo="tree")).direct == 0
+    assert ra.ringar_plan_coll("reduce_scatter", 1 << 17, "float32", 8, 4, "Simple", d).direct == 0
+    # the small form is not used with the direct form
+    small = ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple", d)
+    assert small.small_slices == 0 and ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple").small_slices == 1
