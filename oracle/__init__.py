@@ -36,7 +36,7 @@ DTYPES = {
     "float32": (4, np.float32, 4),
     "float64": (5, np.float64, 8),
 }
-OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 

@@ -47,7 +47,7 @@
 
 /* Codes private to this file; the Python wrapper maps names onto them. */
 enum { OR_I8 = 0, OR_I32 = 1, OR_F16 = 2, OR_BF16 = 3, OR_F32 = 4, OR_F64 = 5 };
-enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3 };
+enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3, OR_AVG = 4 };
 
 static size_t elem_size(int dtype) {
   switch (dtype) {
@@ -212,6 +212,55 @@ static void combine(int dtype, int op, const void* recv, const void* local,
 }
 
 /* ---------------------------------------------------------------------
+ * The average.  [ARCH] §九.4 marks the step where a chunk becomes final
+ * (recvReduceCopySend) with postOp=true; the pages say nothing more.
+ * Reading: avg folds every hop like sum, and only the final value is divided
+ * by the rank count, once, where the chunk becomes final; the quotient is
+ * what is stored and forwarded.  Integers: signed division truncating toward
+ * zero (C).  fp32 / fp64: one IEEE division.  fp16 / bf16: widen exactly to
+ * fp32, divide in fp32, round to nearest-even (fp32 has more than twice the
+ * 16-bit formats' precision plus two bits, so this is the correctly rounded
+ * 16-bit quotient).
+ * --------------------------------------------------------------------- */
+static int hop_op(int op) { return op == OR_AVG ? OR_SUM : op; }
+
+static void average(int dtype, void* buf, size_t len, int n) {
+  size_t e;
+  switch (dtype) {
+    case OR_I8: {
+      uint8_t* b = buf;
+      for (e = 0; e < len; e++) b[e] = (uint8_t)(int8_t)((int)(int8_t)b[e] / n);
+      break;
+    }
+    case OR_I32: {
+      uint32_t* b = buf;
+      for (e = 0; e < len; e++) b[e] = (uint32_t)((int32_t)b[e] / (int32_t)n);
+      break;
+    }
+    case OR_F16: {
+      uint16_t* b = buf;
+      for (e = 0; e < len; e++) b[e] = f16_encode_rne(f16_decode(b[e]) / (float)n);
+      break;
+    }
+    case OR_BF16: {
+      uint16_t* b = buf;
+      for (e = 0; e < len; e++) b[e] = bf16_encode_rne(bf16_decode(b[e]) / (float)n);
+      break;
+    }
+    case OR_F32: {
+      float* b = buf;
+      for (e = 0; e < len; e++) b[e] = b[e] / (float)n;
+      break;
+    }
+    default: {
+      double* b = buf;
+      for (e = 0; e < len; e++) b[e] = b[e] / (double)n;
+      break;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------
  * Partition (steps 1-3 of the header).
  * --------------------------------------------------------------------- */
 
@@ -288,11 +337,12 @@ static void ring_loop(int n, int dtype, int op, size_t es, const int* ring,
         memcpy(pay_new[i], mine, len * es);
       } else if (s <= n - 2) {
         /* recvReduceSend: reduce the received chunk with our own, forward */
-        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);
+        combine(dtype, hop_op(op), pay_old[prev], mine, pay_new[i], len);
       } else if (s == n - 1) {
-        /* recvReduceCopySend: last reduction, the chunk is final: keep it
-         * in our output and forward it */
-        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);
+        /* recvReduceCopySend: last reduction, the chunk is final (postOp):
+         * keep it in our output and forward it */
+        combine(dtype, hop_op(op), pay_old[prev], mine, pay_new[i], len);
+        if (op == OR_AVG) average(dtype, pay_new[i], len, n);
         memcpy(out, pay_new[i], len * es);
       } else if (s <= 2 * n - 3) {
         /* recvCopySend: all-gather hop: keep the final chunk and forward */
@@ -319,7 +369,7 @@ int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
                           int nchannels, size_t chunk_elems, const int* ring,
                           const void* const* x, void* const* y) {
   size_t es = elem_size(dtype);
-  if (!es || op < OR_SUM || op > OR_MAX || nranks < 1 || nchannels < 1) return -1;
+  if (!es || op < OR_SUM || op > OR_AVG || nranks < 1 || nchannels < 1) return -1;
   if (chunk_elems == 0 || chunk_elems % (16 / es)) return -1;
   int* order = malloc(sizeof(int) * (size_t)nranks);
   if (!order) return -1;
@@ -410,7 +460,7 @@ static void free_payloads(int n, unsigned char** p) {
 int oracle_ring_reduce_scatter(int nranks, size_t count, int dtype, int op, const int* ring,
                                const void* const* x, void* const* y) {
   size_t es = elem_size(dtype);
-  if (!es || op < OR_SUM || op > OR_MAX || nranks < 1) return -1;
+  if (!es || op < OR_SUM || op > OR_AVG || nranks < 1) return -1;
   int n = nranks;
   int* order = ring_order_copy(n, ring);
   if (!order) return -1;
@@ -430,9 +480,11 @@ int oracle_ring_reduce_scatter(int nranks, size_t count, int dtype, int op, cons
       if (s == 0)
         memcpy(pb[i], mine, count * es);                       /* send */
       else if (s <= n - 2)
-        combine(dtype, op, pa[prev], mine, pb[i], count);      /* recvReduceSend */
-      else
-        combine(dtype, op, pa[prev], mine, y[order[i]], count); /* recvReduceCopy */
+        combine(dtype, hop_op(op), pa[prev], mine, pb[i], count);      /* recvReduceSend */
+      else {
+        combine(dtype, hop_op(op), pa[prev], mine, y[order[i]], count); /* recvReduceCopy */
+        if (op == OR_AVG) average(dtype, y[order[i]], count, n);        /* postOp */
+      }
     }
     unsigned char** t = pa; pa = pb; pb = t;
   }
@@ -563,7 +615,7 @@ int oracle_tree_allreduce(int nranks, size_t count, int dtype, int op, int nchan
                           size_t chunk_elems, const void* const* x, void* const* y) {
   size_t es = elem_size(dtype);
   int n = nranks;
-  if (!es || op < OR_SUM || op > OR_MAX || n < 1 || nchannels < 1 || chunk_elems == 0) return -1;
+  if (!es || op < OR_SUM || op > OR_AVG || n < 1 || nchannels < 1 || chunk_elems == 0) return -1;
   if (n == 1) {
     memmove(y[0], x[0], count * es);
     return 0;
@@ -600,8 +652,9 @@ int oracle_tree_allreduce(int nranks, size_t count, int dtype, int op, int nchan
         memcpy(P[v], (const unsigned char*)x[v] + off * es, len * es);
         for (int s = 0; s < 2; s++) {
           int ch = dn[2 * v + s];
-          if (ch >= 0) combine(dtype, op, P[ch], P[v], P[v], len);
+          if (ch >= 0) combine(dtype, hop_op(op), P[ch], P[v], P[v], len);
         }
+        if (v == root && op == OR_AVG) average(dtype, P[v], len, n);   /* final: postOp */
       }
       /* broadcast: down the tree */
       for (int j = n - 1; j >= 0; j--) {

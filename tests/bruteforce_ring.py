@@ -17,7 +17,7 @@ import threading
 
 import numpy as np
 
-from refs import hop
+from refs import divide, hop, hop_op
 from ring_allreduce_reduce_amd.workloads import ELEM_BYTES
 
 NCCL_STEPS = 8
@@ -92,9 +92,11 @@ def run(xs, dtype: str, op: str, nchannels: int, chunk_elems: int, ring=None):
                 send(k, own(k))
                 for _ in range(n - 2):
                     k, v = recv()
-                    send(k, hop(dtype, op, v, own(k)))
+                    send(k, hop(dtype, hop_op(op), v, own(k)))
                 k, v = recv()
-                fin = hop(dtype, op, v, own(k))
+                fin = hop(dtype, hop_op(op), v, own(k))
+                if op == "avg":
+                    fin = divide(dtype, fin, n)
                 put(k, fin)
                 send(k, fin)
                 for _ in range(n - 2):
@@ -189,11 +191,12 @@ def run_reduce_scatter(xs, dtype: str, op: str, nchannels: int, chunk_elems: int
             send(q, own(q))
             for _ in range(n - 2):
                 q, v = recv()
-                send(q, hop(dtype, op, v, own(q)))
+                send(q, hop(dtype, hop_op(op), v, own(q)))
             q, v = recv()
             if q != me:
                 raise RuntimeError(f"ring index {i} ends with the block of rank {q}")
-            ys[me][a:b] = hop(dtype, op, v, own(q))
+            fin = hop(dtype, hop_op(op), v, own(q))
+            ys[me][a:b] = divide(dtype, fin, n) if op == "avg" else fin
     _threads(n, body)
     return ys
 

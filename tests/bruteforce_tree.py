@@ -13,14 +13,15 @@ shifted by one for odd n.
 The reduction is a recursion over the tree, evaluated elementwise with the
 numpy/torch hop of ``refs.py``: value(v) = x_v folded with value(child 0),
 then value(child 1), each as op(received, local).  Channel c uses tree c mod 2
-and the channel ranges come from the oracle's pinned partition.
+and the channel ranges come from the oracle's pinned partition.  The average
+folds like sum and divides the root's value by n once.
 """
 from __future__ import annotations
 
 import numpy as np
 
 import oracle
-from refs import hop
+from refs import divide, hop, hop_op
 
 
 def _btree_parent(n: int, r: int) -> int:
@@ -61,7 +62,7 @@ def tree_value(xs, dtype: str, op: str, kids, v: int, lo: int, hi: int) -> np.nd
     acc = np.array(xs[v][lo:hi], copy=True)
     for k in kids[v]:
         if k >= 0:
-            acc = hop(dtype, op, tree_value(xs, dtype, op, kids, k, lo, hi), acc)
+            acc = hop(dtype, hop_op(op), tree_value(xs, dtype, op, kids, k, lo, hi), acc)
     return acc
 
 
@@ -78,5 +79,6 @@ def run(xs, dtype: str, op: str, nchannels: int):
             continue
         parent, kids = tree_links(n, c % 2)
         root = parent.index(-1)
-        out[lo:hi] = tree_value(xs, dtype, op, kids, root, lo, hi)
+        val = tree_value(xs, dtype, op, kids, root, lo, hi)
+        out[lo:hi] = divide(dtype, val, n) if op == "avg" else val
     return [out.copy() for _ in range(n)]

@@ -59,6 +59,25 @@ def hop(dtype: str, op: str, a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.where(b > a, b, a)
 
 
+def divide(dtype: str, a: np.ndarray, n: int) -> np.ndarray:
+    """a / n elementwise in the element type: integers truncate toward zero
+    (exact integer arithmetic), floats divide in numpy / torch (16-bit floats
+    compute in fp32 and round to nearest-even)."""
+    if dtype == "bfloat16":
+        return torch_to_bf16_bits(bf16_bits_to_torch(a) / n)
+    if dtype in ("int8", "int32"):
+        w = np.asarray(a).astype(np.int64)
+        q = np.abs(w) // n * np.sign(w)
+        return q.astype(STORAGE[dtype])
+    a = np.asarray(a, dtype=STORAGE[dtype])
+    return (a / np.asarray(n, dtype=STORAGE[dtype])).astype(STORAGE[dtype])
+
+
+def hop_op(op: str) -> str:
+    """The per-hop operation: avg folds like sum."""
+    return "sum" if op == "avg" else op
+
+
 def exact_reduce(xs, dtype: str, op: str) -> np.ndarray:
     """The plain definition for the order-free cases (integers with
     wraparound, min and max of anything): numpy's reduction over ranks."""

@@ -22,7 +22,7 @@ MUTATIONS = {
     "chunk index off by one": ("int k = ((i + n - 1 - s) % n + n) % n;       /* chunk of this stage */",
                                "int k = ((i + n - s) % n + n) % n;       /* chunk of this stage */"),
     "reduce dropped (forward only)": (
-        "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        combine(dtype, op, pay_old[prev], mine, pay_new[i], len);",
+        "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        combine(dtype, hop_op(op), pay_old[prev], mine, pay_new[i], len);",
         "      } else if (s <= n - 2) {\n        /* recvReduceSend: reduce the received chunk with our own, forward */\n        memcpy(pay_new[i], pay_old[prev], len * es);"),
     "final recv missing": ("for (int s = 0; s <= 2 * n - 2; s++)", "for (int s = 0; s < 2 * n - 2; s++)"),
     "ring direction reversed": ("int prev = (i + n - 1) % n;                  /* ring predecessor */",
@@ -49,8 +49,8 @@ MUTATIONS = {
         "(const unsigned char*)x[order[i]] + (size_t)order[k] * count * es;",
         "(const unsigned char*)x[order[i]] + (size_t)k * count * es;"),
     "reduce-scatter drops its last reduction": (
-        "        combine(dtype, op, pa[prev], mine, y[order[i]], count); /* recvReduceCopy */",
-        "        memcpy(y[order[i]], pa[prev], count * es);              /* recvReduceCopy */"),
+        "        combine(dtype, hop_op(op), pa[prev], mine, y[order[i]], count); /* recvReduceCopy */",
+        "        memcpy(y[order[i]], pa[prev], count * es);                      /* recvReduceCopy */"),
     "all-gather block off by one": ("      int k = ((i - s) % n + n) % n;", "      int k = ((i - s + 1) % n + n) % n;"),
     "all-gather skips its final recv": ("  for (int s = 0; s <= n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;",
                                         "  for (int s = 0; s < n - 1 && rc == 0; s++) {\n    for (int i = 0; i < n; i++) {\n      int prev = (i + n - 1) % n;\n      int k = ((i - s) % n + n) % n;"),
@@ -64,6 +64,15 @@ MUTATIONS = {
                                   "        if (v != root) memcpy((unsigned char*)y[v] + off * es, P[v], len * es);"),
     "tree vertex drops its own input": ("        memcpy(P[v], (const unsigned char*)x[v] + off * es, len * es);",
                                         "        memset(P[v], 0, len * es);"),
+    "avg divides on every hop": ("        combine(dtype, hop_op(op), pay_old[prev], mine, pay_new[i], len);\n      } else if (s == n - 1) {",
+                                 "        combine(dtype, hop_op(op), pay_old[prev], mine, pay_new[i], len);\n        if (op == OR_AVG) average(dtype, pay_new[i], len, n);\n      } else if (s == n - 1) {"),
+    "avg never divides on the ring": ("        if (op == OR_AVG) average(dtype, pay_new[i], len, n);\n        memcpy(out, pay_new[i], len * es);",
+                                      "        memcpy(out, pay_new[i], len * es);"),
+    "avg divides by n - 1": ("      for (e = 0; e < len; e++) b[e] = b[e] / (float)n;",
+                             "      for (e = 0; e < len; e++) b[e] = b[e] / (float)(n - 1);"),
+    "tree avg not divided": ("        if (v == root && op == OR_AVG) average(dtype, P[v], len, n);   /* final: postOp */\n", ""),
+    "integer avg floors": ("      for (e = 0; e < len; e++) b[e] = (uint32_t)((int32_t)b[e] / (int32_t)n);",
+                           "      for (e = 0; e < len; e++) { int32_t v = (int32_t)b[e]; b[e] = (uint32_t)(v >= 0 ? v / (int32_t)n : -((-v + (int32_t)n - 1) / (int32_t)n)); }"),
     "fp64 min uses max": ("    case OR_MIN: return (b < a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void",
                           "    case OR_MIN: return (b > a) ? b : a;\n    default: return (b > a) ? b : a;\n  }\n}\n\nstatic void"),
 }
@@ -150,6 +159,25 @@ def _battery(lib) -> list:
         want = brute_tree(xs, "float32", "sum", 2)
         if got is None or not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
             fails.append(f"tree brute force {n}")
+    # average: the brute-force ring and tree, integers truncating
+    from refs import divide
+    for dtype, n in (("float32", 5), ("int32", 3), ("float32", 4)):
+        xs = W.inputs(f"mavg-{dtype}-{n}", n, 53, dtype, "uniform", -9, 9)
+        try:
+            got = oracle.ring_allreduce(xs, dtype, "avg", 2, 16 // W.ELEM_BYTES[dtype], lib=lib)
+            gt = oracle.tree_allreduce(xs, dtype, "avg", 2, 4, lib=lib)
+        except ValueError:
+            fails.append(f"avg rejected {dtype}")
+            continue
+        want = brute_run(xs, dtype, "avg", 2, 16 // W.ELEM_BYTES[dtype])
+        if not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(got, want)):
+            fails.append(f"avg ring {dtype} {n}")
+        if not all(np.array_equal(g.view(np.uint8), w.view(np.uint8)) for g, w in zip(gt, brute_tree(xs, dtype, "avg", 2))):
+            fails.append(f"avg tree {dtype} {n}")
+        if dtype == "int32":
+            ref = divide(dtype, exact_reduce(xs, dtype, "sum"), n)
+            if not all(np.array_equal(g, ref) for g in got):
+                fails.append("avg int closed form")
     # codecs against numpy / torch
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = bits.view(np.float16).astype(np.float32)
