@@ -61,8 +61,13 @@ typedef enum {
 } ringar_dtype_t;
 
 /* sum and prod wrap for integers; fp16/bf16 apply the op in fp32 and round to
- * nearest-even on every hop; min/max keep the received value on ties. */
-typedef enum { RINGAR_SUM = 0, RINGAR_PROD = 1, RINGAR_MIN = 2, RINGAR_MAX = 3 } ringar_op_t;
+ * nearest-even on every hop; min/max keep the received value on ties.
+ * avg folds every hop like sum and divides each final value by nranks once,
+ * at the step where it becomes final (the postOp of [ARCH] §九.4's
+ * recvReduceCopySend; for the tree, at the root): integers truncate toward
+ * zero, fp32/fp64 divide once, fp16/bf16 divide in fp32 and round to
+ * nearest-even. */
+typedef enum { RINGAR_SUM = 0, RINGAR_PROD = 1, RINGAR_MIN = 2, RINGAR_MAX = 3, RINGAR_AVG = 4 } ringar_op_t;
 
 /* Protocol codes follow the pages' protocol table order {LL, LL128, Simple}.
  *   LL:     8-byte FIFO lines, 4 B data + 4 B flag, one 64-bit store each.

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libringar.so")
 
 SUCCESS, INVALID_ARGUMENT, INVALID_USAGE, INTERNAL, DEVICE, ABORTED, TIMEOUT = range(7)
 DTYPES = {"int8": 0, "int32": 1, "float16": 2, "bfloat16": 3, "float32": 4, "float64": 5}
-OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 PROTOS = {"auto": -1, "LL": 0, "LL128": 1, "Simple": 2}
 PROTO_NAMES = {v: k for k, v in PROTOS.items()}
 ALGOS = {"ring": 0, "tree": 1, "auto": 2}

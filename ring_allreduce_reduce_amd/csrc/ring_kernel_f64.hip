@@ -18,7 +18,8 @@ const void* kernel_for_f64(int op, int proto, bool small) {
     case 0: return by_proto_kernel_f64<0>(proto, small);
     case 1: return by_proto_kernel_f64<1>(proto, small);
     case 2: return by_proto_kernel_f64<2>(proto, small);
-    default: return by_proto_kernel_f64<3>(proto, small);
+    case 3: return by_proto_kernel_f64<3>(proto, small);
+    default: return by_proto_kernel_f64<4>(proto, small);
   }
 }
 

@@ -46,11 +46,14 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // ----------------------------------------------------------------- elements
 // op(received a, local b); integers wrap, 16-bit floats go through fp32 and
-// round to nearest-even, min/max keep the received value on ties.
+// round to nearest-even, min/max keep the received value on ties.  OP codes:
+// 0 sum, 1 prod, 2 min, 3 max, 4 avg (folds like sum; div() is its postOp:
+// integers truncate toward zero, floats divide once in fp32 / fp64).
 struct I8 {
   using T = uint8_t;
+  __device__ static T div(T a, int n) { return (T)(int8_t)((int)(int8_t)a / n); }
   template <int OP> __device__ static T op(T a, T b) {
-    if (OP == 0) return (T)(a + b);
+    if (OP == 0 || OP == 4) return (T)(a + b);
     if (OP == 1) return (T)((uint32_t)a * (uint32_t)b);
     int8_t sa = (int8_t)a, sb = (int8_t)b;
     if (OP == 2) return sb < sa ? b : a;
@@ -59,8 +62,9 @@ struct I8 {
 };
 struct I32 {
   using T = uint32_t;
+  __device__ static T div(T a, int n) { return (T)((int32_t)a / n); }
   template <int OP> __device__ static T op(T a, T b) {
-    if (OP == 0) return a + b;
+    if (OP == 0 || OP == 4) return a + b;
     if (OP == 1) return a * b;
     int32_t sa = (int32_t)a, sb = (int32_t)b;
     if (OP == 2) return sb < sa ? b : a;
@@ -68,13 +72,16 @@ struct I32 {
   }
 };
 template <int OP> __device__ __forceinline__ float fop(float a, float b) {
-  if (OP == 0) return a + b;
+  if (OP == 0 || OP == 4) return a + b;
   if (OP == 1) return a * b;
   if (OP == 2) return b < a ? b : a;
   return b > a ? b : a;
 }
 struct F16 {
   using T = uint16_t;
+  __device__ static T div(T a, int n) {
+    return __builtin_bit_cast(uint16_t, (_Float16)((float)__builtin_bit_cast(_Float16, a) / (float)n));
+  }
   template <int OP> __device__ static T op(T a, T b) {
     float fa = (float)__builtin_bit_cast(_Float16, a);
     float fb = (float)__builtin_bit_cast(_Float16, b);
@@ -91,15 +98,18 @@ struct BF16 {
     return (T)(u >> 16);
   }
   template <int OP> __device__ static T op(T a, T b) { return narrow(fop<OP>(widen(a), widen(b))); }
+  __device__ static T div(T a, int n) { return narrow(widen(a) / (float)n); }
 };
 struct F32 {
   using T = float;
+  __device__ static T div(T a, int n) { return a / (float)n; }
   template <int OP> __device__ static T op(T a, T b) { return fop<OP>(a, b); }
 };
 struct F64 {
   using T = double;
+  __device__ static T div(T a, int n) { return a / (double)n; }
   template <int OP> __device__ static T op(T a, T b) {
-    if (OP == 0) return a + b;
+    if (OP == 0 || OP == 4) return a + b;
     if (OP == 1) return a * b;
     if (OP == 2) return b < a ? b : a;
     return b > a ? b : a;
@@ -115,6 +125,17 @@ template <class E, int OP> __device__ __forceinline__ u32x4 vop(u32x4 a, u32x4 b
 #pragma unroll
   for (int e = 0; e < N; e++) pr.v[e] = E::template op<OP>(pa.v[e], pb.v[e]);
   return __builtin_bit_cast(u32x4, pr);
+}
+
+// Elementwise postOp division over a 16-byte packet.
+template <class E> __device__ __forceinline__ u32x4 vdiv(u32x4 a, int n) {
+  using T = typename E::T;
+  constexpr int N = 16 / sizeof(T);
+  struct P { T v[N]; };
+  P pa = __builtin_bit_cast(P, a);
+#pragma unroll
+  for (int e = 0; e < N; e++) pa.v[e] = E::div(pa.v[e], n);
+  return __builtin_bit_cast(u32x4, pa);
 }
 
 // ----------------------------------------------------------------- memory
@@ -285,7 +306,10 @@ struct Lane {
 // Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
 // output 0, and output 1 with kSend2), read the own send buffer, write the
 // own receive buffer.
-enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8, kRecv2 = 16, kSend2 = 32 };
+enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8, kRecv2 = 16, kSend2 = 32, kPost = 64 };
+// kPost: the primitive where a chunk becomes final applies the op's postOp
+// (the average's division by n, [ARCH] §九.4 recvReduceCopySend's postOp).
+template <int OP> constexpr int post_flag() { return OP == 4 ? kPost : 0; }
 
 // Frees the input slots just read: publishes head = base + step + 1.  Every
 // load of a slot has returned its data (the values were consumed above),
@@ -328,12 +352,14 @@ constexpr int kUnroll = 8;   // 16-byte packets per lane in flight per source
 // Result of one packet: the local operand b folded with what was received
 // from input 0 (a) and then input 1 (a2), each hop as op(received, local);
 // or the received packet alone when there is no local operand.
-template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 a2, u32x4 b) {
+template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4 a, u32x4 a2, u32x4 b, int n) {
   static_assert(!(F & kRecv2) || ((F & kRecv) && (F & kSrc)), "a second input is folded into a local operand");
   static_assert(!(F & kSend2) || (F & kSend), "a second output needs the first");
+  static_assert(!(F & kPost) || ((F & kRecv) && (F & kSrc)), "the postOp follows the last fold");
   if constexpr ((F & kRecv) && (F & kSrc)) {
     u32x4 r = vop<E, OP>(a, b);
     if constexpr (F & kRecv2) r = vop<E, OP>(a2, r);
+    if constexpr (F & kPost) r = vdiv<E>(r, n);
     return r;
   } else if constexpr (F & kRecv) {
     return a;
@@ -375,7 +401,7 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
     for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
-      const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u]);
+      const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u], a.nranks);
       if (F & kSend) st16<kSC1>(r, rout, p * 16);
       if (F & kSend2) st16<kSC1>(r, rout2, p * 16);
       if (F & kDst) st16<kNT>(r, rdst, p * 16);
@@ -390,7 +416,7 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
     if (F & kRecv) x = ld16<kSC1>(rin, off);
     if (F & kRecv2) x2 = ld16<kSC1>(rin2, off);
     if (F & kSrc) y = ld_part<E, kNT>(rsrc_, off, nb);
-    const u32x4 r = combine<E, OP, F>(x, x2, y);
+    const u32x4 r = combine<E, OP, F>(x, x2, y, a.nranks);
     if (F & kSend) st16<kSC1>(r, rout, off);
     if (F & kSend2) st16<kSC1>(r, rout2, off);
     if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
@@ -512,7 +538,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
     for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
-      const u32x4 r = combine<E, OP, F>(va[0][u], va[NI - 1][u], vb[u]);
+      const u32x4 r = combine<E, OP, F>(va[0][u], va[NI - 1][u], vb[u], a.nranks);
       if (F & kSend) ll_send4(lout, p, r, fout);
       if (F & kSend2) ll_send4(lout2, p, r, fout);
       if (F & kDst) st16<kNT>(r, rdst, p * 16);
@@ -535,7 +561,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
       }
       if (failed) break;
     }
-    const u32x4 r = combine<E, OP, F>(x[0], x[NI - 1], y);
+    const u32x4 r = combine<E, OP, F>(x[0], x[NI - 1], y, a.nranks);
     if (F & kSend) ll_send4(lout, p, r, fout);
     if (F & kSend2) ll_send4(lout2, p, r, fout);
     if (F & kDst) st_part<E, kNT>(r, rdst, off, nb);
@@ -651,7 +677,7 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       if ((g + 1) * kLL128Group * 8 < nl)
         partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g + 1, L.lane, vec, vbn);
 #pragma unroll
-      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], va2[v], vb[v]);
+      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], va2[v], vb[v], a.nranks);
       // Packets that end inside their column: element-wise on the user side.
 #pragma unroll 1
       for (uint32_t bits = part; bits; bits &= bits - 1) {
@@ -663,7 +689,7 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
         if (F & kRecv) x = ld16<kSC1>(rin[0], line * 128 + col * 16);
         if (F & kRecv2) x2 = ld16<kSC1>(rin[1], line * 128 + col * 16);
         if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
-        const u32x4 r = combine<E, OP, F>(x, x2, y);
+        const u32x4 r = combine<E, OP, F>(x, x2, y, a.nranks);
         if (F & kSend) {
 #pragma unroll
           for (int o = 0; o < NO; o++) {
@@ -777,7 +803,7 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
     for (int i = 0; i < NI; i++)
       va[i] = u32x4{(uint32_t)ln[i][0], (uint32_t)ln[i][1], (uint32_t)ln[i][2], (uint32_t)ln[i][3]};
   }
-  const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb);
+  const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb, a.nranks);
   if (F & kSend) {
 #pragma unroll
     for (int o = 0; o < NO; o++) {
@@ -807,7 +833,7 @@ __device__ __forceinline__ bool slice_simple_small(Lane& L, uint64_t es0, uint64
   if (F & kRecv) va = ld16<kSC1>(make_rsrc(L.in[0].fifo + rslot, npk * 16), p * 16);
   if (F & kRecv2) va2 = ld16<kSC1>(make_rsrc(L.in[1].fifo + rslot, npk * 16), p * 16);
   if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
-  const u32x4 r = combine<E, OP, F>(va, va2, vb);
+  const u32x4 r = combine<E, OP, F>(va, va2, vb, a.nranks);
   if (F & kSend) st16<kSC1>(r, make_rsrc(L.out[0].fifo + sslot, npk * 16), p * 16);
   if (F & kSend2) st16<kSC1>(r, make_rsrc(L.out[1].fifo + sslot, npk * 16), p * 16);
   if (F & kDst) small_user_store<E>(L, doff, nbytes, r);
@@ -853,7 +879,7 @@ __device__ __forceinline__ bool slice_direct(Lane& L, uint64_t e0, uint32_t nele
     for (int u = 0; u < kUnroll; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
-      const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u]);
+      const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u], a.nranks);
       if (F & kSend) st16<kSC1>(r, rpeer, p * 16);
       if (F & kDst) st16<kNT>(r, rdst, p * 16);
     }
@@ -864,7 +890,7 @@ __device__ __forceinline__ bool slice_direct(Lane& L, uint64_t e0, uint32_t nele
     u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
     if (F & kRecv) x = ld_part<E, kSC1>(rin, o, nb);
     if (F & kSrc) y = ld_part<E, kNT>(rsrc_, o, nb);
-    const u32x4 r = combine<E, OP, F>(x, x, y);
+    const u32x4 r = combine<E, OP, F>(x, x, y, a.nranks);
     if (F & kSend) st_part<E, kSC1>(r, rpeer, o, nb);
     if (F & kDst) st_part<E, kNT>(r, rdst, o, nb);
   }
@@ -973,7 +999,7 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
           bool ok;
           if (s == 0) ok = primitive_direct<E, OP, kSrc | kSend>(L, e0, ll);
           else if (s <= n - 2) ok = primitive_direct<E, OP, kRecv | kSrc | kSend>(L, e0, ll);
-          else if (s == n - 1) ok = primitive_direct<E, OP, kRecv | kSrc | kSend | kDst>(L, e0, ll);
+          else if (s == n - 1) ok = primitive_direct<E, OP, kRecv | kSrc | kSend | kDst | post_flag<OP>()>(L, e0, ll);
           else if (s <= 2 * n - 3) ok = primitive_direct<E, OP, kRecv | kSend>(L, e0, ll);
           else ok = primitive_direct<E, OP, kRecv>(L, e0, ll);
           if (!ok) return;
@@ -997,7 +1023,7 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
         bool ok;
         if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, e0, e0, ll);
         else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, e0, e0, ll);
-        else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst, SMALL>(L, e0, e0, ll);
+        else if (s == n - 1) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend | kDst | post_flag<OP>(), SMALL>(L, e0, e0, ll);
         else if (s <= 2 * n - 3) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, e0, e0, ll);
         else ok = primitive<E, OP, PROTO, kRecv | kDst, SMALL>(L, e0, e0, ll);
         if (!ok) return;
@@ -1019,7 +1045,7 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
         if (COLL == kReduceScatter) {
           if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend, SMALL>(L, blk, 0, ll);
           else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSrc | kSend, SMALL>(L, blk, 0, ll);
-          else ok = primitive<E, OP, PROTO, kRecv | kSrc | kDst, SMALL>(L, blk, pos, ll);
+          else ok = primitive<E, OP, PROTO, kRecv | kSrc | kDst | post_flag<OP>(), SMALL>(L, blk, pos, ll);
         } else {
           if (s == 0) ok = primitive<E, OP, PROTO, kSrc | kSend | kDst, SMALL>(L, pos, blk, ll);
           else if (s <= n - 2) ok = primitive<E, OP, PROTO, kRecv | kSend | kDst, SMALL>(L, 0, blk, ll);
@@ -1124,8 +1150,9 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   const uint64_t len = hi - lo;
   if (!bcast && v == root) {
     // (n >= 2, so the root has at least one child)
-    if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kDst | kSend>(L, lo, len, l, es);
-    else tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kRecv2 | kDst | kSend | kSend2>(L, lo, len, l, es);
+    constexpr int P = post_flag<OP>();
+    if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kDst | kSend | P>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kRecv2 | kDst | kSend | kSend2 | P>(L, lo, len, l, es);
   } else if (!bcast) {
     if (nk == 0) tree_chunks<E, OP, PROTO, SMALL, kSrc | kSend>(L, lo, len, l, es);
     else if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kSrc | kRecv | kSend>(L, lo, len, l, es);

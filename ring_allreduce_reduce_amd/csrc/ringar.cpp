@@ -49,7 +49,7 @@ size_t elem_size(int dtype) {
 
 const char* kProtoName[3] = {"LL", "LL128", "Simple"};
 const char* kDtypeName[6] = {"int8", "int32", "float16", "bfloat16", "float32", "float64"};
-const char* kOpName[4] = {"sum", "prod", "min", "max"};
+const char* kOpName[5] = {"sum", "prod", "min", "max", "avg"};
 const char* kCollName[4] = {"AllReduce", "ReduceScatter", "AllGather", "Tree AllReduce"};
 
 // ---------------------------------------------------------------- env
@@ -564,7 +564,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   if (ndev == 0) return 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const long long key = ((((long long)dev * 4 + coll) * 8 + dtype) * 4 + op) * 3 + proto;
+  const long long key = ((((long long)dev * 4 + coll) * 8 + dtype) * 5 + op) * 3 + proto;
   // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
@@ -792,7 +792,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
                                int udtype, int op, int nranks, int nchannels, int proto,
                                ringar_stream_t stream, const ringar_config_t* cfg) {
   const size_t ues = elem_size(udtype);
-  if (!ues || op < RINGAR_SUM || op > RINGAR_MAX) return RINGAR_ERR_INVALID_ARGUMENT;
+  if (!ues || op < RINGAR_SUM || op > RINGAR_AVG) return RINGAR_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
   size_t kcount;
   int dtype;
@@ -825,7 +825,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   const bool small = P.small && vec;
   const long long okey =
-      ((((long long)P.kind * 8 + dtype) * 4 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
+      ((((long long)P.kind * 8 + dtype) * 5 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;

@@ -18,7 +18,8 @@ const void* kernel_tree_for_f16(int op, int proto, bool small) {
     case 0: return tree_by_proto_f16<0>(proto, small);
     case 1: return tree_by_proto_f16<1>(proto, small);
     case 2: return tree_by_proto_f16<2>(proto, small);
-    default: return tree_by_proto_f16<3>(proto, small);
+    case 3: return tree_by_proto_f16<3>(proto, small);
+    default: return tree_by_proto_f16<4>(proto, small);
   }
 }
 

@@ -18,7 +18,8 @@ const void* kernel_tree_for_i32(int op, int proto, bool small) {
     case 0: return tree_by_proto_i32<0>(proto, small);
     case 1: return tree_by_proto_i32<1>(proto, small);
     case 2: return tree_by_proto_i32<2>(proto, small);
-    default: return tree_by_proto_i32<3>(proto, small);
+    case 3: return tree_by_proto_i32<3>(proto, small);
+    default: return tree_by_proto_i32<4>(proto, small);
   }
 }
 
