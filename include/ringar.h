@@ -238,6 +238,9 @@ typedef struct {
  *   proto: a protocol, or RINGAR_PROTO_AUTO = the model's fastest.
  *   stream: the work is enqueued on this stream; results are valid after the
  *       stream has been synchronised.  nranks == 1 enqueues a device copy.
+ *       A stream in graph capture is refused with RINGAR_ERR_INVALID_USAGE
+ *       (nothing is enqueued): every call fixes its FIFO step numbers when it
+ *       is enqueued, so replays of a captured call would reuse them.
  * Errors are reported before anything is enqueued; a wait that times out or
  * is aborted inside the kernel is reported by ringar_get_async_error.
  */

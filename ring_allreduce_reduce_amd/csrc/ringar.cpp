@@ -811,6 +811,16 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     return RINGAR_SUCCESS;
   }
   count = kcount;
+  // A call's step numbers are fixed when it is enqueued: a captured call
+  // would replay with the same numbers and could take the flags of the
+  // previous replay for fresh data (and a first call allocates).  Refuse a
+  // capturing stream before anything is enqueued.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(st, &capture));
+  if (capture != hipStreamCaptureStatusNone) {
+    t_last_error = "stream capture is not supported: step numbers are fixed at enqueue time";
+    return RINGAR_ERR_INVALID_USAGE;
+  }
 
   std::lock_guard<std::mutex> lock(g_mu);
   Resources* R = nullptr;
