@@ -254,6 +254,16 @@ struct Waiter {
   }
 };
 
+// The first lane's value of a 64-bit word, as a wavefront-uniform value.
+// readfirstlane returns a signed int: each half is taken back as unsigned
+// before it is widened, or a low half with bit 31 set would sign-extend into
+// the high half (and a counter at or above 2^31 would look enormous).
+__device__ __forceinline__ uint64_t first_lane_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Waits until *p >= v (wavefront-uniform).  `seen` is the largest value of
 // *p this wavefront has observed; counters only grow, so a wait it already
 // satisfies costs no memory round trip, and a poll records what it saw.
@@ -264,8 +274,7 @@ __device__ __forceinline__ bool wait_ge(Waiter& w, const uint64_t* p, uint64_t v
     const uint64_t x = ld_relaxed(p);
     // every lane loads the same word; vote so the exit is uniform
     if (__all(x >= v)) {
-      seen = __builtin_amdgcn_readfirstlane((uint32_t)x) |
-             ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
+      seen = first_lane_u64(x);
       break;
     }
     if (!w.idle()) return false;

@@ -535,6 +535,10 @@ ringar_result_t get_resources(hipStream_t st, Resources** out) {
     HIP_TRY(hipDeviceGetAttribute(&R.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
     HIP_TRY(hipMalloc((void**)&R.error, 8));
     HIP_TRY(launch_fill(R.error, 1, 0, st));
+    // Test hook: RINGAR_STEP_BASE, read when a stream's resources are
+    // created, starts its step numbers there (e.g. just below the point
+    // where the 32-bit LL flags are restarted).
+    if (const char* v = getenv("RINGAR_STEP_BASE")) R.base = strtoull(v, nullptr, 0);
     it = g_res.emplace(key, R).first;
   }
   *out = &it->second;
