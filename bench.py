@@ -17,6 +17,11 @@ AllReduce (double binary tree, channel c on tree c % 2) on the AllReduce
 workload; its busbw keeps the AllReduce convention algbw x 2(n-1)/n.
 `--direct` times the direct form of the ring AllReduce (Simple, each slice
 written straight into the successor's receive buffer, no FIFO).
+`--sweep` prints a table instead of the JSON line: every workload's sizes
+(int32 Simple at 4 ranks; the LL sweep at 8 channels; the bf16 LL128 sweep
+with automatic channels; the automatic protocol over 8 B .. 1 GiB per rank,
+ring only and with the model choosing ring or tree), each timed with HIP
+events (median) and reported as busbw and algorithmic HBM GB/s.
 """
 import argparse
 import glob
@@ -85,6 +90,80 @@ def alg_bytes(n, s, e=1.0, coll="allreduce"):
     return n * s + s + 2 * (n - 1) * s * e
 
 
+FIFO_EXPANSION = {"LL": 2.0, "LL128": 128.0 / 120.0, "Simple": 1.0}
+
+
+def sweep(reps_small=200, reps_big=20):
+    """One table line per (workload, size); see the module docstring."""
+    import torch
+
+    import ring_allreduce_reduce_amd as ra
+
+    dev = torch.device("cuda:0")
+    st = torch.cuda.Stream()
+    tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}
+
+    def timed(n, count, dtype, proto, nch, chunk=0, algo="ring"):
+        if dtype == "int32":
+            xs = [torch.randint(-1000, 1001, (count,), dtype=torch.int32, device=dev) for _ in range(n)]
+        else:
+            xs = [torch.randn(count, device=dev).to(tdt[dtype]) for _ in range(n)]
+        ys = [torch.empty_like(x) for x in xs]
+        cfg = ra.make_config(chunk_bytes=chunk, algo=algo)
+        sp, rp = [x.data_ptr() for x in xs], [y.data_ptr() for y in ys]
+        plan = ra.ringar_plan(count, dtype, n, nch, proto, cfg)
+
+        def call():
+            code = ra.ringar_allreduce_ex(sp, rp, count, dtype, "sum", n, nch, proto, st.cuda_stream, cfg)
+            if code:
+                raise RuntimeError(ra.ringar_result_string(code))
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        es = xs[0].element_size()
+        reps = reps_big if count * es >= (8 << 20) else reps_small
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(st)
+            call()
+            b.record(st)
+        torch.cuda.synchronize()
+        if ra.ringar_get_async_error(st.cuda_stream):
+            raise RuntimeError("asynchronous error")
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
+        del xs, ys
+        s = count * es
+        pname = ra.PROTO_NAMES[plan.proto]
+        alg = s / (t * 1e-6) / 1e9
+        hbm = alg_bytes(n, s, FIFO_EXPANSION[pname]) / (t * 1e-6) / 1e9
+        return dict(bytes=s, us=t, proto=pname, algo=ra.ALGO_NAMES[plan.algo], nch=plan.nchannels,
+                    algbw=alg, busbw=alg * 2 * (n - 1) / n, hbm=hbm)
+
+    rows = []
+
+    def emit(name, r):
+        line = (f"{name:34s} {r['bytes']:>11d} {r['algo']:>5s} {r['proto']:>7s} {r['nch']:>4d} "
+                f"{r['us']:>10.1f} {r['algbw']:>8.2f} {r['busbw']:>8.2f} {r['hbm']:>8.1f} "
+                f"{100 * r['hbm'] / HBM_PEAK_GBS:>6.1f}")
+        rows.append(line)
+        print(line, flush=True)
+
+    print(f"{'workload':34s} {'bytes/rank':>11s} {'algo':>5s} {'proto':>7s} {'nch':>4s} {'us':>10s} "
+          f"{'algbw':>8s} {'busbw':>8s} {'hbmGB/s':>8s} {'%peak':>6s}", flush=True)
+    emit("int32 sum n=4 Simple 2ch 16KiB", timed(4, 65536, "int32", "Simple", 2, 16384))
+    emit("fp32 sum n=8 Simple 16ch 512KiB", timed(8, 16 << 20, "float32", "Simple", 16, 512 << 10))
+    for sh in range(13, 21):
+        emit("fp32 sum n=8 LL 8ch", timed(8, (1 << sh) // 4, "float32", "LL", 8))
+    for sh in range(20, 27):
+        emit("bf16 sum n=8 LL128 auto ch", timed(8, (1 << sh) // 2, "bfloat16", "LL128", 0))
+    for sh in range(3, 31, 3):
+        emit("fp32 sum n=8 auto (ring)", timed(8, max(1, (1 << sh) // 4), "float32", "auto", 0))
+    for sh in range(3, 31, 3):
+        emit("fp32 sum n=8 auto (ring or tree)", timed(8, max(1, (1 << sh) // 4), "float32", "auto", 0,
+                                                     algo="auto"))
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +176,8 @@ def main():
                     help="the AllReduce (default) or one of its halves on the same 8 x 64 MiB shape")
     ap.add_argument("--algo", default="ring", choices=["ring", "tree"],
                     help="AllReduce algorithm: the ring (default) or the double binary tree")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print a table over every workload's sizes instead of the JSON line")
     ap.add_argument("--direct", action="store_true",
                     help="the ring AllReduce's direct form (no FIFO: the successor's receive buffer)")
     args = ap.parse_args()
@@ -104,6 +185,10 @@ def main():
         print(f"bench.py runs on one GPU only: the {NRANKS} ranks are virtual ranks inside one MI355X; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep()
+        return
 
     import numpy as np
     import torch

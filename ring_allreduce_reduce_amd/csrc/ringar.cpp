@@ -439,6 +439,20 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
       lanes /= 2;
     while (lanes < kMaxLanes && slices_for(lanes) > kMaxSlicesPerPart) lanes *= 2;
   }
+  // Automatic lane counts need not be powers of two (only whole workgroups
+  // of 4): when a part needs more than one slice, take the smallest larger
+  // multiple of 4 lanes that the GPU holds and that needs fewer slices; a
+  // short trailing slice costs a whole flag round trip (bf16 LL128 at 64 MiB
+  // per rank: 8 lanes of 32 KiB parts need a 30 KiB and a 2 KiB slice each,
+  // 12 lanes need one).
+  if (!forced_lanes && lanes >= 4 && slices_for(lanes) > 1) {
+    const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
+    for (int L = lanes + 4; L <= kMaxLanes && waves_per_lane * L <= cap; L += 4)
+      if (slices_for(L) < slices_for(lanes)) {
+        lanes = L;
+        break;
+      }
+  }
   if (slices_for(lanes) > kMaxSlicesPerPart)
     return forced_lanes ? RINGAR_ERR_INVALID_USAGE : RINGAR_ERR_INVALID_ARGUMENT;
   P.lanes = lanes;

@@ -213,3 +213,28 @@ def test_abort_flag_ends_waits():
                              abort_flag=flag.data_ptr())
     assert code == ra.ABORTED
     check(xs, "float32", "sum", "Simple", 2)
+
+
+def test_unaligned_buffers_take_the_elementwise_path():
+    n, count = 5, 10007
+    for dtype in ["int8", "float16", "float32", "float64"]:
+        xs = W.inputs(f"tree-unal-{dtype}", n, count, dtype, "uniform", -4, 4)
+        for proto in ["LL", "LL128", "Simple"]:
+            big = [W.to_torch(np.concatenate([np.zeros(1, x.dtype), x]), dtype, DEV) for x in xs]
+            sends = [b[1:] for b in big]
+            recvs = [torch.zeros(count + 1, dtype=b.dtype, device=DEV)[1:] for b in big]
+            ra.allreduce(sends, recvs, op="sum", nchannels=3, proto=proto, algo="tree")
+            torch.cuda.synchronize()
+            assert ra.ringar_get_async_error(torch.cuda.current_stream().cuda_stream) == 0
+            plan = ra.ringar_plan(count, dtype, n, 3, proto, ra.make_config(algo="tree"))
+            want = oracle.tree_allreduce(xs, dtype, "sum", plan.nchannels, plan.chunk_elems)
+            for r in range(n):
+                assert np.array_equal(_bits(W.from_torch(recvs[r], dtype)), _bits(want[r])), (dtype, proto, r)
+
+
+def test_ring_order_does_not_apply_to_the_tree():
+    xs = W.inputs("tree-order", 6, 50001, "float32", "normal")
+    a, _ = check(xs, "float32", "sum", "Simple", 3, 0)
+    b, _ = check(xs, "float32", "sum", "Simple", 3, 0, ring_order=[3, 1, 5, 0, 2, 4])
+    for x, y in zip(a, b):
+        assert np.array_equal(_bits(x), _bits(y))
