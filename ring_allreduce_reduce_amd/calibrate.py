@@ -17,7 +17,8 @@ virtual rank one vertex ([BOOK] Japanese edition ch. 5 §四):
 
 with busBw = nch * bw * treeEff for Simple, that / llDiv (capped at llMax)
 for LL and that * ll128Factor for LL128; tbase and tstep are fitted to small
-calls at n = 2..16, treeEff, llDiv and ll128Factor to large calls.  It prints
+calls at n = 2..16, treeEff and ll128Factor to 8 MiB calls and llDiv to
+1 MiB calls (where tree and ring compete).  It prints
 the fitted model (the JSON layout of `ringar_model_t`) and a tuning table: for
 each size the model's time per (algorithm, protocol), the measured time, and
 which pair each picks.
@@ -159,17 +160,21 @@ def main(argv=None):
         m["tree_hw_lat_us"][p] = round(step, 3)
         log(f"tree {proto}: base {base:.2f} us, step per level {step:.3f} us")
 
-    # tree bandwidth at the largest channel count
+    # tree bandwidth at the largest channel count, fitted at the sizes where
+    # the model has to choose between tree and ring (8 MiB per rank, LL at
+    # 1 MiB): far above them the ring wins anyway, and the tree runs closer
+    # to its model there than at medium sizes (the pages' reason for a
+    # size correction of the tree's bandwidth)
     def tree_bus_at(proto, p, nbytes):
         us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10, algo="tree")
         lat = m["tree_base_lat_us"][p] + 2.0 * _flog2(n) * m["tree_hw_lat_us"][p]
         return 2.0 * nbytes / (1000.0 * max(us - lat, 1e-3))
-    tsimple = tree_bus_at("Simple", 2, big)
+    tsimple = tree_bus_at("Simple", 2, 8 << 20)
     m["tree_allreduce_eff"] = round(tsimple / (maxc * m["bw_per_channel"]), 4)
     m["tree_per_channel_max_bw"] = 1e9
-    tll = tree_bus_at("LL", 0, 64 << 20)
+    tll = tree_bus_at("LL", 0, 1 << 20)
     m["tree_ll_divisor"] = round(tsimple / tll, 4) if tll < m["ll_max_bw"] else 1.0
-    tll128 = tree_bus_at("LL128", 1, big)
+    tll128 = tree_bus_at("LL128", 1, 8 << 20)
     m["tree_ll128_factor"] = round(tll128 / tsimple, 4)
     m["tree_ll128_per_channel_max_bw"] = 1e9
     m["tree_correction"] = 0

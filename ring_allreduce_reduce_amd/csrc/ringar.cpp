@@ -124,12 +124,12 @@ const Env& env() {
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 8.469;
-  m.ll_max_bw = 55.1;
-  m.ll128_per_channel_max_bw = 4.132;
+  m.bw_per_channel = 8.46;
+  m.ll_max_bw = 55.15;
+  m.ll128_per_channel_max_bw = 4.139;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 4.87; m.base_lat_us[1] = 6.33; m.base_lat_us[2] = 5.38;
-  m.hw_lat_us[0] = 1.431; m.hw_lat_us[1] = 2.414; m.hw_lat_us[2] = 1.566;
+  m.base_lat_us[0] = 4.39; m.base_lat_us[1] = 4.71; m.base_lat_us[2] = 4.14;
+  m.hw_lat_us[0] = 1.436; m.hw_lat_us[1] = 2.493; m.hw_lat_us[2] = 1.636;
   m.max_channels = 32;
   m.max_pairs = 256;
   m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;
@@ -138,14 +138,15 @@ ringar_model_t default_model() {
   m.default_chunk_bytes[1] = 491520;
   m.default_chunk_bytes[2] = 524288;
   // Tree rows: the pages' form with MI355X constants fitted the same way
-  // (latency over n = 2..16 as base + 2 floor(log2 n) x step per level).
-  m.tree_allreduce_eff = 0.915;
+  // (latency over n = 2..16 as base + 2 floor(log2 n) x step per level;
+  // bandwidth at 8 MiB per rank, LL at 1 MiB, where tree and ring compete).
+  m.tree_allreduce_eff = 0.7525;
   m.tree_per_channel_max_bw = 1e9;
-  m.tree_ll_divisor = 5.3379;
-  m.tree_ll128_factor = 0.3388;
+  m.tree_ll_divisor = 4.725;
+  m.tree_ll128_factor = 0.313;
   m.tree_ll128_per_channel_max_bw = 1e9;
-  m.tree_base_lat_us[0] = 4.59; m.tree_base_lat_us[1] = 7.71; m.tree_base_lat_us[2] = 6.82;
-  m.tree_hw_lat_us[0] = 1.695; m.tree_hw_lat_us[1] = 2.168; m.tree_hw_lat_us[2] = 1.742;
+  m.tree_base_lat_us[0] = 4.71; m.tree_base_lat_us[1] = 6.28; m.tree_base_lat_us[2] = 5.51;
+  m.tree_hw_lat_us[0] = 1.553; m.tree_hw_lat_us[1] = 2.33; m.tree_hw_lat_us[2] = 1.833;
   m.tree_correction = 0;
   return m;
 }
@@ -401,11 +402,21 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   memcpy(P.times, tree ? P.tree_times : P.ring_times, sizeof(P.times));
   P.proto = proto >= 0 ? proto : (n == 1 ? (int)kSimple : best);
   P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc, !tree));
+  P.per_channel = channel_len(count, P.nch, (uint32_t)es);
   P.chunk_bytes = chunk_bytes ? chunk_bytes : m.default_chunk_bytes[P.proto];
+  if (tree && !chunk_bytes) {
+    // The tree moves a whole chunk up and then down, so a channel needs
+    // several chunks for the two directions to overlap: a quarter of the
+    // channel, kept between 8 KiB (4 KiB for LL) and 64 KiB.  Measured on
+    // MI355X at n = 8, 32 channels: 2 MiB per rank 47.5 -> 37.9 us, 8 MiB
+    // 133.7 -> 99.4 us, 64 MiB 620 -> 534 us against 512 KiB chunks.
+    const uint64_t lo = P.proto == kLL ? 4096 : 8192;
+    const uint64_t hi = std::min<uint64_t>(65536, P.chunk_bytes);
+    P.chunk_bytes = std::min(hi, std::max(lo, align_up(P.per_channel * es / 4, 16)));
+  }
   if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)
     return RINGAR_ERR_INVALID_ARGUMENT;
   P.chunk_elems = P.chunk_bytes / es;
-  P.per_channel = channel_len(count, P.nch, (uint32_t)es);
 
   // Lanes: wavefronts sharing each (rank, channel) chunk, each with its own
   // FIFO.  A primitive's part of a chunk may fill at most half the FIFO
