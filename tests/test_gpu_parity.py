@@ -283,3 +283,13 @@ def test_abort_flag_ends_waits():
                                abort_flag=flag.data_ptr())
     assert code == ra.ABORTED
     check(xs, "float32", "sum", "Simple", 2)
+
+
+@pytest.mark.parametrize("n", [9, 16, 33, 64])
+def test_many_ranks(n):
+    """Up to the library's 64 ranks: 2(n-1) stages per loop, every protocol,
+    ragged counts, and a ring order that is not the identity."""
+    for j, proto in enumerate(["LL", "LL128", "Simple"]):
+        xs = W.inputs(f"many-{n}-{proto}", n, 20011 + 7 * j, "float32", "normal")
+        ring = list(np.random.default_rng(n).permutation(n)) if j == 1 else None
+        check(xs, "float32", "sum", proto, 2, 0, ring=ring)
