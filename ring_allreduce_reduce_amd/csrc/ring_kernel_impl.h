@@ -396,7 +396,33 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
   // three sources in flight (a tree vertex with two children) take half the
   // unroll, so that the kernel keeps the ring's register budget
   constexpr int U = (F & kRecv2) ? kUnroll / 2 : kUnroll;
-  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
+  // Whole groups of 64U packets: every lane in range, so the loads carry no
+  // condition and all of a group's loads are issued before its first store.
+  // (A per-lane condition turns each load into its own branch, and the
+  // compiler then waits for every outstanding store at the top of each
+  // group.)
+  const uint32_t nmain = nfull - nfull % (64u * U);
+  for (uint32_t p0 = 0; p0 < nmain; p0 += 64 * U) {
+    u32x4 va[U], va2[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t off = (p0 + u * 64 + L.lane) * 16;
+      if (F & kRecv) va[u] = ld16<kSC1>(rin, off);
+      if (F & kRecv2) va2[u] = ld16<kSC1>(rin2, off);
+      if (F & kSrc) vb[u] = ld16<kNT>(rsrc_, off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t off = (p0 + u * 64 + L.lane) * 16;
+      const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u], a.nranks);
+      if (F & kSend) st16<kSC1>(r, rout, off);
+      if (F & kSend2) st16<kSC1>(r, rout2, off);
+      if (F & kDst) st16<kNT>(r, rdst, off);
+    }
+  }
+  // the last partial group: per-lane conditions
+  for (uint32_t p0 = nmain; p0 < nfull; p0 += 64 * U) {
     u32x4 va[U], va2[U], vb[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -875,7 +901,26 @@ __device__ __forceinline__ bool slice_direct(Lane& L, uint64_t e0, uint32_t nele
   rsrc_t rdst = rin;
   const uint32_t npk = (nbytes + 15) / 16;
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
-  for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * kUnroll) {
+  // whole groups without per-lane conditions, as in slice_simple
+  const uint32_t nmain = nfull - nfull % (64u * kUnroll);
+  for (uint32_t p0 = 0; p0 < nmain; p0 += 64 * kUnroll) {
+    u32x4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t o = (p0 + u * 64 + L.lane) * 16;
+      if (F & kRecv) va[u] = ld16<kSC1>(rin, o);
+      if (F & kSrc) vb[u] = ld16<kNT>(rsrc_, o);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const uint32_t o = (p0 + u * 64 + L.lane) * 16;
+      const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u], a.nranks);
+      if (F & kSend) st16<kSC1>(r, rpeer, o);
+      if (F & kDst) st16<kNT>(r, rdst, o);
+    }
+  }
+  for (uint32_t p0 = nmain; p0 < nfull; p0 += 64 * kUnroll) {
     u32x4 va[kUnroll], vb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
