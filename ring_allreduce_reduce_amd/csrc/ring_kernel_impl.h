@@ -616,12 +616,13 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
 constexpr uint32_t kLL128Batch = 128;
 constexpr int kLL128Group = 4;
 
-// User-side packets of group g of the batch at line b0 (nl lines): loads the
+// User-side packets of the group at line b0 + g0 of the batch at line b0 (nl
+// lines): loads the
 // whole packets into vb and returns the mask of packets that end inside
 // their column (those go element-wise).
 template <class E, int F>
 __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, uint32_t b0, uint32_t nl,
-                                                     uint32_t g, int lane, bool vec,
+                                                     uint32_t g0, int lane, bool vec,
                                                      u32x4 (&vb)[kLL128Group]) {
   const int col = lane & 7;
   const uint32_t psize = col == 7 ? 8u : 16u;
@@ -629,7 +630,7 @@ __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, 
   uint32_t part = 0;
 #pragma unroll
   for (int v = 0; v < kLL128Group; v++) {
-    const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (lane >> 3);
+    const uint32_t line = b0 + g0 + 8 * v + (lane >> 3);
     const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
     const bool live = line < b0 + nl && valid > 0;
     const bool full = live && vec && (uint32_t)valid >= psize;
@@ -638,6 +639,47 @@ __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, 
     if ((F & kSrc) && full) vb[v] = col == 7 ? ld8<kNT>(r, line * 120 + 112) : ld16<kNT>(r, line * 120 + coff);
   }
   return part;
+}
+
+// Whole lines (all 120 data bytes inside the part, 16-byte aligned user
+// buffers): every lane moves one 16-byte packet per line with one load and
+// one store width.  Column 7 takes the line's last 16 data bytes (104..119)
+// instead of its 8, so it shares bytes 104..111 with column 6; both lanes
+// compute them from the same inputs and store the same values, and all of
+// a group's loads complete before any of its stores, so this holds in place
+// too.  The flag bytes (120..127) are never touched here.  Loads and stores
+// carry no per-lane condition, so all of a group's loads are in flight
+// together and a group does not wait for the previous group's stores.
+
+// Packets per lane per whole group (8 lines each); half with two inputs, to
+// stay within the register budget (occupancy 3).
+template <int F>
+constexpr int ll128_whole_packets() { return (F & kRecv2) ? 2 : 4; }
+
+template <class E, int OP, int F, int NO>
+__device__ __forceinline__ void ll128_whole_group(const rsrc_t (&rin)[2], const rsrc_t (&rout)[2], rsrc_t rsrc_,
+                                                  rsrc_t rdst, uint32_t line0, int lane, int nranks) {
+  constexpr int G = ll128_whole_packets<F>();
+  const uint32_t coff = (lane & 7) == 7 ? 104u : (uint32_t)(lane & 7) * 16u;
+  u32x4 va[G], va2[G], vb[G];
+#pragma unroll
+  for (int v = 0; v < G; v++) {
+    const uint32_t line = line0 + 8 * v + (lane >> 3);
+    if (F & kRecv) va[v] = ld16<kSC1>(rin[0], line * 128 + coff);
+    if (F & kRecv2) va2[v] = ld16<kSC1>(rin[1], line * 128 + coff);
+    if (F & kSrc) vb[v] = ld16<kNT>(rsrc_, line * 120 + coff);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < G; v++) {
+    const uint32_t line = line0 + 8 * v + (lane >> 3);
+    const u32x4 r = combine<E, OP, F>(va[v], va2[v], vb[v], nranks);
+    if (F & kSend) {
+#pragma unroll
+      for (int o = 0; o < NO; o++) st16<kSC1>(r, rout[o], line * 128 + coff);
+    }
+    if (F & kDst) st16<kNT>(r, rdst, line * 120 + coff);
+  }
 }
 
 template <class E, int OP, int F>
@@ -662,11 +704,18 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
   const int col = L.lane & 7;
   const uint32_t psize = col == 7 ? 8u : 16u;
   const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;   // data bytes of the column
+  const uint32_t whole_lines = vec ? nbytes / 120 : 0;   // lines with all 120 bytes in the part
   for (uint32_t b0 = 0; b0 < nlines; b0 += kLL128Batch) {
     const uint32_t nl = min(kLL128Batch, nlines - b0);
-    // the first group's user data is requested before the flags are polled
+    // lines [0, nw) of the batch go in whole groups of WL lines, the rest
+    // packet by packet
+    constexpr uint32_t WL = 8 * ll128_whole_packets<F>();
+    const uint32_t nw = whole_lines > b0 ? min(nl, whole_lines - b0) / WL * WL : 0;
+    // the first packet-by-packet group's user data is requested before the
+    // flags are polled when there is no whole group
     u32x4 vb[kLL128Group];
-    uint32_t part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, 0, L.lane, vec, vb);
+    uint32_t part = 0;
+    if (nw == 0) part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, 0, L.lane, vec, vb);
     if (F & kRecv) {
       // flags first, then data: lane t watches lines b0 + t and b0 + 64 + t
       // of every input
@@ -695,12 +744,15 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       }
       compiler_fence();
     }
+    for (uint32_t g0 = 0; g0 < nw; g0 += WL)
+      ll128_whole_group<E, OP, F, NO>(rin, rout, rsrc_, rdst, b0 + g0, L.lane, a.nranks);
+    if (nw > 0 && nw < nl) part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, nw, L.lane, vec, vb);
 #pragma unroll 1
-    for (uint32_t g = 0; g * kLL128Group * 8 < nl; g++) {
+    for (uint32_t g0 = nw; g0 < nl; g0 += kLL128Group * 8) {
       u32x4 va[kLL128Group], va2[kLL128Group];
 #pragma unroll
       for (int v = 0; v < kLL128Group; v++) {
-        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
         va[v] = u32x4{0u, 0u, 0u, 0u};
         va2[v] = va[v];
         if ((F & kRecv) && line < b0 + nl) va[v] = ld16<kSC1>(rin[0], line * 128 + col * 16);
@@ -709,15 +761,15 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       // the next group's user data is requested while this group computes
       u32x4 vbn[kLL128Group] = {};
       uint32_t partn = 0;
-      if ((g + 1) * kLL128Group * 8 < nl)
-        partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g + 1, L.lane, vec, vbn);
+      if (g0 + kLL128Group * 8 < nl)
+        partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g0 + kLL128Group * 8, L.lane, vec, vbn);
 #pragma unroll
       for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], va2[v], vb[v], a.nranks);
       // Packets that end inside their column: element-wise on the user side.
 #pragma unroll 1
       for (uint32_t bits = part; bits; bits &= bits - 1) {
         const int v = __builtin_ctz(bits);
-        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
         const uint32_t uoff = line * 120 + coff;
         const uint32_t nb = min(psize, nbytes - uoff);
         u32x4 x = u32x4{0u, 0u, 0u, 0u}, x2 = x, y = x;
@@ -736,7 +788,7 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       }
 #pragma unroll
       for (int v = 0; v < kLL128Group; v++) {
-        const uint32_t line = b0 + 8 * (g * kLL128Group + v) + (L.lane >> 3);
+        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
         const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
         if (line >= b0 + nl || valid <= 0 || (part >> v) & 1u) continue;
         if (F & kSend) {
