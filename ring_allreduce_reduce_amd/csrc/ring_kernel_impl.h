@@ -656,18 +656,22 @@ __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, 
 template <int F>
 constexpr int ll128_whole_packets() { return (F & kRecv2) ? 2 : 4; }
 
+// Lines [line0, line0 + 8G) through resources that end at the last whole
+// line of the group run (FIFO: lim lines of 128 bytes, user: lim lines of
+// 120): a lane past it reads zeros and its stores are dropped by the range
+// check, with no per-lane condition.
 template <class E, int OP, int F, int NO>
-__device__ __forceinline__ void ll128_whole_group(const rsrc_t (&rin)[2], const rsrc_t (&rout)[2], rsrc_t rsrc_,
-                                                  rsrc_t rdst, uint32_t line0, int lane, int nranks) {
+__device__ __forceinline__ void ll128_whole_group(const rsrc_t (&win)[2], const rsrc_t (&wout)[2], rsrc_t wsrc,
+                                                  rsrc_t wdst, uint32_t line0, int lane, int nranks) {
   constexpr int G = ll128_whole_packets<F>();
   const uint32_t coff = (lane & 7) == 7 ? 104u : (uint32_t)(lane & 7) * 16u;
   u32x4 va[G], va2[G], vb[G];
 #pragma unroll
   for (int v = 0; v < G; v++) {
     const uint32_t line = line0 + 8 * v + (lane >> 3);
-    if (F & kRecv) va[v] = ld16<kSC1>(rin[0], line * 128 + coff);
-    if (F & kRecv2) va2[v] = ld16<kSC1>(rin[1], line * 128 + coff);
-    if (F & kSrc) vb[v] = ld16<kNT>(rsrc_, line * 120 + coff);
+    if (F & kRecv) va[v] = ld16<kSC1>(win[0], line * 128 + coff);
+    if (F & kRecv2) va2[v] = ld16<kSC1>(win[1], line * 128 + coff);
+    if (F & kSrc) vb[v] = ld16<kNT>(wsrc, line * 120 + coff);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -676,9 +680,9 @@ __device__ __forceinline__ void ll128_whole_group(const rsrc_t (&rin)[2], const 
     const u32x4 r = combine<E, OP, F>(va[v], va2[v], vb[v], nranks);
     if (F & kSend) {
 #pragma unroll
-      for (int o = 0; o < NO; o++) st16<kSC1>(r, rout[o], line * 128 + coff);
+      for (int o = 0; o < NO; o++) st16<kSC1>(r, wout[o], line * 128 + coff);
     }
-    if (F & kDst) st16<kNT>(r, rdst, line * 120 + coff);
+    if (F & kDst) st16<kNT>(r, wdst, line * 120 + coff);
   }
 }
 
@@ -708,9 +712,12 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
   for (uint32_t b0 = 0; b0 < nlines; b0 += kLL128Batch) {
     const uint32_t nl = min(kLL128Batch, nlines - b0);
     // lines [0, nw) of the batch go in whole groups of WL lines, the rest
-    // packet by packet
+    // packet by packet.  Whole lines left after the full groups take a last,
+    // partly masked group when they fill at least half of one; fewer go
+    // packet by packet, with the ragged last line, in the same pass.
     constexpr uint32_t WL = 8 * ll128_whole_packets<F>();
-    const uint32_t nw = whole_lines > b0 ? min(nl, whole_lines - b0) / WL * WL : 0;
+    const uint32_t wl = whole_lines > b0 ? min(nl, whole_lines - b0) : 0;
+    const uint32_t nw = wl % WL >= WL / 2 ? wl : wl / WL * WL;
     // the first packet-by-packet group's user data is requested before the
     // flags are polled when there is no whole group
     u32x4 vb[kLL128Group];
@@ -744,8 +751,15 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       }
       compiler_fence();
     }
-    for (uint32_t g0 = 0; g0 < nw; g0 += WL)
-      ll128_whole_group<E, OP, F, NO>(rin, rout, rsrc_, rdst, b0 + g0, L.lane, a.nranks);
+    if (nw > 0) {
+      const uint32_t lim = b0 + nw;
+      const rsrc_t win[2] = {make_rsrc(sin[0], lim * 128), make_rsrc(sin[1], lim * 128)};
+      const rsrc_t wout[2] = {make_rsrc(sout[0], lim * 128), make_rsrc(sout[1], lim * 128)};
+      const rsrc_t wsrc = make_rsrc(L.src + es0 * sizeof(typename E::T), lim * 120);
+      const rsrc_t wdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), lim * 120);
+      for (uint32_t g0 = 0; g0 < nw; g0 += WL)
+        ll128_whole_group<E, OP, F, NO>(win, wout, wsrc, wdst, b0 + g0, L.lane, a.nranks);
+    }
     if (nw > 0 && nw < nl) part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, nw, L.lane, vec, vb);
 #pragma unroll 1
     for (uint32_t g0 = nw; g0 < nl; g0 += kLL128Group * 8) {
