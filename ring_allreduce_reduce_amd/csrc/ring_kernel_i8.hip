@@ -6,9 +6,9 @@ namespace ringar {
 
 template <int OP>
 static const void* by_proto_kernel_i8(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel<I8, OP, kLL, true, kAllReduce>
-                                 : (const void*)&ring_kernel<I8, OP, kLL, false, kAllReduce>;
-  if (proto == kLL128) return (const void*)&ring_kernel<I8, OP, kLL128, false, kAllReduce>;
+  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<I8, OP, kLL, true, kAllReduce>
+                                 : (const void*)&ring_kernel_lines<I8, OP, kLL, false, kAllReduce>;
+  if (proto == kLL128) return (const void*)&ring_kernel_lines<I8, OP, kLL128, false, kAllReduce>;
   return small ? (const void*)&ring_kernel<I8, OP, kSimple, true, kAllReduce>
                : (const void*)&ring_kernel<I8, OP, kSimple, false, kAllReduce>;
 }

@@ -42,6 +42,8 @@ namespace ringar {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // ----------------------------------------------------------------- elements
@@ -58,6 +60,25 @@ struct I8 {
     int8_t sa = (int8_t)a, sb = (int8_t)b;
     if (OP == 2) return sb < sa ? b : a;
     return sb > sa ? b : a;
+  }
+  // The same op on the four bytes of a word at once: the sum with the carry
+  // kept out of each byte's top bit; products and signed min / max on the
+  // even and odd bytes as 16-bit lanes (packed 16-bit instructions), the
+  // product's low byte and the sign-extended extremum packed back.  Fewer
+  // instructions and registers than byte by byte, same results.
+  template <int OP> __device__ static uint32_t op4(uint32_t a, uint32_t b) {
+    if (OP == 0 || OP == 4) return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
+    if (OP == 1) {
+      const u16x2 pe = __builtin_bit_cast(u16x2, a & 0x00ff00ffu) * __builtin_bit_cast(u16x2, b & 0x00ff00ffu);
+      const u16x2 po =
+          __builtin_bit_cast(u16x2, (a >> 8) & 0x00ff00ffu) * __builtin_bit_cast(u16x2, (b >> 8) & 0x00ff00ffu);
+      return (__builtin_bit_cast(uint32_t, pe) & 0x00ff00ffu) | ((__builtin_bit_cast(uint32_t, po) & 0x00ff00ffu) << 8);
+    }
+    const s16x2 ae = __builtin_bit_cast(s16x2, a << 8) >> 8, be = __builtin_bit_cast(s16x2, b << 8) >> 8;
+    const s16x2 ao = __builtin_bit_cast(s16x2, a) >> 8, bo = __builtin_bit_cast(s16x2, b) >> 8;
+    const s16x2 re = OP == 2 ? __builtin_elementwise_min(ae, be) : __builtin_elementwise_max(ae, be);
+    const s16x2 ro = OP == 2 ? __builtin_elementwise_min(ao, bo) : __builtin_elementwise_max(ao, bo);
+    return (__builtin_bit_cast(uint32_t, re) & 0x00ff00ffu) | ((__builtin_bit_cast(uint32_t, ro) & 0x00ff00ffu) << 8);
   }
 };
 struct I32 {
@@ -91,12 +112,8 @@ struct F16 {
 struct BF16 {
   using T = uint16_t;
   __device__ static float widen(T h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
-  __device__ static T narrow(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (T)((u >> 16) | 0x40u);   // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                       // nearest-even
-    return (T)(u >> 16);
-  }
+  // round to nearest even: gfx950's conversion instruction (v_cvt_pk_bf16_f32)
+  __device__ static T narrow(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
   template <int OP> __device__ static T op(T a, T b) { return narrow(fop<OP>(widen(a), widen(b))); }
   __device__ static T div(T a, int n) { return narrow(widen(a) / (float)n); }
 };
@@ -118,6 +135,8 @@ struct F64 {
 
 // Elementwise op over a 16-byte packet.
 template <class E, int OP> __device__ __forceinline__ u32x4 vop(u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<E, I8>::value)
+    return u32x4{I8::op4<OP>(a.x, b.x), I8::op4<OP>(a.y, b.y), I8::op4<OP>(a.z, b.z), I8::op4<OP>(a.w, b.w)};
   using T = typename E::T;
   constexpr int N = 16 / sizeof(T);
   struct P { T v[N]; };
@@ -393,9 +412,10 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
-  // three sources in flight (a tree vertex with two children) take half the
-  // unroll, so that the kernel keeps the ring's register budget
-  constexpr int U = (F & kRecv2) ? kUnroll / 2 : kUnroll;
+  // three sources in flight (a tree vertex with two children) or the
+  // division of an average take half the unroll, so that the kernel keeps
+  // the ring's register budget (occupancy 4)
+  constexpr int U = (F & (kRecv2 | kPost)) ? kUnroll / 2 : kUnroll;
   // Whole groups of 64U packets: every lane in range, so the loads carry no
   // condition and all of a group's loads are issued before its first store.
   // (A per-lane condition turns each load into its own branch, and the
@@ -967,36 +987,38 @@ __device__ __forceinline__ bool slice_direct(Lane& L, uint64_t e0, uint32_t nele
   rsrc_t rdst = rin;
   const uint32_t npk = (nbytes + 15) / 16;
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
-  // whole groups without per-lane conditions, as in slice_simple
-  const uint32_t nmain = nfull - nfull % (64u * kUnroll);
-  for (uint32_t p0 = 0; p0 < nmain; p0 += 64 * kUnroll) {
-    u32x4 va[kUnroll], vb[kUnroll];
+  // whole groups without per-lane conditions, as in slice_simple (half the
+  // unroll for the division of an average)
+  constexpr int U = (F & kPost) ? kUnroll / 2 : kUnroll;
+  const uint32_t nmain = nfull - nfull % (64u * U);
+  for (uint32_t p0 = 0; p0 < nmain; p0 += 64 * U) {
+    u32x4 va[U], vb[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t o = (p0 + u * 64 + L.lane) * 16;
       if (F & kRecv) va[u] = ld16<kSC1>(rin, o);
       if (F & kSrc) vb[u] = ld16<kNT>(rsrc_, o);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t o = (p0 + u * 64 + L.lane) * 16;
       const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u], a.nranks);
       if (F & kSend) st16<kSC1>(r, rpeer, o);
       if (F & kDst) st16<kNT>(r, rdst, o);
     }
   }
-  for (uint32_t p0 = nmain; p0 < nfull; p0 += 64 * kUnroll) {
-    u32x4 va[kUnroll], vb[kUnroll];
+  for (uint32_t p0 = nmain; p0 < nfull; p0 += 64 * U) {
+    u32x4 va[U], vb[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       const bool in = p < nfull;
       if (F & kRecv) va[u] = in ? ld16<kSC1>(rin, p * 16) : u32x4{0u, 0u, 0u, 0u};
       if (F & kSrc) vb[u] = in ? ld16<kNT>(rsrc_, p * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
       const uint32_t p = p0 + u * 64 + L.lane;
       if (p >= nfull) continue;
       const u32x4 r = combine<E, OP, F>(va[u], va[u], vb[u], a.nranks);
@@ -1074,7 +1096,7 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t es0, uint64_t ed0, u
 // wavefront of every virtual rank.  COLL: kAllReduce (2n-1 stages per loop),
 // kReduceScatter or kAllGather (n stages per loop, whole blocks by rank).
 template <class E, int OP, int PROTO, bool SMALL, int COLL>
-__global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
+__device__ __forceinline__ void ring_body(const KernelArgs& a) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const int wave = threadIdx.x >> 6;
   const int group = blockIdx.x / a.nranks;     // (channel, lane block)
@@ -1175,6 +1197,22 @@ __global__ void __launch_bounds__(256) ring_kernel(const KernelArgs a) {
       }
     }
   }
+}
+
+// The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
+// (occupancy 4: the 4096-wavefront launches of large calls; a few registers
+// of the direct form's outer loop may go to scratch).  The line protocols
+// (LL, LL128) keep their registers: their poll and line paths would spill
+// under that bound.
+template <class E, int OP, int PROTO, bool SMALL, int COLL>
+__global__ void __launch_bounds__(256, 4) ring_kernel(const KernelArgs a) {
+  static_assert(PROTO == kSimple, "the line protocols run ring_kernel_lines");
+  ring_body<E, OP, PROTO, SMALL, COLL>(a);
+}
+template <class E, int OP, int PROTO, bool SMALL, int COLL>
+__global__ void __launch_bounds__(256) ring_kernel_lines(const KernelArgs a) {
+  static_assert(PROTO != kSimple, "Simple runs ring_kernel");
+  ring_body<E, OP, PROTO, SMALL, COLL>(a);
 }
 
 // ----------------------------------------------------------------- tree

@@ -6,9 +6,9 @@ namespace ringar {
 
 template <int OP>
 static const void* by_proto_kernel_rs_f64(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel<F64, OP, kLL, true, kReduceScatter>
-                                 : (const void*)&ring_kernel<F64, OP, kLL, false, kReduceScatter>;
-  if (proto == kLL128) return (const void*)&ring_kernel<F64, OP, kLL128, false, kReduceScatter>;
+  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<F64, OP, kLL, true, kReduceScatter>
+                                 : (const void*)&ring_kernel_lines<F64, OP, kLL, false, kReduceScatter>;
+  if (proto == kLL128) return (const void*)&ring_kernel_lines<F64, OP, kLL128, false, kReduceScatter>;
   return small ? (const void*)&ring_kernel<F64, OP, kSimple, true, kReduceScatter>
                : (const void*)&ring_kernel<F64, OP, kSimple, false, kReduceScatter>;
 }

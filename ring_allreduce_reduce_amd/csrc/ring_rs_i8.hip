@@ -6,9 +6,9 @@ namespace ringar {
 
 template <int OP>
 static const void* by_proto_kernel_rs_i8(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel<I8, OP, kLL, true, kReduceScatter>
-                                 : (const void*)&ring_kernel<I8, OP, kLL, false, kReduceScatter>;
-  if (proto == kLL128) return (const void*)&ring_kernel<I8, OP, kLL128, false, kReduceScatter>;
+  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<I8, OP, kLL, true, kReduceScatter>
+                                 : (const void*)&ring_kernel_lines<I8, OP, kLL, false, kReduceScatter>;
+  if (proto == kLL128) return (const void*)&ring_kernel_lines<I8, OP, kLL128, false, kReduceScatter>;
   return small ? (const void*)&ring_kernel<I8, OP, kSimple, true, kReduceScatter>
                : (const void*)&ring_kernel<I8, OP, kSimple, false, kReduceScatter>;
 }
