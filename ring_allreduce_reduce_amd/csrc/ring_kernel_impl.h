@@ -54,7 +54,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 struct I8 {
   using T = uint8_t;
   __device__ static T div(T a, int n) { return (T)(int8_t)((int)(int8_t)a / n); }
-  template <int OP> __device__ static T op(T a, T b) {
+  template <int OP> __host__ __device__ static T op(T a, T b) {
     if (OP == 0 || OP == 4) return (T)(a + b);
     if (OP == 1) return (T)((uint32_t)a * (uint32_t)b);
     int8_t sa = (int8_t)a, sb = (int8_t)b;
@@ -66,7 +66,7 @@ struct I8 {
   // even and odd bytes as 16-bit lanes (packed 16-bit instructions), the
   // product's low byte and the sign-extended extremum packed back.  Fewer
   // instructions and registers than byte by byte, same results.
-  template <int OP> __device__ static uint32_t op4(uint32_t a, uint32_t b) {
+  template <int OP> __host__ __device__ static uint32_t op4(uint32_t a, uint32_t b) {
     if (OP == 0 || OP == 4) return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
     if (OP == 1) {
       const u16x2 pe = __builtin_bit_cast(u16x2, a & 0x00ff00ffu) * __builtin_bit_cast(u16x2, b & 0x00ff00ffu);
