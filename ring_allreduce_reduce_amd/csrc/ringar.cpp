@@ -464,15 +464,20 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
         break;
       }
   }
-  // LL128 moves whole lines fastest in groups of 32 (3840 data bytes per
-  // part): when the parts above are shorter and the largest power of two of
-  // lanes whose part holds a whole group is still at least 2, take it
-  // (measured, bf16 at n = 8, 32 channels: 2 MiB per rank 8 -> 2 lanes
-  // 67.6 -> 54.6 us, 4 MiB 8 -> 4 lanes 95.6 -> 79.2 us; a single lane was
-  // slower at 512 KiB and 1 MiB, so those keep their lanes).
-  if (!forced_lanes && P.proto == kLL128 && !tree) {
+  // The slices stream whole groups without per-lane conditions (Simple:
+  // 64 x 8 packets = 8 KiB; LL128: 32 lines = 3840 data bytes) and a
+  // shorter remainder lane by lane.  When the parts above are shorter than
+  // one group and the largest power of two of lanes whose part holds a whole
+  // group is still at least 2, take it.  Measured at n = 8, 32 channels:
+  // bf16 LL128 2 MiB per rank 8 -> 2 lanes 67.6 -> 54.6 us, 4 MiB 8 -> 4
+  // lanes 95.6 -> 79.2 us; fp32 Simple 8 MiB 16 -> 4 lanes 68.1 -> 64.6 us,
+  // 16 MiB 16 -> 8 lanes 118.5 -> 110.8 us.  A single lane was slower, and
+  // Simple parts of the small-slice form (at most 1 KiB) keep their lanes.
+  const uint64_t group_bytes = P.proto == kLL128 ? 3840 : P.proto == kSimple ? 8192 : 0;
+  if (!forced_lanes && group_bytes && !tree &&
+      (P.proto != kSimple || lane_part(first_chunk, lanes, (uint32_t)es) * es > kSmallSliceBytes)) {
     int whole = 1;
-    while ((uint64_t)(whole * 2) * 3840 <= first_chunk * es) whole *= 2;
+    while ((uint64_t)(whole * 2) * group_bytes <= first_chunk * es) whole *= 2;
     if (whole >= 2 && whole < lanes) lanes = whole;
   }
   if (slices_for(lanes) > kMaxSlicesPerPart)
