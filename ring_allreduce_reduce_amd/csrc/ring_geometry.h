@@ -41,6 +41,15 @@ constexpr uint32_t kLLSlotBytes = kLLSlotLines * 8;        // FIFO bytes per slo
 constexpr uint32_t kLL128SlotLines = 256;                  // 128-byte lines per slot (30 KiB of data)
 constexpr uint32_t kLL128SlotBytes = kLL128SlotLines * 128;// FIFO bytes per slot
 
+// Groups the slices stream without per-lane conditions (a one-input
+// primitive; two inputs take half): Simple, kUnroll 16-byte packets per
+// lane of a 64-lane wavefront; LL128, kLL128WholePackets packets per lane,
+// 8 lanes per 128-byte line.  The plan sizes lane parts by them.
+constexpr int kUnroll = 8;
+constexpr uint32_t kSimpleGroupBytes = 64u * kUnroll * 16u;                 // 8 KiB
+constexpr int kLL128WholePackets = 4;
+constexpr uint32_t kLL128GroupDataBytes = 8u * kLL128WholePackets * 120u;  // 32 lines
+
 enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
 // Launch kinds: the ring AllReduce and its halves (the public collective
 // codes), and the tree AllReduce.

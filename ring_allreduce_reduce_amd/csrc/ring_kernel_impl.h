@@ -375,7 +375,7 @@ template <int F> __device__ __forceinline__ void publish_tails(Lane& L) {
   L.sstep++;
 }
 
-constexpr int kUnroll = 8;   // 16-byte packets per lane in flight per source
+// kUnroll (ring_geometry.h): 16-byte packets per lane in flight per source
 
 // Result of one packet: the local operand b folded with what was received
 // from input 0 (a) and then input 1 (a2), each hop as op(received, local);
@@ -674,7 +674,7 @@ __device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, 
 // Packets per lane per whole group (8 lines each); half with two inputs, to
 // stay within the register budget (occupancy 3).
 template <int F>
-constexpr int ll128_whole_packets() { return (F & kRecv2) ? 2 : 4; }
+constexpr int ll128_whole_packets() { return (F & kRecv2) ? kLL128WholePackets / 2 : kLL128WholePackets; }
 
 // Lines [line0, line0 + 8G) through resources that end at the last whole
 // line of the group run (FIFO: lim lines of 128 bytes, user: lim lines of

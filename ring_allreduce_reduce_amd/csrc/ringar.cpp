@@ -473,7 +473,8 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // lanes 95.6 -> 79.2 us; fp32 Simple 8 MiB 16 -> 4 lanes 68.1 -> 64.6 us,
   // 16 MiB 16 -> 8 lanes 118.5 -> 110.8 us.  A single lane was slower, and
   // Simple parts of the small-slice form (at most 1 KiB) keep their lanes.
-  const uint64_t group_bytes = P.proto == kLL128 ? 3840 : P.proto == kSimple ? 8192 : 0;
+  const uint64_t group_bytes =
+      P.proto == kLL128 ? kLL128GroupDataBytes : P.proto == kSimple ? kSimpleGroupBytes : 0;
   if (!forced_lanes && group_bytes && !tree &&
       (P.proto != kSimple || lane_part(first_chunk, lanes, (uint32_t)es) * es > kSmallSliceBytes)) {
     int whole = 1;
