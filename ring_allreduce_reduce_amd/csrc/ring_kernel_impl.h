@@ -1200,10 +1200,9 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a) {
 }
 
 // The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
-// (occupancy 4: the 4096-wavefront launches of large calls; a few registers
-// of the direct form's outer loop may go to scratch).  The line protocols
-// (LL, LL128) keep their registers: their poll and line paths would spill
-// under that bound.
+// (occupancy 4: the 4096-wavefront launches of large calls), without
+// scratch.  The line protocols (LL, LL128) keep their registers: their poll
+// and line paths would spill under that bound.
 template <class E, int OP, int PROTO, bool SMALL, int COLL>
 __global__ void __launch_bounds__(256, 4) ring_kernel(const KernelArgs a) {
   static_assert(PROTO == kSimple, "the line protocols run ring_kernel_lines");
