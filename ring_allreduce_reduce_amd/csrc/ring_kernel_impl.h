@@ -329,6 +329,7 @@ struct Lane {
   uint64_t head_seen[2];  // largest head of each output connection seen so far
   int lane;            // lane within the wavefront
   Waiter w;
+  bool cap;            // a captured call (the kernel instance's constant)
 };
 
 // Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
@@ -343,11 +344,27 @@ template <int OP> constexpr int post_flag() { return OP == 4 ? kPost : 0; }
 // load of a slot has returned its data (the values were consumed above),
 // so the producer may overwrite it; the wavefront's own stores need not be
 // complete, and waiting for them here would add a round trip to every step.
+// Captured calls (a graph may replay one any number of times) run kernel
+// instances of their own: their steps count from zero on counters of their
+// own, and they leave every counter and flag they consumed at zero (the
+// receiver of a connection zeroes the LL lines / LL128 flags it read before
+// handing the slot back, and its tail and head after its last step).  Eager
+// calls count from 2^31 up, so no flag either kind leaves behind can match
+// the other's.
 template <int F> __device__ __forceinline__ void release_slot(Lane& L) {
+  if (L.cap) wait_mem();   // the consumed lines' zeroing stores first
   compiler_fence();
   st_relaxed(L.in[0].head, L.a->base + L.rstep + 1);
   if (F & kRecv2) st_relaxed(L.in[1].head, L.a->base + L.rstep + 1);
   L.rstep++;
+}
+
+// After a captured call's last step on it: a receiver's input connection
+// back to zero (its producer has published its last tail and read its last
+// head by then).
+__device__ __forceinline__ void reset_input(const Conn& c) {
+  st_relaxed(c.tail, 0);
+  st_relaxed(c.head, 0);
 }
 
 // Waits for the tails of the inputs and for free slots on the outputs of
@@ -588,6 +605,18 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
 #pragma unroll
         for (int u = 0; u < U; u++)
           va[i][u] = u32x4{(uint32_t)ln[i][u][0], (uint32_t)ln[i][u][1], (uint32_t)ln[i][u][2], (uint32_t)ln[i][u][3]};
+      if (L.cap) {
+        // the lines read, back to zero (see release_slot)
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+          for (int u = 0; u < U; u++) {
+            const uint32_t p = p0 + u * 64 + L.lane;
+            if (p < nfull)
+#pragma unroll
+              for (int q = 0; q < 4; q++) st_relaxed(const_cast<uint64_t*>(lin[i]) + 4 * p + q, 0);
+          }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -613,6 +642,9 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
         uint64_t ln[4];
         if (!ll_recv4(L.w, lin[i], p, true, fin, ln)) { failed = true; break; }
         x[i] = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
+        if (L.cap)
+#pragma unroll
+          for (int q = 0; q < 4; q++) st_relaxed(const_cast<uint64_t*>(lin[i]) + 4 * p + q, 0);
       }
       if (failed) break;
     }
@@ -841,6 +873,14 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       for (int v = 0; v < kLL128Group; v++) vb[v] = vbn[v];
       part = partn;
     }
+    if ((F & kRecv) && L.cap) {
+      // the batch's flags, back to zero (see release_slot)
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int w = 0; w < 2; w++)
+          if (64 * w + L.lane < (int)nl) st_relaxed((uint64_t*)(sin[i] + (size_t)(b0 + 64 * w + L.lane) * 128 + 120), 0);
+    }
     if (F & kSend) {
       wait_mem();   // all data of the batch is visible before any of its flags
 #pragma unroll
@@ -923,6 +963,13 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
 #pragma unroll
     for (int i = 0; i < NI; i++)
       va[i] = u32x4{(uint32_t)ln[i][0], (uint32_t)ln[i][1], (uint32_t)ln[i][2], (uint32_t)ln[i][3]};
+    if (L.cap)
+      // the lines read, back to zero (see release_slot); lanes past the
+      // part are dropped by the range check
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) ll_store(ri[i], p * 32 + q * 8, 0u, 0u);
   }
   const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb, a.nranks);
   if (F & kSend) {
@@ -1096,7 +1143,7 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t es0, uint64_t ed0, u
 // wavefront of every virtual rank.  COLL: kAllReduce (2n-1 stages per loop),
 // kReduceScatter or kAllGather (n stages per loop, whole blocks by rank).
 template <class E, int OP, int PROTO, bool SMALL, int COLL>
-__device__ __forceinline__ void ring_body(const KernelArgs& a) {
+__device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const int wave = threadIdx.x >> 6;
   const int group = blockIdx.x / a.nranks;     // (channel, lane block)
@@ -1112,6 +1159,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a) {
   L.a = &a;
   L.w.a = &a;
   L.lane = threadIdx.x & 63;
+  L.cap = cap;
   L.sstep = 0;
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;   // below any value a wait of this call asks for
@@ -1197,21 +1245,24 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a) {
       }
     }
   }
+  if (cap) reset_input(L.in[0]);
 }
 
 // The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
 // (occupancy 4: the 4096-wavefront launches of large calls), without
 // scratch.  The line protocols (LL, LL128) keep their registers: their poll
 // and line paths would spill under that bound.
-template <class E, int OP, int PROTO, bool SMALL, int COLL>
+// CAP: the captured form (its own instances, so that the eager ones carry
+// none of its code).
+template <class E, int OP, int PROTO, bool SMALL, int COLL, bool CAP = false>
 __global__ void __launch_bounds__(256, 4) ring_kernel(const KernelArgs a) {
   static_assert(PROTO == kSimple, "the line protocols run ring_kernel_lines");
-  ring_body<E, OP, PROTO, SMALL, COLL>(a);
+  ring_body<E, OP, PROTO, SMALL, COLL>(a, CAP);
 }
-template <class E, int OP, int PROTO, bool SMALL, int COLL>
+template <class E, int OP, int PROTO, bool SMALL, int COLL, bool CAP = false>
 __global__ void __launch_bounds__(256) ring_kernel_lines(const KernelArgs a) {
   static_assert(PROTO != kSimple, "Simple runs ring_kernel");
-  ring_body<E, OP, PROTO, SMALL, COLL>(a);
+  ring_body<E, OP, PROTO, SMALL, COLL>(a, CAP);
 }
 
 // ----------------------------------------------------------------- tree
@@ -1271,6 +1322,7 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   L.a = &a;
   L.w.a = &a;
   L.lane = threadIdx.x & 63;
+  L.cap = false;   // the tree has no captured form
   L.sstep = 0;
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;

@@ -523,11 +523,24 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
 // FIFO memory, counters and the error word of one (device, stream).  All
 // counters and flags are absolute step numbers below `base`, so memory that
 // is reused by a later call (of any shape or protocol) can never look fresh.
+// Eager calls number their steps from 2^31 (up to the 32-bit LL flags'
+// restart point); captured calls from zero on counters of their own, leaving
+// every counter and flag they consumed at zero.  No flag either kind leaves
+// in a FIFO slot can match a step number of the other.
+constexpr uint64_t kEagerBase = 1ull << 31;
+
 struct Resources {
   int device = 0;
   char* fifo[3] = {nullptr, nullptr, nullptr};
   uint64_t fifo_conns[3] = {0, 0, 0};
   uint64_t* counters = nullptr;
+  uint64_t* cap_counters = nullptr;   // captured calls' own counters, kept at zero between calls
+  // A captured graph holds the addresses of the FIFO and counters it was
+  // captured with.  Once the stream has captured a call, buffers replaced by
+  // a larger allocation are kept here, alive for those graphs, until
+  // ringar_release.
+  bool captured_ever = false;
+  std::vector<void*> retired;
   uint64_t counter_conns = 0;
   uint64_t* error = nullptr;
   uint64_t base = 0;
@@ -543,9 +556,18 @@ std::map<long long, int> g_occupancy;   // (kernel, block) -> blocks per CU
 
 // FIFO slots (unless `counters_only`) and counters for `conns` connections.
 ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t conns, bool counters_only) {
+  auto drop = [&R](void* p) -> ringar_result_t {
+    if (!p) return RINGAR_SUCCESS;
+    if (R.captured_ever)
+      R.retired.push_back(p);
+    else
+      HIP_TRY(hipFree(p));
+    return RINGAR_SUCCESS;
+  };
+  ringar_result_t r;
   if (!counters_only && R.fifo_conns[proto] < conns) {
     HIP_TRY(hipStreamSynchronize(st));
-    if (R.fifo[proto]) HIP_TRY(hipFree(R.fifo[proto]));
+    if ((r = drop(R.fifo[proto])) != RINGAR_SUCCESS) return r;
     R.fifo[proto] = nullptr;
     R.fifo_conns[proto] = 0;
     const uint64_t bytes = conns * fifo_conn_bytes(proto);
@@ -555,11 +577,14 @@ ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t c
   }
   if (R.counter_conns < conns) {
     HIP_TRY(hipStreamSynchronize(st));
-    if (R.counters) HIP_TRY(hipFree(R.counters));
-    R.counters = nullptr;
+    if ((r = drop(R.counters)) != RINGAR_SUCCESS) return r;
+    if ((r = drop(R.cap_counters)) != RINGAR_SUCCESS) return r;
+    R.counters = R.cap_counters = nullptr;
     R.counter_conns = 0;
     HIP_TRY(hipMalloc((void**)&R.counters, conns * kCounterWords * 8));
     HIP_TRY(launch_fill(R.counters, conns * kCounterWords, 0, st));
+    HIP_TRY(hipMalloc((void**)&R.cap_counters, conns * kCounterWords * 8));
+    HIP_TRY(launch_fill(R.cap_counters, conns * kCounterWords, 0, st));
     R.counter_conns = conns;
   }
   return RINGAR_SUCCESS;
@@ -577,6 +602,7 @@ ringar_result_t get_resources(hipStream_t st, Resources** out) {
     HIP_TRY(hipDeviceGetAttribute(&R.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
     HIP_TRY(hipMalloc((void**)&R.error, 8));
     HIP_TRY(launch_fill(R.error, 1, 0, st));
+    R.base = kEagerBase;
     // Test hook: RINGAR_STEP_BASE, read when a stream's resources are
     // created, starts its step numbers there (e.g. just below the point
     // where the 32-bit LL flags are restarted).
@@ -587,12 +613,13 @@ ringar_result_t get_resources(hipStream_t st, Resources** out) {
   return RINGAR_SUCCESS;
 }
 
-// Restart all step numbers at zero: clear every flag and counter first.
+// Restart the eager step numbers at kEagerBase: clear every flag and counter
+// first.
 ringar_result_t reset_steps(Resources& R, hipStream_t st) {
   for (int p = 0; p < 3; p++)
     if (R.fifo[p]) HIP_TRY(launch_fill((uint64_t*)R.fifo[p], R.fifo_conns[p] * fifo_conn_bytes(p) / 8, 0, st));
   if (R.counters) HIP_TRY(launch_fill(R.counters, R.counter_conns * kCounterWords, 0, st));
-  R.base = 0;
+  R.base = kEagerBase;
   return RINGAR_SUCCESS;
 }
 
@@ -618,7 +645,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      max_active_blocks(coll, dtype, op, proto, false, 256, &per_cu) != hipSuccess)
+      max_active_blocks(coll, dtype, op, proto, false, false, 256, &per_cu) != hipSuccess)
     return 0;
   uint64_t w = (uint64_t)cus * (uint64_t)per_cu * 4;   // 4 wavefronts per 256-thread block
   cache.emplace(key, w);
@@ -857,20 +884,35 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     return RINGAR_SUCCESS;
   }
   count = kcount;
-  // A call's step numbers are fixed when it is enqueued: a captured call
-  // would replay with the same numbers and could take the flags of the
-  // previous replay for fresh data (and a first call allocates).  Refuse a
-  // capturing stream before anything is enqueued.
+  // Under stream capture (a graph replays the call any number of times) the
+  // ring AllReduce runs its captured form: steps from zero on the captured
+  // counters, every consumed flag and counter left at zero, nothing
+  // allocated or cleared during capture.  The stream's resources must hold
+  // the call's connections already (an eager call of the same shape on the
+  // stream allocates them); the tree, the halves and the direct form are
+  // refused.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(st, &capture));
-  if (capture != hipStreamCaptureStatusNone) {
-    t_last_error = "stream capture is not supported: step numbers are fixed at enqueue time";
-    return RINGAR_ERR_INVALID_USAGE;
-  }
+  const bool captured = capture != hipStreamCaptureStatusNone;
 
   std::lock_guard<std::mutex> lock(g_mu);
   Resources* R = nullptr;
-  if ((r = get_resources(st, &R)) != RINGAR_SUCCESS) return r;
+  if (captured) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    auto it = g_res.find(std::make_pair(dev, st));
+    if (P.kind != kAllReduce) {
+      t_last_error = "under stream capture only the ring AllReduce runs (not the tree or the halves)";
+      return RINGAR_ERR_INVALID_USAGE;
+    }
+    if (it == g_res.end() || it->second.counter_conns < P.conns || it->second.fifo_conns[P.proto] < P.conns) {
+      t_last_error = "under stream capture nothing is allocated: make one call of this shape on the stream first";
+      return RINGAR_ERR_INVALID_USAGE;
+    }
+    R = &it->second;
+  } else if ((r = get_resources(st, &R)) != RINGAR_SUCCESS) {
+    return r;
+  }
 
   // All (rank, channel, lane) wavefronts wait on each other, so the whole
   // grid must be resident at once.
@@ -880,12 +922,12 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   for (int q = 0; q < nranks; q++)
     if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   const bool small = P.small && vec;
-  const long long okey =
-      ((((long long)P.kind * 8 + dtype) * 5 + op) * 3 + P.proto) * 2048 + (small ? 1024 : 0) + P.block;
+  const long long okey = ((((long long)P.kind * 8 + dtype) * 5 + op) * 3 + P.proto) * 4096 +
+                         (captured ? 2048 : 0) + (small ? 1024 : 0) + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;
-    HIP_TRY(max_active_blocks(P.kind, dtype, op, P.proto, small, P.block, &per_cu));
+    HIP_TRY(max_active_blocks(P.kind, dtype, op, P.proto, small, captured, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
   if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
@@ -894,10 +936,17 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   bool direct = P.direct;
   for (int q = 0; q < nranks && direct; q++)
     if (sendbuffs[q] == recvbuffs[q]) direct = false;
-  if ((r = ensure_conns(*R, st, P.proto, P.conns, direct)) != RINGAR_SUCCESS) return r;
-  // LL flags are 32-bit step numbers: restart the numbering before it wraps.
-  if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
-    if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;
+  if (captured && direct) {
+    t_last_error = "the direct form has no captured form";
+    return RINGAR_ERR_INVALID_USAGE;
+  }
+  if (captured) R->captured_ever = true;
+  if (!captured) {
+    if ((r = ensure_conns(*R, st, P.proto, P.conns, direct)) != RINGAR_SUCCESS) return r;
+    // LL flags are 32-bit step numbers: restart the numbering before it wraps.
+    if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
+      if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;
+  }
 
   KernelArgs A;
   memset(&A, 0, sizeof(A));
@@ -911,8 +960,8 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   A.count = count;
   A.per_channel = P.per_channel;
   A.chunk_elems = P.chunk_elems;
-  A.base = R->base;
-  A.counters = R->counters;
+  A.base = captured ? 0 : R->base;
+  A.counters = captured ? R->cap_counters : R->counters;
   A.error = R->error;
   A.abort_flag = cfg ? cfg->abort_flag : nullptr;
   uint32_t spin_ms = (cfg && cfg->spin_limit_ms) ? cfg->spin_limit_ms : env().spin_limit_ms;
@@ -954,9 +1003,9 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
       }
     HIP_TRY(launch_tree(dtype, op, P.proto, small, T, P.grid, P.block, st));
   } else {
-    HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, A, P.grid, P.block, st));
+    HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, captured, A, P.grid, P.block, st));
   }
-  R->base += P.max_steps + 1;
+  if (!captured) R->base += P.max_steps + 1;
 
   if (env().debug) {
     fprintf(stderr,
@@ -1046,6 +1095,8 @@ ringar_result_t ringar_release(void) {
     for (int p = 0; p < 3; p++)
       if (R.fifo[p]) HIP_TRY(hipFree(R.fifo[p]));
     if (R.counters) HIP_TRY(hipFree(R.counters));
+    if (R.cap_counters) HIP_TRY(hipFree(R.cap_counters));
+    for (void* p : R.retired) HIP_TRY(hipFree(p));
     if (R.error) HIP_TRY(hipFree(R.error));
   }
   g_res.clear();

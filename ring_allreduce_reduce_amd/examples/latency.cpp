@@ -3,6 +3,8 @@
 // and reports the device time per call (HIP events around the loop) and the
 // host time to enqueue one call.  With the host faster than the device the
 // first is the device-bound rate, free of any binding's per-call overhead.
+// Ring cases are also captured into a HIP graph (the 2000 calls) and the
+// graph's replay is timed the same way.
 //
 // Build (from the repository root, after the library is built):
 //   hipcc -O2 -I include -o /tmp/ringar_latency ring_allreduce_reduce_amd/examples/latency.cpp \
@@ -78,9 +80,40 @@ int main() {
     CHECK_HIP(hipEventElapsedTime(&ms, start, stop));
     const double host_us = std::chrono::duration<double, std::micro>(h1 - h0).count() / calls;
     const ringar_result_t err = ringar_get_async_error(stream);
-    std::printf("%-22s device %6.2f us per call, host enqueue %5.2f us per call%s\n", c.name, ms * 1e3 / calls,
+    std::printf("%-22s device %6.2f us per call, host enqueue %5.2f us per call%s", c.name, ms * 1e3 / calls,
                 host_us, err == RINGAR_SUCCESS ? "" : " (async error)");
     if (err != RINGAR_SUCCESS) return 1;
+    if (c.algo == RINGAR_ALGO_RING) {
+      // the same calls captured into a graph, then one replay of it
+      hipGraph_t graph;
+      hipGraphExec_t exec;
+      CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+      ringar_result_t cr = RINGAR_SUCCESS;
+      for (int k = 0; k < calls && cr == RINGAR_SUCCESS; k++)
+        cr = ringar_allreduce_ex(send.data(), recv.data(), c.count, RINGAR_FLOAT32, RINGAR_SUM, n, 0, c.proto, stream,
+                                 &cfg);
+      CHECK_HIP(hipStreamEndCapture(stream, &graph));
+      if (cr != RINGAR_SUCCESS) {
+        std::printf("\n%s under capture: %s\n", c.name, ringar_result_string(cr));
+        return 1;
+      }
+      CHECK_HIP(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+      CHECK_HIP(hipGraphLaunch(exec, stream));   // first replay: warm
+      CHECK_HIP(hipStreamSynchronize(stream));
+      CHECK_HIP(hipEventRecord(start, stream));
+      CHECK_HIP(hipGraphLaunch(exec, stream));
+      CHECK_HIP(hipEventRecord(stop, stream));
+      CHECK_HIP(hipStreamSynchronize(stream));
+      CHECK_HIP(hipEventElapsedTime(&ms, start, stop));
+      if (ringar_get_async_error(stream) != RINGAR_SUCCESS) {
+        std::printf("\n%s: async error in the graph\n", c.name);
+        return 1;
+      }
+      std::printf(", graph replay %6.2f us per call", ms * 1e3 / calls);
+      CHECK_HIP(hipGraphExecDestroy(exec));
+      CHECK_HIP(hipGraphDestroy(graph));
+    }
+    std::printf("\n");
     CHECK_HIP(hipEventDestroy(start));
     CHECK_HIP(hipEventDestroy(stop));
   }

@@ -1,6 +1,15 @@
-"""A call on a stream in graph capture is refused before anything is
-enqueued (its FIFO step numbers would be replayed), and the library keeps
-working afterwards."""
+"""Ring AllReduce calls captured in a HIP graph and replayed, bit-exact
+against the oracle on every replay: the captured form numbers its steps
+from zero on counters of its own and leaves every counter and flag it
+consumed at zero, so each replay starts clean, while eager calls on the same
+stream, made between the replays, keep their own step numbers.  Every
+protocol (LL in both forms, LL128, Simple in both forms), several dtypes and
+ops, ragged sizes.  Each replay gets fresh inputs, copied in before it (no
+clear of any library memory is recorded in the graph).  The tree, the halves,
+the direct form and a shape the stream has not run yet are refused under
+capture, before anything is enqueued, and the capture goes on.  A graph
+keeps working after eager calls on its stream have grown the FIFO memory and
+counters it was captured with."""
 import numpy as np
 import pytest
 import torch
@@ -12,27 +21,180 @@ from ring_allreduce_reduce_amd import workloads as W
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
+# (n, count, dtype, op, proto, nchannels)
+SHAPES = [
+    (8, 4096, "float32", "sum", "LL", 0),          # small LL form
+    (8, 200003, "float32", "sum", "LL", 4),        # LL, ragged
+    (4, 300001, "bfloat16", "sum", "LL128", 4),    # LL128, ragged
+    (8, 1 << 20, "float32", "sum", "Simple", 0),   # Simple
+    (3, 5000, "int32", "max", "Simple", 2),        # Simple, small form
+    (5, 77777, "float16", "avg", "LL128", 3),
+]
 
-def test_capture_is_refused_and_later_calls_work():
-    n, count = 4, 4096
-    xs = W.inputs("capture", n, count, "float32", "normal")
-    sends = [W.to_torch(x, "float32", DEV) for x in xs]
-    recvs = [torch.zeros_like(s) for s in sends]
-    torch.cuda.synchronize()
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def _want(xs, shape):
+    n, count, dtype, op, proto, nch = shape
+    plan = ra.ringar_plan(count, dtype, n, nch, proto)
+    return oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems)
+
+
+def _raw(sends, recvs, shape, stream, cfg=None):
+    n, count, dtype, op, proto, nch = shape
+    return ra.ringar_allreduce_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count, dtype, op,
+                                  n, nch, proto, stream.cuda_stream, cfg)
+
+
+def _check(recvs, want, what):
+    for r, (got, w) in enumerate(zip(recvs, want)):
+        assert np.array_equal(_bits(W.from_torch(got, what[2])), _bits(w)), (what, r)
+
+
+def _inputs(shape, key):
+    n, count, dtype, op, proto, nch = shape
+    return W.inputs(key, n, count, dtype, "uniform", -4, 4)
+
+
+def test_capture_replays_match_the_oracle():
+    st = torch.cuda.Stream()
+    bufs = []
+    with torch.cuda.stream(st):
+        for i, shape in enumerate(SHAPES):
+            n, count, dtype = shape[0], shape[1], shape[2]
+            xs = _inputs(shape, f"cap-warm-{i}")
+            sends = [W.to_torch(x, dtype, DEV) for x in xs]
+            recvs = [torch.zeros_like(s) for s in sends]
+            print(f"case capture warm-up {shape}", flush=True)
+            assert _raw(sends, recvs, shape, st) == ra.SUCCESS      # allocates the stream's connections
+            bufs.append((sends, recvs))
+    st.synchronize()
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    for i, shape in enumerate(SHAPES):
+        _check(bufs[i][1], _want(_inputs(shape, f"cap-warm-{i}"), shape), shape)
+
     g = torch.cuda.CUDAGraph()
     codes = []
-    with torch.cuda.graph(g):
-        st = torch.cuda.current_stream().cuda_stream
-        for algo in ("ring", "tree"):
-            codes.append(ra.ringar_allreduce_ex([s.data_ptr() for s in sends], [r.data_ptr() for r in recvs],
-                                                count, "float32", "sum", n, 2, "Simple", st,
-                                                ra.make_config(algo=algo)))
-    assert codes == [ra.INVALID_USAGE, ra.INVALID_USAGE]
+    with torch.cuda.graph(g, stream=st):
+        for (sends, recvs), shape in zip(bufs, SHAPES):
+            codes.append(_raw(sends, recvs, shape, st))
+    assert codes == [ra.SUCCESS] * len(SHAPES), [ra.ringar_result_string(c) for c in codes]
+
+    for rep in range(4):
+        xs_all = [_inputs(shape, f"cap-rep{rep}-{i}") for i, shape in enumerate(SHAPES)]
+        with torch.cuda.stream(st):
+            for (sends, recvs), xs, shape in zip(bufs, xs_all, SHAPES):
+                for t, x in zip(sends, xs):
+                    t.copy_(W.to_torch(x, shape[2], DEV))
+                for t in recvs:
+                    t.zero_()
+        st.synchronize()
+        print(f"case capture replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        for (sends, recvs), xs, shape in zip(bufs, xs_all, SHAPES):
+            _check(recvs, _want(xs, shape), shape)
+        # eager work on the capturing stream between replays
+        shape = SHAPES[rep % len(SHAPES)]
+        xs = _inputs(shape, f"cap-eager-{rep}")
+        sends = [W.to_torch(x, shape[2], DEV) for x in xs]
+        recvs = [torch.zeros_like(s) for s in sends]
+        print(f"case capture eager between replays {shape}", flush=True)
+        assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+        st.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        _check(recvs, _want(xs, shape), shape)
+
+    # back-to-back replays with no synchronisation between them: each one
+    # starts from the zeros the previous one left (the inputs are those of
+    # the last checked replay, so the outputs must not change)
+    print("case capture 16 back-to-back replays", flush=True)
+    for _ in range(16):
+        g.replay()
     torch.cuda.synchronize()
-    ra.allreduce(sends, recvs, op="sum", nchannels=2, proto="Simple")
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    for (sends, recvs), xs, shape in zip(bufs, xs_all, SHAPES):
+        _check(recvs, _want(xs, shape), shape)
+
+
+def test_refused_under_capture_and_capture_goes_on():
+    st = torch.cuda.Stream()
+    n, count = 4, 4096
+    xs = W.inputs("cap-refuse", n, count, "float32", "normal")
+    sends = [W.to_torch(x, "float32", DEV) for x in xs]
+    recvs = [torch.zeros_like(s) for s in sends]
+    shape = (n, count, "float32", "sum", "Simple", 2)
+    with torch.cuda.stream(st):
+        assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+        assert _raw(sends, recvs, shape, st, ra.make_config(algo="tree")) == ra.SUCCESS
+    st.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        refused = [
+            _raw(sends, recvs, shape, st, ra.make_config(algo="tree")),        # the tree
+            _raw(sends, recvs, shape, st, ra.make_config(direct=1)),           # the direct form
+            _raw(sends, recvs, (n, count, "float32", "sum", "LL128", 16), st),  # shape not run yet
+        ]
+        rs = ra.ringar_reduce_scatter_ex([t.data_ptr() for t in sends], [t[:count // n].data_ptr() for t in recvs],
+                                         count // n, "float32", "sum", n, 2, "Simple", st.cuda_stream, None)
+        ok = _raw(sends, recvs, shape, st)
+    assert refused == [ra.INVALID_USAGE] * 3 and rs == ra.INVALID_USAGE and ok == ra.SUCCESS
+    for t in recvs:
+        t.zero_()
     torch.cuda.synchronize()
-    assert ra.ringar_get_async_error(torch.cuda.current_stream().cuda_stream) == 0
-    plan = ra.ringar_plan(count, "float32", n, 2, "Simple")
-    want = oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
-    for r in range(n):
-        assert np.array_equal(W.from_torch(recvs[r], "float32"), want[r])
+    g.replay()
+    torch.cuda.synchronize()
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    _check(recvs, _want(xs, shape), shape)
+
+
+def test_replays_after_the_stream_grew_its_buffers():
+    # the graph's kernels hold the FIFO and counter addresses of the capture;
+    # eager calls that need more connections allocate larger buffers and keep
+    # the old ones alive for the graph
+    st = torch.cuda.Stream()
+    small = [(4, 50000, "float32", "sum", "Simple", 2), (4, 30001, "bfloat16", "max", "LL", 2),
+             (3, 40000, "int32", "sum", "LL128", 2)]
+    large = [(8, 1 << 21, "float32", "sum", "Simple", 16), (8, 1 << 18, "float32", "sum", "LL", 16),
+             (8, 1 << 20, "int32", "sum", "LL128", 16)]
+    bufs = []
+    with torch.cuda.stream(st):
+        for i, shape in enumerate(small):
+            sends = [W.to_torch(x, shape[2], DEV) for x in _inputs(shape, f"grow-warm-{i}")]
+            recvs = [torch.zeros_like(t) for t in sends]
+            print(f"case capture grow warm-up {shape}", flush=True)
+            assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+            bufs.append((sends, recvs))
+    st.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        codes = [_raw(sends, recvs, shape, st) for (sends, recvs), shape in zip(bufs, small)]
+    assert codes == [ra.SUCCESS] * len(small), [ra.ringar_result_string(c) for c in codes]
+    for rep, grow in enumerate(large):
+        # an eager call of a larger shape on the capturing stream first
+        xs = _inputs(grow, f"grow-eager-{rep}")
+        sends = [W.to_torch(x, grow[2], DEV) for x in xs]
+        recvs = [torch.zeros_like(t) for t in sends]
+        print(f"case capture grow eager {grow}", flush=True)
+        assert _raw(sends, recvs, grow, st) == ra.SUCCESS
+        st.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        _check(recvs, _want(xs, grow), grow)
+        del sends, recvs
+        xs_all = [_inputs(shape, f"grow-rep{rep}-{i}") for i, shape in enumerate(small)]
+        with torch.cuda.stream(st):
+            for (sends, recvs), xs, shape in zip(bufs, xs_all, small):
+                for t, x in zip(sends, xs):
+                    t.copy_(W.to_torch(x, shape[2], DEV))
+                for t in recvs:
+                    t.zero_()
+        st.synchronize()
+        print(f"case capture grow replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        for (sends, recvs), xs, shape in zip(bufs, xs_all, small):
+            _check(recvs, _want(xs, shape), shape)
