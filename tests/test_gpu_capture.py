@@ -9,7 +9,8 @@ clear of any library memory is recorded in the graph).  The tree, the halves,
 the direct form and a shape the stream has not run yet are refused under
 capture, before anything is enqueued, and the capture goes on.  A graph
 keeps working after eager calls on its stream have grown the FIFO memory and
-counters it was captured with."""
+counters it was captured with.  Randomly drawn calls (every knob of a ring AllReduce at
+once) captured into one graph replay bit-exact too."""
 import numpy as np
 import pytest
 import torch
@@ -198,3 +199,90 @@ def test_replays_after_the_stream_grew_its_buffers():
         assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
         for (sends, recvs), xs, shape in zip(bufs, xs_all, small):
             _check(recvs, _want(xs, shape), shape)
+
+
+def _draw(rng):
+    n = int(rng.integers(2, 17)) if rng.random() < 0.85 else int(rng.integers(17, 33))
+    if rng.random() < 0.04:
+        n = 1
+    count = int(np.exp(rng.uniform(0, np.log(300_000))))
+    if rng.random() < 0.04:
+        count = 0
+    dtype = list(W.STORAGE)[int(rng.integers(0, len(W.STORAGE)))]
+    op = ["sum", "prod", "min", "max", "avg"][int(rng.integers(0, 5))]
+    proto = ["LL", "LL128", "Simple", "auto"][int(rng.integers(0, 4))]
+    cfg = dict(chunk_bytes=0 if rng.random() < 0.5 else int(rng.integers(1, 4096)) * 16,
+               lanes=0 if rng.random() < 0.6 else int(2 ** rng.integers(0, 6)),
+               fifo_depth=0 if rng.random() < 0.7 else int([2, 4, 8][rng.integers(0, 3)]),
+               force_general=int(rng.random() < 0.2),
+               ring_order=[int(r) for r in rng.permutation(n)] if rng.random() < 0.3 else None)
+    return n, count, dtype, op, proto, int(rng.integers(0, 17)), cfg, rng.random() < 0.2, rng.random() < 0.15
+
+
+def test_random_calls_captured_in_one_graph():
+    rng = np.random.default_rng(606)
+    st = torch.cuda.Stream()
+    cases = []
+    with torch.cuda.stream(st):
+        for i in range(48):
+            n, count, dtype, op, proto, nch, cfg, inplace, unaligned = _draw(rng)
+            try:
+                plan = ra.ringar_plan(count, dtype, n, nch, proto, ra.make_config(**cfg))
+            except ra.RingarError:
+                continue
+            desc = (f"case captured random {i}: n={n} count={count} {dtype} {op} {proto} nch={nch} {cfg} "
+                    f"inplace={inplace} unaligned={unaligned} -> {ra.PROTO_NAMES[plan.proto]} ch={plan.nchannels} "
+                    f"lanes={plan.lanes} depth={plan.fifo_depth}")
+            xs = W.inputs(f"cap-rand-warm-{i}", n, count, dtype, "uniform", -4, 4)
+            if unaligned and not inplace:
+                sends = [W.to_torch(np.concatenate([np.zeros(1, x.dtype), x]), dtype, DEV)[1:] for x in xs]
+                recvs = [torch.zeros(count + 1, dtype=sends[0].dtype, device=DEV)[1:] for _ in xs]
+            else:
+                sends = [W.to_torch(x, dtype, DEV) for x in xs]
+                recvs = sends if inplace else [torch.zeros_like(t) for t in sends]
+            cfgo = ra.make_config(**cfg)
+            print(desc, flush=True)
+            code = ra.ringar_allreduce_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count,
+                                          dtype, op, n, nch, proto, st.cuda_stream, cfgo)
+            if code != ra.SUCCESS:
+                assert code in (ra.INVALID_ARGUMENT, ra.INVALID_USAGE), desc
+                continue
+            want = oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems, ring=cfg["ring_order"])
+            cases.append(dict(desc=desc, n=n, count=count, dtype=dtype, op=op, nch=nch, proto=proto, cfg=cfgo,
+                              order=cfg["ring_order"], plan=plan, sends=sends, recvs=recvs, want=want))
+    st.synchronize()
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    for c in cases:
+        for r in range(c["n"]):
+            assert np.array_equal(_bits(W.from_torch(c["recvs"][r], c["dtype"])), _bits(c["want"][r])), (c["desc"], r)
+    assert len(cases) >= 36, len(cases)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for c in cases:
+            c["code"] = ra.ringar_allreduce_ex([t.data_ptr() for t in c["sends"]], [t.data_ptr() for t in c["recvs"]],
+                                               c["count"], c["dtype"], c["op"], c["n"], c["nch"], c["proto"],
+                                               st.cuda_stream, c["cfg"])
+    bad = [(c["desc"], ra.ringar_result_string(c["code"])) for c in cases if c["code"] != ra.SUCCESS]
+    assert not bad, bad
+
+    for rep in range(3):
+        with torch.cuda.stream(st):
+            for i, c in enumerate(cases):
+                xs = W.inputs(f"cap-rand-rep{rep}-{i}", c["n"], c["count"], c["dtype"], "uniform", -4, 4)
+                for t, x in zip(c["sends"], xs):
+                    t.copy_(W.to_torch(x, c["dtype"], DEV))
+                if c["recvs"] is not c["sends"]:
+                    for t in c["recvs"]:
+                        t.zero_()
+                c["want"] = oracle.ring_allreduce(xs, c["dtype"], c["op"], c["plan"].nchannels,
+                                                  c["plan"].chunk_elems, ring=c["order"])
+        st.synchronize()
+        print(f"case captured random replay {rep} of {len(cases)} calls", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        for c in cases:
+            for r in range(c["n"]):
+                got = W.from_torch(c["recvs"][r], c["dtype"])
+                assert np.array_equal(_bits(got), _bits(c["want"][r])), (rep, c["desc"], r)
