@@ -241,12 +241,12 @@ typedef struct {
  *   stream: the work is enqueued on this stream; results are valid after the
  *       stream has been synchronised.  nranks == 1 enqueues a device copy.
  *       Under stream capture (a HIP graph, replayed any number of times)
- *       the ring AllReduce runs a captured form: its steps count from zero
- *       on counters of its own and it leaves every counter and flag it
- *       consumed at zero, so each replay starts clean and eager calls on
- *       the stream keep working between replays.  Nothing is allocated or
- *       cleared during capture: the stream must have run a call of the same
- *       shape first (else RINGAR_ERR_INVALID_USAGE).  The tree, the halves
+ *       the AllReduce (ring or tree) runs a captured form: its steps count
+ *       from zero on counters of its own and it leaves every counter and
+ *       flag it consumed at zero, so each replay starts clean and eager
+ *       calls on the stream keep working between replays.  Nothing is
+ *       allocated or cleared during capture: the stream must have run a call
+ *       of the same shape first (else RINGAR_ERR_INVALID_USAGE).  The halves
  *       and the direct form are refused under capture
  *       (RINGAR_ERR_INVALID_USAGE, nothing enqueued).  Replays share the
  *       stream's FIFO memory with its eager calls: run them in order (one

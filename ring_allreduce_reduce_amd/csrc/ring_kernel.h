@@ -18,7 +18,7 @@ hipError_t launch_ring(int coll, int dtype, int op, int proto, bool small, bool 
                        int grid, int block, hipStream_t stream);
 
 // Tree AllReduce launch (kernel_for(kTreeAllReduce, ...)).
-hipError_t launch_tree(int dtype, int op, int proto, bool small, const TreeArgs& args, int grid, int block,
+hipError_t launch_tree(int dtype, int op, int proto, bool small, bool cap, const TreeArgs& args, int grid, int block,
                        hipStream_t stream);
 
 hipError_t max_active_blocks(int coll, int dtype, int op, int proto, bool small, bool cap, int block, int* per_cu);

@@ -1295,7 +1295,10 @@ __device__ __forceinline__ bool tree_chunks(Lane& L, uint64_t lo, uint64_t len, 
   return true;
 }
 
-template <class E, int OP, int PROTO, bool SMALL>
+// CAP: the captured form, as for the ring: steps from zero, every consumed
+// flag and counter left at zero (a vertex resets the connections it receives
+// on, the children's up connections or its parent's down connection).
+template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
 __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const KernelArgs& a = ta.k;
@@ -1322,7 +1325,7 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   L.a = &a;
   L.w.a = &a;
   L.lane = threadIdx.x & 63;
-  L.cap = false;   // the tree has no captured form
+  L.cap = CAP;
   L.sstep = 0;
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;
@@ -1370,6 +1373,11 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
     if (nk == 0) tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst>(L, lo, len, l, es);
     else if (nk == 1) tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst | kSend>(L, lo, len, l, es);
     else tree_chunks<E, OP, PROTO, SMALL, kRecv | kDst | kSend | kSend2>(L, lo, len, l, es);
+  }
+  if (CAP) {
+    // only real inputs: a leaf's unused input slot points at its own output
+    if (bcast || nk >= 1) reset_input(L.in[0]);
+    if (!bcast && nk == 2) reset_input(L.in[1]);
   }
 }
 

@@ -885,12 +885,11 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   }
   count = kcount;
   // Under stream capture (a graph replays the call any number of times) the
-  // ring AllReduce runs its captured form: steps from zero on the captured
-  // counters, every consumed flag and counter left at zero, nothing
+  // ring and tree AllReduce run their captured form: steps from zero on the
+  // captured counters, every consumed flag and counter left at zero, nothing
   // allocated or cleared during capture.  The stream's resources must hold
   // the call's connections already (an eager call of the same shape on the
-  // stream allocates them); the tree, the halves and the direct form are
-  // refused.
+  // stream allocates them); the halves and the direct form are refused.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(st, &capture));
   const bool captured = capture != hipStreamCaptureStatusNone;
@@ -901,8 +900,8 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     auto it = g_res.find(std::make_pair(dev, st));
-    if (P.kind != kAllReduce) {
-      t_last_error = "under stream capture only the ring AllReduce runs (not the tree or the halves)";
+    if (P.kind != kAllReduce && P.kind != kTreeAllReduce) {
+      t_last_error = "under stream capture only the AllReduce runs (not the halves)";
       return RINGAR_ERR_INVALID_USAGE;
     }
     if (it == g_res.end() || it->second.counter_conns < P.conns || it->second.fifo_conns[P.proto] < P.conns) {
@@ -1001,7 +1000,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
         T.child[t][1][v] = (int8_t)c1;
         if (u < 0) T.root[t] = v;
       }
-    HIP_TRY(launch_tree(dtype, op, P.proto, small, T, P.grid, P.block, st));
+    HIP_TRY(launch_tree(dtype, op, P.proto, small, captured, T, P.grid, P.block, st));
   } else {
     HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, captured, A, P.grid, P.block, st));
   }

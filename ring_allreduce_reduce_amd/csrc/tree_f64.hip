@@ -4,23 +4,28 @@
 
 namespace ringar {
 
-template <int OP>
+template <int OP, bool CAP>
 static const void* tree_by_proto_f64(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&tree_kernel<F64, OP, kLL, true>
-                                 : (const void*)&tree_kernel<F64, OP, kLL, false>;
-  if (proto == kLL128) return (const void*)&tree_kernel<F64, OP, kLL128, false>;
-  return small ? (const void*)&tree_kernel<F64, OP, kSimple, true>
-               : (const void*)&tree_kernel<F64, OP, kSimple, false>;
+  if (proto == kLL) return small ? (const void*)&tree_kernel<F64, OP, kLL, true, CAP>
+                                 : (const void*)&tree_kernel<F64, OP, kLL, false, CAP>;
+  if (proto == kLL128) return (const void*)&tree_kernel<F64, OP, kLL128, false, CAP>;
+  return small ? (const void*)&tree_kernel<F64, OP, kSimple, true, CAP>
+               : (const void*)&tree_kernel<F64, OP, kSimple, false, CAP>;
 }
 
-const void* kernel_tree_for_f64(int op, int proto, bool small) {
+template <bool CAP>
+static const void* tree_by_op_f64(int op, int proto, bool small) {
   switch (op) {
-    case 0: return tree_by_proto_f64<0>(proto, small);
-    case 1: return tree_by_proto_f64<1>(proto, small);
-    case 2: return tree_by_proto_f64<2>(proto, small);
-    case 3: return tree_by_proto_f64<3>(proto, small);
-    default: return tree_by_proto_f64<4>(proto, small);
+    case 0: return tree_by_proto_f64<0, CAP>(proto, small);
+    case 1: return tree_by_proto_f64<1, CAP>(proto, small);
+    case 2: return tree_by_proto_f64<2, CAP>(proto, small);
+    case 3: return tree_by_proto_f64<3, CAP>(proto, small);
+    default: return tree_by_proto_f64<4, CAP>(proto, small);
   }
+}
+
+const void* kernel_tree_for_f64(int op, int proto, bool small, bool cap) {
+  return cap ? tree_by_op_f64<true>(op, proto, small) : tree_by_op_f64<false>(op, proto, small);
 }
 
 }  // namespace ringar

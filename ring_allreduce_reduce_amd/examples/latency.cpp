@@ -3,7 +3,7 @@
 // and reports the device time per call (HIP events around the loop) and the
 // host time to enqueue one call.  With the host faster than the device the
 // first is the device-bound rate, free of any binding's per-call overhead.
-// Ring cases are also captured into a HIP graph (the 2000 calls) and the
+// Each case is also captured into a HIP graph (the 2000 calls) and the
 // graph's replay is timed the same way.
 //
 // Build (from the repository root, after the library is built):
@@ -83,7 +83,7 @@ int main() {
     std::printf("%-22s device %6.2f us per call, host enqueue %5.2f us per call%s", c.name, ms * 1e3 / calls,
                 host_us, err == RINGAR_SUCCESS ? "" : " (async error)");
     if (err != RINGAR_SUCCESS) return 1;
-    if (c.algo == RINGAR_ALGO_RING) {
+    {
       // the same calls captured into a graph, then one replay of it
       hipGraph_t graph;
       hipGraphExec_t exec;

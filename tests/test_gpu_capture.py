@@ -1,12 +1,12 @@
 """Ring AllReduce calls captured in a HIP graph and replayed, bit-exact
-against the oracle on every replay: the captured form numbers its steps
+against the oracle on every replay: the captured form (ring and tree) numbers its steps
 from zero on counters of its own and leaves every counter and flag it
 consumed at zero, so each replay starts clean, while eager calls on the same
 stream, made between the replays, keep their own step numbers.  Every
-protocol (LL in both forms, LL128, Simple in both forms), several dtypes and
-ops, ragged sizes.  Each replay gets fresh inputs, copied in before it (no
-clear of any library memory is recorded in the graph).  The tree, the halves,
-the direct form and a shape the stream has not run yet are refused under
+protocol (LL in both forms, LL128, Simple in both forms) under both
+algorithms, several dtypes and ops, ragged sizes.  Each replay gets fresh inputs, copied in before it (no
+clear of any library memory is recorded in the graph).  The halves, the
+direct form and a shape the stream has not run yet are refused under
 capture, before anything is enqueued, and the capture goes on.  A graph
 keeps working after eager calls on its stream have grown the FIFO memory and
 counters it was captured with.  Randomly drawn calls (every knob of a ring AllReduce at
@@ -22,7 +22,7 @@ from ring_allreduce_reduce_amd import workloads as W
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
-# (n, count, dtype, op, proto, nchannels)
+# (n, count, dtype, op, proto, nchannels[, algorithm])
 SHAPES = [
     (8, 4096, "float32", "sum", "LL", 0),          # small LL form
     (8, 200003, "float32", "sum", "LL", 4),        # LL, ragged
@@ -30,6 +30,11 @@ SHAPES = [
     (8, 1 << 20, "float32", "sum", "Simple", 0),   # Simple
     (3, 5000, "int32", "max", "Simple", 2),        # Simple, small form
     (5, 77777, "float16", "avg", "LL128", 3),
+    (8, 4096, "float32", "sum", "LL", 0, "tree"),          # tree, small LL form
+    (7, 100003, "bfloat16", "max", "LL128", 4, "tree"),
+    (16, 1 << 20, "float32", "avg", "Simple", 8, "tree"),
+    (5, 3000, "int8", "sum", "Simple", 2, "tree"),          # tree, small Simple form
+    (6, 50001, "float64", "prod", "LL", 3, "tree"),
 ]
 
 
@@ -37,14 +42,20 @@ def _bits(a):
     return np.ascontiguousarray(a).view(np.uint8)
 
 
+def _cfg(shape):
+    return ra.make_config(algo=shape[6]) if len(shape) > 6 else None
+
+
 def _want(xs, shape):
-    n, count, dtype, op, proto, nch = shape
-    plan = ra.ringar_plan(count, dtype, n, nch, proto)
-    return oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems)
+    n, count, dtype, op, proto, nch = shape[:6]
+    plan = ra.ringar_plan(count, dtype, n, nch, proto, _cfg(shape))
+    run = oracle.tree_allreduce if plan.algo == 1 else oracle.ring_allreduce
+    return run(xs, dtype, op, plan.nchannels, plan.chunk_elems)
 
 
 def _raw(sends, recvs, shape, stream, cfg=None):
-    n, count, dtype, op, proto, nch = shape
+    n, count, dtype, op, proto, nch = shape[:6]
+    cfg = cfg if cfg is not None else _cfg(shape)
     return ra.ringar_allreduce_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count, dtype, op,
                                   n, nch, proto, stream.cuda_stream, cfg)
 
@@ -55,8 +66,9 @@ def _check(recvs, want, what):
 
 
 def _inputs(shape, key):
-    n, count, dtype, op, proto, nch = shape
-    return W.inputs(key, n, count, dtype, "uniform", -4, 4)
+    n, count, dtype, op = shape[:4]
+    dist = ("uniform", 0.9, 1.1) if (op == "prod" and dtype in W.FLOATS) else ("uniform", -4, 4)
+    return W.inputs(key, n, count, dtype, *dist)
 
 
 def test_capture_replays_match_the_oracle():
@@ -130,19 +142,17 @@ def test_refused_under_capture_and_capture_goes_on():
     shape = (n, count, "float32", "sum", "Simple", 2)
     with torch.cuda.stream(st):
         assert _raw(sends, recvs, shape, st) == ra.SUCCESS
-        assert _raw(sends, recvs, shape, st, ra.make_config(algo="tree")) == ra.SUCCESS
     st.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=st):
         refused = [
-            _raw(sends, recvs, shape, st, ra.make_config(algo="tree")),        # the tree
             _raw(sends, recvs, shape, st, ra.make_config(direct=1)),           # the direct form
             _raw(sends, recvs, (n, count, "float32", "sum", "LL128", 16), st),  # shape not run yet
         ]
         rs = ra.ringar_reduce_scatter_ex([t.data_ptr() for t in sends], [t[:count // n].data_ptr() for t in recvs],
                                          count // n, "float32", "sum", n, 2, "Simple", st.cuda_stream, None)
         ok = _raw(sends, recvs, shape, st)
-    assert refused == [ra.INVALID_USAGE] * 3 and rs == ra.INVALID_USAGE and ok == ra.SUCCESS
+    assert refused == [ra.INVALID_USAGE] * 2 and rs == ra.INVALID_USAGE and ok == ra.SUCCESS
     for t in recvs:
         t.zero_()
     torch.cuda.synchronize()
@@ -216,7 +226,15 @@ def _draw(rng):
                fifo_depth=0 if rng.random() < 0.7 else int([2, 4, 8][rng.integers(0, 3)]),
                force_general=int(rng.random() < 0.2),
                ring_order=[int(r) for r in rng.permutation(n)] if rng.random() < 0.3 else None)
+    cfg["algo"] = ["ring", "tree", "auto"][int(rng.integers(0, 3))]
     return n, count, dtype, op, proto, int(rng.integers(0, 17)), cfg, rng.random() < 0.2, rng.random() < 0.15
+
+
+def _want_plan(xs, dtype, op, plan, order):
+    # the tree runs over ranks 0..n-1 whatever the ring order
+    if plan.algo == 1:
+        return oracle.tree_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems)
+    return oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems, ring=order)
 
 
 def test_random_calls_captured_in_one_graph():
@@ -231,9 +249,10 @@ def test_random_calls_captured_in_one_graph():
             except ra.RingarError:
                 continue
             desc = (f"case captured random {i}: n={n} count={count} {dtype} {op} {proto} nch={nch} {cfg} "
-                    f"inplace={inplace} unaligned={unaligned} -> {ra.PROTO_NAMES[plan.proto]} ch={plan.nchannels} "
+                    f"inplace={inplace} unaligned={unaligned} -> {ra.ALGO_NAMES[plan.algo]} {ra.PROTO_NAMES[plan.proto]} "
+                    f"ch={plan.nchannels} "
                     f"lanes={plan.lanes} depth={plan.fifo_depth}")
-            xs = W.inputs(f"cap-rand-warm-{i}", n, count, dtype, "uniform", -4, 4)
+            xs = _inputs((n, count, dtype, op), f"cap-rand-warm-{i}")
             if unaligned and not inplace:
                 sends = [W.to_torch(np.concatenate([np.zeros(1, x.dtype), x]), dtype, DEV)[1:] for x in xs]
                 recvs = [torch.zeros(count + 1, dtype=sends[0].dtype, device=DEV)[1:] for _ in xs]
@@ -247,7 +266,7 @@ def test_random_calls_captured_in_one_graph():
             if code != ra.SUCCESS:
                 assert code in (ra.INVALID_ARGUMENT, ra.INVALID_USAGE), desc
                 continue
-            want = oracle.ring_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems, ring=cfg["ring_order"])
+            want = _want_plan(xs, dtype, op, plan, cfg["ring_order"])
             cases.append(dict(desc=desc, n=n, count=count, dtype=dtype, op=op, nch=nch, proto=proto, cfg=cfgo,
                               order=cfg["ring_order"], plan=plan, sends=sends, recvs=recvs, want=want))
     st.synchronize()
@@ -269,14 +288,13 @@ def test_random_calls_captured_in_one_graph():
     for rep in range(3):
         with torch.cuda.stream(st):
             for i, c in enumerate(cases):
-                xs = W.inputs(f"cap-rand-rep{rep}-{i}", c["n"], c["count"], c["dtype"], "uniform", -4, 4)
+                xs = _inputs((c["n"], c["count"], c["dtype"], c["op"]), f"cap-rand-rep{rep}-{i}")
                 for t, x in zip(c["sends"], xs):
                     t.copy_(W.to_torch(x, c["dtype"], DEV))
                 if c["recvs"] is not c["sends"]:
                     for t in c["recvs"]:
                         t.zero_()
-                c["want"] = oracle.ring_allreduce(xs, c["dtype"], c["op"], c["plan"].nchannels,
-                                                  c["plan"].chunk_elems, ring=c["order"])
+                c["want"] = _want_plan(xs, c["dtype"], c["op"], c["plan"], c["order"])
         st.synchronize()
         print(f"case captured random replay {rep} of {len(cases)} calls", flush=True)
         g.replay()
