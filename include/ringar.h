@@ -241,22 +241,23 @@ typedef struct {
  *   stream: the work is enqueued on this stream; results are valid after the
  *       stream has been synchronised.  nranks == 1 enqueues a device copy.
  *       Under stream capture (a HIP graph, replayed any number of times)
- *       the AllReduce (ring or tree) runs a captured form: its steps count
- *       from zero on counters of its own and it leaves every counter and
- *       flag it consumed at zero, so each replay starts clean and eager
- *       calls on the stream keep working between replays.  Nothing is
- *       allocated or cleared during capture: the stream must have run a call
- *       of the same shape first (else RINGAR_ERR_INVALID_USAGE).  The halves
- *       and the direct form are refused under capture
- *       (RINGAR_ERR_INVALID_USAGE, nothing enqueued).  Replays share the
- *       stream's FIFO memory with its eager calls: run them in order (one
- *       stream, or synchronised).  A graph holds the addresses of the
- *       stream's FIFO memory and counters: later eager calls that need more
- *       of them keep the old buffers alive for it, and ringar_release frees
- *       them, so a graph captured before ringar_release must not be
- *       replayed after it.  After an asynchronous error in a replay the
- *       captured counters are no longer zero: destroy the graph, call
- *       ringar_release, make an eager call and capture again.
+ *       every collective here (AllReduce by ring or tree, ReduceScatter,
+ *       AllGather) runs a captured form: its steps count from zero on
+ *       counters of its own and it leaves every counter and flag it
+ *       consumed at zero, so each replay starts clean and eager calls on
+ *       the stream keep working between replays.  Nothing is allocated or
+ *       cleared during capture: the stream must have run a call of the same
+ *       shape first (else RINGAR_ERR_INVALID_USAGE).  The direct form is
+ *       refused under capture (RINGAR_ERR_INVALID_USAGE, nothing enqueued).
+ *       Replays share the stream's FIFO memory with its eager calls: run
+ *       them in order (one stream, or synchronised).  A graph holds the
+ *       addresses of the stream's FIFO memory and counters: later eager
+ *       calls that need more of them keep the old buffers alive for it, and
+ *       ringar_release frees them, so a graph captured before
+ *       ringar_release must not be replayed after it.  After an
+ *       asynchronous error in a replay the captured counters are no longer
+ *       zero: destroy the graph, call ringar_release, make an eager call and
+ *       capture again.
  * Errors are reported before anything is enqueued; a wait that times out or
  * is aborted inside the kernel is reported by ringar_get_async_error.
  */

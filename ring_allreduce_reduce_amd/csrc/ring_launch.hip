@@ -13,13 +13,13 @@ const void* kernel_for_f16(int op, int proto, bool small, bool cap);
 const void* kernel_for_bf16(int op, int proto, bool small, bool cap);
 const void* kernel_for_f32(int op, int proto, bool small, bool cap);
 const void* kernel_for_f64(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_i8(int op, int proto, bool small);
-const void* kernel_rs_for_i32(int op, int proto, bool small);
-const void* kernel_rs_for_f16(int op, int proto, bool small);
-const void* kernel_rs_for_bf16(int op, int proto, bool small);
-const void* kernel_rs_for_f32(int op, int proto, bool small);
-const void* kernel_rs_for_f64(int op, int proto, bool small);
-const void* kernel_ag_for(int proto, bool small);
+const void* kernel_rs_for_i8(int op, int proto, bool small, bool cap);
+const void* kernel_rs_for_i32(int op, int proto, bool small, bool cap);
+const void* kernel_rs_for_f16(int op, int proto, bool small, bool cap);
+const void* kernel_rs_for_bf16(int op, int proto, bool small, bool cap);
+const void* kernel_rs_for_f32(int op, int proto, bool small, bool cap);
+const void* kernel_rs_for_f64(int op, int proto, bool small, bool cap);
+const void* kernel_ag_for(int proto, bool small, bool cap);
 const void* kernel_tree_for_i8(int op, int proto, bool small, bool cap);
 const void* kernel_tree_for_i32(int op, int proto, bool small, bool cap);
 const void* kernel_tree_for_f16(int op, int proto, bool small, bool cap);
@@ -29,7 +29,7 @@ const void* kernel_tree_for_f64(int op, int proto, bool small, bool cap);
 
 const void* kernel_for(int coll, int dtype, int op, int proto, bool small, bool cap) {
   small = small && proto != kLL128;
-  if (coll == kAllGather) return kernel_ag_for(proto, small);
+  if (coll == kAllGather) return kernel_ag_for(proto, small, cap);
   if (coll == kTreeAllReduce) {
     switch (dtype) {
       case 0: return kernel_tree_for_i8(op, proto, small, cap);
@@ -42,12 +42,12 @@ const void* kernel_for(int coll, int dtype, int op, int proto, bool small, bool 
   }
   if (coll == kReduceScatter) {
     switch (dtype) {
-      case 0: return kernel_rs_for_i8(op, proto, small);
-      case 1: return kernel_rs_for_i32(op, proto, small);
-      case 2: return kernel_rs_for_f16(op, proto, small);
-      case 3: return kernel_rs_for_bf16(op, proto, small);
-      case 4: return kernel_rs_for_f32(op, proto, small);
-      default: return kernel_rs_for_f64(op, proto, small);
+      case 0: return kernel_rs_for_i8(op, proto, small, cap);
+      case 1: return kernel_rs_for_i32(op, proto, small, cap);
+      case 2: return kernel_rs_for_f16(op, proto, small, cap);
+      case 3: return kernel_rs_for_bf16(op, proto, small, cap);
+      case 4: return kernel_rs_for_f32(op, proto, small, cap);
+      default: return kernel_rs_for_f64(op, proto, small, cap);
     }
   }
   switch (dtype) {

@@ -884,12 +884,12 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     return RINGAR_SUCCESS;
   }
   count = kcount;
-  // Under stream capture (a graph replays the call any number of times) the
-  // ring and tree AllReduce run their captured form: steps from zero on the
+  // Under stream capture (a graph replays the call any number of times)
+  // every collective runs its captured form: steps from zero on the
   // captured counters, every consumed flag and counter left at zero, nothing
   // allocated or cleared during capture.  The stream's resources must hold
   // the call's connections already (an eager call of the same shape on the
-  // stream allocates them); the halves and the direct form are refused.
+  // stream allocates them); the direct form is refused.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(st, &capture));
   const bool captured = capture != hipStreamCaptureStatusNone;
@@ -900,10 +900,6 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     auto it = g_res.find(std::make_pair(dev, st));
-    if (P.kind != kAllReduce && P.kind != kTreeAllReduce) {
-      t_last_error = "under stream capture only the AllReduce runs (not the halves)";
-      return RINGAR_ERR_INVALID_USAGE;
-    }
     if (it == g_res.end() || it->second.counter_conns < P.conns || it->second.fifo_conns[P.proto] < P.conns) {
       t_last_error = "under stream capture nothing is allocated: make one call of this shape on the stream first";
       return RINGAR_ERR_INVALID_USAGE;

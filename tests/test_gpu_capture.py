@@ -5,8 +5,9 @@ consumed at zero, so each replay starts clean, while eager calls on the same
 stream, made between the replays, keep their own step numbers.  Every
 protocol (LL in both forms, LL128, Simple in both forms) under both
 algorithms, several dtypes and ops, ragged sizes.  Each replay gets fresh inputs, copied in before it (no
-clear of any library memory is recorded in the graph).  The halves, the
-direct form and a shape the stream has not run yet are refused under
+clear of any library memory is recorded in the graph).  ReduceScatter and
+AllGather, out of place and in place, replay bit-exact too.  The direct
+form and a shape the stream has not run yet are refused under
 capture, before anything is enqueued, and the capture goes on.  A graph
 keeps working after eager calls on its stream have grown the FIFO memory and
 counters it was captured with.  Randomly drawn calls (every knob of a ring AllReduce at
@@ -149,10 +150,8 @@ def test_refused_under_capture_and_capture_goes_on():
             _raw(sends, recvs, shape, st, ra.make_config(direct=1)),           # the direct form
             _raw(sends, recvs, (n, count, "float32", "sum", "LL128", 16), st),  # shape not run yet
         ]
-        rs = ra.ringar_reduce_scatter_ex([t.data_ptr() for t in sends], [t[:count // n].data_ptr() for t in recvs],
-                                         count // n, "float32", "sum", n, 2, "Simple", st.cuda_stream, None)
         ok = _raw(sends, recvs, shape, st)
-    assert refused == [ra.INVALID_USAGE] * 2 and rs == ra.INVALID_USAGE and ok == ra.SUCCESS
+    assert refused == [ra.INVALID_USAGE] * 2 and ok == ra.SUCCESS
     for t in recvs:
         t.zero_()
     torch.cuda.synchronize()
@@ -304,3 +303,89 @@ def test_random_calls_captured_in_one_graph():
             for r in range(c["n"]):
                 got = W.from_torch(c["recvs"][r], c["dtype"])
                 assert np.array_equal(_bits(got), _bits(c["want"][r])), (rep, c["desc"], r)
+
+
+# (collective, n, count per block, dtype, op, proto, nchannels, in place)
+HALVES = [
+    ("reduce_scatter", 8, 65536, "float32", "sum", "Simple", 4, False),
+    ("reduce_scatter", 5, 30001, "bfloat16", "max", "LL", 2, False),
+    ("reduce_scatter", 4, 20000, "int32", "sum", "LL128", 3, True),
+    ("reduce_scatter", 3, 1000, "float64", "avg", "Simple", 0, False),   # small form
+    ("all_gather", 8, 65536, "float32", None, "Simple", 4, False),
+    ("all_gather", 6, 9999, "float16", None, "LL", 0, True),
+    ("all_gather", 3, 50000, "int8", None, "LL128", 2, False),
+]
+
+
+def _halves_buffers(case, xs):
+    coll, n, count, dtype, op, proto, nch, inplace = case
+    sends = [W.to_torch(x, dtype, DEV) for x in xs]
+    if coll == "reduce_scatter":
+        recvs = ([t[r * count:(r + 1) * count] for r, t in enumerate(sends)] if inplace else
+                 [torch.zeros(count, dtype=sends[0].dtype, device=DEV) for _ in range(n)])
+        return sends, recvs
+    full = [torch.zeros(n * count, dtype=sends[0].dtype, device=DEV) for _ in range(n)]
+    if inplace:
+        for r in range(n):
+            full[r][r * count:(r + 1) * count].copy_(sends[r])
+        sends = [full[r][r * count:(r + 1) * count] for r in range(n)]
+    return sends, full
+
+
+def _halves_call(case, sends, recvs, st):
+    coll, n, count, dtype, op, proto, nch, inplace = case
+    if coll == "reduce_scatter":
+        return ra.ringar_reduce_scatter_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count,
+                                           dtype, op, n, nch, proto, st.cuda_stream, None)
+    return ra.ringar_all_gather_ex([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count, dtype, n,
+                                   nch, proto, st.cuda_stream, None)
+
+
+def _halves_inputs(case, key):
+    coll, n, count, dtype, op = case[:5]
+    return W.inputs(key, n, n * count if coll == "reduce_scatter" else count, dtype, "uniform", -4, 4)
+
+
+def _halves_want(case, xs):
+    coll, n, count, dtype, op = case[:5]
+    if coll == "reduce_scatter":
+        return oracle.ring_reduce_scatter(xs, dtype, op)
+    return oracle.ring_all_gather(xs, dtype)
+
+
+def test_halves_captured_and_replayed():
+    st = torch.cuda.Stream()
+    bufs = []
+    with torch.cuda.stream(st):
+        for i, case in enumerate(HALVES):
+            xs = _halves_inputs(case, f"cap-halves-warm-{i}")
+            sends, recvs = _halves_buffers(case, xs)
+            print(f"case capture halves warm-up {case}", flush=True)
+            assert _halves_call(case, sends, recvs, st) == ra.SUCCESS
+            bufs.append((sends, recvs, xs))
+    st.synchronize()
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    for (sends, recvs, xs), case in zip(bufs, HALVES):
+        for got, w in zip(recvs, _halves_want(case, xs)):
+            assert np.array_equal(_bits(W.from_torch(got, case[3])), _bits(w)), case
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        codes = [_halves_call(case, sends, recvs, st) for (sends, recvs, _), case in zip(bufs, HALVES)]
+    assert codes == [ra.SUCCESS] * len(HALVES), [ra.ringar_result_string(c) for c in codes]
+    for rep in range(3):
+        xs_all = [_halves_inputs(case, f"cap-halves-rep{rep}-{i}") for i, case in enumerate(HALVES)]
+        with torch.cuda.stream(st):
+            for (sends, recvs, _), xs, case in zip(bufs, xs_all, HALVES):
+                if not case[7]:
+                    for t in recvs:
+                        t.zero_()
+                for t, x in zip(sends, xs):
+                    t.copy_(W.to_torch(x, case[3], DEV))
+        st.synchronize()
+        print(f"case capture halves replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        for (sends, recvs, _), xs, case in zip(bufs, xs_all, HALVES):
+            for r, (got, w) in enumerate(zip(recvs, _halves_want(case, xs))):
+                assert np.array_equal(_bits(W.from_torch(got, case[3])), _bits(w)), (rep, case, r)
