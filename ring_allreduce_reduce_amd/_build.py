@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libringar.so")
 _TYPES = ("i8", "i32", "f16", "bf16", "f32", "f64")
 SOURCES = ([f"tree_{t}.hip" for t in _TYPES] + [f"ring_kernel_{t}.hip" for t in _TYPES] +
-           [f"ring_rs_{t}.hip" for t in _TYPES] + ["ring_ag.hip", "ring_launch.hip", "ringar.cpp"])
+           [f"ring_rs_{t}.hip" for t in _TYPES] + [f"captured_{t}.hip" for t in _TYPES] +
+           ["ring_ag.hip", "ring_launch.hip", "ringar.cpp"])
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

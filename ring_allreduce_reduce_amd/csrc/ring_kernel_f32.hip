@@ -1,32 +1,11 @@
-// Ring AllReduce kernels for one element type (one translation unit per type
-// so the instances compile in parallel).
-#include "ring_kernel_impl.h"
+// Ring AllReduce kernels for one element type, eager form (one translation
+// unit per type so the instances compile in parallel).
+#include "ring_instances.h"
 
 namespace ringar {
 
-template <int OP, bool CAP>
-static const void* by_proto_kernel_f32(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<F32, OP, kLL, true, kAllReduce, CAP>
-                                 : (const void*)&ring_kernel_lines<F32, OP, kLL, false, kAllReduce, CAP>;
-  if (proto == kLL128) return (const void*)&ring_kernel_lines<F32, OP, kLL128, false, kAllReduce, CAP>;
-  return small ? (const void*)&ring_kernel<F32, OP, kSimple, true, kAllReduce, CAP>
-               : (const void*)&ring_kernel<F32, OP, kSimple, false, kAllReduce, CAP>;
-}
-
-template <bool CAP>
-static const void* by_op_kernel_f32(int op, int proto, bool small) {
-  switch (op) {
-    case 0: return by_proto_kernel_f32<0, CAP>(proto, small);
-    case 1: return by_proto_kernel_f32<1, CAP>(proto, small);
-    case 2: return by_proto_kernel_f32<2, CAP>(proto, small);
-    case 3: return by_proto_kernel_f32<3, CAP>(proto, small);
-    default: return by_proto_kernel_f32<4, CAP>(proto, small);
-  }
-}
-
-// cap: the captured form (stream capture)
-const void* kernel_for_f32(int op, int proto, bool small, bool cap) {
-  return cap ? by_op_kernel_f32<true>(op, proto, small) : by_op_kernel_f32<false>(op, proto, small);
+const void* kernel_for_f32(int op, int proto, bool small) {
+  return ring_instance_by_op<F32, kAllReduce, false>(op, proto, small);
 }
 
 }  // namespace ringar

@@ -1249,8 +1249,9 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
 }
 
 // The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
-// (occupancy 4: the 4096-wavefront launches of large calls), without
-// scratch.  The line protocols (LL, LL128) keep their registers: their poll
+// (occupancy 4: the 4096-wavefront launches of large calls); the eager
+// instances need no scratch, the captured AllReduce ones spill 12-28 bytes
+// per lane.  The line protocols (LL, LL128) keep their registers: their poll
 // and line paths would spill under that bound.
 // CAP: the captured form (its own instances, so that the eager ones carry
 // none of its code).

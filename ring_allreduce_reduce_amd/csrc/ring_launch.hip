@@ -7,56 +7,74 @@
 
 namespace ringar {
 
-const void* kernel_for_i8(int op, int proto, bool small, bool cap);
-const void* kernel_for_i32(int op, int proto, bool small, bool cap);
-const void* kernel_for_f16(int op, int proto, bool small, bool cap);
-const void* kernel_for_bf16(int op, int proto, bool small, bool cap);
-const void* kernel_for_f32(int op, int proto, bool small, bool cap);
-const void* kernel_for_f64(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_i8(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_i32(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_f16(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_bf16(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_f32(int op, int proto, bool small, bool cap);
-const void* kernel_rs_for_f64(int op, int proto, bool small, bool cap);
-const void* kernel_ag_for(int proto, bool small, bool cap);
-const void* kernel_tree_for_i8(int op, int proto, bool small, bool cap);
-const void* kernel_tree_for_i32(int op, int proto, bool small, bool cap);
-const void* kernel_tree_for_f16(int op, int proto, bool small, bool cap);
-const void* kernel_tree_for_bf16(int op, int proto, bool small, bool cap);
-const void* kernel_tree_for_f32(int op, int proto, bool small, bool cap);
-const void* kernel_tree_for_f64(int op, int proto, bool small, bool cap);
+const void* kernel_for_i8(int op, int proto, bool small);
+const void* kernel_for_i32(int op, int proto, bool small);
+const void* kernel_for_f16(int op, int proto, bool small);
+const void* kernel_for_bf16(int op, int proto, bool small);
+const void* kernel_for_f32(int op, int proto, bool small);
+const void* kernel_for_f64(int op, int proto, bool small);
+const void* kernel_rs_for_i8(int op, int proto, bool small);
+const void* kernel_rs_for_i32(int op, int proto, bool small);
+const void* kernel_rs_for_f16(int op, int proto, bool small);
+const void* kernel_rs_for_bf16(int op, int proto, bool small);
+const void* kernel_rs_for_f32(int op, int proto, bool small);
+const void* kernel_rs_for_f64(int op, int proto, bool small);
+const void* kernel_ag_for(int proto, bool small);
+const void* kernel_tree_for_i8(int op, int proto, bool small);
+const void* kernel_tree_for_i32(int op, int proto, bool small);
+const void* kernel_tree_for_f16(int op, int proto, bool small);
+const void* kernel_tree_for_bf16(int op, int proto, bool small);
+const void* kernel_tree_for_f32(int op, int proto, bool small);
+const void* kernel_tree_for_f64(int op, int proto, bool small);
+const void* kernel_captured_for_i8(int coll, int op, int proto, bool small);
+const void* kernel_captured_for_i32(int coll, int op, int proto, bool small);
+const void* kernel_captured_for_f16(int coll, int op, int proto, bool small);
+const void* kernel_captured_for_bf16(int coll, int op, int proto, bool small);
+const void* kernel_captured_for_f32(int coll, int op, int proto, bool small);
+const void* kernel_captured_for_f64(int coll, int op, int proto, bool small);
 
+// cap: the captured form (stream capture), whose instances sit in
+// translation units of their own
 const void* kernel_for(int coll, int dtype, int op, int proto, bool small, bool cap) {
   small = small && proto != kLL128;
-  if (coll == kAllGather) return kernel_ag_for(proto, small, cap);
+  if (cap) {
+    switch (coll == kAllGather ? 0 : dtype) {
+      case 0: return kernel_captured_for_i8(coll, op, proto, small);
+      case 1: return kernel_captured_for_i32(coll, op, proto, small);
+      case 2: return kernel_captured_for_f16(coll, op, proto, small);
+      case 3: return kernel_captured_for_bf16(coll, op, proto, small);
+      case 4: return kernel_captured_for_f32(coll, op, proto, small);
+      default: return kernel_captured_for_f64(coll, op, proto, small);
+    }
+  }
+  if (coll == kAllGather) return kernel_ag_for(proto, small);
   if (coll == kTreeAllReduce) {
     switch (dtype) {
-      case 0: return kernel_tree_for_i8(op, proto, small, cap);
-      case 1: return kernel_tree_for_i32(op, proto, small, cap);
-      case 2: return kernel_tree_for_f16(op, proto, small, cap);
-      case 3: return kernel_tree_for_bf16(op, proto, small, cap);
-      case 4: return kernel_tree_for_f32(op, proto, small, cap);
-      default: return kernel_tree_for_f64(op, proto, small, cap);
+      case 0: return kernel_tree_for_i8(op, proto, small);
+      case 1: return kernel_tree_for_i32(op, proto, small);
+      case 2: return kernel_tree_for_f16(op, proto, small);
+      case 3: return kernel_tree_for_bf16(op, proto, small);
+      case 4: return kernel_tree_for_f32(op, proto, small);
+      default: return kernel_tree_for_f64(op, proto, small);
     }
   }
   if (coll == kReduceScatter) {
     switch (dtype) {
-      case 0: return kernel_rs_for_i8(op, proto, small, cap);
-      case 1: return kernel_rs_for_i32(op, proto, small, cap);
-      case 2: return kernel_rs_for_f16(op, proto, small, cap);
-      case 3: return kernel_rs_for_bf16(op, proto, small, cap);
-      case 4: return kernel_rs_for_f32(op, proto, small, cap);
-      default: return kernel_rs_for_f64(op, proto, small, cap);
+      case 0: return kernel_rs_for_i8(op, proto, small);
+      case 1: return kernel_rs_for_i32(op, proto, small);
+      case 2: return kernel_rs_for_f16(op, proto, small);
+      case 3: return kernel_rs_for_bf16(op, proto, small);
+      case 4: return kernel_rs_for_f32(op, proto, small);
+      default: return kernel_rs_for_f64(op, proto, small);
     }
   }
   switch (dtype) {
-    case 0: return kernel_for_i8(op, proto, small, cap);
-    case 1: return kernel_for_i32(op, proto, small, cap);
-    case 2: return kernel_for_f16(op, proto, small, cap);
-    case 3: return kernel_for_bf16(op, proto, small, cap);
-    case 4: return kernel_for_f32(op, proto, small, cap);
-    default: return kernel_for_f64(op, proto, small, cap);
+    case 0: return kernel_for_i8(op, proto, small);
+    case 1: return kernel_for_i32(op, proto, small);
+    case 2: return kernel_for_f16(op, proto, small);
+    case 3: return kernel_for_bf16(op, proto, small);
+    case 4: return kernel_for_f32(op, proto, small);
+    default: return kernel_for_f64(op, proto, small);
   }
 }
 

@@ -1,31 +1,11 @@
-// Ring ReduceScatter kernels for one element type (one translation unit per type
-// so the instances compile in parallel).
-#include "ring_kernel_impl.h"
+// Ring ReduceScatter kernels for one element type, eager form (one
+// translation unit per type so the instances compile in parallel).
+#include "ring_instances.h"
 
 namespace ringar {
 
-template <int OP, bool CAP>
-static const void* by_proto_kernel_rs_f16(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<F16, OP, kLL, true, kReduceScatter, CAP>
-                                 : (const void*)&ring_kernel_lines<F16, OP, kLL, false, kReduceScatter, CAP>;
-  if (proto == kLL128) return (const void*)&ring_kernel_lines<F16, OP, kLL128, false, kReduceScatter, CAP>;
-  return small ? (const void*)&ring_kernel<F16, OP, kSimple, true, kReduceScatter, CAP>
-               : (const void*)&ring_kernel<F16, OP, kSimple, false, kReduceScatter, CAP>;
-}
-
-template <bool CAP>
-static const void* by_op_kernel_rs_f16(int op, int proto, bool small) {
-  switch (op) {
-    case 0: return by_proto_kernel_rs_f16<0, CAP>(proto, small);
-    case 1: return by_proto_kernel_rs_f16<1, CAP>(proto, small);
-    case 2: return by_proto_kernel_rs_f16<2, CAP>(proto, small);
-    case 3: return by_proto_kernel_rs_f16<3, CAP>(proto, small);
-    default: return by_proto_kernel_rs_f16<4, CAP>(proto, small);
-  }
-}
-
-const void* kernel_rs_for_f16(int op, int proto, bool small, bool cap) {
-  return cap ? by_op_kernel_rs_f16<true>(op, proto, small) : by_op_kernel_rs_f16<false>(op, proto, small);
+const void* kernel_rs_for_f16(int op, int proto, bool small) {
+  return ring_instance_by_op<F16, kReduceScatter, false>(op, proto, small);
 }
 
 }  // namespace ringar

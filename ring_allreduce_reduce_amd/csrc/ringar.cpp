@@ -625,7 +625,7 @@ ringar_result_t reset_steps(Resources& R, hipStream_t st) {
 
 // Resident wavefronts of the (dtype, op, proto) kernel on the current device,
 // or 0 when no device is visible.  Cached per device and kernel.
-uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
+uint64_t capacity_waves(int coll, int dtype, int op, int proto, bool cap) {
   static const int ndev = [] {
     int c = 0;
     if (hipGetDeviceCount(&c) != hipSuccess) {
@@ -637,7 +637,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   if (ndev == 0) return 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const long long key = ((((long long)dev * 4 + coll) * 8 + dtype) * 5 + op) * 3 + proto;
+  const long long key = (((((long long)dev * 4 + coll) * 8 + dtype) * 5 + op) * 3 + proto) * 2 + (cap ? 1 : 0);
   // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
@@ -645,7 +645,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto) {
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      max_active_blocks(coll, dtype, op, proto, false, false, 256, &per_cu) != hipSuccess)
+      max_active_blocks(coll, dtype, op, proto, false, cap, 256, &per_cu) != hipSuccess)
     return 0;
   uint64_t w = (uint64_t)cus * (uint64_t)per_cu * 4;   // 4 wavefronts per 256-thread block
   cache.emplace(key, w);
@@ -784,13 +784,15 @@ static void kernel_shape(int coll, size_t count, int dtype, size_t* kcount, int*
   *kdtype = coll == kAllGather ? (int)RINGAR_INT8 : dtype;
 }
 
-// The plan a launch uses: first without, then with the kernel's residency.
+// The plan a launch uses: first without, then with the kernel's residency
+// (`captured`: that of the captured form, whose line-protocol kernels hold
+// fewer wavefronts; a lower residency only ever takes fewer lanes).
 static ringar_result_t plan_for_launch(int coll, size_t count, int dtype, int op, int nranks, int nchannels,
-                                int proto, const ringar_config_t* cfg, Plan* P) {
+                                int proto, const ringar_config_t* cfg, Plan* P, bool captured = false) {
   ringar_result_t r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, 0, P);
   if (r != RINGAR_SUCCESS) return r;
   if (count > 0 && nranks > 1) {
-    const uint64_t cap = capacity_waves(P->kind, dtype, op, P->proto);
+    const uint64_t cap = capacity_waves(P->kind, dtype, op, P->proto, captured);
     if (cap && (r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, cap, P)) != RINGAR_SUCCESS)
       return r;
   }
@@ -893,6 +895,9 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(st, &capture));
   const bool captured = capture != hipStreamCaptureStatusNone;
+  if (captured && (r = plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, cfg, &P, true)) !=
+                      RINGAR_SUCCESS)
+    return r;
 
   std::lock_guard<std::mutex> lock(g_mu);
   Resources* R = nullptr;

@@ -267,7 +267,8 @@ def test_random_calls_captured_in_one_graph():
                 continue
             want = _want_plan(xs, dtype, op, plan, cfg["ring_order"])
             cases.append(dict(desc=desc, n=n, count=count, dtype=dtype, op=op, nch=nch, proto=proto, cfg=cfgo,
-                              order=cfg["ring_order"], plan=plan, sends=sends, recvs=recvs, want=want))
+                              order=cfg["ring_order"], plan=plan, sends=sends, recvs=recvs, want=want,
+                              forced_lanes=cfg["lanes"] != 0))
     st.synchronize()
     assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
     for c in cases:
@@ -281,8 +282,14 @@ def test_random_calls_captured_in_one_graph():
             c["code"] = ra.ringar_allreduce_ex([t.data_ptr() for t in c["sends"]], [t.data_ptr() for t in c["recvs"]],
                                                c["count"], c["dtype"], c["op"], c["n"], c["nch"], c["proto"],
                                                st.cuda_stream, c["cfg"])
-    bad = [(c["desc"], ra.ringar_result_string(c["code"])) for c in cases if c["code"] != ra.SUCCESS]
+    # the captured line-protocol kernels hold fewer wavefronts: a plan takes
+    # fewer lanes under capture, and only a forced lane count beyond that
+    # residency is refused
+    bad = [(c["desc"], ra.ringar_result_string(c["code"])) for c in cases
+           if c["code"] != ra.SUCCESS and not (c["forced_lanes"] and c["code"] == ra.INVALID_USAGE)]
     assert not bad, bad
+    cases = [c for c in cases if c["code"] == ra.SUCCESS]
+    assert len(cases) >= 32, len(cases)
 
     for rep in range(3):
         with torch.cuda.stream(st):
