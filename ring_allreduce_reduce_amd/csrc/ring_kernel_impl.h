@@ -330,6 +330,7 @@ struct Lane {
   int lane;            // lane within the wavefront
   Waiter w;
   bool cap;            // a captured call (the kernel instance's constant)
+  uint32_t zbytes;     // captured line protocols: most slot bytes a slice read
 };
 
 // Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
@@ -344,25 +345,38 @@ template <int OP> constexpr int post_flag() { return OP == 4 ? kPost : 0; }
 // load of a slot has returned its data (the values were consumed above),
 // so the producer may overwrite it; the wavefront's own stores need not be
 // complete, and waiting for them here would add a round trip to every step.
-// Captured calls (a graph may replay one any number of times) run kernel
-// instances of their own: their steps count from zero on counters of their
-// own, and they leave every counter and flag they consumed at zero (the
-// receiver of a connection zeroes the LL lines / LL128 flags it read before
-// handing the slot back, and its tail and head after its last step).  Eager
-// calls count from 2^31 up, so no flag either kind leaves behind can match
-// the other's.
 template <int F> __device__ __forceinline__ void release_slot(Lane& L) {
-  if (L.cap) wait_mem();   // the consumed lines' zeroing stores first
   compiler_fence();
   st_relaxed(L.in[0].head, L.a->base + L.rstep + 1);
   if (F & kRecv2) st_relaxed(L.in[1].head, L.a->base + L.rstep + 1);
   L.rstep++;
 }
 
-// After a captured call's last step on it: a receiver's input connection
-// back to zero (its producer has published its last tail and read its last
-// head by then).
-__device__ __forceinline__ void reset_input(const Conn& c) {
+// Captured calls (a graph may replay one any number of times) run kernel
+// instances of their own: their steps count from zero on counters of their
+// own, and they leave every counter and flag they consumed at zero.  Within
+// a call every flag is a distinct step number, so a slot's lines need to be
+// clean only for the next replay: after its last step the receiver of a
+// connection zeroes the slot bytes it read (the largest slice's prefix of
+// every slot the call used) and the tail and head.  Its producer has
+// written its last line, published its last tail and read its last head by
+// then.  Eager calls count from 2^31 up, so no flag either kind leaves
+// behind can match the other's.
+template <int PROTO> __device__ __forceinline__ void finish_input(const Lane& L, const Conn& c) {
+  if (PROTO != kSimple) {
+    const uint32_t slot = PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+    const uint64_t nslots = min_u64(L.rstep, (uint64_t)L.a->depth);
+    for (uint64_t sl = 0; sl < nslots; sl++) {
+      char* base = c.fifo + sl * slot;
+      if (PROTO == kLL) {
+        for (uint32_t off = (uint32_t)L.lane * 8u; off < L.zbytes; off += 64u * 8u)
+          st_relaxed((uint64_t*)(base + off), 0);   // whole lines: data and flag
+      } else {
+        for (uint32_t line = (uint32_t)L.lane; line * 128u < L.zbytes; line += 64u)
+          st_relaxed((uint64_t*)(base + (size_t)line * 128u + 120u), 0);   // the flag
+      }
+    }
+  }
   st_relaxed(c.tail, 0);
   st_relaxed(c.head, 0);
 }
@@ -559,6 +573,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
+  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, npk * 32u);   // slot bytes read (see finish_input)
   constexpr int U = NI == 2 ? 2 : 4;   // packets per lane per poll (registers)
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
     u32x4 va[NI][U], vb[U];
@@ -605,18 +620,6 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
 #pragma unroll
         for (int u = 0; u < U; u++)
           va[i][u] = u32x4{(uint32_t)ln[i][u][0], (uint32_t)ln[i][u][1], (uint32_t)ln[i][u][2], (uint32_t)ln[i][u][3]};
-      if (L.cap) {
-        // the lines read, back to zero (see release_slot)
-#pragma unroll
-        for (int i = 0; i < NI; i++)
-#pragma unroll
-          for (int u = 0; u < U; u++) {
-            const uint32_t p = p0 + u * 64 + L.lane;
-            if (p < nfull)
-#pragma unroll
-              for (int q = 0; q < 4; q++) st_relaxed(const_cast<uint64_t*>(lin[i]) + 4 * p + q, 0);
-          }
-      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -642,9 +645,6 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
         uint64_t ln[4];
         if (!ll_recv4(L.w, lin[i], p, true, fin, ln)) { failed = true; break; }
         x[i] = u32x4{(uint32_t)ln[0], (uint32_t)ln[1], (uint32_t)ln[2], (uint32_t)ln[3]};
-        if (L.cap)
-#pragma unroll
-          for (int q = 0; q < 4; q++) st_relaxed(const_cast<uint64_t*>(lin[i]) + 4 * p + q, 0);
       }
       if (failed) break;
     }
@@ -757,6 +757,7 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const bool vec = a.vec_ok;
   const uint32_t nlines = (nbytes + 119) / 120;
+  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, nlines * 128u);   // slot bytes read (see finish_input)
   const int col = L.lane & 7;
   const uint32_t psize = col == 7 ? 8u : 16u;
   const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;   // data bytes of the column
@@ -873,14 +874,6 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
       for (int v = 0; v < kLL128Group; v++) vb[v] = vbn[v];
       part = partn;
     }
-    if ((F & kRecv) && L.cap) {
-      // the batch's flags, back to zero (see release_slot)
-#pragma unroll
-      for (int i = 0; i < NI; i++)
-#pragma unroll
-        for (int w = 0; w < 2; w++)
-          if (64 * w + L.lane < (int)nl) st_relaxed((uint64_t*)(sin[i] + (size_t)(b0 + 64 * w + L.lane) * 128 + 120), 0);
-    }
     if (F & kSend) {
       wait_mem();   // all data of the batch is visible before any of its flags
 #pragma unroll
@@ -932,6 +925,7 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
   const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   const bool act = p < npk;
+  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, npk * 32u);   // slot bytes read (see finish_input)
   u32x4 va[NI], vb = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < NI; i++) va[i] = vb;
@@ -963,13 +957,6 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
 #pragma unroll
     for (int i = 0; i < NI; i++)
       va[i] = u32x4{(uint32_t)ln[i][0], (uint32_t)ln[i][1], (uint32_t)ln[i][2], (uint32_t)ln[i][3]};
-    if (L.cap)
-      // the lines read, back to zero (see release_slot); lanes past the
-      // part are dropped by the range check
-#pragma unroll
-      for (int i = 0; i < NI; i++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) ll_store(ri[i], p * 32 + q * 8, 0u, 0u);
   }
   const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb, a.nranks);
   if (F & kSend) {
@@ -1160,6 +1147,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
   L.w.a = &a;
   L.lane = threadIdx.x & 63;
   L.cap = cap;
+  L.zbytes = 0;
   L.sstep = 0;
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;   // below any value a wait of this call asks for
@@ -1245,7 +1233,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
       }
     }
   }
-  if (cap) reset_input(L.in[0]);
+  if (cap) finish_input<PROTO>(L, L.in[0]);
 }
 
 // The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
@@ -1327,6 +1315,7 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   L.w.a = &a;
   L.lane = threadIdx.x & 63;
   L.cap = CAP;
+  L.zbytes = 0;
   L.sstep = 0;
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;
@@ -1377,8 +1366,8 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   }
   if (CAP) {
     // only real inputs: a leaf's unused input slot points at its own output
-    if (bcast || nk >= 1) reset_input(L.in[0]);
-    if (!bcast && nk == 2) reset_input(L.in[1]);
+    if (bcast || nk >= 1) finish_input<PROTO>(L, L.in[0]);
+    if (!bcast && nk == 2) finish_input<PROTO>(L, L.in[1]);
   }
 }
 
