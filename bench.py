@@ -215,9 +215,12 @@ def main():
         sends = [W.to_torch(x, "float32", dev) for x in xs]
         recvs = [torch.empty(count if coll == "allreduce" else block, device=dev) for _ in sends]
     stream = torch.cuda.Stream()
-    cfg = ra.make_config(chunk_bytes=CHUNK_BYTES, algo=algo, direct=int(direct))
+    # the tree moves a whole chunk per channel up and then down: it takes its
+    # own chunk rule rather than the ring's 512 KiB
+    cfg = ra.make_config(chunk_bytes=0 if algo == "tree" else CHUNK_BYTES, algo=algo, direct=int(direct))
     plan = ra.ringar_plan_coll(coll, count if coll == "allreduce" else block, "float32", NRANKS, NCHANNELS,
                                "Simple", cfg)
+    chunk_bytes = plan.chunk_elems * 4 if algo == "tree" else CHUNK_BYTES
     send_ptrs = [s.data_ptr() for s in sends]
     recv_ptrs = [r.data_ptr() for r in recvs]
 
@@ -332,9 +335,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{what[0]}, 8 virtual ranks, fp32{' sum' if coll != 'all_gather' else ''}, "
                                f"{what[1]}, Simple, "
-                               "16 channels, 512 KiB chunks",
+                               f"16 channels, {chunk_bytes >> 10} KiB chunks",
                    "nranks": NRANKS, "bytes_per_rank": s, "proto": "Simple", "nchannels": NCHANNELS,
-                   "chunk_bytes": CHUNK_BYTES, "lanes": plan.lanes, "fifo_depth": plan.fifo_depth,
+                   "chunk_bytes": chunk_bytes, "lanes": plan.lanes, "fifo_depth": plan.fifo_depth,
                    "workgroups": plan.workgroups},
         "algbw_gbs": round(algbw, 3),
         "busbw_gbs": round(busbw, 3),

@@ -407,11 +407,15 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   if (tree && !chunk_bytes) {
     // The tree moves a whole chunk up and then down, so a channel needs
     // several chunks for the two directions to overlap: a quarter of the
-    // channel, kept between 8 KiB (4 KiB for LL) and 64 KiB.  Measured on
-    // MI355X at n = 8, 32 channels: 2 MiB per rank 47.5 -> 37.9 us, 8 MiB
-    // 133.7 -> 99.4 us, 64 MiB 620 -> 534 us against 512 KiB chunks.
+    // channel, kept between 8 KiB (4 KiB for LL) and 2 MiB / channels (at
+    // least 64 KiB), so that all channels together keep about 2 MiB in
+    // flight.  Measured on MI355X at n = 8, fp32: 32 channels, against
+    // 512 KiB chunks, 2 MiB per rank 47.5 -> 37.9 us, 8 MiB 133.7 -> 99.4
+    // us, 64 MiB 620 -> 534 us; at 64 MiB the best chunk is 64 KiB at 32
+    // channels (529 us), 128 KiB at 16 (550 against 593 us at 64 KiB) and
+    // 256 KiB at 8 (531 against 659 us).
     const uint64_t lo = P.proto == kLL ? 4096 : 8192;
-    const uint64_t hi = std::min<uint64_t>(65536, P.chunk_bytes);
+    const uint64_t hi = std::min<uint64_t>(std::max<uint64_t>(65536, (2u << 20) / (uint64_t)P.nch), P.chunk_bytes);
     P.chunk_bytes = std::min(hi, std::max(lo, align_up(P.per_channel * es / 4, 16)));
   }
   if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)
