@@ -247,8 +247,12 @@ typedef struct {
  *       consumed at zero, so each replay starts clean and eager calls on
  *       the stream keep working between replays.  Nothing is allocated or
  *       cleared during capture: the stream must have run a call of the same
- *       shape first (else RINGAR_ERR_INVALID_USAGE).  The direct form is
- *       refused under capture (RINGAR_ERR_INVALID_USAGE, nothing enqueued).
+ *       shape first (else RINGAR_ERR_INVALID_USAGE).  The captured kernels
+ *       may hold fewer wavefronts per CU, so a captured call can take fewer
+ *       lanes than the same call made eagerly (same results); a forced lane
+ *       count beyond what they hold is RINGAR_ERR_INVALID_USAGE.  The direct
+ *       form is refused under capture (RINGAR_ERR_INVALID_USAGE, nothing
+ *       enqueued).
  *       Replays share the stream's FIFO memory with its eager calls: run
  *       them in order (one stream, or synchronised).  A graph holds the
  *       addresses of the stream's FIFO memory and counters: later eager
