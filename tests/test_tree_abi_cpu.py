@@ -166,3 +166,27 @@ def test_direct_form_is_planned_only_where_it_applies():
     # the small form is not used with the direct form
     small = ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple", d)
     assert small.small_slices == 0 and ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple").small_slices == 1
+
+
+def test_tree_chunk_rule():
+    # without a configured chunk the tree takes a quarter of a channel's
+    # bytes, between 8 KiB (LL: 4 KiB) and 2 MiB / channels (at least 64 KiB),
+    # and never above the protocol's default chunk
+    cfg = ra.make_config(algo="tree")
+    defaults = dict(zip(("LL", "LL128", "Simple"), golden_model_dict()["default_chunk_bytes"]))
+    for proto in ("LL", "LL128", "Simple"):
+        for nch in (1, 2, 4, 8, 16, 32):
+            for mib in (0.25, 1, 4, 64):
+                count = int(mib * (1 << 18))
+                p = ra.ringar_plan(count, "float32", 8, nch, proto, cfg)
+                per = -(-count // nch)
+                per = -(-per // 4) * 4
+                hi = min(max(64 << 10, (2 << 20) // nch), defaults[proto])
+                lo = 4096 if proto == "LL" else 8192
+                quarter = -(-(per * 4 // 4) // 16) * 16
+                assert p.chunk_elems * 4 == min(hi, max(lo, quarter)), (proto, nch, mib)
+    # a configured chunk is taken as it is
+    p = ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", ra.make_config(algo="tree", chunk_bytes=512 << 10))
+    assert p.chunk_elems * 4 == 512 << 10
+    # the bench shape: 64 MiB per rank, 16 channels -> 128 KiB
+    assert ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", cfg).chunk_elems * 4 == 128 << 10
