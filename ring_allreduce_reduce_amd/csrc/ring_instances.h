@@ -14,9 +14,14 @@ namespace ringar {
 // kAllGather); LL128 has no small-slice form.
 template <class E, int COLL, int OP, bool CAP>
 const void* ring_instance(int proto, bool small) {
-  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<E, OP, kLL, true, COLL, CAP>
-                                 : (const void*)&ring_kernel_lines<E, OP, kLL, false, COLL, CAP>;
-  if (proto == kLL128) return (const void*)&ring_kernel_lines<E, OP, kLL128, false, COLL, CAP>;
+  if constexpr (CAP) {
+    if (proto == kLL) return small ? (const void*)&ring_kernel_lines_captured<E, OP, kLL, true, COLL>
+                                   : (const void*)&ring_kernel_lines_captured<E, OP, kLL, false, COLL>;
+    if (proto == kLL128) return (const void*)&ring_kernel_lines_captured<E, OP, kLL128, false, COLL>;
+  }
+  if (proto == kLL) return small ? (const void*)&ring_kernel_lines<E, OP, kLL, true, COLL>
+                                 : (const void*)&ring_kernel_lines<E, OP, kLL, false, COLL>;
+  if (proto == kLL128) return (const void*)&ring_kernel_lines<E, OP, kLL128, false, COLL>;
   return small ? (const void*)&ring_kernel<E, OP, kSimple, true, COLL, CAP>
                : (const void*)&ring_kernel<E, OP, kSimple, false, COLL, CAP>;
 }

@@ -1253,6 +1253,13 @@ __global__ void __launch_bounds__(256) ring_kernel_lines(const KernelArgs a) {
   static_assert(PROTO != kSimple, "Simple runs ring_kernel");
   ring_body<E, OP, PROTO, SMALL, COLL>(a, CAP);
 }
+// The captured line kernels, held to the eager ones' occupancy of 3 (at
+// most 168 VGPRs); without the bound captured LL128 took 169 and ran at 2.
+template <class E, int OP, int PROTO, bool SMALL, int COLL>
+__global__ void __launch_bounds__(256, 3) ring_kernel_lines_captured(const KernelArgs a) {
+  static_assert(PROTO != kSimple, "Simple runs ring_kernel");
+  ring_body<E, OP, PROTO, SMALL, COLL>(a, true);
+}
 
 // ----------------------------------------------------------------- tree
 // One launch of the tree AllReduce over the double binary tree of
