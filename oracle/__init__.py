@@ -55,6 +55,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz,
         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.oracle_ring_allreduce.restype = ctypes.c_int
+    lib.oracle_ring_allreduce_channels.argtypes = [
+        ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz,
+        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int]
+    lib.oracle_ring_allreduce_channels.restype = ctypes.c_int
     lib.oracle_element_chunks.argtypes = [sz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz, vp]
     lib.oracle_element_chunks.restype = ctypes.c_int
     lib.oracle_channel_range.argtypes = [sz, sz, ctypes.c_int, ctypes.c_int,
@@ -139,6 +143,42 @@ def ring_allreduce(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
     if rc != 0:
         raise ValueError("oracle_ring_allreduce rejected its arguments")
     return ys
+
+
+def ring_allreduce_threaded(xs, dtype: str, op: str, nchannels: int, chunk_elems: int,
+                            ring=None, threads: int | None = None, lib: ctypes.CDLL | None = None,
+                            out=None):
+    """The same ring AllReduce as ``ring_allreduce``, with the channels spread
+    over ``threads`` host threads (default: one per available core, at most
+    one per channel).  Channels own disjoint element ranges, so the result is
+    the same bytes; only the wall time differs.  Returns (outputs, threads
+    used)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    lib = lib or load()
+    code, npt, esize = DTYPES[dtype]
+    n = len(xs)
+    xs = [np.ascontiguousarray(x, dtype=npt) for x in xs]
+    count = xs[0].size if n else 0
+    assert all(x.size == count for x in xs)
+    ys = out if out is not None else [_sentinel(count, npt) for _ in range(n)]
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    rp = (ctypes.c_int * n)(*[int(r) for r in ring]) if ring is not None else None
+    if threads is None:
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(int(threads), nchannels))
+    bounds = [(nchannels * t // threads, nchannels * (t + 1) // threads) for t in range(threads)]
+
+    def run(b):
+        return lib.oracle_ring_allreduce_channels(n, count, code, OPS[op], nchannels, chunk_elems, rp, xp, yp,
+                                                  b[0], b[1])
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        codes = list(pool.map(run, bounds))
+    if any(codes):
+        raise ValueError("oracle_ring_allreduce_channels rejected its arguments")
+    return ys, threads
 
 
 def ring_reduce_scatter(xs, dtype: str, op: str, ring=None, lib: ctypes.CDLL | None = None, out=None):

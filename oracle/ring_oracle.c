@@ -358,25 +358,38 @@ static void ring_loop(int n, int dtype, int op, size_t es, const int* ring,
 }
 
 /*
- * Ring AllReduce over n virtual ranks.
+ * Ring AllReduce over n virtual ranks, channels [c_begin, c_end) only.
+ * Channels own disjoint element ranges and run independently of each other
+ * ([ARCH] §九.3: one channel is one block on its own slice of the buffer), so
+ * calls for disjoint channel ranges may run at the same time (the benchmark's
+ * threaded timing does); together they compute exactly what one call over
+ * every channel computes.
  *   x[r], y[r]: rank r's input and output (count elements each; may alias).
  *   ring[i]:    rank at ring index i (NULL = identity); i sends to i+1 mod n.
  *   chunk_elems: per-rank, per-channel chunk of a full loop, a multiple of
  *               16 bytes.
  * Returns 0, or -1 on bad arguments.
  */
-int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
-                          int nchannels, size_t chunk_elems, const int* ring,
-                          const void* const* x, void* const* y) {
+int oracle_ring_allreduce_channels(int nranks, size_t count, int dtype, int op,
+                                   int nchannels, size_t chunk_elems, const int* ring,
+                                   const void* const* x, void* const* y,
+                                   int c_begin, int c_end) {
   size_t es = elem_size(dtype);
   if (!es || op < OR_SUM || op > OR_AVG || nranks < 1 || nchannels < 1) return -1;
   if (chunk_elems == 0 || chunk_elems % (16 / es)) return -1;
+  if (c_begin < 0 || c_end > nchannels || c_begin > c_end) return -1;
   int* order = malloc(sizeof(int) * (size_t)nranks);
   if (!order) return -1;
   for (int i = 0; i < nranks; i++) order[i] = ring ? ring[i] : i;
 
   if (nranks == 1) {                   /* a single rank only copies */
-    if (x[order[0]] != y[order[0]]) memcpy(y[order[0]], x[order[0]], count * es);
+    for (int c = c_begin; c < c_end; c++) {
+      size_t lo, hi;
+      oracle_channel_range(count, es, nchannels, c, &lo, &hi);
+      if (x[order[0]] != y[order[0]] && hi > lo)
+        memcpy((unsigned char*)y[order[0]] + lo * es, (const unsigned char*)x[order[0]] + lo * es,
+               (hi - lo) * es);
+    }
     free(order);
     return 0;
   }
@@ -392,7 +405,7 @@ int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
   }
   if (!pa || !pb) rc = -1;
 
-  for (int c = 0; c < nchannels && rc == 0; c++) {
+  for (int c = c_begin; c < c_end && rc == 0; c++) {
     size_t lo, hi;
     oracle_channel_range(count, es, nchannels, c, &lo, &hi);
     size_t len = hi - lo;
@@ -410,6 +423,14 @@ int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
   free(pb);
   free(order);
   return rc;
+}
+
+/* Ring AllReduce over every channel (arguments as above). */
+int oracle_ring_allreduce(int nranks, size_t count, int dtype, int op,
+                          int nchannels, size_t chunk_elems, const int* ring,
+                          const void* const* x, void* const* y) {
+  return oracle_ring_allreduce_channels(nranks, count, dtype, op, nchannels, chunk_elems, ring, x, y, 0,
+                                        nchannels);
 }
 
 /* ---------------------------------------------------------------------

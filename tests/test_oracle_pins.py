@@ -254,3 +254,20 @@ def test_rejects_bad_arguments():
         oracle.ring_allreduce(xs, "int32", "sum", 1, 3)       # chunk not 16-byte multiple
     with pytest.raises(ValueError):
         oracle.ring_allreduce(xs, "int32", "sum", 0, 4)       # no channel
+
+
+# ---------------------------------------------------------------- channel ranges
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_channel_ranges_compose_to_the_whole_call(dtype):
+    """Channels own disjoint ranges ([ARCH] §九.3: a channel is one block on
+    its own slice), so the oracle run channel range by channel range, on
+    threads, gives the bytes of one call over every channel."""
+    for n, count, nch, units in [(1, 1000, 3, 1), (4, 50021, 7, 3), (8, 100000, 16, 64)]:
+        xs = W.inputs(f"chan-{dtype}-{n}", n, count, dtype, "uniform", -4, 4)
+        chunk = units * _a(dtype)
+        want = oracle.ring_allreduce(xs, dtype, "sum", nch, chunk)
+        for threads in (1, 3, nch):
+            got, used = oracle.ring_allreduce_threaded(xs, dtype, "sum", nch, chunk, threads=threads)
+            assert used == min(threads, nch)
+            for g, w in zip(got, want):
+                assert np.array_equal(g.view(np.uint8), w.view(np.uint8))
