@@ -24,7 +24,17 @@
  * Threading: calls are host-thread safe.  Calls on one stream run in stream
  * order and share that stream's FIFO memory; calls on different streams use
  * different FIFO memory and may run concurrently if the GPU has room for both
- * grids (the library checks only its own grid against the GPU's capacity).
+ * grids.
+ *
+ * Co-residency: every wavefront of a launch waits on others of the same
+ * launch, so the whole grid must be resident at once.  The library checks its
+ * own grid against what the GPU holds of that kernel, but it cannot see other
+ * work: a call that overlaps another large kernel (another ringar call on a
+ * second stream, or another process's kernels) may find part of its grid
+ * unscheduled until that work ends.  Its waits then run into the spin limit
+ * and the call reports RINGAR_ERR_TIMEOUT through ringar_get_async_error
+ * (bounded, never a hang).  Do not overlap large calls with other large
+ * kernels on the same GPU.
  */
 #ifndef RINGAR_H
 #define RINGAR_H
@@ -259,9 +269,8 @@ typedef struct {
  *       calls that need more of them keep the old buffers alive for it, and
  *       ringar_release frees them, so a graph captured before
  *       ringar_release must not be replayed after it.  After an
- *       asynchronous error in a replay the captured counters are no longer
- *       zero: destroy the graph, call ringar_release, make an eager call and
- *       capture again.
+ *       asynchronous error in a replay, call ringar_get_async_error (it
+ *       resets what the failed replay left behind) before replaying again.
  * Errors are reported before anything is enqueued; a wait that times out or
  * is aborted inside the kernel is reported by ringar_get_async_error.
  */
@@ -318,7 +327,17 @@ ringar_result_t ringar_all_gather_ex(void* const* sendbuffs, void* const* recvbu
                                      ringar_stream_t stream, const ringar_config_t* cfg);
 
 /* Host only, no GPU needed: the plan ringar_allreduce_ex would use for these
- * arguments (cfg may be NULL).  Returns the same argument errors. */
+ * arguments (cfg may be NULL).  Returns the same argument errors.
+ *   The partition follows the pages: channels own contiguous ranges of the
+ *   buffer ([BOOK] §2.2), a loop covers nranks chunks of chunk_elems and the
+ *   last loop's chunks are alignUp(ceil(rem / nranks), 16 B / element size)
+ *   elements ([BOOK] §2.3, RingARAlgorithm::getNextSendAddr); with
+ *   nchannels == 0 the channel count comes from the size rule of [ARCH] §六.4
+ *   (drop a channel while bytes < nch x threads x threshold), and with
+ *   proto == RINGAR_PROTO_AUTO the protocol from the alpha-beta model of
+ *   [ARCH] §八.1-八.2.  lanes, fifo_depth and small_slices are this
+ *   library's own (they change no result).
+ *   out: caller-owned, filled on success, untouched on error. */
 ringar_result_t ringar_plan(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
                             ringar_proto_t proto, const ringar_config_t* cfg, ringar_plan_t* out);
 
@@ -356,30 +375,55 @@ ringar_result_t ringar_select_algo(size_t bytes, int nranks, int nchannels, cons
  * its children in child-slot order, -1 = none. */
 ringar_result_t ringar_tree(int nranks, int tree, int rank, int* parent, int* child0, int* child1);
 
-/* Host only: the built-in MI355X model constants. */
+/* Host only: the built-in MI355X model constants, in the form of the pages'
+ * tuning model ([ARCH] §八.1-八.2; the pages' own constants are NVIDIA's);
+ * the values are fitted to this library's calls on MI355X, which no page
+ * gives.  out: caller-owned; RINGAR_ERR_INVALID_ARGUMENT if NULL. */
 ringar_result_t ringar_default_model(ringar_model_t* out);
 
 /* Host only: element range [lo, hi) of channel c and, for the loop starting
  * at element `loop_off` of that channel, chunk k's range [klo, khi)
- * (absolute element indices; empty ranges have klo == khi). */
+ * (absolute element indices; empty ranges have klo == khi): the channel
+ * split of [BOOK] §2.2 and the chunk rule of [BOOK] §2.3
+ * (RingARAlgorithm::getNextSendAddr), as the kernels use them.  chunk_elems
+ * must be a multiple of 16 bytes; every output pointer must be non-NULL,
+ * else RINGAR_ERR_INVALID_ARGUMENT. */
 ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nranks, int nchannels,
                                    size_t chunk_elems, int c, size_t loop_off, int k,
                                    size_t* lo, size_t* hi, size_t* klo, size_t* khi);
 
-/* Waits for `stream`, then returns (and clears) the first error a kernel on
- * this stream recorded: RINGAR_ERR_TIMEOUT or RINGAR_ERR_ABORTED, else
- * RINGAR_SUCCESS.  After such an error the library's FIFO state is still
- * valid for later calls. */
+/* Asynchronous errors ([BOOK] §1.4: ncclCommGetAsyncError reports what went
+ * wrong after the call returned; [ARCH] §九.5: a kernel only leaves its wait
+ * loops through the abort flag).  Waits for `stream`, then returns (and
+ * clears) the first error a kernel enqueued on this stream recorded:
+ * RINGAR_ERR_TIMEOUT (a wait passed the spin limit), RINGAR_ERR_ABORTED (the
+ * abort word was set), RINGAR_ERR_INTERNAL (a part larger than the FIFO
+ * allows reached the kernel), else RINGAR_SUCCESS.  Eager calls and replays
+ * of captured calls record their errors in separate words, so neither can
+ * hide the other's; one call returns one error (call it again for the next).
+ * After an eager call's error the FIFO state stays valid for later calls.
+ * After a replay's error this call also clears the counters and line flags
+ * the captured form expects to find at zero (the replay that gave up left
+ * some behind), so the graph may be replayed again; call it once the replay
+ * has completed (synchronise the stream it was replayed on first).
+ * RINGAR_ERR_DEVICE if a HIP call fails. */
 ringar_result_t ringar_get_async_error(ringar_stream_t stream);
 
-/* Synchronises the device and frees every FIFO, counter and scratch buffer
- * the library holds (they are re-created on the next call).  Graphs
- * captured before this call hold freed addresses: do not replay them. */
+/* Resource cleanup, the analogue of ncclCommDestroy ([BOOK] §1.4: free the
+ * local resources once nothing uses them any more).  Synchronises every
+ * device the library has used and frees every FIFO, counter and error word
+ * it allocated (they are re-created on the next call).  Graphs captured
+ * before this call hold freed addresses: do not replay them.  Returns
+ * RINGAR_ERR_DEVICE if a HIP call fails. */
 ringar_result_t ringar_release(void);
 
+/* Static text naming a result code (the error classes of [BOOK] Japanese
+ * edition ch. 5-6: invalid argument, invalid usage, internal error); never
+ * NULL, "unknown result" for codes outside the enum. */
 const char* ringar_result_string(ringar_result_t r);
 
-/* Text of the last HIP error seen by this thread ("" if none). */
+/* Text of the last HIP error or refusal reason seen by this thread ("" if
+ * none); valid until this thread's next call into the library. */
 const char* ringar_last_error(void);
 
 #ifdef __cplusplus

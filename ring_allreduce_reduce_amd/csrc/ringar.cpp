@@ -544,8 +544,11 @@ struct Resources {
   // a larger allocation are kept here, alive for those graphs, until
   // ringar_release.
   bool captured_ever = false;
-  std::vector<void*> retired;
+  std::vector<std::pair<void*, uint64_t>> retired;   // (address, bytes)
   uint64_t counter_conns = 0;
+  // Two error words: [0] for eager calls, (call id << 8) | code, call ids
+  // growing; [1] for captured calls, whose replays all carry the call id of
+  // their capture and so need a word of their own.
   uint64_t* error = nullptr;
   uint64_t base = 0;
   uint64_t call_id = 0;
@@ -560,10 +563,10 @@ std::map<long long, int> g_occupancy;   // (kernel, block) -> blocks per CU
 
 // FIFO slots (unless `counters_only`) and counters for `conns` connections.
 ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t conns, bool counters_only) {
-  auto drop = [&R](void* p) -> ringar_result_t {
+  auto drop = [&R](void* p, uint64_t bytes) -> ringar_result_t {
     if (!p) return RINGAR_SUCCESS;
     if (R.captured_ever)
-      R.retired.push_back(p);
+      R.retired.emplace_back(p, bytes);
     else
       HIP_TRY(hipFree(p));
     return RINGAR_SUCCESS;
@@ -571,7 +574,7 @@ ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t c
   ringar_result_t r;
   if (!counters_only && R.fifo_conns[proto] < conns) {
     HIP_TRY(hipStreamSynchronize(st));
-    if ((r = drop(R.fifo[proto])) != RINGAR_SUCCESS) return r;
+    if ((r = drop(R.fifo[proto], R.fifo_conns[proto] * fifo_conn_bytes(proto))) != RINGAR_SUCCESS) return r;
     R.fifo[proto] = nullptr;
     R.fifo_conns[proto] = 0;
     const uint64_t bytes = conns * fifo_conn_bytes(proto);
@@ -581,8 +584,8 @@ ringar_result_t ensure_conns(Resources& R, hipStream_t st, int proto, uint64_t c
   }
   if (R.counter_conns < conns) {
     HIP_TRY(hipStreamSynchronize(st));
-    if ((r = drop(R.counters)) != RINGAR_SUCCESS) return r;
-    if ((r = drop(R.cap_counters)) != RINGAR_SUCCESS) return r;
+    if ((r = drop(R.counters, R.counter_conns * kCounterWords * 8)) != RINGAR_SUCCESS) return r;
+    if ((r = drop(R.cap_counters, R.counter_conns * kCounterWords * 8)) != RINGAR_SUCCESS) return r;
     R.counters = R.cap_counters = nullptr;
     R.counter_conns = 0;
     HIP_TRY(hipMalloc((void**)&R.counters, conns * kCounterWords * 8));
@@ -604,8 +607,8 @@ ringar_result_t get_resources(hipStream_t st, Resources** out) {
     R.device = dev;
     HIP_TRY(hipDeviceGetAttribute(&R.wall_khz, hipDeviceAttributeWallClockRate, dev));
     HIP_TRY(hipDeviceGetAttribute(&R.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
-    HIP_TRY(hipMalloc((void**)&R.error, 8));
-    HIP_TRY(launch_fill(R.error, 1, 0, st));
+    HIP_TRY(hipMalloc((void**)&R.error, 16));
+    HIP_TRY(launch_fill(R.error, 2, 0, st));
     R.base = kEagerBase;
     // Test hook: RINGAR_STEP_BASE, read when a stream's resources are
     // created, starts its step numbers there (e.g. just below the point
@@ -966,7 +969,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   A.chunk_elems = P.chunk_elems;
   A.base = captured ? 0 : R->base;
   A.counters = captured ? R->cap_counters : R->counters;
-  A.error = R->error;
+  A.error = captured ? R->error + 1 : R->error;
   A.abort_flag = cfg ? cfg->abort_flag : nullptr;
   uint32_t spin_ms = (cfg && cfg->spin_limit_ms) ? cfg->spin_limit_ms : env().spin_limit_ms;
   A.spin_ticks = (uint64_t)spin_ms * (uint64_t)R->wall_khz;
@@ -1072,18 +1075,38 @@ ringar_result_t ringar_get_async_error(ringar_stream_t stream) {
   std::lock_guard<std::mutex> lock(g_mu);
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
-  auto it = g_res.find(std::make_pair(dev, st));
-  if (it == g_res.end()) return RINGAR_SUCCESS;
-  Resources& R = it->second;
-  uint64_t word = 0;
-  HIP_TRY(hipMemcpy(&word, R.error, 8, hipMemcpyDeviceToHost));
-  uint64_t call = word >> 8;
-  if (call > R.reported_call) {
-    R.reported_call = call;
-    int code = (int)(word & 0xff);
+  auto code_of = [](uint64_t w) {
+    const int code = (int)(w & 0xff);
     if (code == RINGAR_ERR_ABORTED || code == RINGAR_ERR_TIMEOUT || code == RINGAR_ERR_INTERNAL)
       return (ringar_result_t)code;
     return RINGAR_ERR_INTERNAL;
+  };
+  auto it = g_res.find(std::make_pair(dev, st));
+  if (it != g_res.end()) {
+    Resources& R = it->second;
+    uint64_t word[2] = {0, 0};
+    HIP_TRY(hipMemcpy(word, R.error, 16, hipMemcpyDeviceToHost));
+    const uint64_t call = word[0] >> 8;
+    if (call > R.reported_call) {
+      R.reported_call = call;
+      return code_of(word[0]);
+    }
+    if (word[1] != 0) {
+      // A captured call gave up: the wavefronts that stopped early left
+      // counters and line flags behind that the next replay would take for
+      // fresh ones.  Clear the word and everything the captured form counts
+      // on being zero (its counters, the line-protocol FIFOs, and the
+      // retired buffers older graphs may still use; eager calls never expect
+      // zeros to be fresh, so clearing is safe for them too), so the graph
+      // can be replayed again.
+      if (R.cap_counters) HIP_TRY(launch_fill(R.cap_counters, R.counter_conns * kCounterWords, 0, st));
+      for (int p = kLL; p <= kLL128; p++)
+        if (R.fifo[p]) HIP_TRY(launch_fill((uint64_t*)R.fifo[p], R.fifo_conns[p] * fifo_conn_bytes(p) / 8, 0, st));
+      for (auto& b : R.retired) HIP_TRY(launch_fill((uint64_t*)b.first, b.second / 8, 0, st));
+      HIP_TRY(launch_fill(R.error + 1, 1, 0, st));
+      HIP_TRY(hipStreamSynchronize(st));
+      return code_of(word[1]);
+    }
   }
   return RINGAR_SUCCESS;
 }
@@ -1100,7 +1123,7 @@ ringar_result_t ringar_release(void) {
       if (R.fifo[p]) HIP_TRY(hipFree(R.fifo[p]));
     if (R.counters) HIP_TRY(hipFree(R.counters));
     if (R.cap_counters) HIP_TRY(hipFree(R.cap_counters));
-    for (void* p : R.retired) HIP_TRY(hipFree(p));
+    for (auto& p : R.retired) HIP_TRY(hipFree(p.first));
     if (R.error) HIP_TRY(hipFree(R.error));
   }
   g_res.clear();

@@ -396,3 +396,58 @@ def test_halves_captured_and_replayed():
         for (sends, recvs, _), xs, case in zip(bufs, xs_all, HALVES):
             for r, (got, w) in enumerate(zip(recvs, _halves_want(case, xs))):
                 assert np.array_equal(_bits(W.from_torch(got, case[3])), _bits(w)), (rep, case, r)
+
+
+def test_replay_error_is_reported_after_an_eager_error_and_the_graph_recovers():
+    """A replay that gives up must be reported even when an eager call on the
+    stream failed, and was reported, after the capture (captured calls keep
+    their capture's call id, so they record errors in a word of their own);
+    reporting it clears what the failed replay left behind, so the next
+    replay of a good graph is bit-exact again.  The failure is forced from
+    the host: one rank's wavefronts return at once and the others give up
+    after a 20 ms spin limit."""
+    st = torch.cuda.Stream()
+    for proto in ["Simple", "LL", "LL128"]:
+        shape = (4, 100003, "float32", "sum", proto, 2)
+        n, count, dtype = shape[:3]
+        xs = _inputs(shape, f"cap-err-{proto}")
+        sends = [W.to_torch(x, dtype, DEV) for x in xs]
+        recvs = [torch.zeros_like(s) for s in sends]
+        bad = ra.make_config(skip_rank=2, spin_limit_ms=20)
+        print(f"case capture error {proto}: eager warm-up", flush=True)
+        with torch.cuda.stream(st):
+            assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+        st.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        g_bad, g_good = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_bad, stream=st):
+            assert _raw(sends, recvs, shape, st, bad) == ra.SUCCESS
+        with torch.cuda.graph(g_good, stream=st):
+            assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+        # an eager failure, reported, after the capture
+        print(f"case capture error {proto}: eager failure", flush=True)
+        with torch.cuda.stream(st):
+            assert _raw(sends, recvs, shape, st, bad) == ra.SUCCESS
+        st.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.TIMEOUT
+        # the failing replay is still reported
+        print(f"case capture error {proto}: failing replay", flush=True)
+        with torch.cuda.stream(st):
+            g_bad.replay()
+        st.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.TIMEOUT
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        # and a good replay afterwards starts from clean counters and flags
+        for rep in range(2):
+            xs2 = _inputs(shape, f"cap-err-{proto}-{rep}")
+            with torch.cuda.stream(st):
+                for t, x in zip(sends, xs2):
+                    t.copy_(W.to_torch(x, dtype, DEV))
+                for t in recvs:
+                    t.zero_()
+                print(f"case capture error {proto}: good replay {rep}", flush=True)
+                g_good.replay()
+            st.synchronize()
+            assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+            _check(recvs, _want(xs2, shape), shape)
+        del g_bad, g_good
