@@ -82,8 +82,14 @@ def rank_input(key: str, rank: int, count: int, dtype: str, dist: str,
 
 
 def inputs(key: str, nranks: int, count: int, dtype: str, dist: str,
-           lo: float = -1.0, hi: float = 1.0) -> list:
-    return [rank_input(key, r, count, dtype, dist, lo, hi) for r in range(nranks)]
+           lo: float = -1.0, hi: float = 1.0, threads: int = 1) -> list:
+    """Every rank's input; ``threads`` > 1 draws ranks on host threads (each
+    rank has its own generator, so the bytes are the same)."""
+    if threads <= 1 or nranks <= 1:
+        return [rank_input(key, r, count, dtype, dist, lo, hi) for r in range(nranks)]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(threads, nranks)) as pool:
+        return list(pool.map(lambda r: rank_input(key, r, count, dtype, dist, lo, hi), range(nranks)))
 
 
 # The five workloads: (nranks, dtype, op, proto, nchannels, chunk bytes, sizes
