@@ -291,6 +291,35 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
  * float results follow the tree's fold order, not the ring's. */
 
 /*
+ * The same AllReduce as ringar_allreduce_ex, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * hipMalloc): this entry point calls no hipMalloc, hipFree or other
+ * allocating routine.  Its FIFO slots, counters and error word live in one
+ * fixed device array of the library (64 MiB of FIFO slots, counters for 4096
+ * connections, an error word; each GPU the library runs on holds its own copy
+ * from the library's first use of that GPU until the process ends).  The
+ * caller passes inputs and outputs as for ringar_allreduce_ex, with the same
+ * meaning, checks and results: every choice that decides a result (protocol,
+ * channels, chunk, algorithm, ring order) is the one ringar_plan reports; the
+ * plan may take fewer lanes so that its connections fit the array (lanes
+ * change no result).  A call whose connections do not fit even with one lane
+ * per (rank, channel) (about 2 x nranks x nchannels x chunk bytes of FIFO),
+ * or whose forced lane count does not fit, is refused with
+ * RINGAR_ERR_INVALID_USAGE before anything is enqueued, the reason in
+ * ringar_last_error().  Refused under stream capture (no captured form).
+ * Every call on a GPU shares that GPU's array, which keeps what the last
+ * call left: calls that overlap on one GPU (on different streams, or with
+ * another thread's calls) race and must be avoided; calls in stream order,
+ * or synchronised, are safe.  Asynchronous errors are reported by
+ * ringar_get_async_error (synchronise the call's stream first).
+ * ringar_release does not touch the array.
+ */
+ringar_result_t ringar_allreduce_noalloc(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                         ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                         ringar_proto_t proto, ringar_stream_t stream,
+                                         const ringar_config_t* cfg);
+
+/*
  * Ring ReduceScatter, the first half of the ring AllReduce as a call of its
  * own ([ARCH] §七.1; the pages give no buffer layout, the plain one is
  * taken): sendbuffs[r] holds nranks blocks of recvcount elements, and

@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
     vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.ringar_allreduce.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i, i, i, i, i, vp]
     lib.ringar_allreduce_ex.argtypes = lib.ringar_allreduce.argtypes + [ctypes.POINTER(ringar_config_t)]
+    lib.ringar_allreduce_noalloc.argtypes = lib.ringar_allreduce_ex.argtypes
     lib.ringar_plan.argtypes = [sz, i, i, i, i, ctypes.POINTER(ringar_config_t), ctypes.POINTER(ringar_plan_t)]
     lib.ringar_plan_coll.argtypes = [i] + lib.ringar_plan.argtypes
     lib.ringar_reduce_scatter.argtypes = lib.ringar_allreduce.argtypes
@@ -127,7 +128,7 @@ def load() -> ctypes.CDLL:
     lib.ringar_result_string.restype = ctypes.c_char_p
     lib.ringar_last_error.argtypes = []
     lib.ringar_last_error.restype = ctypes.c_char_p
-    for name in ("ringar_allreduce", "ringar_allreduce_ex", "ringar_plan", "ringar_select", "ringar_plan_coll",
+    for name in ("ringar_allreduce", "ringar_allreduce_ex", "ringar_allreduce_noalloc", "ringar_plan", "ringar_select", "ringar_plan_coll",
                  "ringar_select_algo", "ringar_tree",
                  "ringar_reduce_scatter", "ringar_reduce_scatter_ex", "ringar_all_gather", "ringar_all_gather_ex",
                  "ringar_default_model", "ringar_chunk_range", "ringar_get_async_error", "ringar_release"):
@@ -185,6 +186,16 @@ def ringar_allreduce_ex(sendbuffs, recvbuffs, count, dtype, op, nranks, nchannel
                                       _enum(OPS, op), nranks, nchannels, _enum(PROTOS, proto),
                                       ctypes.c_void_p(stream or 0),
                                       ctypes.byref(cfg) if cfg is not None else None)
+
+
+def ringar_allreduce_noalloc(sendbuffs, recvbuffs, count, dtype, op, nranks, nchannels, proto, stream,
+                             cfg=None) -> int:
+    """The allocation-free AllReduce (the library's scratch array instead of
+    allocated FIFO memory); same arguments and results as ringar_allreduce_ex."""
+    return load().ringar_allreduce_noalloc(_ptrs(sendbuffs), _ptrs(recvbuffs), count, _enum(DTYPES, dtype),
+                                           _enum(OPS, op), nranks, nchannels, _enum(PROTOS, proto),
+                                           ctypes.c_void_p(stream or 0),
+                                           ctypes.byref(cfg) if cfg is not None else None)
 
 
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}

@@ -868,11 +868,81 @@ ringar_result_t ringar_chunk_range(size_t count, ringar_dtype_t dtype, int nrank
   return RINGAR_SUCCESS;
 }
 
+// ---------------------------------------------------------------- scratch
+// Memory of ringar_allreduce_noalloc, for callers that cannot allocate: FIFO
+// slots, counters and an error word in one file-scope device array of fixed
+// size, so that the entry point itself allocates nothing.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the array's name is only a stand-in: its device address on each device is
+// taken once with hipGetSymbolAddress and kept in NoAllocState::base_ptr,
+// which is what kernels and fills receive.
+constexpr uint64_t kNoAllocFifoBytes = 64ull << 20;                  // FIFO slots
+constexpr uint64_t kNoAllocCounterConns = 4096;                      // counter lines
+constexpr uint64_t kNoAllocCounterBytes = kNoAllocCounterConns * kCounterWords * 8;
+constexpr uint64_t kNoAllocBytes = kNoAllocFifoBytes + kNoAllocCounterBytes + 256;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+struct NoAllocState {
+  bool ready = false;
+  unsigned char* base_ptr = nullptr;   // device address of `scratch` on this device
+  char* fifo = nullptr;                // [0, kNoAllocFifoBytes)
+  uint64_t* counters = nullptr;        // kNoAllocCounterConns connections
+  uint64_t* error = nullptr;           // (call id << 8) | code of the first failure
+  uint64_t base = 0;                   // step base of the next call
+  uint64_t call_id = 0;
+  uint64_t reported_call = 0;
+  int last_proto = -1;                 // protocol whose data the FIFO bytes hold
+  uint64_t dirty_bytes = 0;            // FIFO bytes calls have written since the last clear
+  int wall_khz = 100000;
+  int num_cus = 0;
+};
+NoAllocState g_noalloc[kMaxDevices];   // guarded by g_mu
+
+// Set-up on the first call on a device (that device current): the scratch
+// array's device address, checked, then one clear of all of it.
+ringar_result_t noalloc_state(hipStream_t st, NoAllocState** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return RINGAR_ERR_INVALID_USAGE;
+  NoAllocState& S = g_noalloc[dev];
+  if (!S.ready) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr || (uintptr_t)ptr % 256) {
+      t_last_error = "hipGetSymbolAddress returned no usable address for the scratch array";
+      return RINGAR_ERR_INTERNAL;
+    }
+    S.base_ptr = (unsigned char*)ptr;
+    S.fifo = (char*)S.base_ptr;
+    S.counters = (uint64_t*)(S.base_ptr + kNoAllocFifoBytes);
+    S.error = (uint64_t*)(S.base_ptr + kNoAllocFifoBytes + kNoAllocCounterBytes);
+    HIP_TRY(hipDeviceGetAttribute(&S.wall_khz, hipDeviceAttributeWallClockRate, dev));
+    HIP_TRY(hipDeviceGetAttribute(&S.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+    HIP_TRY(launch_fill((uint64_t*)S.base_ptr, kNoAllocBytes / 8, 0, st));
+    S.base = kEagerBase;
+    S.ready = true;
+  }
+  *out = &S;
+  return RINGAR_SUCCESS;
+}
+
+// Scratch bytes a plan needs: FIFO slots of every connection (none for the
+// direct form) and their counters.
+bool noalloc_fits(const Plan& P, bool direct) {
+  const uint64_t fifo = direct ? 0 : P.conns * fifo_conn_bytes(P.proto);
+  return fifo <= kNoAllocFifoBytes && P.conns <= kNoAllocCounterConns;
+}
+
 // One ring collective.  count: elements per rank for the AllReduce, per
 // block for ReduceScatter (recvcount) and AllGather (sendcount).
+// noalloc: run on the device's scratch array instead of the stream's
+// allocated resources; the plan keeps every choice that decides results
+// (protocol, channels, chunk, algorithm) and takes fewer lanes when the
+// scratch cannot hold the connections of the usual lane count.
 static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* const* recvbuffs, size_t count,
                                int udtype, int op, int nranks, int nchannels, int proto,
-                               ringar_stream_t stream, const ringar_config_t* cfg) {
+                               ringar_stream_t stream, const ringar_config_t* cfg, bool noalloc = false) {
   const size_t ues = elem_size(udtype);
   if (!ues || op < RINGAR_SUM || op > RINGAR_AVG) return RINGAR_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks) return RINGAR_ERR_INVALID_ARGUMENT;
@@ -902,13 +972,63 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(st, &capture));
   const bool captured = capture != hipStreamCaptureStatusNone;
+  if (captured && noalloc) {
+    t_last_error = "the allocation-free entry point has no captured form";
+    return RINGAR_ERR_INVALID_USAGE;
+  }
   if (captured && (r = plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, cfg, &P, true)) !=
                       RINGAR_SUCCESS)
     return r;
 
+  // the direct form needs every rank out of place
+  bool direct = P.direct;
+  for (int q = 0; q < nranks && direct; q++)
+    if (sendbuffs[q] == recvbuffs[q]) direct = false;
+  if (captured && direct) {
+    t_last_error = "the direct form has no captured form";
+    return RINGAR_ERR_INVALID_USAGE;
+  }
+  if (noalloc && !noalloc_fits(P, direct)) {
+    // lanes change no result: take the most (a power of two below the
+    // plan's) whose connections the scratch holds, unless they were forced
+    const bool forced = (cfg && cfg->lanes) || env().lanes;
+    bool found = false;
+    if (!forced) {
+      ringar_config_t c2;
+      if (cfg) c2 = *cfg;
+      else {
+        memset(&c2, 0, sizeof(c2));
+        c2.skip_rank = -1;
+      }
+      int L = 1;
+      while (L * 2 < P.lanes) L *= 2;
+      for (; L >= 1 && !found; L /= 2) {
+        c2.lanes = L;
+        Plan Q;
+        if (plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, &c2, &Q) == RINGAR_SUCCESS &&
+            noalloc_fits(Q, direct)) {
+          P = Q;
+          found = true;
+        }
+      }
+    }
+    if (!found) {
+      char msg[256];
+      snprintf(msg, sizeof(msg),
+               "ringar_allreduce_noalloc: the call needs more than the %llu MiB of FIFO slots / %llu "
+               "connections its scratch holds; use fewer channels or a smaller chunk",
+               (unsigned long long)(kNoAllocFifoBytes >> 20), (unsigned long long)kNoAllocCounterConns);
+      t_last_error = msg;
+      return RINGAR_ERR_INVALID_USAGE;
+    }
+  }
+
   std::lock_guard<std::mutex> lock(g_mu);
   Resources* R = nullptr;
-  if (captured) {
+  NoAllocState* S = nullptr;
+  if (noalloc) {
+    if ((r = noalloc_state(st, &S)) != RINGAR_SUCCESS) return r;
+  } else if (captured) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     auto it = g_res.find(std::make_pair(dev, st));
@@ -920,6 +1040,8 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   } else if ((r = get_resources(st, &R)) != RINGAR_SUCCESS) {
     return r;
   }
+  const int num_cus = noalloc ? S->num_cus : R->num_cus;
+  const int wall_khz = noalloc ? S->wall_khz : R->wall_khz;
 
   // All (rank, channel, lane) wavefronts wait on each other, so the whole
   // grid must be resident at once.
@@ -937,18 +1059,26 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
     HIP_TRY(max_active_blocks(P.kind, dtype, op, P.proto, small, captured, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
-  if ((long long)oc->second * R->num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
+  if ((long long)oc->second * num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
 
-  // the direct form needs every rank out of place
-  bool direct = P.direct;
-  for (int q = 0; q < nranks && direct; q++)
-    if (sendbuffs[q] == recvbuffs[q]) direct = false;
-  if (captured && direct) {
-    t_last_error = "the direct form has no captured form";
-    return RINGAR_ERR_INVALID_USAGE;
-  }
   if (captured) R->captured_ever = true;
-  if (!captured) {
+  if (noalloc) {
+    // The FIFO bytes are shared by every protocol: data that another
+    // protocol left in them could pass for a line flag, so they are cleared
+    // whenever the protocol changes.  LL flags are 32-bit step numbers:
+    // restart the numbering (clearing every flag and counter) before it wraps.
+    const uint64_t touched = direct ? 0 : P.conns * fifo_conn_bytes(P.proto);
+    if (!direct && P.proto != S->last_proto) {
+      if (S->dirty_bytes) HIP_TRY(launch_fill((uint64_t*)S->fifo, S->dirty_bytes / 8, 0, st));
+      S->dirty_bytes = 0;
+      S->last_proto = P.proto;
+    }
+    S->dirty_bytes = std::max(S->dirty_bytes, touched);
+    if (S->base + P.max_steps + 1 >= 0xFFFFFFF0ull) {
+      HIP_TRY(launch_fill((uint64_t*)S->base_ptr, (kNoAllocFifoBytes + kNoAllocCounterBytes) / 8, 0, st));
+      S->base = kEagerBase;
+    }
+  } else if (!captured) {
     if ((r = ensure_conns(*R, st, P.proto, P.conns, direct)) != RINGAR_SUCCESS) return r;
     // LL flags are 32-bit step numbers: restart the numbering before it wraps.
     if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
@@ -967,13 +1097,20 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   A.count = count;
   A.per_channel = P.per_channel;
   A.chunk_elems = P.chunk_elems;
-  A.base = captured ? 0 : R->base;
-  A.counters = captured ? R->cap_counters : R->counters;
-  A.error = captured ? R->error + 1 : R->error;
+  if (noalloc) {
+    A.base = S->base;
+    A.counters = S->counters;
+    A.error = S->error;
+    A.call_id = ++S->call_id;
+  } else {
+    A.base = captured ? 0 : R->base;
+    A.counters = captured ? R->cap_counters : R->counters;
+    A.error = captured ? R->error + 1 : R->error;
+    A.call_id = ++R->call_id;
+  }
   A.abort_flag = cfg ? cfg->abort_flag : nullptr;
   uint32_t spin_ms = (cfg && cfg->spin_limit_ms) ? cfg->spin_limit_ms : env().spin_limit_ms;
-  A.spin_ticks = (uint64_t)spin_ms * (uint64_t)R->wall_khz;
-  A.call_id = ++R->call_id;
+  A.spin_ticks = (uint64_t)spin_ms * (uint64_t)wall_khz;
   A.nranks = nranks;
   A.nchannels = P.nch;
   A.lanes = P.lanes;
@@ -986,7 +1123,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   }
   A.vec_ok = vec;
   A.direct = direct ? 1 : 0;
-  A.fifo = direct ? nullptr : R->fifo[P.proto];
+  A.fifo = direct ? nullptr : noalloc ? S->fifo : R->fifo[P.proto];
 
   if (P.kind == kTreeAllReduce) {
     // the tree runs over ranks 0..n-1 (a ring order does not apply)
@@ -1012,15 +1149,16 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   } else {
     HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, captured, A, P.grid, P.block, st));
   }
-  if (!captured) R->base += P.max_steps + 1;
+  if (noalloc) S->base += P.max_steps + 1;
+  else if (!captured) R->base += P.max_steps + 1;
 
   if (env().debug) {
     fprintf(stderr,
-            "ringar: %s %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
+            "ringar: %s%s %zu bytes %s %s n=%d -> proto %s channels %d chunk %zu lanes %d "
             "depth %d%s%s grid %d x %d predicted LL %.1f LL128 %.1f Simple %.1f us\n",
-            kCollName[P.kind], count * es, kDtypeName[dtype], kOpName[op], nranks, kProtoName[P.proto], P.nch,
-            P.chunk_bytes, P.lanes, P.depth, small ? " small" : "", direct ? " direct" : "", P.grid, P.block,
-            P.times[0], P.times[1], P.times[2]);
+            kCollName[P.kind], noalloc ? " (no alloc)" : "", count * es, kDtypeName[dtype], kOpName[op], nranks,
+            kProtoName[P.proto], P.nch, P.chunk_bytes, P.lanes, P.depth, small ? " small" : "",
+            direct ? " direct" : "", P.grid, P.block, P.times[0], P.times[1], P.times[2]);
   }
   return RINGAR_SUCCESS;
 }
@@ -1031,6 +1169,14 @@ ringar_result_t ringar_allreduce_ex(void* const* sendbuffs, void* const* recvbuf
                                     const ringar_config_t* cfg) {
   return run_collective(kAllReduce, sendbuffs, recvbuffs, count, dtype, op, nranks, nchannels, proto,
                         stream, cfg);
+}
+
+ringar_result_t ringar_allreduce_noalloc(void* const* sendbuffs, void* const* recvbuffs, size_t count,
+                                         ringar_dtype_t dtype, ringar_op_t op, int nranks, int nchannels,
+                                         ringar_proto_t proto, ringar_stream_t stream,
+                                         const ringar_config_t* cfg) {
+  return run_collective(kAllReduce, sendbuffs, recvbuffs, count, dtype, op, nranks, nchannels, proto, stream,
+                        cfg, true);
 }
 
 ringar_result_t ringar_reduce_scatter_ex(void* const* sendbuffs, void* const* recvbuffs, size_t recvcount,
@@ -1106,6 +1252,17 @@ ringar_result_t ringar_get_async_error(ringar_stream_t stream) {
       HIP_TRY(launch_fill(R.error + 1, 1, 0, st));
       HIP_TRY(hipStreamSynchronize(st));
       return code_of(word[1]);
+    }
+  }
+  // the device's allocation-free calls (whatever stream they ran on)
+  if (dev >= 0 && dev < kMaxDevices && g_noalloc[dev].ready) {
+    NoAllocState& S = g_noalloc[dev];
+    uint64_t word = 0;
+    HIP_TRY(hipMemcpy(&word, S.error, 8, hipMemcpyDeviceToHost));
+    const uint64_t call = word >> 8;
+    if (call > S.reported_call) {
+      S.reported_call = call;
+      return code_of(word);
     }
   }
   return RINGAR_SUCCESS;
