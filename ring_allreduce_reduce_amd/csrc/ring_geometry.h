@@ -32,6 +32,9 @@ constexpr int kMaxSteps = 8;
 constexpr int kMinSteps = 2;
 constexpr int kMaxSlicesPerPart = kMaxSteps / 2;
 constexpr uint32_t kLaneGranBytes = 1024; // lane parts start on 1 KiB boundaries
+// LL128 lane parts: multiples of 8 lines of 120 data bytes, so that a part
+// ends on a whole line (960 bytes, a multiple of 16 and of every element size)
+constexpr uint32_t kLL128LaneGranBytes = 960;
 constexpr uint32_t kSmallSliceBytes = 1024; // lane parts of the small-slice form (64 x 16 B)
 
 // FIFO slot geometry per protocol.
@@ -42,13 +45,13 @@ constexpr uint32_t kLL128SlotLines = 256;                  // 128-byte lines per
 constexpr uint32_t kLL128SlotBytes = kLL128SlotLines * 128;// FIFO bytes per slot
 
 // Groups the slices stream without per-lane conditions (a one-input
-// primitive; two inputs take half): Simple, kUnroll 16-byte packets per
-// lane of a 64-lane wavefront; LL128, kLL128WholePackets packets per lane,
-// 8 lanes per 128-byte line.  The plan sizes lane parts by them.
+// primitive; two inputs take less): Simple, kUnroll 16-byte packets per
+// lane of a 64-lane wavefront (the plan sizes Simple lane parts by it);
+// LL128, kLL128WholeRows rows of 8 lines (one 16-byte packet per lane and
+// row).
 constexpr int kUnroll = 8;
 constexpr uint32_t kSimpleGroupBytes = 64u * kUnroll * 16u;                 // 8 KiB
-constexpr int kLL128WholePackets = 4;
-constexpr uint32_t kLL128GroupDataBytes = 8u * kLL128WholePackets * 120u;  // 32 lines
+constexpr int kLL128WholeRows = 8;
 
 enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
 // Launch kinds: the ring AllReduce and its halves (the public collective
@@ -101,8 +104,9 @@ RA_HD int stage_chunk(int i, int s, int nranks) { return (i - 1 - s + 2 * nranks
 
 // Lane part size of a loop whose chunks hold `cur` elements: the chunk size
 // split over the lanes, rounded up to whole 1 KiB units.
-RA_HD uint64_t lane_part(uint64_t cur, int lanes, uint32_t esize) {
-  return align_up(div_up(cur, (uint64_t)lanes), kLaneGranBytes / esize);
+RA_HD uint32_t lane_gran_bytes(int proto) { return proto == kLL128 ? kLL128LaneGranBytes : kLaneGranBytes; }
+RA_HD uint64_t lane_part(uint64_t cur, int lanes, uint32_t esize, int proto) {
+  return align_up(div_up(cur, (uint64_t)lanes), lane_gran_bytes(proto) / esize);
 }
 
 // Lane l's part of a chunk of `clen` elements (clen <= the loop's chunk

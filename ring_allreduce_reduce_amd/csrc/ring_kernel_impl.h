@@ -407,6 +407,7 @@ template <int F> __device__ __forceinline__ void publish_tails(Lane& L) {
 }
 
 // kUnroll (ring_geometry.h): 16-byte packets per lane in flight per source
+constexpr int kTwoInputUnroll = kUnroll / 2;
 
 // Result of one packet: the local operand b folded with what was received
 // from input 0 (a) and then input 1 (a2), each hop as op(received, local);
@@ -443,10 +444,10 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
-  // three sources in flight (a tree vertex with two children) or the
-  // division of an average take half the unroll, so that the kernel keeps
-  // the ring's register budget (occupancy 4)
-  constexpr int U = (F & (kRecv2 | kPost)) ? kUnroll / 2 : kUnroll;
+  // three sources in flight (a tree vertex with two children) take a
+  // smaller unroll and the division of an average half of it, so that the
+  // kernel keeps the ring's register budget (occupancy 4)
+  constexpr int U = (F & kPost) ? kUnroll / 2 : (F & kRecv2) ? kTwoInputUnroll : kUnroll;
   // Whole groups of 64U packets: every lane in range, so the loads carry no
   // condition and all of a group's loads are issued before its first store.
   // (A per-lane condition turns each load into its own branch, and the
@@ -660,81 +661,108 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
 }
 
 // --- LL128: 128-byte lines, 120 data bytes + 8-byte flag -------------------
-// A batch is up to kLL128Batch lines with one flag round trip: lane t watches
-// (and publishes) the flags of lines b0 + t and b0 + 64 + t.  The data moves
-// in groups of 4 packets per lane; packet u of a lane covers line
-// b0 + 8u + lane/8, 16-byte column lane%8 (column 7 carries 8 data bytes and
-// the flag).
-constexpr uint32_t kLL128Batch = 128;
-constexpr int kLL128Group = 4;
+// Every line carries its flag (the step number) in bytes 120..127.  gfx950
+// does not promise that a 128-byte line stored by 8 lanes becomes visible at
+// once (the pages rely on NVLink for that), so visibility is ordered per
+// batch instead: the producer stores the batch's data (whole lines with
+// their flags in one full-line store), waits until those stores have
+// completed, and only then stores the flag of the batch's last line; the
+// consumer waits for that one flag, which orders every line of the batch,
+// and then reads the data.  A batch is one FIFO slice (up to a slot of 256
+// lines).  Data moves in rows of 8 lines, one 16-byte packet per lane: row r
+// covers lines 8r .. 8r + 7, lane l takes line 8r + l / 8, column l % 8
+// (columns 0..6: data bytes 16c .. 16c + 15; column 7 holds data bytes
+// 112..119 and the flag).
+constexpr uint32_t kLL128Batch = kLL128SlotLines;
+constexpr int kLL128FlagsPerLane = (int)(kLL128Batch / 64);
 
-// User-side packets of the group at line b0 + g0 of the batch at line b0 (nl
-// lines): loads the
-// whole packets into vb and returns the mask of packets that end inside
-// their column (those go element-wise).
-template <class E, int F>
-__device__ __forceinline__ uint32_t ll128_user_group(rsrc_t r, uint32_t nbytes, uint32_t b0, uint32_t nl,
-                                                     uint32_t g0, int lane, bool vec,
-                                                     u32x4 (&vb)[kLL128Group]) {
-  const int col = lane & 7;
-  const uint32_t psize = col == 7 ? 8u : 16u;
-  const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;
-  uint32_t part = 0;
-#pragma unroll
-  for (int v = 0; v < kLL128Group; v++) {
-    const uint32_t line = b0 + g0 + 8 * v + (lane >> 3);
-    const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
-    const bool live = line < b0 + nl && valid > 0;
-    const bool full = live && vec && (uint32_t)valid >= psize;
-    if (live && !full) part |= 1u << v;
-    vb[v] = u32x4{0u, 0u, 0u, 0u};
-    if ((F & kSrc) && full) vb[v] = col == 7 ? ld8<kNT>(r, line * 120 + 112) : ld16<kNT>(r, line * 120 + coff);
-  }
-  return part;
-}
-
-// Whole lines (all 120 data bytes inside the part, 16-byte aligned user
-// buffers): every lane moves one 16-byte packet per line with one load and
-// one store width.  Column 7 takes the line's last 16 data bytes (104..119)
-// instead of its 8, so it shares bytes 104..111 with column 6; both lanes
-// compute them from the same inputs and store the same values, and all of
-// a group's loads complete before any of its stores, so this holds in place
-// too.  The flag bytes (120..127) are never touched here.  Loads and stores
-// carry no per-lane condition, so all of a group's loads are in flight
-// together and a group does not wait for the previous group's stores.
-
-// Packets per lane per whole group (8 lines each); half with two inputs, to
-// stay within the register budget (occupancy 3).
+// Rows of whole lines (all 120 data bytes inside the part, 16-byte aligned
+// user buffers): every lane moves one 16-byte packet per row with one load
+// and one store width.  Column 7 reads the line's last 16 data bytes
+// (104..119) instead of its 8, so it shares bytes 104..111 with column 6;
+// both lanes compute them from the same inputs and store the same values to
+// the user buffer, and all of an iteration's loads complete before any of
+// its stores, so this holds in place too.  Towards the FIFO, column 7 stores
+// bytes 112..127 of the line: its 8 data bytes and the line's flag, so each
+// line leaves in one full 128-byte store.  (The batch's last line never
+// goes this way: its flag is stored only once all of the batch's data stores
+// have completed, and that one flag is what a consumer waits for.)
+// The resources end at the last whole line (FIFO: lim lines of 128 bytes,
+// user: lim lines of 120), so the lanes of a row past it read zeros and their
+// stores are dropped by the range check: no per-lane condition anywhere, and
+// all of an iteration's loads are in flight together.
 template <int F>
-constexpr int ll128_whole_packets() { return (F & kRecv2) ? kLL128WholePackets / 2 : kLL128WholePackets; }
+constexpr int ll128_rows() { return (F & kRecv2) ? kLL128WholeRows / 2 : kLL128WholeRows; }
 
-// Lines [line0, line0 + 8G) through resources that end at the last whole
-// line of the group run (FIFO: lim lines of 128 bytes, user: lim lines of
-// 120): a lane past it reads zeros and its stores are dropped by the range
-// check, with no per-lane condition.
 template <class E, int OP, int F, int NO>
-__device__ __forceinline__ void ll128_whole_group(const rsrc_t (&win)[2], const rsrc_t (&wout)[2], rsrc_t wsrc,
-                                                  rsrc_t wdst, uint32_t line0, int lane, int nranks) {
-  constexpr int G = ll128_whole_packets<F>();
-  const uint32_t coff = (lane & 7) == 7 ? 104u : (uint32_t)(lane & 7) * 16u;
-  u32x4 va[G], va2[G], vb[G];
+__device__ __forceinline__ void ll128_rows_iter(const rsrc_t (&win)[2], const rsrc_t (&wout)[2], rsrc_t wsrc,
+                                                rsrc_t wdst, uint32_t line0, int lane, int nranks, uint64_t flag) {
+  constexpr int R = ll128_rows<F>();
+  const bool c7 = (lane & 7) == 7;
+  const uint32_t coff = c7 ? 104u : (uint32_t)(lane & 7) * 16u;
+  const uint32_t soff = c7 ? 112u : coff;   // FIFO store offset in the line
+  const uint32_t lrow = (uint32_t)(lane >> 3);
+  u32x4 va[R], va2[R], vb[R];
 #pragma unroll
-  for (int v = 0; v < G; v++) {
-    const uint32_t line = line0 + 8 * v + (lane >> 3);
-    if (F & kRecv) va[v] = ld16<kSC1>(win[0], line * 128 + coff);
-    if (F & kRecv2) va2[v] = ld16<kSC1>(win[1], line * 128 + coff);
-    if (F & kSrc) vb[v] = ld16<kNT>(wsrc, line * 120 + coff);
+  for (int u = 0; u < R; u++) {
+    const uint32_t line = line0 + 8 * u + lrow;
+    if (F & kRecv) va[u] = ld16<kSC1>(win[0], line * 128 + coff);
+    if (F & kRecv2) va2[u] = ld16<kSC1>(win[1], line * 128 + coff);
+    if (F & kSrc) vb[u] = ld16<kNT>(wsrc, line * 120 + coff);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int v = 0; v < G; v++) {
-    const uint32_t line = line0 + 8 * v + (lane >> 3);
-    const u32x4 r = combine<E, OP, F>(va[v], va2[v], vb[v], nranks);
+  for (int u = 0; u < R; u++) {
+    const uint32_t line = line0 + 8 * u + lrow;
+    const u32x4 r = combine<E, OP, F>(va[u], va2[u], vb[u], nranks);
     if (F & kSend) {
+      const u32x4 w = c7 ? u32x4{r.z, r.w, (uint32_t)flag, (uint32_t)(flag >> 32)} : r;
 #pragma unroll
-      for (int o = 0; o < NO; o++) st16<kSC1>(r, wout[o], line * 128 + coff);
+      for (int o = 0; o < NO; o++) st16<kSC1>(w, wout[o], line * 128 + soff);
     }
     if (F & kDst) st16<kNT>(r, wdst, line * 120 + coff);
+  }
+}
+
+// Lines [l0, l1) packet by packet: the batch's last line, and every line
+// when a user buffer is not 16-byte aligned (then element-wise on the user
+// side, as is a packet that the part ends inside).  Column 7 moves its 8 data
+// bytes only; the flags of these lines are stored after the batch's data.
+template <class E, int OP, int F, int NO>
+__device__ __forceinline__ void ll128_packets(const rsrc_t (&rin)[2], const rsrc_t (&rout)[2], rsrc_t rsrc_,
+                                              rsrc_t rdst, uint32_t nbytes, int vec, uint32_t l0, uint32_t l1,
+                                              int lane, int nranks) {
+#pragma unroll 1
+  for (uint32_t p = l0 * 8 + (uint32_t)lane; p < l1 * 8; p += 64) {
+    const uint32_t line = p >> 3, col = p & 7;
+    const uint32_t uoff = line * 120 + col * 16;
+    if (uoff >= nbytes) continue;
+    const uint32_t psize = col == 7 ? 8u : 16u;
+    const uint32_t nb = min(psize, nbytes - uoff);
+    const bool whole = vec && nb == psize;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u}, x2 = x, y = x;
+    if (F & kRecv) x = col == 7 ? ld8<kSC1>(rin[0], line * 128 + 112) : ld16<kSC1>(rin[0], line * 128 + col * 16);
+    if (F & kRecv2) x2 = col == 7 ? ld8<kSC1>(rin[1], line * 128 + 112) : ld16<kSC1>(rin[1], line * 128 + col * 16);
+    if (F & kSrc) {
+      if (whole) y = col == 7 ? ld8<kNT>(rsrc_, uoff) : ld16<kNT>(rsrc_, uoff);
+      else y = ld_part<E, kNT>(rsrc_, uoff, nb);
+    }
+    const u32x4 r = combine<E, OP, F>(x, x2, y, nranks);
+    if (F & kSend) {
+#pragma unroll
+      for (int o = 0; o < NO; o++) {
+        if (col == 7) st8<kSC1>(r, rout[o], line * 128 + 112);
+        else st16<kSC1>(r, rout[o], line * 128 + col * 16);
+      }
+    }
+    if (F & kDst) {
+      if (whole) {
+        if (col == 7) st8<kNT>(r, rdst, uoff);
+        else st16<kNT>(r, rdst, uoff);
+      } else {
+        st_part<E, kNT>(r, rdst, uoff, nb);
+      }
+    }
   }
 }
 
@@ -745,142 +773,69 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
   if (!wait_outputs<F>(L)) return false;
   constexpr int NI = (F & kRecv2) ? 2 : 1;   // inputs
   constexpr int NO = (F & kSend2) ? 2 : 1;   // outputs
+  constexpr uint32_t RL = 8 * ll128_rows<F>();   // lines per iteration of whole rows
   const uint64_t fin = a.base + L.rstep + 1;
   const uint64_t fout = a.base + L.sstep + 1;
   const uint64_t rslot = (L.rstep & (a.depth - 1)) * kLL128SlotBytes;
   const uint64_t sslot = (L.sstep & (a.depth - 1)) * kLL128SlotBytes;
   char* sin[2] = {L.in[0].fifo + rslot, L.in[NI - 1].fifo + rslot};
   char* sout[2] = {L.out[0].fifo + sslot, L.out[NO - 1].fifo + sslot};
-  rsrc_t rin[2] = {make_rsrc(sin[0], kLL128SlotBytes), make_rsrc(sin[1], kLL128SlotBytes)};
-  rsrc_t rout[2] = {make_rsrc(sout[0], kLL128SlotBytes), make_rsrc(sout[1], kLL128SlotBytes)};
-  rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
-  rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
-  const bool vec = a.vec_ok;
+  const rsrc_t rin[2] = {make_rsrc(sin[0], kLL128SlotBytes), make_rsrc(sin[1], kLL128SlotBytes)};
+  const rsrc_t rout[2] = {make_rsrc(sout[0], kLL128SlotBytes), make_rsrc(sout[1], kLL128SlotBytes)};
+  const char* src = L.src + es0 * sizeof(typename E::T);
+  char* dst = L.dst + ed0 * sizeof(typename E::T);
+  const rsrc_t rsrc_ = make_rsrc(src, nbytes);
+  const rsrc_t rdst = make_rsrc(dst, nbytes);
   const uint32_t nlines = (nbytes + 119) / 120;
+  // lines with all 120 data bytes in the part go in whole rows
+  const uint32_t whole = a.vec_ok ? nbytes / 120 : 0;
   if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, nlines * 128u);   // slot bytes read (see finish_input)
-  const int col = L.lane & 7;
-  const uint32_t psize = col == 7 ? 8u : 16u;
-  const uint32_t coff = col == 7 ? 112u : (uint32_t)col * 16u;   // data bytes of the column
-  const uint32_t whole_lines = vec ? nbytes / 120 : 0;   // lines with all 120 bytes in the part
   for (uint32_t b0 = 0; b0 < nlines; b0 += kLL128Batch) {
-    const uint32_t nl = min(kLL128Batch, nlines - b0);
-    // lines [0, nw) of the batch go in whole groups of WL lines, the rest
-    // packet by packet.  Whole lines left after the full groups take a last,
-    // partly masked group when they fill at least half of one; fewer go
-    // packet by packet, with the ragged last line, in the same pass.
-    constexpr uint32_t WL = 8 * ll128_whole_packets<F>();
-    const uint32_t wl = whole_lines > b0 ? min(nl, whole_lines - b0) : 0;
-    const uint32_t nw = wl % WL >= WL / 2 ? wl : wl / WL * WL;
-    // the first packet-by-packet group's user data is requested before the
-    // flags are polled when there is no whole group
-    u32x4 vb[kLL128Group];
-    uint32_t part = 0;
-    if (nw == 0) part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, 0, L.lane, vec, vb);
+    const uint32_t b1 = min(nlines, b0 + kLL128Batch);
     if (F & kRecv) {
-      // flags first, then data: lane t watches lines b0 + t and b0 + 64 + t
-      // of every input
-      const bool w0 = L.lane < (int)nl, w1 = 64 + L.lane < (int)nl;
-      const uint64_t* fp[NI][2];
-      uint64_t f[NI][2];
+      // Flag first, then data.  The producer stores the flag of the batch's
+      // last line only after all of the batch's data stores have completed,
+      // so once seen it orders every line of the batch: the wavefront waits
+      // for that one flag (one line per poll for the whole wavefront) and
+      // then reads the data.
+      const uint64_t* lp[NI];
 #pragma unroll
-      for (int i = 0; i < NI; i++) {
-        fp[i][0] = (const uint64_t*)(sin[i] + (size_t)(b0 + L.lane) * 128 + 120);
-        fp[i][1] = (const uint64_t*)(sin[i] + (size_t)(b0 + 64 + L.lane) * 128 + 120);
-        f[i][0] = w0 ? ld_relaxed(fp[i][0]) : fin;
-        f[i][1] = w1 ? ld_relaxed(fp[i][1]) : fin;
-      }
+      for (int i = 0; i < NI; i++) lp[i] = (const uint64_t*)(sin[i] + (size_t)(b1 - 1) * 128 + 120);
       L.w.start();
       while (true) {
         bool ok = true;
 #pragma unroll
-        for (int i = 0; i < NI; i++) ok = ok && f[i][0] == fin && f[i][1] == fin;
+        for (int i = 0; i < NI; i++) ok = ok && ld_relaxed(lp[i]) == fin;
         if (__all(ok)) break;
         if (!L.w.idle()) return false;
-#pragma unroll
-        for (int i = 0; i < NI; i++) {
-          if (f[i][0] != fin) f[i][0] = ld_relaxed(fp[i][0]);
-          if (f[i][1] != fin) f[i][1] = ld_relaxed(fp[i][1]);
-        }
       }
       compiler_fence();
     }
-    if (nw > 0) {
-      const uint32_t lim = b0 + nw;
-      const rsrc_t win[2] = {make_rsrc(sin[0], lim * 128), make_rsrc(sin[1], lim * 128)};
-      const rsrc_t wout[2] = {make_rsrc(sout[0], lim * 128), make_rsrc(sout[1], lim * 128)};
-      const rsrc_t wsrc = make_rsrc(L.src + es0 * sizeof(typename E::T), lim * 120);
-      const rsrc_t wdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), lim * 120);
-      for (uint32_t g0 = 0; g0 < nw; g0 += WL)
-        ll128_whole_group<E, OP, F, NO>(win, wout, wsrc, wdst, b0 + g0, L.lane, a.nranks);
+    // whole lines of the batch but its last: [b0, bw) go by rows
+    const uint32_t bw = min(b1 - 1, max(b0, whole));
+    if (bw > b0) {
+      const rsrc_t win[2] = {make_rsrc(sin[0], bw * 128), make_rsrc(sin[1], bw * 128)};
+      const rsrc_t wout[2] = {make_rsrc(sout[0], bw * 128), make_rsrc(sout[1], bw * 128)};
+      const rsrc_t wsrc = make_rsrc(src, bw * 120);
+      const rsrc_t wdst = make_rsrc(dst, bw * 120);
+      for (uint32_t l0 = b0; l0 < bw; l0 += RL)
+        ll128_rows_iter<E, OP, F, NO>(win, wout, wsrc, wdst, l0, L.lane, a.nranks, fout);
     }
-    if (nw > 0 && nw < nl) part = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, nw, L.lane, vec, vb);
-#pragma unroll 1
-    for (uint32_t g0 = nw; g0 < nl; g0 += kLL128Group * 8) {
-      u32x4 va[kLL128Group], va2[kLL128Group];
-#pragma unroll
-      for (int v = 0; v < kLL128Group; v++) {
-        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
-        va[v] = u32x4{0u, 0u, 0u, 0u};
-        va2[v] = va[v];
-        if ((F & kRecv) && line < b0 + nl) va[v] = ld16<kSC1>(rin[0], line * 128 + col * 16);
-        if ((F & kRecv2) && line < b0 + nl) va2[v] = ld16<kSC1>(rin[1], line * 128 + col * 16);
-      }
-      // the next group's user data is requested while this group computes
-      u32x4 vbn[kLL128Group] = {};
-      uint32_t partn = 0;
-      if (g0 + kLL128Group * 8 < nl)
-        partn = ll128_user_group<E, F>(rsrc_, nbytes, b0, nl, g0 + kLL128Group * 8, L.lane, vec, vbn);
-#pragma unroll
-      for (int v = 0; v < kLL128Group; v++) va[v] = combine<E, OP, F>(va[v], va2[v], vb[v], a.nranks);
-      // Packets that end inside their column: element-wise on the user side.
-#pragma unroll 1
-      for (uint32_t bits = part; bits; bits &= bits - 1) {
-        const int v = __builtin_ctz(bits);
-        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
-        const uint32_t uoff = line * 120 + coff;
-        const uint32_t nb = min(psize, nbytes - uoff);
-        u32x4 x = u32x4{0u, 0u, 0u, 0u}, x2 = x, y = x;
-        if (F & kRecv) x = ld16<kSC1>(rin[0], line * 128 + col * 16);
-        if (F & kRecv2) x2 = ld16<kSC1>(rin[1], line * 128 + col * 16);
-        if (F & kSrc) y = ld_part<E, kNT>(rsrc_, uoff, nb);
-        const u32x4 r = combine<E, OP, F>(x, x2, y, a.nranks);
-        if (F & kSend) {
-#pragma unroll
-          for (int o = 0; o < NO; o++) {
-            if (col == 7) st8<kSC1>(r, rout[o], line * 128 + 112);
-            else st16<kSC1>(r, rout[o], line * 128 + col * 16);
-          }
-        }
-        if (F & kDst) st_part<E, kNT>(r, rdst, uoff, nb);
-      }
-#pragma unroll
-      for (int v = 0; v < kLL128Group; v++) {
-        const uint32_t line = b0 + g0 + 8 * v + (L.lane >> 3);
-        const int32_t valid = (int32_t)nbytes - (int32_t)(line * 120 + coff);
-        if (line >= b0 + nl || valid <= 0 || (part >> v) & 1u) continue;
-        if (F & kSend) {
-#pragma unroll
-          for (int o = 0; o < NO; o++) {
-            if (col == 7) st8<kSC1>(va[v], rout[o], line * 128 + 112);
-            else st16<kSC1>(va[v], rout[o], line * 128 + col * 16);
-          }
-        }
-        if (F & kDst) {
-          if (col == 7) st8<kNT>(va[v], rdst, line * 120 + 112);
-          else st16<kNT>(va[v], rdst, line * 120 + coff);
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < kLL128Group; v++) vb[v] = vbn[v];
-      part = partn;
-    }
+    // the rest of the batch (its last line, and every line of unaligned
+    // buffers): packet by packet
+    ll128_packets<E, OP, F, NO>(rin, rout, rsrc_, rdst, nbytes, a.vec_ok, bw, b1, L.lane, a.nranks);
     if (F & kSend) {
-      wait_mem();   // all data of the batch is visible before any of its flags
+      // all data of the batch is visible before the flags written now, those
+      // of the lines that went packet by packet: the batch's last line
+      // among them (the whole rows wrote their lines' flags with the data)
+      wait_mem();
 #pragma unroll
-      for (int o = 0; o < NO; o++) {
-        if (L.lane < (int)nl) st_relaxed((uint64_t*)(sout[o] + (size_t)(b0 + L.lane) * 128 + 120), fout);
-        if (64 + L.lane < (int)nl) st_relaxed((uint64_t*)(sout[o] + (size_t)(b0 + 64 + L.lane) * 128 + 120), fout);
-      }
+      for (int o = 0; o < NO; o++)
+#pragma unroll
+        for (int j = 0; j < kLL128FlagsPerLane; j++) {
+          const uint32_t line = bw + 64 * j + L.lane;
+          if (line < b1) st_relaxed((uint64_t*)(sout[o] + (size_t)line * 128 + 120), fout);
+        }
     }
   }
   if (F & kSend) L.sstep++;
@@ -1132,7 +1087,7 @@ __device__ __forceinline__ bool primitive(Lane& L, uint64_t es0, uint64_t ed0, u
 template <class E, int OP, int PROTO, bool SMALL, int COLL>
 __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps lane-derived values scalar
   const int group = blockIdx.x / a.nranks;     // (channel, lane block)
   const int ri = blockIdx.x % a.nranks;        // ring index
   const int lane_blocks = a.lanes / a.lanes_per_block;
@@ -1167,7 +1122,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
       for (uint64_t off = 0; off < len; off += loop) {
         const uint64_t rem = len - off;
         const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
-        const uint64_t part = lane_part(cur, a.lanes, es);
+        const uint64_t part = lane_part(cur, a.lanes, es, PROTO);
         for (int s = 0; s <= 2 * n - 2; s++) {
           const int k = stage_chunk(ri, s, n);
           uint64_t ks, kl, ls, ll;
@@ -1191,7 +1146,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
     for (uint64_t off = 0; off < len; off += loop) {
       const uint64_t rem = len - off;
       const uint64_t cur = loop_chunk(len, off, n, a.chunk_elems, es);
-      const uint64_t part = lane_part(cur, a.lanes, es);
+      const uint64_t part = lane_part(cur, a.lanes, es, PROTO);
       for (int s = 0; s <= 2 * n - 2; s++) {
         const int k = stage_chunk(ri, s, n);
         uint64_t ks, kl, ls, ll;
@@ -1212,7 +1167,7 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
     // of every block, and the block of rank q starts at q * a.count.
     for (uint64_t off = 0; off < len; off += a.chunk_elems) {
       const uint64_t cur = min_u64(a.chunk_elems, len - off);
-      const uint64_t part = lane_part(cur, a.lanes, es);
+      const uint64_t part = lane_part(cur, a.lanes, es, PROTO);
       uint64_t ls, ll;
       lane_bounds(cur, part, l, &ls, &ll);
       const uint64_t pos = lo + off + ls;           // element offset inside a block
@@ -1282,7 +1237,7 @@ __device__ __forceinline__ bool tree_chunks(Lane& L, uint64_t lo, uint64_t len, 
   const KernelArgs& a = *L.a;
   for (uint64_t off = 0; off < len; off += a.chunk_elems) {
     const uint64_t cur = min_u64(a.chunk_elems, len - off);
-    const uint64_t part = lane_part(cur, a.lanes, es);
+    const uint64_t part = lane_part(cur, a.lanes, es, PROTO);
     uint64_t ls, ll;
     lane_bounds(cur, part, l, &ls, &ll);
     const uint64_t e0 = lo + off + ls;
@@ -1300,7 +1255,7 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   const KernelArgs& a = ta.k;
   const int n = a.nranks;
   const int R = tree_roles(n);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps lane-derived values scalar
   const int role = blockIdx.x % R;
   const int group = blockIdx.x / R;
   const int lane_blocks = a.lanes / a.lanes_per_block;

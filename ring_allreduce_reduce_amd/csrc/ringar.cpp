@@ -340,6 +340,12 @@ constexpr uint64_t kTargetWaves = 4096;
 // 256 MB Infinity Cache (64 MiB per rank over 16 channels: 436 us at depth
 // 8 with 512 MiB in flight, 432 us at depth 2 with 128 MiB).
 constexpr uint64_t kFifoBudgetBytes = 128ull << 20;
+// LL128 runs fewer, longer lanes (below) and gains from the deeper FIFO up to
+// twice that footprint (bf16, 8 lanes, 32 MiB per rank: depth 4 234 us, 136
+// MiB in flight; 16 MiB depth 8 138 us against depth 4 137 us).
+constexpr uint64_t kLL128FifoBudgetBytes = 256ull << 20;
+constexpr uint64_t kLL128LaneBytes = 8192;
+constexpr int kLL128MaxAutoLanes = 8;
 
 // FIFO bytes that carry `bytes` of data in one slot of the protocol.
 uint64_t fifo_bytes_for(int proto, uint64_t bytes) {
@@ -441,12 +447,12 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
           ? P.chunk_elems
           : align_up(div_up(std::max<uint64_t>(1, P.per_channel), (uint64_t)n), align_elems((uint32_t)es));
   const uint64_t slot = slot_elems(P.proto, (uint32_t)es);
-  auto slices_for = [&](int L) { return div_up(lane_part(first_chunk, L, (uint32_t)es), slot); };
+  auto slices_for = [&](int L) { return div_up(lane_part(first_chunk, L, (uint32_t)es, P.proto), slot); };
   // wavefronts per lane: one per rank on the ring, 2n - 1 roles on the tree
   const uint64_t waves_per_lane = (uint64_t)(tree ? tree_roles(n) : n) * P.nch;
   const bool forced_lanes = lanes != 0;
   if (!forced_lanes) {
-    const uint64_t want = std::max<uint64_t>(1, div_up(first_chunk * es, kLaneGranBytes));
+    const uint64_t want = std::max<uint64_t>(1, div_up(first_chunk * es, lane_gran_bytes(P.proto)));
     lanes = 1;
     while (lanes < (int)std::min<uint64_t>(want, kMaxLanes)) lanes *= 2;
     const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
@@ -460,7 +466,9 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // short trailing slice costs a whole flag round trip (bf16 LL128 at 64 MiB
   // per rank: 8 lanes of 32 KiB parts need a 30 KiB and a 2 KiB slice each,
   // 12 lanes need one).
-  if (!forced_lanes && lanes >= 4 && slices_for(lanes) > 1) {
+  // LL128 on the ring takes its own rule below.
+  const bool ll128_ring = P.proto == kLL128 && !tree;
+  if (!forced_lanes && !ll128_ring && lanes >= 4 && slices_for(lanes) > 1) {
     const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
     for (int L = lanes + 4; L <= kMaxLanes && waves_per_lane * L <= cap; L += 4)
       if (slices_for(L) < slices_for(lanes)) {
@@ -477,13 +485,25 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // lanes 95.6 -> 79.2 us; fp32 Simple 8 MiB 16 -> 4 lanes 68.1 -> 64.6 us,
   // 16 MiB 16 -> 8 lanes 118.5 -> 110.8 us.  A single lane was slower, and
   // Simple parts of the small-slice form (at most 1 KiB) keep their lanes.
-  const uint64_t group_bytes =
-      P.proto == kLL128 ? kLL128GroupDataBytes : P.proto == kSimple ? kSimpleGroupBytes : 0;
-  if (!forced_lanes && group_bytes && !tree &&
-      (P.proto != kSimple || lane_part(first_chunk, lanes, (uint32_t)es) * es > kSmallSliceBytes)) {
+  if (!forced_lanes && P.proto == kSimple && !tree &&
+      lane_part(first_chunk, lanes, (uint32_t)es, P.proto) * es > kSmallSliceBytes) {
     int whole = 1;
-    while ((uint64_t)(whole * 2) * group_bytes <= first_chunk * es) whole *= 2;
+    while ((uint64_t)(whole * 2) * kSimpleGroupBytes <= first_chunk * es) whole *= 2;
     if (whole >= 2 && whole < lanes) lanes = whole;
+  }
+  // LL128 on the ring (and its halves): a lane per 8 KiB of chunk, a power
+  // of two between 2 and 8 (then more only if a part would need more than
+  // half the FIFO).  Longer parts stream several 64-line row iterations per
+  // flag round trip; more lanes than that only crowd the memory system.
+  // Measured on MI355X, bf16 sum, n = 8, 32 channels, lanes / depth: 1 MiB
+  // per rank 2 lanes 54 us against 8 lanes 64 us; 2 MiB 57 against 84 (16
+  // lanes); 16 MiB 4 lanes 132 us; 32 MiB 8 lanes 234 against 256 (16); 64
+  // MiB 8 lanes 456 against 468 (4) and 479 (16); fp32 at 128 MiB 8 lanes
+  // 927 against 972 (16) and 939 (4).
+  if (!forced_lanes && ll128_ring) {
+    lanes = 2;
+    while (lanes < kLL128MaxAutoLanes && (uint64_t)(lanes * 2) * kLL128LaneBytes <= first_chunk * es) lanes *= 2;
+    while (lanes < kMaxLanes && slices_for(lanes) > kMaxSlicesPerPart) lanes *= 2;
   }
   if (slices_for(lanes) > kMaxSlicesPerPart)
     return forced_lanes ? RINGAR_ERR_INVALID_USAGE : RINGAR_ERR_INVALID_ARGUMENT;
@@ -493,20 +513,21 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // kFifoBudgetBytes, but always at least twice the slots of a part.
   const uint64_t waves = waves_per_lane * lanes;
   const uint64_t step_bytes =
-      fifo_bytes_for(P.proto, std::min<uint64_t>(lane_part(first_chunk, lanes, (uint32_t)es), slot) * es);
+      fifo_bytes_for(P.proto, std::min<uint64_t>(lane_part(first_chunk, lanes, (uint32_t)es, P.proto), slot) * es);
   if (depth) {
     if ((uint64_t)slices_for(lanes) > (uint64_t)depth / 2) return RINGAR_ERR_INVALID_USAGE;
     P.depth = depth;
   } else {
     P.depth = kMaxSteps;
-    while (P.depth > kMinSteps && waves * P.depth * step_bytes > kFifoBudgetBytes &&
+    const uint64_t budget = P.proto == kLL128 ? kLL128FifoBudgetBytes : kFifoBudgetBytes;
+    while (P.depth > kMinSteps && waves * P.depth * step_bytes > budget &&
            (uint64_t)slices_for(lanes) <= (uint64_t)P.depth / 4)
       P.depth /= 2;
   }
   // Lane parts of at most 1 KiB (one 16-byte packet per lane and step) run
   // the straight-line form of LL and Simple when the buffers are aligned.
   P.direct = cfg && cfg->direct && P.kind == kAllReduce && P.proto == kSimple && n > 1;
-  P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es) * es <= kSmallSliceBytes &&
+  P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es, P.proto) * es <= kSmallSliceBytes &&
             !(cfg && cfg->force_general) && !P.direct;
   P.lanes_per_block = std::min(lanes, 4);
   P.block = 64 * P.lanes_per_block;

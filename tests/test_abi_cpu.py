@@ -182,7 +182,8 @@ def test_parts_never_exceed_half_the_fifo():
                 per_channel = -(-count // 16) * 4
                 first = chunk if per_channel >= 8 * chunk else -(-(-(-per_channel // 8)) // 16) * 16
                 part = -(-first // plan.lanes)
-                part = -(-part // 1024) * 1024
+                gran = 960 if proto == "LL128" else 1024     # lane parts: 8 whole lines under LL128
+                part = -(-part // gran) * gran
                 assert plan.fifo_depth in (2, 4, 8)
                 assert -(-part // slot) <= plan.fifo_depth // 2, (proto, chunk, plan.lanes, plan.fifo_depth)
     # forcing too few lanes for the chunk is refused
@@ -198,9 +199,8 @@ def test_parts_never_exceed_half_the_fifo():
 
 def test_fifo_depth_follows_the_footprint_budget():
     # the deepest of 8, 4, 2 slots whose in-flight footprint (wavefronts x
-    # depth x FIFO bytes of one step) stays within 128 MiB, unless the part
+    # depth x FIFO bytes of one step) stays within 128 MiB (LL128: 256 MiB), unless the part
     # needs more slots
-    budget = 128 << 20
     seen = set()
     for proto in SLOT_DATA:
         for count in [1 << 12, 1 << 18, 1 << 22, 1 << 24, 1 << 26]:
@@ -212,10 +212,12 @@ def test_fifo_depth_follows_the_footprint_budget():
                     first = (plan.chunk_elems if per_ch >= n * plan.chunk_elems
                              else -(-(-(-max(1, per_ch) // n)) // 4) * 4)
                     part = -(-(first * 4) // plan.lanes)
-                    part = -(-part // 1024) * 1024
+                    gran = 960 if proto == "LL128" else 1024
+                    part = -(-part // gran) * gran
                     slices = -(-part // SLOT_DATA[proto])
                     step = SLOT_FIFO[proto](min(part, SLOT_DATA[proto]))
                     d = plan.fifo_depth
+                    budget = (256 if proto == "LL128" else 128) << 20    # LL128 runs fewer, longer lanes
                     seen.add(d)
                     assert slices <= d // 2
                     if d < 8:   # it was halved: the deeper FIFO was over budget
@@ -256,7 +258,8 @@ def test_small_form_rule():
                 first = (plan.chunk_elems if per_ch >= 8 * plan.chunk_elems
                          else -(-(-(-max(1, per_ch) // 8)) // 4) * 4)
                 part = -(-(first * 4) // plan.lanes)
-                part = -(-part // 1024) * 1024
+                gran = 960 if proto == "LL128" else 1024
+                part = -(-part // gran) * gran
                 assert plan.small_slices == int(proto != "LL128" and part <= 1024), (proto, count, nch)
                 if proto != "LL128" and first * 4 <= 32 * 1024:
                     assert plan.small_slices == 1, (proto, count, nch, plan.lanes)

@@ -1,12 +1,13 @@
 """LL128 lane parts sized to reach each path of the line loop, bit-exact
-against the oracle: whole 32-line groups only, whole groups plus a partly
-masked group (at least half a group of whole lines left over), whole groups
-plus a few whole lines and a ragged line taken packet by packet, parts that
-cross the 128-line flag batch, a full 256-line slot, and parts under one
-group.  Every dtype, ring (one input) and tree (vertices with two inputs,
-where a group is 16 lines), in place and out of place: in the whole-line
-path lane 7 of a line moves data bytes 104..119 and so shares 104..111 with
-lane 6, which the in-place cases check.
+against the oracle: whole 64-line row iterations only, iterations plus a
+partly masked one, a part under one iteration, a part that is one line or
+less, a ragged last line, a full 256-line slot and parts of two slices (a
+flag round trip each).  The last line of every slice goes packet by packet
+(its flag is the one stored after the slice's data).  Every dtype, ring (one
+input) and tree (vertices with two inputs, where an iteration is 32 lines),
+in place and out of place: in the whole rows lane 7 of a line moves data
+bytes 104..119 and so shares 104..111 with lane 6, which the in-place cases
+check.
 
 With one channel and one lane, a ring part is one chunk, count / n
 elements; its bytes are chosen as 120 x lines (+ a ragged tail) rounded to
@@ -24,7 +25,8 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 # part bytes: (whole lines, ragged bytes) -> rounded up to 16-byte units
-PARTS = [(32, 0), (48, 0), (37, 0), (52, 56), (64, 40), (20, 0), (17, 104), (140, 0), (150, 72), (256, 0), (9, 8)]
+PARTS = [(64, 0), (65, 0), (128, 0), (100, 56), (63, 40), (20, 0), (17, 104), (140, 0), (192, 72), (256, 0),
+         (9, 8), (300, 24), (1, 0), (0, 40), (257, 0), (33, 0)]
 
 
 def _bits(a):

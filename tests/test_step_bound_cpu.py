@@ -15,6 +15,9 @@ import ring_allreduce_reduce_amd as ra
 from libutil import lib
 
 SLOT_DATA = {"Simple": 32768, "LL": 8192, "LL128": 30720}
+# lane parts are whole multiples of this many bytes: 1 KiB, and 8 lines of
+# 120 data bytes under LL128 (so a part ends on a whole line)
+LANE_GRAN = {"Simple": 1024, "LL": 1024, "LL128": 960}
 ES = {"int8": 1, "int32": 4, "float16": 2, "bfloat16": 2, "float32": 4, "float64": 8}
 
 
@@ -23,9 +26,9 @@ def _lib():
     lib()
 
 
-def _lane_parts(clen, cur, lanes, es):
+def _lane_parts(clen, cur, lanes, es, proto):
     part = -(-cur // lanes)
-    g = 1024 // es
+    g = LANE_GRAN[proto] // es
     part = -(-part // g) * g
     out = []
     for l in range(lanes):
@@ -45,7 +48,7 @@ def _loop_slices(rem, cur, n, lanes, es, proto):
     for k in range(n):
         ks = min(rem, k * cur)
         kl = min(cur, rem - ks) if ks < rem else 0
-        for l, ll in enumerate(_lane_parts(kl, cur, lanes, es)):
+        for l, ll in enumerate(_lane_parts(kl, cur, lanes, es, proto)):
             per_lane[l] += _slices(ll, es, proto)
     return per_lane
 
@@ -79,11 +82,11 @@ def blocked_steps(count, dtype, plan, proto, primitives_per_chunk):
         length = hi - lo
         full = length // plan.chunk_elems
         per_lane = full * np.array([_slices(ll, es, proto) for ll in
-                                    _lane_parts(plan.chunk_elems, plan.chunk_elems, plan.lanes, es)], dtype=np.int64)
+                                    _lane_parts(plan.chunk_elems, plan.chunk_elems, plan.lanes, es, proto)], dtype=np.int64)
         tail = length - full * plan.chunk_elems
         if tail:
             per_lane = per_lane + np.array([_slices(ll, es, proto) for ll in
-                                            _lane_parts(tail, tail, plan.lanes, es)], dtype=np.int64)
+                                            _lane_parts(tail, tail, plan.lanes, es, proto)], dtype=np.int64)
         worst = max(worst, int(per_lane.max()))
     return worst * primitives_per_chunk
 
