@@ -124,6 +124,14 @@ RA_HD uint64_t slot_elems(int proto, uint32_t esize) {
   return (kLL128SlotLines * 120) / esize;
 }
 
+// LL lines of a slot: packet p (16 data bytes, 4 lines) keeps its word q in
+// line (p / 64) * 256 + 64 q + p % 64, so that the 64 lanes of a wavefront,
+// one packet each, load and store 64 consecutive lines (512 contiguous bytes)
+// per instruction instead of every fourth line.
+RA_HD uint32_t ll_line_index(uint32_t p, uint32_t q) { return (p >> 6) * 256u + q * 64u + (p & 63u); }
+// Bytes of the slot prefix holding the lines of packets [0, npk).
+RA_HD uint32_t ll_prefix_bytes(uint32_t npk) { return ((npk + 63u) / 64u) * 256u * 8u; }
+
 // FIFO bytes of one slot and of one connection (kMaxSteps slots).
 RA_HD uint64_t slot_bytes(int proto) {
   if (proto == kSimple) return kSimpleSlotBytes;

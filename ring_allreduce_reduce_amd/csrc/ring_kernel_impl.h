@@ -527,7 +527,7 @@ __device__ __forceinline__ bool ll_ready(uint64_t line, uint32_t flag) {
 __device__ __forceinline__ bool ll_recv4(Waiter& w, const uint64_t* lin, uint32_t p, bool active,
                                          uint32_t flag, uint64_t (&ln)[4]) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) ln[q] = active ? ld_relaxed(lin + 4 * p + q) : ll_line(0, flag);
+  for (int q = 0; q < 4; q++) ln[q] = active ? ld_relaxed(lin + ll_line_index(p, q)) : ll_line(0, flag);
   w.start();
   while (true) {
     bool ok = ll_ready(ln[0], flag) && ll_ready(ln[1], flag) && ll_ready(ln[2], flag) &&
@@ -536,7 +536,7 @@ __device__ __forceinline__ bool ll_recv4(Waiter& w, const uint64_t* lin, uint32_
     if (!w.idle()) return false;
 #pragma unroll
     for (int q = 0; q < 4; q++)
-      if (!ll_ready(ln[q], flag)) ln[q] = ld_relaxed(lin + 4 * p + q);
+      if (!ll_ready(ln[q], flag)) ln[q] = ld_relaxed(lin + ll_line_index(p, q));
   }
 }
 
@@ -550,10 +550,10 @@ __device__ __forceinline__ void ll_store(rsrc_t r, uint32_t off, uint32_t data, 
 }
 
 __device__ __forceinline__ void ll_send4(uint64_t* lout, uint32_t p, u32x4 r, uint32_t flag) {
-  st_relaxed(lout + 4 * p + 0, ll_line(r.x, flag));
-  st_relaxed(lout + 4 * p + 1, ll_line(r.y, flag));
-  st_relaxed(lout + 4 * p + 2, ll_line(r.z, flag));
-  st_relaxed(lout + 4 * p + 3, ll_line(r.w, flag));
+  st_relaxed(lout + ll_line_index(p, 0), ll_line(r.x, flag));
+  st_relaxed(lout + ll_line_index(p, 1), ll_line(r.y, flag));
+  st_relaxed(lout + ll_line_index(p, 2), ll_line(r.z, flag));
+  st_relaxed(lout + ll_line_index(p, 3), ll_line(r.w, flag));
 }
 
 template <class E, int OP, int F>
@@ -574,7 +574,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;   // a packet = 16 data bytes = 4 lines
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;
-  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, npk * 32u);   // slot bytes read (see finish_input)
+  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, ll_prefix_bytes(npk));   // slot bytes read (see finish_input)
   constexpr int U = NI == 2 ? 2 : 4;   // packets per lane per poll (registers)
   for (uint32_t p0 = 0; p0 < nfull; p0 += 64 * U) {
     u32x4 va[NI][U], vb[U];
@@ -593,7 +593,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
         for (int u = 0; u < U; u++) {
           const uint32_t p = p0 + u * 64 + L.lane;
 #pragma unroll
-          for (int q = 0; q < 4; q++) ln[i][u][q] = (p < nfull) ? ld_relaxed(lin[i] + 4 * p + q) : ll_line(0, fin);
+          for (int q = 0; q < 4; q++) ln[i][u][q] = (p < nfull) ? ld_relaxed(lin[i] + ll_line_index(p, q)) : ll_line(0, fin);
         }
       L.w.start();
       while (true) {
@@ -613,7 +613,7 @@ __device__ __forceinline__ bool slice_ll(Lane& L, uint64_t es0, uint64_t ed0, ui
             const uint32_t p = p0 + u * 64 + L.lane;
 #pragma unroll
             for (int q = 0; q < 4; q++)
-              if (!ll_ready(ln[i][u][q], fin)) ln[i][u][q] = ld_relaxed(lin[i] + 4 * p + q);
+              if (!ll_ready(ln[i][u][q], fin)) ln[i][u][q] = ld_relaxed(lin[i] + ll_line_index(p, q));
           }
       }
 #pragma unroll
@@ -848,9 +848,9 @@ __device__ __forceinline__ bool slice_ll128(Lane& L, uint64_t es0, uint64_t ed0,
 // buffers are 16-byte aligned: the sizes where a ring step's time is mostly
 // the instructions of the step itself, so the code is straight-line.  Lane p
 // handles packet p; a lane past the last packet points its accesses just past
-// the buffer resources, so its loads read zeros and its stores are dropped by
-// the range check.  The lane of a ragged last packet goes element-wise on the
-// user side.
+// the buffer resources (LL: one per line column of the interleaved slot), so
+// its loads read zeros and its stores are dropped by the range check.  The
+// lane of a ragged last packet goes element-wise on the user side.
 template <class E>
 __device__ __forceinline__ u32x4 small_user_load(const Lane& L, uint64_t soff, uint32_t nbytes) {
   const uint32_t nfull = nbytes / 16, p = (uint32_t)L.lane;
@@ -880,19 +880,24 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
   const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   const bool act = p < npk;
-  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, npk * 32u);   // slot bytes read (see finish_input)
+  if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, ll_prefix_bytes(npk));   // slot bytes read (see finish_input)
   u32x4 va[NI], vb = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < NI; i++) va[i] = vb;
   if (F & kSrc) vb = small_user_load<E>(L, soff, nbytes);
   if (F & kRecv) {
-    rsrc_t ri[NI];
+    // one resource per line column q, holding lines 64 q .. 64 q + npk - 1
+    // (lanes past the last packet read zeros without a memory access)
+    rsrc_t ri[NI][4];
     uint64_t ln[NI][4];
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      ri[i] = make_rsrc(L.in[i].fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
 #pragma unroll
-      for (int q = 0; q < 4; q++) ln[i][q] = ll_load(ri[i], p * 32 + q * 8);
+      for (int q = 0; q < 4; q++) {
+        ri[i][q] = make_rsrc(L.in[i].fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes + ll_line_index(0, q) * 8,
+                             npk * 8);
+        ln[i][q] = ll_load(ri[i][q], p * 8);
+      }
     }
     L.w.start();
     while (true) {
@@ -907,7 +912,7 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
       for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int q = 0; q < 4; q++)
-          if (!ll_ready(ln[i][q], fin)) ln[i][q] = ll_load(ri[i], p * 32 + q * 8);
+          if (!ll_ready(ln[i][q], fin)) ln[i][q] = ll_load(ri[i][q], p * 8);
     }
 #pragma unroll
     for (int i = 0; i < NI; i++)
@@ -917,11 +922,10 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
   if (F & kSend) {
 #pragma unroll
     for (int o = 0; o < NO; o++) {
-      const rsrc_t ro = make_rsrc(L.out[o].fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes, npk * 32);
-      ll_store(ro, p * 32 + 0, r.x, fout);
-      ll_store(ro, p * 32 + 8, r.y, fout);
-      ll_store(ro, p * 32 + 16, r.z, fout);
-      ll_store(ro, p * 32 + 24, r.w, fout);
+      char* so = L.out[o].fifo + (L.sstep & (a.depth - 1)) * kLLSlotBytes;
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) ll_store(make_rsrc(so + ll_line_index(0, q) * 8, npk * 8), p * 8, w[q], fout);
     }
     L.sstep++;
   }
