@@ -42,8 +42,8 @@ const void* tree_instance(int proto, bool small) {
   if (proto == kLL) return small ? (const void*)&tree_kernel<E, OP, kLL, true, CAP>
                                  : (const void*)&tree_kernel<E, OP, kLL, false, CAP>;
   if (proto == kLL128) return (const void*)&tree_kernel<E, OP, kLL128, false, CAP>;
-  return small ? (const void*)&tree_kernel<E, OP, kSimple, true, CAP>
-               : (const void*)&tree_kernel<E, OP, kSimple, false, CAP>;
+  return small ? (const void*)&tree_kernel_simple<E, OP, kSimple, true, CAP>
+               : (const void*)&tree_kernel_simple<E, OP, kSimple, false, CAP>;
 }
 
 template <class E, bool CAP>

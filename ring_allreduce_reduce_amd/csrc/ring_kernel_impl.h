@@ -406,8 +406,11 @@ template <int F> __device__ __forceinline__ void publish_tails(Lane& L) {
   L.sstep++;
 }
 
-// kUnroll (ring_geometry.h): 16-byte packets per lane in flight per source
-constexpr int kTwoInputUnroll = kUnroll / 2;
+// kUnroll (ring_geometry.h): 16-byte packets per lane in flight per source.
+// Three sources (a tree vertex with two children) take 6 packets each (tree
+// Simple, fp32 sum, n = 8, 64 MiB per rank, 32 channels on MI355X: 529 us
+// with 4, 505 us with 6; the tree kernels keep their occupancy).
+constexpr int kTwoInputUnroll = 6;
 
 // Result of one packet: the local operand b folded with what was received
 // from input 0 (a) and then input 1 (a2), each hop as op(received, local);
@@ -445,8 +448,8 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
   const uint32_t nfull = a.vec_ok ? nbytes / 16 : 0;     // taken on the vector path
   // three sources in flight (a tree vertex with two children) take a
-  // smaller unroll and the division of an average half of it, so that the
-  // kernel keeps the ring's register budget (occupancy 4)
+  // smaller unroll and the division of an average half, so that the kernel
+  // keeps the ring's register budget (occupancy 4)
   constexpr int U = (F & kPost) ? kUnroll / 2 : (F & kRecv2) ? kTwoInputUnroll : kUnroll;
   // Whole groups of 64U packets: every lane in range, so the loads carry no
   // condition and all of a group's loads are issued before its first store.
@@ -1253,8 +1256,8 @@ __device__ __forceinline__ bool tree_chunks(Lane& L, uint64_t lo, uint64_t len, 
 // CAP: the captured form, as for the ring: steps from zero, every consumed
 // flag and counter left at zero (a vertex resets the connections it receives
 // on, the children's up connections or its parent's down connection).
-template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
-__global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
+template <class E, int OP, int PROTO, bool SMALL, bool CAP>
+__device__ __forceinline__ void tree_body(const TreeArgs& ta) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const KernelArgs& a = ta.k;
   const int n = a.nranks;
@@ -1337,4 +1340,18 @@ __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
   }
 }
 
+
+// The tree's Simple kernels carry the ring's launch bound (4 workgroups of
+// 256 per CU, so at most 128 VGPRs: the 3840-wavefront launches of large
+// calls need occupancy 4); the line protocols keep their registers.
+template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
+__global__ void __launch_bounds__(256, 4) tree_kernel_simple(const TreeArgs ta) {
+  static_assert(PROTO == kSimple, "the line protocols run tree_kernel");
+  tree_body<E, OP, PROTO, SMALL, CAP>(ta);
+}
+template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
+__global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {
+  static_assert(PROTO != kSimple, "Simple runs tree_kernel_simple");
+  tree_body<E, OP, PROTO, SMALL, CAP>(ta);
+}
 }  // namespace ringar
