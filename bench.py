@@ -59,22 +59,38 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the device code: the kernel sources (`.hip` files and the
+    headers they include) with comments and whitespace removed, so that a
+    comment edit or a host-side change leaves a counter record valid."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "ring_allreduce_reduce_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "ring_allreduce_reduce_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.basename(p).encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def plan_key(cfg):
+    """The launch shape a counter record was taken with."""
+    return f"lanes={cfg['lanes']} fifo_depth={cfg['fifo_depth']} workgroups={cfg['workgroups']}"
+
+
+def read_traffic(cfg):
     """Measured HBM bytes per launch from the committed counter summary, if it
-    was taken on the current kernel sources."""
+    was taken on the current kernel code with the same launch shape."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_plan = re.search(r"plan:\s*([^\n]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or not m_plan or m_hash.group(1) != kernel_source_hash():
+        return None
+    if m_plan.group(1).strip() != plan_key(cfg):
         return None
     return float(m_bytes.group(1))
 
@@ -346,7 +362,8 @@ def main():
     algbw = s / (ms_per_step * 1e-3) / 1e9
     bus_factor = (2 if coll == "allreduce" else 1) * (NRANKS - 1) / NRANKS
     busbw = algbw * bus_factor
-    traffic = read_traffic() if headline else None
+    traffic = read_traffic({"lanes": plan.lanes, "fifo_depth": plan.fifo_depth,
+                            "workgroups": plan.workgroups}) if headline else None
 
     def run_oracle(threaded=False, threads=1):
         if coll == "allreduce" and algo == "tree":

@@ -1199,10 +1199,10 @@ __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
 }
 
 // The Simple kernels are held to 128 VGPRs so that 16 wavefronts fit a CU
-// (occupancy 4: the 4096-wavefront launches of large calls); the eager
-// instances need no scratch, the captured AllReduce ones spill 12-28 bytes
-// per lane.  The line protocols (LL, LL128) keep their registers: their poll
-// and line paths would spill under that bound.
+// (occupancy 4: the 4096-wavefront launches of large calls); none of them,
+// eager or captured, needs scratch under that bound.  The line protocols (LL,
+// LL128) keep their registers: LL's general form (131-134 VGPRs) would spill
+// under it.
 // CAP: the captured form (its own instances, so that the eager ones carry
 // none of its code).
 template <class E, int OP, int PROTO, bool SMALL, int COLL, bool CAP = false>
@@ -1215,8 +1215,9 @@ __global__ void __launch_bounds__(256) ring_kernel_lines(const KernelArgs a) {
   static_assert(PROTO != kSimple, "Simple runs ring_kernel");
   ring_body<E, OP, PROTO, SMALL, COLL>(a, CAP);
 }
-// The captured line kernels, held to the eager ones' occupancy of 3 (at
-// most 168 VGPRs); without the bound captured LL128 took 169 and ran at 2.
+// The captured line kernels, held to occupancy 3 or more (at most 168
+// VGPRs), the eager line kernels' lowest; they take 105-136 VGPRs, so the
+// bound only keeps a later change from dropping them to 2.
 template <class E, int OP, int PROTO, bool SMALL, int COLL>
 __global__ void __launch_bounds__(256, 3) ring_kernel_lines_captured(const KernelArgs a) {
   static_assert(PROTO != kSimple, "Simple runs ring_kernel");

@@ -124,12 +124,12 @@ const Env& env() {
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 9.146;
-  m.ll_max_bw = 55.15;
-  m.ll128_per_channel_max_bw = 5.546;
+  m.bw_per_channel = 9.25;
+  m.ll_max_bw = 145.27;
+  m.ll128_per_channel_max_bw = 8.528;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 4.35; m.base_lat_us[1] = 5.24; m.base_lat_us[2] = 4.2;
-  m.hw_lat_us[0] = 1.47; m.hw_lat_us[1] = 2.494; m.hw_lat_us[2] = 1.658;
+  m.base_lat_us[0] = 5.07; m.base_lat_us[1] = 4.59; m.base_lat_us[2] = 4.38;
+  m.hw_lat_us[0] = 1.163; m.hw_lat_us[1] = 2.753; m.hw_lat_us[2] = 1.612;
   m.max_channels = 32;
   m.max_pairs = 256;
   m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;
@@ -140,13 +140,13 @@ ringar_model_t default_model() {
   // Tree rows: the pages' form with MI355X constants fitted the same way
   // (latency over n = 2..16 as base + 2 floor(log2 n) x step per level;
   // bandwidth at 8 MiB per rank, LL at 1 MiB, where tree and ring compete).
-  m.tree_allreduce_eff = 0.8039;
+  m.tree_allreduce_eff = 0.7983;
   m.tree_per_channel_max_bw = 1e9;
-  m.tree_ll_divisor = 5.5437;
-  m.tree_ll128_factor = 0.4117;
+  m.tree_ll_divisor = 1.8801;
+  m.tree_ll128_factor = 0.8804;
   m.tree_ll128_per_channel_max_bw = 1e9;
-  m.tree_base_lat_us[0] = 4.74; m.tree_base_lat_us[1] = 6.17; m.tree_base_lat_us[2] = 6.52;
-  m.tree_hw_lat_us[0] = 1.547; m.tree_hw_lat_us[1] = 2.408; m.tree_hw_lat_us[2] = 1.681;
+  m.tree_base_lat_us[0] = 5.68; m.tree_base_lat_us[1] = 4.85; m.tree_base_lat_us[2] = 6.71;
+  m.tree_hw_lat_us[0] = 1.405; m.tree_hw_lat_us[1] = 3.856; m.tree_hw_lat_us[2] = 1.76;
   m.tree_correction = 0;
   return m;
 }
