@@ -194,7 +194,12 @@ typedef struct {
  *                    primitives, [ARCH] §九.4): fewer bytes moved, same
  *                    results.  Used when the call is a ring AllReduce with
  *                    the Simple protocol and every rank is out of place;
- *                    otherwise the call runs with FIFOs as usual. */
+ *                    otherwise the call runs with FIFOs as usual.
+ *   block_map:       which workgroup runs which (rank, channel, lane): 0 =
+ *                    by size (the XCD-major mapping up to 512 KiB per rank,
+ *                    LL128 up to 32 KiB, else linear), 1 = linear, 2 =
+ *                    XCD-major (every rank of a channel on one of MI355X's
+ *                    8 XCDs).  Changes speed only, never a result. */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;
@@ -207,6 +212,7 @@ typedef struct {
   int force_general;
   int algo;
   int direct;
+  int block_map;
 } ringar_config_t;
 
 /* The resolved plan of a call (what ringar_allreduce would launch). */
@@ -233,6 +239,7 @@ typedef struct {
   double predicted_ring_us[3];  /* Ring model times */
   int direct;              /* 1: runs the direct form when every rank is out
                               of place */
+  int xcd_major;           /* 1: XCD-major block mapping (see block_map) */
 } ringar_plan_t;
 
 /*

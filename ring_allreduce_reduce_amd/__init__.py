@@ -69,6 +69,7 @@ class ringar_config_t(ctypes.Structure):
         ("force_general", ctypes.c_int),
         ("algo", ctypes.c_int),
         ("direct", ctypes.c_int),
+        ("block_map", ctypes.c_int),
     ]
 
 
@@ -91,6 +92,7 @@ class ringar_plan_t(ctypes.Structure):
         ("predicted_tree_us", ctypes.c_double * 3),
         ("predicted_ring_us", ctypes.c_double * 3),
         ("direct", ctypes.c_int),
+        ("xcd_major", ctypes.c_int),
     ]
 
 
@@ -151,7 +153,8 @@ def _enum(table, v):
 
 
 def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_ms=0,
-                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0, algo="ring", direct=0):
+                abort_flag=0, skip_rank=-1, fifo_depth=0, force_general=0, algo="ring", direct=0,
+                block_map=0):
     """A ringar_config_t; keeps the ring-order array alive on the object."""
     cfg = ringar_config_t()
     cfg.chunk_bytes = chunk_bytes
@@ -170,6 +173,7 @@ def make_config(chunk_bytes=0, ring_order=None, model=None, lanes=0, spin_limit_
     cfg.force_general = force_general
     cfg.algo = _enum(ALGOS, algo)
     cfg.direct = int(direct)
+    cfg.block_map = int(block_map)
     return cfg
 
 

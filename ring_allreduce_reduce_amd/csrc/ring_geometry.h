@@ -145,6 +145,31 @@ constexpr int kCounterWords = 32;   // uint64 words per connection (2 x 128 B)
 constexpr int kTailWord = 0;
 constexpr int kHeadWord = 16;
 
+// MI355X dispatches the workgroups of a launch round-robin over its 8 XCDs
+// (accelerator complex dies, each with its own L2): workgroup b runs on XCD
+// b % 8.  A launch is `groups` groups of `members` workgroups (the ring
+// indices of one channel and lane block, or the tree's roles).  The linear
+// mapping puts member m of group g in workgroup g * members + m, so that
+// neighbouring members sit on different XCDs.  The XCD-major mapping puts
+// every member of group g on XCD g % 8: workgroup (g / 8 * members + m) * 8 +
+// g % 8.  Its grid is 8 * members * ceil(groups / 8); the workgroups of a
+// group number >= groups have no work.  Only speed depends on the mapping:
+// every FIFO access is device-coherent.
+constexpr int kXcds = 8;
+RA_HD int launch_grid(int members, int groups, bool xcd_major) {
+  return xcd_major ? kXcds * members * (int)div_up((uint64_t)groups, kXcds) : members * groups;
+}
+RA_HD void block_group(int b, int members, bool xcd_major, int* group, int* member) {
+  if (!xcd_major) {
+    *group = b / members;
+    *member = b % members;
+    return;
+  }
+  const int rest = b / kXcds;
+  *member = rest % members;
+  *group = (rest / members) * kXcds + b % kXcds;
+}
+
 // Connection feeding ring index i on channel c, lane l.
 RA_HD uint64_t conn_index(int c, int i, int l, int nranks, int lanes) {
   return ((uint64_t)c * nranks + i) * lanes + l;
@@ -185,6 +210,7 @@ struct KernelArgs {
   int skip_ring_index;           // -1: none
   int vec_ok;                    // all user pointers 16-byte aligned
   int direct;                    // Simple AllReduce writing the successor's receive buffer
+  int xcd_major;                 // block ids map XCD-major (see block_group)
 };
 
 // Arguments of a tree AllReduce launch: the ring's, plus the two trees

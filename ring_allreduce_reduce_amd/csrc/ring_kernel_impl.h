@@ -883,6 +883,14 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
   const uint64_t soff = es0 * sizeof(typename E::T), doff = ed0 * sizeof(typename E::T);
   const uint32_t npk = (nbytes + 15) / 16, p = (uint32_t)L.lane;
   const bool act = p < npk;
+  if (npk == 0) {
+    // an empty slice (a chunk past the end of a short buffer) moves and
+    // polls no line; it still takes its step on both sides and frees its
+    // input slot, so that the heads keep counting every step
+    if (F & kSend) L.sstep++;
+    if (F & kRecv) release_slot<F>(L);
+    return true;
+  }
   if ((F & kRecv) && L.cap) L.zbytes = max(L.zbytes, ll_prefix_bytes(npk));   // slot bytes read (see finish_input)
   u32x4 va[NI], vb = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -892,34 +900,55 @@ __device__ __forceinline__ bool slice_ll_small(Lane& L, uint64_t es0, uint64_t e
     // one resource per line column q, holding lines 64 q .. 64 q + npk - 1
     // (lanes past the last packet read zeros without a memory access)
     rsrc_t ri[NI][4];
-    uint64_t ln[NI][4];
+    uint64_t ln[2][NI][4];
 #pragma unroll
-    for (int i = 0; i < NI; i++) {
+    for (int i = 0; i < NI; i++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
+      for (int q = 0; q < 4; q++)
         ri[i][q] = make_rsrc(L.in[i].fifo + (L.rstep & (a.depth - 1)) * kLLSlotBytes + ll_line_index(0, q) * 8,
                              npk * 8);
-        ln[i][q] = ll_load(ri[i][q], p * 8);
-      }
-    }
-    L.w.start();
-    while (true) {
+    // Two polls of the packet's lines in flight: each round waits for the
+    // older one only and re-issues it, so a line that lands is seen about
+    // half a load round trip sooner than with one poll at a time.  Flags only
+    // move forward within the call, so either poll alone is a valid view.
+#pragma unroll
+    for (int k = 0; k < 2; k++)
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) ln[k][i][q] = ll_load(ri[i][q], p * 8);
+    auto ready = [&](const uint64_t (&x)[NI][4]) {
       bool ok = true;
 #pragma unroll
       for (int i = 0; i < NI; i++)
-        ok = ok && (!act || (ll_ready(ln[i][0], fin) && ll_ready(ln[i][1], fin) && ll_ready(ln[i][2], fin) &&
-                             ll_ready(ln[i][3], fin)));
-      if (__all(ok)) break;
+        ok = ok && (!act || (ll_ready(x[i][0], fin) && ll_ready(x[i][1], fin) && ll_ready(x[i][2], fin) &&
+                             ll_ready(x[i][3], fin)));
+      return __all(ok);
+    };
+    L.w.start();
+    int k = 0;
+    while (true) {
+      if (ready(ln[0])) break;
       if (!L.w.idle()) return false;
 #pragma unroll
       for (int i = 0; i < NI; i++)
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-          if (!ll_ready(ln[i][q], fin)) ln[i][q] = ll_load(ri[i][q], p * 8);
+        for (int q = 0; q < 4; q++) ln[0][i][q] = ll_load(ri[i][q], p * 8);
+      if (ready(ln[1])) {
+        k = 1;
+        break;
+      }
+      if (!L.w.idle()) return false;
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) ln[1][i][q] = ll_load(ri[i][q], p * 8);
     }
 #pragma unroll
-    for (int i = 0; i < NI; i++)
-      va[i] = u32x4{(uint32_t)ln[i][0], (uint32_t)ln[i][1], (uint32_t)ln[i][2], (uint32_t)ln[i][3]};
+    for (int i = 0; i < NI; i++) {
+      const uint64_t* x = k ? ln[1][i] : ln[0][i];
+      va[i] = u32x4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
+    }
   }
   const u32x4 r = combine<E, OP, F>(va[0], va[NI - 1], vb, a.nranks);
   if (F & kSend) {
@@ -1095,9 +1124,10 @@ template <class E, int OP, int PROTO, bool SMALL, int COLL>
 __device__ __forceinline__ void ring_body(const KernelArgs& a, bool cap) {
   static_assert(!SMALL || PROTO != kLL128, "no small-slice form of LL128");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps lane-derived values scalar
-  const int group = blockIdx.x / a.nranks;     // (channel, lane block)
-  const int ri = blockIdx.x % a.nranks;        // ring index
+  int group, ri;                               // (channel, lane block), ring index
+  block_group(blockIdx.x, a.nranks, a.xcd_major, &group, &ri);
   const int lane_blocks = a.lanes / a.lanes_per_block;
+  if (group >= a.nchannels * lane_blocks) return;   // XCD-major padding
   const int c = group / lane_blocks;
   const int l = (group % lane_blocks) * a.lanes_per_block + wave;
   if (ri == a.skip_ring_index) return;
@@ -1264,9 +1294,10 @@ __device__ __forceinline__ void tree_body(const TreeArgs& ta) {
   const int n = a.nranks;
   const int R = tree_roles(n);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps lane-derived values scalar
-  const int role = blockIdx.x % R;
-  const int group = blockIdx.x / R;
+  int group, role;
+  block_group(blockIdx.x, R, a.xcd_major, &group, &role);
   const int lane_blocks = a.lanes / a.lanes_per_block;
+  if (group >= a.nchannels * lane_blocks) return;   // XCD-major padding
   const int c = group / lane_blocks;
   const int l = (group % lane_blocks) * a.lanes_per_block + wave;
   const int t = c & 1;

@@ -267,6 +267,30 @@ def test_small_form_rule():
     assert ra.ringar_plan(4096, "float32", 8, 1, "LL", cfg).small_slices == 0
 
 
+def test_block_map_rule_and_grid():
+    # XCD-major up to 512 KiB per rank (LL128: 32 KiB), linear above; the
+    # XCD-major grid holds whole rounds of 8 groups of members (ring: the n
+    # ring indices; tree: its 2n - 1 roles)
+    for proto, limit in (("LL", 512 << 10), ("Simple", 512 << 10), ("LL128", 32 << 10)):
+        for algo in ("ring", "tree"):
+            for nbytes in (8, 4096, limit, limit + 16, 4 << 20):
+                for nch in (0, 3):
+                    cfg = ra.make_config(algo=algo)
+                    plan = ra.ringar_plan(nbytes // 4, "float32", 8, nch, proto, cfg)
+                    assert plan.xcd_major == int(nbytes <= limit), (proto, algo, nbytes, nch)
+                    members = 15 if algo == "tree" else 8
+                    groups = plan.nchannels * (plan.lanes // min(plan.lanes, 4))
+                    want = 8 * members * -(-groups // 8) if plan.xcd_major else members * groups
+                    assert plan.workgroups == want, (proto, algo, nbytes, nch)
+    for m in (1, 2):
+        plan = ra.ringar_plan(1 << 20, "float32", 8, 5, "Simple", ra.make_config(block_map=m))
+        assert plan.xcd_major == (m == 2)
+    for bad in (-1, 3):
+        with pytest.raises(ra.RingarError) as e:
+            ra.ringar_plan(1024, "float32", 8, 1, "LL", ra.make_config(block_map=bad))
+        assert e.value.code == ra.INVALID_ARGUMENT
+
+
 def test_halves_buffer_rules_before_any_device_call():
     n, count = 4, 1000
     E = ra

@@ -3,7 +3,8 @@
 Each case draws every knob of a call at once: rank count (1 to 64), element
 count (0 to about a million, log-uniform), dtype, op, protocol, algorithm,
 direct form, channels, chunk, lanes, FIFO depth, ring order, in-place or
-out-of-place, 16-byte-misaligned buffers and the elementwise kernel form.
+out-of-place, 16-byte-misaligned buffers, the elementwise kernel form and
+the block mapping (linear or XCD-major).
 The fixed tests cover each knob on its own; these cover their combinations.
 A request the library refuses (a grid beyond residency, the direct form in
 place, a forced lane count the FIFO budget cannot hold) is skipped and
@@ -54,6 +55,8 @@ def _draw(rng, halves=False):
     nch = int(rng.integers(0, 17))
     inplace = rng.random() < 0.2
     unaligned = (not inplace) and rng.random() < 0.15
+    # block mapping: by size, or either mapping forced at any size
+    cfg["block_map"] = int(rng.integers(0, 3))
     return n, count, dtype, op, proto, nch, cfg, inplace, unaligned
 
 
