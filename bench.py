@@ -31,7 +31,9 @@ written straight into the successor's receive buffer, no FIFO).
 (int32 Simple at 4 ranks; the LL sweep at 8 channels; the bf16 LL128 sweep
 with automatic channels; the automatic protocol over 8 B .. 1 GiB per rank,
 ring only and with the model choosing ring or tree), each timed with HIP
-events (median) and reported as busbw and algorithmic memory GB/s.
+events (median) and reported as busbw and algorithmic memory GB/s (a
+protocol marked "/d" ran the direct form, which the library takes for calls
+whose protocol the model picks, and its bytes are the direct form's).
 """
 import argparse
 import glob
@@ -161,9 +163,12 @@ def sweep(reps_small=200, reps_big=20):
         s = count * es
         pname = ra.PROTO_NAMES[plan.proto]
         alg = s / (t * 1e-6) / 1e9
-        hbm = alg_bytes(n, s, FIFO_EXPANSION[pname]) / (t * 1e-6) / 1e9
-        return dict(bytes=s, us=t, proto=pname, algo=ra.ALGO_NAMES[plan.algo], nch=plan.nchannels,
-                    algbw=alg, busbw=alg * 2 * (n - 1) / n, hbm=hbm)
+        # the direct form (the library's choice for calls whose protocol the
+        # model picks) moves S (5n - 4) bytes instead of the FIFO form's
+        b_alg = alg_bytes(n, s, coll="direct") if plan.direct else alg_bytes(n, s, FIFO_EXPANSION[pname])
+        hbm = b_alg / (t * 1e-6) / 1e9
+        return dict(bytes=s, us=t, proto=pname + ("/d" if plan.direct else ""), algo=ra.ALGO_NAMES[plan.algo],
+                    nch=plan.nchannels, algbw=alg, busbw=alg * 2 * (n - 1) / n, hbm=hbm)
 
     rows = []
 

@@ -188,13 +188,17 @@ typedef struct {
  *                    form for small lane parts (see ringar_plan_t).
  *   algo:            a ringar_algo_t (AllReduce only; the halves run the
  *                    ring).  Zero = RINGAR_ALGO_RING.
- *   direct:          1 = the ring AllReduce under Simple writes each
- *                    outgoing slice straight into the successor's receive
- *                    buffer instead of a FIFO slot (the pages' direct
- *                    primitives, [ARCH] §九.4): fewer bytes moved, same
- *                    results.  Used when the call is a ring AllReduce with
- *                    the Simple protocol and every rank is out of place;
- *                    otherwise the call runs with FIFOs as usual.
+ *   direct:          the direct form: the ring AllReduce under Simple
+ *                    writes each outgoing slice straight into the
+ *                    successor's receive buffer instead of a FIFO slot (the
+ *                    pages' direct primitives, [ARCH] §九.4): fewer bytes
+ *                    moved, same results.  1 = whenever the call is a ring
+ *                    AllReduce with the Simple protocol (a captured call is
+ *                    then refused); 2 = never; 0 = the library's choice:
+ *                    when proto is RINGAR_PROTO_AUTO and the model takes
+ *                    Simple on the ring for at least 256 KiB per rank
+ *                    (outside stream capture).  It needs every rank out of
+ *                    place; otherwise the call runs with FIFOs as usual.
  *   block_map:       which workgroup runs which (rank, channel, lane): 0 =
  *                    by size (the XCD-major mapping up to 512 KiB per rank,
  *                    LL128 up to 32 KiB, else linear), 1 = linear, 2 =

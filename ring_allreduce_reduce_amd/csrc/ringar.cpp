@@ -321,6 +321,7 @@ struct Plan {
   int depth = kMaxSteps;
   bool small = false;      // every lane part fits the small-slice form
   bool direct = false;     // direct form requested and possible (if out of place)
+  bool direct_auto = false;// the library chose it (a captured call then keeps its FIFOs)
   bool xcd_major = false;  // block ids map XCD-major (launch_grid, block_group)
   int lanes_per_block = 1;
   int grid = 0;
@@ -339,6 +340,8 @@ constexpr uint64_t kTargetWaves = 4096;
 // Largest bytes per rank that take the XCD-major block mapping (below).
 constexpr uint64_t kXcdMajorMaxBytes = 512 << 10;
 constexpr uint64_t kXcdMajorLL128MaxBytes = 32 << 10;
+// Smallest bytes per rank for which the library itself takes the direct form.
+constexpr uint64_t kDirectAutoMinBytes = 256 << 10;
 
 // FIFO bytes that all connections of a call write in one step of every
 // lane, summed over the FIFO depth, above which the depth is halved.  The
@@ -533,7 +536,18 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   }
   // Lane parts of at most 1 KiB (one 16-byte packet per lane and step) run
   // the straight-line form of LL and Simple when the buffers are aligned.
-  P.direct = cfg && cfg->direct && P.kind == kAllReduce && P.proto == kSimple && n > 1;
+  // The direct form: on request (direct = 1), or by the library's choice
+  // (direct = 0) when the model chose the protocol and took Simple on the
+  // ring for at least kDirectAutoMinBytes per rank.  Measured on MI355X, ring
+  // Simple, automatic channels, FIFO against direct: n = 8 fp32 256 KiB
+  // 27.0 / 26.1 us, 2 MiB 38.2 / 34.4, 8 MiB 64.6 / 53.6, 64 MiB 413 / 358,
+  // 1 GiB 6531 / 5352; bf16 8 MiB 65.3 / 54.3; n = 16 fp32 64 MiB 852 / 756;
+  // n = 4 fp32 8 MiB 33.4 / 33.8, 64 MiB 195 / 159.
+  const int direct_req = cfg ? cfg->direct : 0;
+  if (direct_req < 0 || direct_req > 2) return RINGAR_ERR_INVALID_ARGUMENT;
+  const bool direct_ok = P.kind == kAllReduce && P.proto == kSimple && n > 1;
+  P.direct_auto = direct_req == 0 && proto < 0 && direct_ok && (uint64_t)bytes >= kDirectAutoMinBytes;
+  P.direct = direct_ok && (direct_req == 1 || P.direct_auto);
   P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es, P.proto) * es <= kSmallSliceBytes &&
             !(cfg && cfg->force_general) && !P.direct;
   P.lanes_per_block = std::min(lanes, 4);
@@ -1027,6 +1041,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   bool direct = P.direct;
   for (int q = 0; q < nranks && direct; q++)
     if (sendbuffs[q] == recvbuffs[q]) direct = false;
+  if (captured && direct && P.direct_auto) direct = false;   // the library's choice: keep the FIFOs
   if (captured && direct) {
     t_last_error = "the direct form has no captured form";
     return RINGAR_ERR_INVALID_USAGE;
@@ -1122,7 +1137,9 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
       S->base = kEagerBase;
     }
   } else if (!captured) {
-    if ((r = ensure_conns(*R, st, P.proto, P.conns, direct)) != RINGAR_SUCCESS) return r;
+    // (the library's own direct choice still allocates the FIFOs, so that
+    // the stream can capture the same call, which keeps them)
+    if ((r = ensure_conns(*R, st, P.proto, P.conns, direct && !P.direct_auto)) != RINGAR_SUCCESS) return r;
     // LL flags are 32-bit step numbers: restart the numbering before it wraps.
     if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
       if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;

@@ -36,6 +36,7 @@ SHAPES = [
     (16, 1 << 20, "float32", "avg", "Simple", 8, "tree"),
     (5, 3000, "int8", "sum", "Simple", 2, "tree"),          # tree, small Simple form
     (6, 50001, "float64", "prod", "LL", 3, "tree"),
+    (8, 1 << 20, "float32", "sum", "auto", 0),     # eager: the library's direct form; captured: FIFOs
 ]
 
 

@@ -5,7 +5,8 @@ The direct form changes where the data travels, not the fold order, so the
 results must equal the ring oracle's bit for bit: ragged shapes over several
 loops, lanes and channel counts, every op and dtype, unaligned buffers, the
 in-place fallback to FIFOs, calls that alternate with the FIFO form on one
-stream, the 64 MiB workload, and the timeout and abort paths.
+stream, the 64 MiB workload, the timeout and abort paths, and the library's
+own choice of the direct form for calls whose protocol the model picks.
 """
 import numpy as np
 import pytest
@@ -129,3 +130,25 @@ def test_abort_flag_ends_waits():
     _, _, code, _ = run(xs, "float32", "sum", 2, skip_rank=1, spin_limit_ms=60000, abort_flag=flag.data_ptr())
     assert code == ra.ABORTED
     check(xs, "float32", "sum", 2)
+
+
+@pytest.mark.parametrize("nbytes", [256 << 10, 4 << 20, 64 << 20])
+def test_library_choice_of_the_direct_form(nbytes):
+    # proto AUTO with direct = 0: the library takes the direct form where the
+    # model takes Simple on the ring; in place keeps the FIFOs; both match
+    # the oracle bit for bit, and so does the same call forced to FIFOs
+    n, count = 8, nbytes // 4
+    xs = W.inputs(f"direct-auto-{nbytes}", n, count, "float32", "normal")
+    plan = ra.ringar_plan(count, "float32", n, 0, "auto")
+    assert plan.direct == int(ra.PROTO_NAMES[plan.proto] == "Simple"), (nbytes, plan.proto)
+    want = oracle.ring_allreduce(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+    for inplace, direct in ((False, 0), (True, 0), (False, 2)):
+        print(f"case library direct choice {nbytes} inplace={inplace} direct={direct} plan.direct={plan.direct}",
+              flush=True)
+        sends = [W.to_torch(x, "float32", DEV) for x in xs]
+        recvs = sends if inplace else [torch.zeros_like(s) for s in sends]
+        ra.allreduce(sends, recvs, op="sum", nchannels=0, proto="auto", direct=direct)
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(torch.cuda.current_stream().cuda_stream) == ra.SUCCESS
+        for r in range(n):
+            assert np.array_equal(_bits(W.from_torch(recvs[r], "float32")), _bits(want[r])), (inplace, direct, r)

@@ -168,6 +168,21 @@ def test_direct_form_is_planned_only_where_it_applies():
     # the small form is not used with the direct form
     small = ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple", d)
     assert small.small_slices == 0 and ra.ringar_plan(64 * 8, "float32", 8, 1, "Simple").small_slices == 1
+    # the library's own choice (direct = 0): only where the model picks the
+    # protocol and takes Simple on the ring, from 256 KiB per rank
+    for nbytes in (64 << 10, 256 << 10, 1 << 20, 64 << 20, 1 << 30):
+        for algo in ("ring", "auto", "tree"):
+            p = ra.ringar_plan(nbytes // 4, "float32", 8, 0, "auto", ra.make_config(algo=algo))
+            want = int(p.algo == 0 and ra.PROTO_NAMES[p.proto] == "Simple" and nbytes >= 256 << 10)
+            assert p.direct == want, (nbytes, algo)
+    assert ra.ringar_plan(1 << 24, "float32", 8, 0, "auto").direct == 1
+    assert ra.ringar_plan(1 << 24, "float32", 8, 0, "auto", ra.make_config(direct=2)).direct == 0
+    assert ra.ringar_plan(1 << 24, "float32", 8, 0, "Simple").direct == 0
+    assert ra.ringar_plan(1 << 24, "float32", 8, 0, "Simple", ra.make_config(direct=2)).direct == 0
+    for bad in (-1, 3):
+        with pytest.raises(ra.RingarError) as e:
+            ra.ringar_plan(1 << 20, "float32", 8, 4, "Simple", ra.make_config(direct=bad))
+        assert e.value.code == ra.INVALID_ARGUMENT
 
 
 def test_tree_chunk_rule():
