@@ -555,8 +555,9 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   const int groups = P.nch * (lanes / P.lanes_per_block);
   // Block mapping: latency-bound calls put every rank (tree: every role) of
   // a channel on one XCD, where a flag or tail store reaches its reader
-  // sooner (a token passed round 8 single-wavefront workgroups: 0.32 us per
-  // hop within one XCD, 0.49 us across XCDs).  Bandwidth-bound calls keep the
+  // sooner (a token passed round 8 single-wavefront workgroups, the example
+  // hop_latency.hip: 0.32-0.54 us per hop within one XCD against 0.49-0.58 us
+  // across XCDs, depending on the box).  Bandwidth-bound calls keep the
   // linear mapping, which spreads each channel's FIFO traffic over the XCDs.
   // Measured at n = 8, fp32 sum, automatic channels (HIP events per call):
   // XCD-major faster up to 512 KiB per rank (ring Simple 8 B 23.1 -> 17.5
