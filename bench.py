@@ -173,13 +173,13 @@ def sweep(reps_small=200, reps_big=20):
     rows = []
 
     def emit(name, r):
-        line = (f"{name:34s} {r['bytes']:>11d} {r['algo']:>5s} {r['proto']:>7s} {r['nch']:>4d} "
+        line = (f"{name:34s} {r['bytes']:>11d} {r['algo']:>5s} {r['proto']:>8s} {r['nch']:>4d} "
                 f"{r['us']:>10.1f} {r['algbw']:>8.2f} {r['busbw']:>8.2f} {r['hbm']:>8.1f} "
                 f"{100 * r['hbm'] / HBM_PEAK_GBS:>6.1f}")
         rows.append(line)
         print(line, flush=True)
 
-    print(f"{'workload':34s} {'bytes/rank':>11s} {'algo':>5s} {'proto':>7s} {'nch':>4s} {'us':>10s} "
+    print(f"{'workload':34s} {'bytes/rank':>11s} {'algo':>5s} {'proto':>8s} {'nch':>4s} {'us':>10s} "
           f"{'algbw':>8s} {'busbw':>8s} {'hbmGB/s':>8s} {'%peak':>6s}", flush=True)
     emit("int32 sum n=4 Simple 2ch 16KiB", timed(4, 65536, "int32", "Simple", 2, 16384))
     emit("fp32 sum n=8 Simple 16ch 512KiB", timed(8, 16 << 20, "float32", "Simple", 16, 512 << 10))
