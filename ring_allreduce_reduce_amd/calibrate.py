@@ -10,15 +10,17 @@ min(nch * bw * eff, nch * perChLL128) for LL128.  This tool fits, per
 protocol, `base` and `step` to small calls at n = 2..8 (least squares over
 2(n-1)), and the bandwidth terms to large calls at the model's largest
 channel count; it keeps the pages' efficiencies and the size rule for the
-channel count.  The tree AllReduce rows take the pages' Tree form with every
+channel count.  Simple's bandwidth is fitted to the direct form, which the
+library runs when the model takes Simple on the ring (from 256 KiB per
+rank), and the tuning table times Ring Simple that way too.  The tree AllReduce rows take the pages' Tree form with every
 virtual rank one vertex ([BOOK] Japanese edition ch. 5 §四):
 
     T = tbase + 2 floor(log2 n) * tstep  +  bytes / (1000 * busBw * 0.5)
 
 with busBw = nch * bw * treeEff for Simple, that / llDiv (capped at llMax)
 for LL and that * ll128Factor for LL128; tbase and tstep are fitted to small
-calls at n = 2..16, treeEff and ll128Factor to 8 MiB calls and llDiv to
-1 MiB calls (where tree and ring compete).  It prints
+calls at n = 2..16, treeEff to 2 MiB calls, llDiv to 1 MiB calls and
+ll128Factor to 8 MiB calls (where tree and ring compete).  It prints
 the fitted model (the JSON layout of `ringar_model_t`) and a tuning table: for
 each size the model's time per (algorithm, protocol), the measured time, and
 which pair each picks.
@@ -33,11 +35,14 @@ import sys
 import time
 
 PROTOS = ("LL", "LL128", "Simple")
+# smallest bytes per rank for which the library takes the direct form itself
+DIRECT_AUTO_MIN_BYTES = 256 << 10
 
 
-def _time_calls(ra, torch, sends, recvs, count, n, nch, proto, stream, iters, cfg=None, algo=None):
-    if algo is not None:
-        cfg = ra.make_config(algo=algo, model=cfg._model_keep if cfg is not None and cfg.model else None)
+def _time_calls(ra, torch, sends, recvs, count, n, nch, proto, stream, iters, cfg=None, algo=None, direct=0):
+    if algo is not None or direct:
+        cfg = ra.make_config(algo=algo or "ring", direct=direct,
+                             model=cfg._model_keep if cfg is not None and cfg.model else None)
     sp = [s.data_ptr() for s in sends[:n]]
     rp = [r.data_ptr() for r in recvs[:n]]
 
@@ -132,9 +137,11 @@ def main(argv=None):
         m["hw_lat_us"][p] = round(step, 3)
         log(f"{proto}: base {base:.2f} us, step {step:.3f} us")
 
-    # bandwidth: the largest call at the largest channel count
+    # bandwidth: the largest call at the largest channel count (Simple in
+    # the direct form, as the library runs it when the model takes Simple)
     def bus_at(proto, p, nbytes):
-        us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10)
+        us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10,
+                         direct=int(proto == "Simple"))
         lat = m["base_lat_us"][p] + 2.0 * (n - 1) * m["hw_lat_us"][p]
         alg = nbytes / (1000.0 * max(us - lat, 1e-3))
         return alg * 2.0 * (n - 1) / n
@@ -161,21 +168,22 @@ def main(argv=None):
         log(f"tree {proto}: base {base:.2f} us, step per level {step:.3f} us")
 
     # tree bandwidth at the largest channel count, fitted at the sizes where
-    # the model has to choose between tree and ring (8 MiB per rank, LL at
-    # 1 MiB): far above them the ring wins anyway, and the tree runs closer
-    # to its model there than at medium sizes (the pages' reason for a
-    # size correction of the tree's bandwidth)
+    # the model has to choose between tree and ring (Simple at 2 MiB per
+    # rank, LL at 1 MiB, LL128 against Simple at 8 MiB): far above them the
+    # ring wins anyway, and the tree runs closer to its model there than at
+    # medium sizes (the pages' reason for a size correction of the tree's
+    # bandwidth)
     def tree_bus_at(proto, p, nbytes):
         us = _time_calls(ra, torch, sends, recvs, nbytes // 4, n, maxc, proto, stream, 10, algo="tree")
         lat = m["tree_base_lat_us"][p] + 2.0 * _flog2(n) * m["tree_hw_lat_us"][p]
         return 2.0 * nbytes / (1000.0 * max(us - lat, 1e-3))
-    tsimple = tree_bus_at("Simple", 2, 8 << 20)
+    tsimple = tree_bus_at("Simple", 2, 2 << 20)
     m["tree_allreduce_eff"] = round(tsimple / (maxc * m["bw_per_channel"]), 4)
     m["tree_per_channel_max_bw"] = 1e9
     tll = tree_bus_at("LL", 0, 1 << 20)
     m["tree_ll_divisor"] = round(tsimple / tll, 4) if tll < m["ll_max_bw"] else 1.0
     tll128 = tree_bus_at("LL128", 1, 8 << 20)
-    m["tree_ll128_factor"] = round(tll128 / tsimple, 4)
+    m["tree_ll128_factor"] = round(tll128 / tree_bus_at("Simple", 2, 8 << 20), 4)
     m["tree_ll128_per_channel_max_bw"] = 1e9
     m["tree_correction"] = 0
     log(f"tree bus bandwidth at {maxc} channels: Simple {tsimple:.1f}, LL {tll:.1f}, LL128 {tll128:.1f} GB/s")
@@ -191,7 +199,10 @@ def main(argv=None):
         line = {"bytes": nbytes}
         for a, proto in pairs:
             p = PROTOS.index(proto)
-            pcfg = ra.make_config(model=ra_model, algo=a.lower())
+            # Ring Simple from 256 KiB per rank: the direct form, which the
+            # library runs when the model picks it
+            direct = int((a, proto) == ("Ring", "Simple") and nbytes >= DIRECT_AUTO_MIN_BYTES)
+            pcfg = ra.make_config(model=ra_model, algo=a.lower(), direct=direct)
             plan = ra.ringar_plan(count, "float32", n, 0, proto, pcfg)
             pred = plan.predicted_us[p]
             us = _time_calls(ra, torch, sends, recvs, count, n, 0, proto, stream,
@@ -211,7 +222,8 @@ def main(argv=None):
     out = [f"# ring and tree AllReduce tuning table, n = {n}, fp32 sum, one MI355X ({time.strftime('%Y-%m-%d')})",
            "# command: python -m ring_allreduce_reduce_amd.calibrate --json <model.json> --table <this file>",
            "# per (algorithm, protocol): channels chosen by the size rule, model us, measured us (median,",
-           "# HIP events)",
+           "# HIP events); Ring Simple from 256 KiB per rank runs the direct form, as the library does when",
+           "# the model picks it",
            "# fitted model: " + json.dumps(m), ""]
     name = lambda pr: f"{pr[0]} {pr[1]}"
     hdr = f"{'bytes/rank':>11s} | " + " | ".join(f"{name(pr):>12s} ch model  meas." for pr in pairs) + \

@@ -126,12 +126,12 @@ const Env& env() {
 ringar_model_t default_model() {
   ringar_model_t m;
   memset(&m, 0, sizeof(m));
-  m.bw_per_channel = 9.25;
-  m.ll_max_bw = 145.27;
-  m.ll128_per_channel_max_bw = 8.528;
+  m.bw_per_channel = 10.279;
+  m.ll_max_bw = 147.03;
+  m.ll128_per_channel_max_bw = 8.554;
   m.eff[0] = 0.5; m.eff[1] = 0.94; m.eff[2] = 1.0;
-  m.base_lat_us[0] = 5.07; m.base_lat_us[1] = 4.59; m.base_lat_us[2] = 4.38;
-  m.hw_lat_us[0] = 1.163; m.hw_lat_us[1] = 2.753; m.hw_lat_us[2] = 1.612;
+  m.base_lat_us[0] = 4.93; m.base_lat_us[1] = 5.09; m.base_lat_us[2] = 4.93;
+  m.hw_lat_us[0] = 1.188; m.hw_lat_us[1] = 2.44; m.hw_lat_us[2] = 1.331;
   m.max_channels = 32;
   m.max_pairs = 256;
   m.threads[0] = 64; m.threads[1] = 64; m.threads[2] = 64;
@@ -141,14 +141,16 @@ ringar_model_t default_model() {
   m.default_chunk_bytes[2] = 524288;
   // Tree rows: the pages' form with MI355X constants fitted the same way
   // (latency over n = 2..16 as base + 2 floor(log2 n) x step per level;
-  // bandwidth at 8 MiB per rank, LL at 1 MiB, where tree and ring compete).
-  m.tree_allreduce_eff = 0.7983;
+  // Simple bandwidth at 2 MiB per rank, LL at 1 MiB, LL128 at 8 MiB, where
+  // tree and ring compete).  The ring's Simple bandwidth is that of the
+  // direct form, which runs when the model takes Simple on the ring.
+  m.tree_allreduce_eff = 0.5419;
   m.tree_per_channel_max_bw = 1e9;
-  m.tree_ll_divisor = 1.8801;
-  m.tree_ll128_factor = 0.8804;
+  m.tree_ll_divisor = 1.7201;
+  m.tree_ll128_factor = 0.877;
   m.tree_ll128_per_channel_max_bw = 1e9;
-  m.tree_base_lat_us[0] = 5.68; m.tree_base_lat_us[1] = 4.85; m.tree_base_lat_us[2] = 6.71;
-  m.tree_hw_lat_us[0] = 1.405; m.tree_hw_lat_us[1] = 3.856; m.tree_hw_lat_us[2] = 1.76;
+  m.tree_base_lat_us[0] = 5.63; m.tree_base_lat_us[1] = 4.81; m.tree_base_lat_us[2] = 5.69;
+  m.tree_hw_lat_us[0] = 1.235; m.tree_hw_lat_us[1] = 3.506; m.tree_hw_lat_us[2] = 1.696;
   m.tree_correction = 0;
   return m;
 }
