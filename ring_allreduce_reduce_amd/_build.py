@@ -63,5 +63,11 @@ def build(out: str = LIB, extra: list | None = None, verbose: bool = False, jobs
 
 
 if __name__ == "__main__":
-    build(verbose=False)
-    print(LIB)
+    import sys
+    if len(sys.argv) == 3 and sys.argv[1] == "--role-profile":
+        # a diagnostic build: the tree kernels record where each wavefront
+        # waited (never the library the package loads)
+        print(build(out=os.path.abspath(sys.argv[2]), extra=["-DRINGAR_ROLE_PROFILE"]))
+    else:
+        build(verbose=False)
+        print(LIB)

@@ -331,7 +331,20 @@ struct Lane {
   Waiter w;
   bool cap;            // a captured call (the kernel instance's constant)
   uint32_t zbytes;     // captured line protocols: most slot bytes a slice read
+#ifdef RINGAR_ROLE_PROFILE
+  uint64_t w_in, w_out, n_sl;   // wall-clock ticks waiting for inputs / output slots, slices
+#endif
 };
+
+#ifdef RINGAR_ROLE_PROFILE
+// Role profile (a diagnostic build, never the library's own): per wavefront
+// of a tree launch, its first and last wall-clock tick, the ticks its Simple
+// slices waited for their inputs and for free output slots, the slices, and
+// its role.  Written by lane 0 of every wavefront of the eager Simple tree
+// kernels of one element type's translation unit.
+constexpr int kRoleProfileWaves = 4096;
+static __device__ unsigned long long g_role_profile[kRoleProfileWaves][8];
+#endif
 
 // Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
 // output 0, and output 1 with kSend2), read the own send buffer, write the
@@ -436,7 +449,17 @@ template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
   const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+#ifdef RINGAR_ROLE_PROFILE
+  const uint64_t t0 = wall_clock64();
+  if (!wait_inputs<F>(L)) return false;
+  const uint64_t t1 = wall_clock64();
+  if (!wait_outputs<F>(L)) return false;
+  L.w_in += t1 - t0;
+  L.w_out += wall_clock64() - t1;
+  L.n_sl++;
+#else
   if (!wait_inputs<F>(L) || !wait_outputs<F>(L)) return false;
+#endif
   const uint32_t rslot = (uint32_t)(L.rstep & (a.depth - 1)) * kSimpleSlotBytes;
   const uint32_t sslot = (uint32_t)(L.sstep & (a.depth - 1)) * kSimpleSlotBytes;
   rsrc_t rin = make_rsrc(L.in[0].fifo + rslot, kSimpleSlotBytes);
@@ -1321,6 +1344,10 @@ __device__ __forceinline__ void tree_body(const TreeArgs& ta) {
   L.rstep = 0;
   L.tail_seen[0] = L.tail_seen[1] = 0;
   L.head_seen[0] = L.head_seen[1] = 0;
+#ifdef RINGAR_ROLE_PROFILE
+  L.w_in = L.w_out = L.n_sl = 0;
+  const uint64_t tstart = wall_clock64();
+#endif
   L.src = a.send[v];
   L.dst = a.recv[v];
   // present children in child-slot order: k0 first, then k1 (-1 = none);
@@ -1370,6 +1397,22 @@ __device__ __forceinline__ void tree_body(const TreeArgs& ta) {
     if (bcast || nk >= 1) finish_input<PROTO>(L, L.in[0]);
     if (!bcast && nk == 2) finish_input<PROTO>(L, L.in[1]);
   }
+#ifdef RINGAR_ROLE_PROFILE
+  if (PROTO == kSimple && !SMALL && !CAP && L.lane == 0) {
+    const uint32_t id = blockIdx.x * (blockDim.x / 64) + wave;
+    if (id < (uint32_t)kRoleProfileWaves) {
+      unsigned long long* r = g_role_profile[id];
+      r[0] = tstart;
+      r[1] = wall_clock64();
+      r[2] = L.w_in;
+      r[3] = L.w_out;
+      r[4] = L.n_sl;
+      r[5] = (uint64_t)v | ((uint64_t)bcast << 8) | ((uint64_t)nk << 16) | ((uint64_t)(v == root) << 24);
+      r[6] = (uint64_t)c;
+      r[7] = (uint64_t)l;
+    }
+  }
+#endif
 }
 
 

@@ -9,3 +9,17 @@ const void* kernel_tree_for_f32(int op, int proto, bool small) {
 }
 
 }  // namespace ringar
+
+#ifdef RINGAR_ROLE_PROFILE
+// Reads the role profile of the last fp32 tree launch (a diagnostic build
+// only: built with -DRINGAR_ROLE_PROFILE, see the role profile example).
+extern "C" int ringar_role_profile(void* host, size_t bytes, int clear) {
+  if (clear) {
+    static unsigned long long zero[ringar::kRoleProfileWaves][8];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(ringar::g_role_profile), zero, sizeof(zero), 0,
+                                  hipMemcpyHostToDevice);
+  }
+  if (bytes > sizeof(ringar::g_role_profile)) bytes = sizeof(ringar::g_role_profile);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(ringar::g_role_profile), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
