@@ -258,7 +258,9 @@ typedef struct {
  *       host arrays are read only during the call.
  *   count: elements per rank.  0 is a successful no-op.
  *   nchannels: 1..64, or 0 = chosen by the model's size rule.
- *   proto: a protocol, or RINGAR_PROTO_AUTO = the model's fastest.
+ *   proto: a protocol, or RINGAR_PROTO_AUTO = the model's fastest (where it
+ *       is Simple from 256 KiB per rank, out of place and outside stream
+ *       capture, the call runs the direct form; see ringar_config_t).
  *   stream: the work is enqueued on this stream; results are valid after the
  *       stream has been synchronised.  nranks == 1 enqueues a device copy.
  *       Under stream capture (a HIP graph, replayed any number of times)
@@ -271,9 +273,10 @@ typedef struct {
  *       shape first (else RINGAR_ERR_INVALID_USAGE).  The captured kernels
  *       may hold fewer wavefronts per CU, so a captured call can take fewer
  *       lanes than the same call made eagerly (same results); a forced lane
- *       count beyond what they hold is RINGAR_ERR_INVALID_USAGE.  The direct
- *       form is refused under capture (RINGAR_ERR_INVALID_USAGE, nothing
- *       enqueued).
+ *       count beyond what they hold is RINGAR_ERR_INVALID_USAGE.  A call that
+ *       asks for the direct form is refused under capture
+ *       (RINGAR_ERR_INVALID_USAGE, nothing enqueued); one for which the
+ *       library chose it keeps its FIFOs.
  *       Replays share the stream's FIFO memory with its eager calls: run
  *       them in order (one stream, or synchronised).  A graph holds the
  *       addresses of the stream's FIFO memory and counters: later eager
