@@ -244,6 +244,11 @@ typedef struct {
   int direct;              /* 1: runs the direct form when every rank is out
                               of place */
   int xcd_major;           /* 1: XCD-major block mapping (see block_map) */
+  int tree_split;          /* 1: the tree's split form: each role that moves
+                              four or more units per element runs as two
+                              wavefronts on halves of every slice */
+  int tree_waves_per_lane; /* the split form's wavefronts per (channel,
+                              lane); 0 otherwise */
 } ringar_plan_t;
 
 /*

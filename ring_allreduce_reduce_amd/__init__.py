@@ -93,6 +93,8 @@ class ringar_plan_t(ctypes.Structure):
         ("predicted_ring_us", ctypes.c_double * 3),
         ("direct", ctypes.c_int),
         ("xcd_major", ctypes.c_int),
+        ("tree_split", ctypes.c_int),
+        ("tree_waves_per_lane", ctypes.c_int),
     ]
 
 

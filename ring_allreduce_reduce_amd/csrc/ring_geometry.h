@@ -57,6 +57,9 @@ enum Proto { kLL = 0, kLL128 = 1, kSimple = 2 };
 // Launch kinds: the ring AllReduce and its halves (the public collective
 // codes), and the tree AllReduce.
 enum Coll { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kTreeAllReduce = 3 };
+// Kernel selector for the split tree form (Simple), in place of the
+// protocol when a tree kernel is looked up; never a protocol of a plan.
+constexpr int kSimpleSplitTree = 3;
 
 RA_HD uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 RA_HD uint64_t align_up(uint64_t a, uint64_t b) { return div_up(a, b) * b; }
@@ -144,6 +147,10 @@ RA_HD uint64_t fifo_conn_bytes(int proto) { return (uint64_t)kMaxSteps * slot_by
 constexpr int kCounterWords = 32;   // uint64 words per connection (2 x 128 B)
 constexpr int kTailWord = 0;
 constexpr int kHeadWord = 16;
+// A connection whose producer (consumer) runs as two half-lane wavefronts
+// (the split tree below) has a second tail (head) word, one per half.
+constexpr int kTail2Word = 8;
+constexpr int kHead2Word = 24;
 
 // MI355X dispatches the workgroups of a launch round-robin over its 8 XCDs
 // (accelerator complex dies, each with its own L2): workgroup b runs on XCD
@@ -221,6 +228,19 @@ struct TreeArgs {
   int8_t parent[2][kMaxRanks];
   int8_t child[2][2][kMaxRanks];
   int root[2];
+  // The split form (Simple): a role that moves four or more units of its
+  // channel per element (the root's reduce role, the reduce and broadcast
+  // roles of a vertex with two children) runs as two wavefronts, each on
+  // half of every slice.  role_of[t][r] = vertex | broadcast << 6 |
+  // half << 7 for the nroles wavefronts of a (channel, lane) on tree t.
+  int nroles;
+  uint8_t role_of[2][4 * kMaxRanks];
 };
+
+// Whether vertex v's reduce (broadcast) role splits in the split tree form:
+// the root's reduce role, and either role of a vertex with two children.
+RA_HD bool tree_role_splits(bool bcast, bool is_root, int nchildren) {
+  return bcast ? nchildren == 2 : (is_root || nchildren == 2);
+}
 
 }  // namespace ringar

@@ -39,6 +39,10 @@ const void* ring_instance_by_op(int op, int proto, bool small) {
 
 template <class E, int OP, bool CAP>
 const void* tree_instance(int proto, bool small) {
+  if (proto == kSimpleSplitTree) {
+    if constexpr (CAP) return nullptr;   // the captured form is never split
+    else return (const void*)&tree_kernel_split<E, OP>;
+  }
   if (proto == kLL) return small ? (const void*)&tree_kernel<E, OP, kLL, true, CAP>
                                  : (const void*)&tree_kernel<E, OP, kLL, false, CAP>;
   if (proto == kLL128) return (const void*)&tree_kernel<E, OP, kLL128, false, CAP>;

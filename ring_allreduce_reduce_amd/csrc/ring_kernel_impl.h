@@ -313,6 +313,9 @@ template <int PROTO> __device__ __forceinline__ Conn conn_at(const KernelArgs& a
   return Conn{a.fifo + idx * fifo_conn_bytes(PROTO), a.counters + idx * kCounterWords + kTailWord,
               a.counters + idx * kCounterWords + kHeadWord};
 }
+// The second half's counter words of a connection (split tree form).
+__device__ __forceinline__ uint64_t* tail2_of(const Conn& c) { return c.tail + (kTail2Word - kTailWord); }
+__device__ __forceinline__ uint64_t* head2_of(const Conn& c) { return c.head + (kHead2Word - kHeadWord); }
 
 // A wavefront's connections: one input and one output on the ring; a tree
 // vertex receives from up to two children and sends to up to two.  All
@@ -331,6 +334,12 @@ struct Lane {
   Waiter w;
   bool cap;            // a captured call (the kernel instance's constant)
   uint32_t zbytes;     // captured line protocols: most slot bytes a slice read
+  // split tree form (primitives flagged kSplit): whether the producer of
+  // each input / the consumer of each output runs as two halves, and
+  // whether this wavefront is one half of its role (and which)
+  bool in_split[2], out_split[2], my_split;
+  int my_half;
+  uint64_t tail2_seen[2], head2_seen[2];
 #ifdef RINGAR_ROLE_PROFILE
   uint64_t w_in, w_out, n_sl;   // wall-clock ticks waiting for inputs / output slots, slices
 #endif
@@ -349,7 +358,10 @@ static __device__ unsigned long long g_role_profile[kRoleProfileWaves][8];
 // Primitive flags: receive (from input 0, and input 1 with kRecv2), send (to
 // output 0, and output 1 with kSend2), read the own send buffer, write the
 // own receive buffer.
-enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8, kRecv2 = 16, kSend2 = 32, kPost = 64 };
+enum : int { kRecv = 1, kSend = 2, kSrc = 4, kDst = 8, kRecv2 = 16, kSend2 = 32, kPost = 64, kSplit = 128 };
+// kSplit: the split tree form; the Lane's split fields say which of the
+// connection's counter words to wait for and write, and the slice is this
+// wavefront's half (see slice_simple).
 // kPost: the primitive where a chunk becomes final applies the op's postOp
 // (the average's division by n, [ARCH] §九.4 recvReduceCopySend's postOp).
 template <int OP> constexpr int post_flag() { return OP == 4 ? kPost : 0; }
@@ -360,8 +372,9 @@ template <int OP> constexpr int post_flag() { return OP == 4 ? kPost : 0; }
 // complete, and waiting for them here would add a round trip to every step.
 template <int F> __device__ __forceinline__ void release_slot(Lane& L) {
   compiler_fence();
-  st_relaxed(L.in[0].head, L.a->base + L.rstep + 1);
-  if (F & kRecv2) st_relaxed(L.in[1].head, L.a->base + L.rstep + 1);
+  const bool second = (F & kSplit) && L.my_split && L.my_half;
+  st_relaxed(second ? head2_of(L.in[0]) : L.in[0].head, L.a->base + L.rstep + 1);
+  if (F & kRecv2) st_relaxed(second ? head2_of(L.in[1]) : L.in[1].head, L.a->base + L.rstep + 1);
   L.rstep++;
 }
 
@@ -398,8 +411,14 @@ template <int PROTO> __device__ __forceinline__ void finish_input(const Lane& L,
 // the next step.
 template <int F> __device__ __forceinline__ bool wait_inputs(Lane& L) {
   const KernelArgs& a = *L.a;
-  if ((F & kRecv) && !wait_ge(L.w, L.in[0].tail, a.base + L.rstep + 1, L.tail_seen[0])) return false;
-  if ((F & kRecv2) && !wait_ge(L.w, L.in[1].tail, a.base + L.rstep + 1, L.tail_seen[1])) return false;
+  const uint64_t need = a.base + L.rstep + 1;
+  if ((F & kRecv) && !wait_ge(L.w, L.in[0].tail, need, L.tail_seen[0])) return false;
+  if ((F & kRecv2) && !wait_ge(L.w, L.in[1].tail, need, L.tail_seen[1])) return false;
+  if constexpr ((F & kSplit) != 0) {
+    // a split producer publishes each half's tail on its own word
+    if ((F & kRecv) && L.in_split[0] && !wait_ge(L.w, tail2_of(L.in[0]), need, L.tail2_seen[0])) return false;
+    if ((F & kRecv2) && L.in_split[1] && !wait_ge(L.w, tail2_of(L.in[1]), need, L.tail2_seen[1])) return false;
+  }
   return true;
 }
 template <int F> __device__ __forceinline__ bool wait_outputs(Lane& L) {
@@ -408,14 +427,20 @@ template <int F> __device__ __forceinline__ bool wait_outputs(Lane& L) {
   const uint64_t need = a.base + L.sstep + 1 - a.depth;
   if ((F & kSend) && !wait_ge(L.w, L.out[0].head, need, L.head_seen[0])) return false;
   if ((F & kSend2) && !wait_ge(L.w, L.out[1].head, need, L.head_seen[1])) return false;
+  if constexpr ((F & kSplit) != 0) {
+    // a split consumer frees each half of a slot on its own word
+    if ((F & kSend) && L.out_split[0] && !wait_ge(L.w, head2_of(L.out[0]), need, L.head2_seen[0])) return false;
+    if ((F & kSend2) && L.out_split[1] && !wait_ge(L.w, head2_of(L.out[1]), need, L.head2_seen[1])) return false;
+  }
   return true;
 }
 
 // Publishes the tails of the outputs after the step's data stores.
 template <int F> __device__ __forceinline__ void publish_tails(Lane& L) {
   wait_mem();
-  st_relaxed(L.out[0].tail, L.a->base + L.sstep + 1);
-  if (F & kSend2) st_relaxed(L.out[1].tail, L.a->base + L.sstep + 1);
+  const bool second = (F & kSplit) && L.my_split && L.my_half;
+  st_relaxed(second ? tail2_of(L.out[0]) : L.out[0].tail, L.a->base + L.sstep + 1);
+  if (F & kSend2) st_relaxed(second ? tail2_of(L.out[1]) : L.out[1].tail, L.a->base + L.sstep + 1);
   L.sstep++;
 }
 
@@ -448,7 +473,7 @@ template <class E, int OP, int F> __device__ __forceinline__ u32x4 combine(u32x4
 template <class E, int OP, int F>
 __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0, uint32_t nelem) {
   const KernelArgs& a = *L.a;
-  const uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
+  uint32_t nbytes = nelem * (uint32_t)sizeof(typename E::T);
 #ifdef RINGAR_ROLE_PROFILE
   const uint64_t t0 = wall_clock64();
   if (!wait_inputs<F>(L)) return false;
@@ -460,12 +485,31 @@ __device__ __forceinline__ bool slice_simple(Lane& L, uint64_t es0, uint64_t ed0
 #else
   if (!wait_inputs<F>(L) || !wait_outputs<F>(L)) return false;
 #endif
-  const uint32_t rslot = (uint32_t)(L.rstep & (a.depth - 1)) * kSimpleSlotBytes;
-  const uint32_t sslot = (uint32_t)(L.sstep & (a.depth - 1)) * kSimpleSlotBytes;
-  rsrc_t rin = make_rsrc(L.in[0].fifo + rslot, kSimpleSlotBytes);
-  rsrc_t rin2 = make_rsrc(L.in[(F & kRecv2) ? 1 : 0].fifo + rslot, kSimpleSlotBytes);
-  rsrc_t rout = make_rsrc(L.out[0].fifo + sslot, kSimpleSlotBytes);
-  rsrc_t rout2 = make_rsrc(L.out[(F & kSend2) ? 1 : 0].fifo + sslot, kSimpleSlotBytes);
+  uint32_t rslot = (uint32_t)(L.rstep & (a.depth - 1)) * kSimpleSlotBytes;
+  uint32_t sslot = (uint32_t)(L.sstep & (a.depth - 1)) * kSimpleSlotBytes;
+  uint32_t slot_bytes = kSimpleSlotBytes;
+  if constexpr ((F & kSplit) != 0) {
+    // one half of a split role: the first (second) half of the slice's
+    // elements, cut at a whole 16-byte unit; in every slot it reads or
+    // writes, the same half (the other wavefront of the role takes the
+    // rest, and an unsplit peer the whole slot)
+    if (L.my_split) {
+      const uint32_t unit = 16 / (uint32_t)sizeof(typename E::T);
+      const uint32_t hb = min((uint32_t)div_up(div_up(nelem, 2), unit) * unit, nelem);
+      const uint32_t skip = L.my_half ? hb : 0;
+      es0 += skip;
+      ed0 += skip;
+      nelem = L.my_half ? nelem - hb : hb;
+      nbytes = nelem * (uint32_t)sizeof(typename E::T);
+      rslot += skip * (uint32_t)sizeof(typename E::T);
+      sslot += skip * (uint32_t)sizeof(typename E::T);
+      slot_bytes -= skip * (uint32_t)sizeof(typename E::T);
+    }
+  }
+  rsrc_t rin = make_rsrc(L.in[0].fifo + rslot, slot_bytes);
+  rsrc_t rin2 = make_rsrc(L.in[(F & kRecv2) ? 1 : 0].fifo + rslot, slot_bytes);
+  rsrc_t rout = make_rsrc(L.out[0].fifo + sslot, slot_bytes);
+  rsrc_t rout2 = make_rsrc(L.out[(F & kSend2) ? 1 : 0].fifo + sslot, slot_bytes);
   rsrc_t rsrc_ = make_rsrc(L.src + es0 * sizeof(typename E::T), nbytes);
   rsrc_t rdst = make_rsrc(L.dst + ed0 * sizeof(typename E::T), nbytes);
   const uint32_t npk = (nbytes + 15) / 16;               // 16-byte packets
@@ -1419,10 +1463,119 @@ __device__ __forceinline__ void tree_body(const TreeArgs& ta) {
 // The tree's Simple kernels carry the ring's launch bound (4 workgroups of
 // 256 per CU, so at most 128 VGPRs: the 3840-wavefront launches of large
 // calls need occupancy 4); the line protocols keep their registers.
+// ----------------------------------------------------------------- split tree (Simple)
+// The split form of the tree AllReduce: every role that moves four or more
+// units of its channel per element (the root's reduce role, the reduce and
+// broadcast roles of a vertex with two children) runs as two wavefronts,
+// each on half of every slice, so that the roles that set the tree's pace
+// have twice the loads in flight.  Its connections keep their slots; a
+// split producer publishes each half's tail on a word of its own and a
+// split consumer frees each half on a word of its own, and the other side
+// waits for both.  Eager calls only (the plan never splits a captured call).
+template <class E, int OP>
+__device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
+  constexpr int PROTO = kSimple;
+  const KernelArgs& a = ta.k;
+  const int n = a.nranks;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int group, role;
+  block_group(blockIdx.x, ta.nroles, a.xcd_major, &group, &role);
+  const int lane_blocks = a.lanes / a.lanes_per_block;
+  if (group >= a.nchannels * lane_blocks) return;   // XCD-major padding
+  const int c = group / lane_blocks;
+  const int l = (group % lane_blocks) * a.lanes_per_block + wave;
+  const int t = c & 1;
+  const int root = ta.root[t];
+  const int entry = ta.role_of[t][role];
+  const int v = entry & 63;
+  const bool bcast = (entry >> 6) & 1;
+  if (v == a.skip_ring_index) return;
+  const uint32_t es = sizeof(typename E::T);
+
+  auto nkids = [&](int u) { return (ta.child[t][0][u] >= 0 ? 1 : 0) + (ta.child[t][1][u] >= 0 ? 1 : 0); };
+  Lane L;
+  L.a = &a;
+  L.w.a = &a;
+  L.lane = threadIdx.x & 63;
+  L.cap = false;
+  L.zbytes = 0;
+  L.sstep = 0;
+  L.rstep = 0;
+  L.tail_seen[0] = L.tail_seen[1] = 0;
+  L.head_seen[0] = L.head_seen[1] = 0;
+  L.tail2_seen[0] = L.tail2_seen[1] = 0;
+  L.head2_seen[0] = L.head2_seen[1] = 0;
+  L.src = a.send[v];
+  L.dst = a.recv[v];
+  const int s0 = ta.child[t][0][v], s1 = ta.child[t][1][v];
+  const int k0 = s0 >= 0 ? s0 : s1;
+  const int k1 = s0 >= 0 ? s1 : -1;
+  const int nk = (k0 >= 0 ? 1 : 0) + (k1 >= 0 ? 1 : 0);
+  const int k0c = k0 >= 0 ? k0 : v, k1c = k1 >= 0 ? k1 : k0c;
+  L.my_split = tree_role_splits(bcast, v == root, nk);
+  L.my_half = (entry >> 7) & 1;
+  L.in_split[0] = L.in_split[1] = false;
+  L.out_split[0] = L.out_split[1] = false;
+  if (!bcast) {
+    // inputs: the children's up connections, written by their reduce roles
+    L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kUp, l, n, a.lanes));
+    L.in[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kUp, l, n, a.lanes));
+    L.in_split[0] = k0 >= 0 && tree_role_splits(false, false, nkids(k0));
+    L.in_split[1] = k1 >= 0 && tree_role_splits(false, false, nkids(k1));
+    if (v == root) {
+      // outputs: the children's down connections, read by their broadcast roles
+      L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
+      L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
+      L.out_split[0] = k0 >= 0 && tree_role_splits(true, false, nkids(k0));
+      L.out_split[1] = k1 >= 0 && tree_role_splits(true, false, nkids(k1));
+    } else {
+      // output: the up connection to the parent, read by its reduce role
+      const int p = ta.parent[t][v];
+      L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kUp, l, n, a.lanes));
+      L.out[1] = L.out[0];
+      L.out_split[0] = L.out_split[1] = tree_role_splits(false, p == root, nkids(p));
+    }
+  } else {
+    // input: the down connection from the parent (its broadcast role, or the
+    // root's reduce role); outputs: the children's down connections
+    const int p = ta.parent[t][v];
+    L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kDown, l, n, a.lanes));
+    L.in[1] = L.in[0];
+    L.in_split[0] = L.in_split[1] = tree_role_splits(p != root, p == root, nkids(p));
+    L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
+    L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
+    L.out_split[0] = k0 >= 0 && tree_role_splits(true, false, nkids(k0));
+    L.out_split[1] = k1 >= 0 && tree_role_splits(true, false, nkids(k1));
+  }
+
+  uint64_t lo, hi;
+  channel_bounds(a.count, a.per_channel, c, &lo, &hi);
+  const uint64_t len = hi - lo;
+  constexpr int S = kSplit;
+  if (!bcast && v == root) {
+    constexpr int P = post_flag<OP>();
+    if (nk == 1) tree_chunks<E, OP, PROTO, false, kSrc | kRecv | kDst | kSend | P | S>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, false, kSrc | kRecv | kRecv2 | kDst | kSend | kSend2 | P | S>(L, lo, len, l, es);
+  } else if (!bcast) {
+    if (nk == 0) tree_chunks<E, OP, PROTO, false, kSrc | kSend | S>(L, lo, len, l, es);
+    else if (nk == 1) tree_chunks<E, OP, PROTO, false, kSrc | kRecv | kSend | S>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, false, kSrc | kRecv | kRecv2 | kSend | S>(L, lo, len, l, es);
+  } else {
+    if (nk == 0) tree_chunks<E, OP, PROTO, false, kRecv | kDst | S>(L, lo, len, l, es);
+    else if (nk == 1) tree_chunks<E, OP, PROTO, false, kRecv | kDst | kSend | S>(L, lo, len, l, es);
+    else tree_chunks<E, OP, PROTO, false, kRecv | kDst | kSend | kSend2 | S>(L, lo, len, l, es);
+  }
+}
+
 template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
 __global__ void __launch_bounds__(256, 4) tree_kernel_simple(const TreeArgs ta) {
   static_assert(PROTO == kSimple, "the line protocols run tree_kernel");
   tree_body<E, OP, PROTO, SMALL, CAP>(ta);
+}
+// The split form, an entry point of its own (its primitives carry kSplit).
+template <class E, int OP>
+__global__ void __launch_bounds__(256, 4) tree_kernel_split(const TreeArgs ta) {
+  tree_body_split<E, OP>(ta);
 }
 template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
 __global__ void __launch_bounds__(256) tree_kernel(const TreeArgs ta) {

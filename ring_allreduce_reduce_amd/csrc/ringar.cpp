@@ -65,6 +65,7 @@ struct Env {
   int lanes = 0;
   int fifo_depth = 0;
   int block_map = 0;           // as ringar_config_t::block_map (a config's nonzero value wins)
+  int tree_split = 1;          // 0: the tree's Simple roles never split
 };
 
 // RINGAR_PROTO / RINGAR_ALGO: comma-separated names (case-insensitive); a
@@ -110,6 +111,7 @@ const Env& env() {
     if (const char* v = getenv("RINGAR_LANES")) e.lanes = atoi(v);
     if (const char* v = getenv("RINGAR_FIFO_DEPTH")) e.fifo_depth = atoi(v);
     if (const char* v = getenv("RINGAR_BLOCK_MAP")) e.block_map = atoi(v);
+    if (const char* v = getenv("RINGAR_TREE_SPLIT")) e.tree_split = atoi(v);
   });
   return e;
 }
@@ -271,6 +273,25 @@ void tree_links(int n, int t, int rank, int* up, int* c0, int* c1) {
   *c1 = back(d1);
 }
 
+// The wavefronts of the split tree form per (channel, lane) on tree t, in
+// vertex order (reduce role, then broadcast role; a split role twice, its
+// halves 0 and 1), written to role_of as vertex | broadcast << 6 | half << 7.
+int tree_split_roles(int n, int t, uint8_t* role_of) {
+  int cnt = 0;
+  for (int v = 0; v < n; v++) {
+    int u, c0, c1;
+    tree_links(n, t, v, &u, &c0, &c1);
+    const int nk = (c0 >= 0 ? 1 : 0) + (c1 >= 0 ? 1 : 0);
+    const int up = tree_role_splits(false, u < 0, nk) ? 2 : 1;
+    for (int h = 0; h < up; h++) role_of[cnt++] = (uint8_t)(v | (h << 7));
+    if (u >= 0) {
+      const int down = tree_role_splits(true, false, nk) ? 2 : 1;
+      for (int h = 0; h < down; h++) role_of[cnt++] = (uint8_t)(v | 64 | (h << 7));
+    }
+  }
+  return cnt;
+}
+
 int model_max_channels(const ringar_model_t& m, int n) {
   int c = std::min(m.max_channels, m.max_pairs / std::max(1, n));
   return std::max(1, std::min(c, kMaxChannels));
@@ -324,6 +345,8 @@ struct Plan {
   bool small = false;      // every lane part fits the small-slice form
   bool direct = false;     // direct form requested and possible (if out of place)
   bool direct_auto = false;// the library chose it (a captured call then keeps its FIFOs)
+  bool tree_split = false; // the split tree form (tree_body_split)
+  int tree_waves = 0;      // its wavefronts per (channel, lane)
   bool xcd_major = false;  // block ids map XCD-major (launch_grid, block_group)
   int lanes_per_block = 1;
   int grid = 0;
@@ -338,6 +361,7 @@ struct Plan {
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 constexpr uint64_t kTargetWaves = 4096;
+constexpr uint64_t kTreeSplitMinChannelBytes = 256 << 10;   // the split tree form's smallest channel
 
 // Largest bytes per rank that take the XCD-major block mapping (below).
 constexpr uint64_t kXcdMajorMaxBytes = 512 << 10;
@@ -372,7 +396,8 @@ uint64_t fifo_bytes_for(int proto, uint64_t bytes) {
 // config) or one of its halves (count = elements per block; AllGather plans
 // bytes, dtype int8).
 ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannels, int proto,
-                          const ringar_config_t* cfg, uint64_t capacity_waves, Plan* out) {
+                          const ringar_config_t* cfg, uint64_t capacity_waves, Plan* out,
+                          bool captured = false) {
   const Env& E = env();
   const size_t es = elem_size(dtype);
   if (!es) return RINGAR_ERR_INVALID_ARGUMENT;
@@ -517,6 +542,32 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
     while (lanes < kLL128MaxAutoLanes && (uint64_t)(lanes * 2) * kLL128LaneBytes <= first_chunk * es) lanes *= 2;
     while (lanes < kMaxLanes && slices_for(lanes) > kMaxSlicesPerPart) lanes *= 2;
   }
+  // The split tree form (eager Simple calls of at least
+  // kTreeSplitMinChannelBytes per channel): the roles that move four or more
+  // units per element run as two wavefronts, so a lane takes more
+  // wavefronts and the grid's 4096 fewer lanes, of any count (whole
+  // workgroups of 4, 2 or 1 wavefronts).  Measured at n = 3..16 on MI355X,
+  // it takes 2-8% off calls of 256 KiB per channel and more, and adds 3-29%
+  // to smaller ones, whose fewer lanes cost more than the halves gain.
+  P.tree_split = false;
+  if (tree && P.proto == kSimple && !captured && E.tree_split && n > 1 &&
+      P.per_channel * es >= kTreeSplitMinChannelBytes) {
+    uint8_t roles[2][4 * kMaxRanks];
+    const int r0 = tree_split_roles(n, 0, roles[0]), r1 = tree_split_roles(n, 1, roles[1]);
+    const uint64_t wpl2 = (uint64_t)r0 * P.nch;
+    const uint64_t cap = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
+    int l2 = lanes;
+    if (!forced_lanes) {
+      const uint64_t want = std::max<uint64_t>(1, div_up(first_chunk * es, lane_gran_bytes(P.proto)));
+      l2 = (int)std::min<uint64_t>(std::min<uint64_t>(want, kMaxLanes), cap / wpl2);
+    }
+    const bool small_parts = l2 >= 1 && lane_part(first_chunk, l2, (uint32_t)es, P.proto) * es <= kSmallSliceBytes;
+    if (r0 == r1 && l2 >= 1 && wpl2 * l2 <= cap && !small_parts && slices_for(l2) <= kMaxSlicesPerPart) {
+      lanes = l2;
+      P.tree_split = true;
+      P.tree_waves = r0;
+    }
+  }
   if (slices_for(lanes) > kMaxSlicesPerPart)
     return forced_lanes ? RINGAR_ERR_INVALID_USAGE : RINGAR_ERR_INVALID_ARGUMENT;
   P.lanes = lanes;
@@ -552,7 +603,8 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   P.direct = direct_ok && (direct_req == 1 || P.direct_auto);
   P.small = P.proto != kLL128 && lane_part(first_chunk, lanes, (uint32_t)es, P.proto) * es <= kSmallSliceBytes &&
             !(cfg && cfg->force_general) && !P.direct;
-  P.lanes_per_block = std::min(lanes, 4);
+  // whole workgroups: 4 lanes, else 2, else 1
+  P.lanes_per_block = lanes % 4 == 0 ? 4 : lanes % 2 == 0 ? 2 : 1;
   P.block = 64 * P.lanes_per_block;
   const int groups = P.nch * (lanes / P.lanes_per_block);
   // Block mapping: latency-bound calls put every rank (tree: every role) of
@@ -570,7 +622,7 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   const int block_map = (cfg && cfg->block_map) ? cfg->block_map : E.block_map;
   if (block_map < 0 || block_map > 2) return RINGAR_ERR_INVALID_ARGUMENT;
   P.xcd_major = block_map ? block_map == 2 : (uint64_t)bytes <= xcd_limit;
-  P.grid = launch_grid(tree ? tree_roles(n) : n, groups, P.xcd_major);
+  P.grid = launch_grid(P.tree_split ? P.tree_waves : tree ? tree_roles(n) : n, groups, P.xcd_major);
   P.conns = (uint64_t)P.nch * n * lanes * (tree ? 2 : 1);
 
   // Upper bound of FIFO steps any connection takes in this call.
@@ -703,7 +755,7 @@ uint64_t capacity_waves(int coll, int dtype, int op, int proto, bool cap) {
   if (ndev == 0) return 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const long long key = (((((long long)dev * 4 + coll) * 8 + dtype) * 5 + op) * 3 + proto) * 2 + (cap ? 1 : 0);
+  const long long key = (((((long long)dev * 4 + coll) * 8 + dtype) * 5 + op) * 4 + proto) * 2 + (cap ? 1 : 0);
   // the general form: the small one needs no more registers
   static std::mutex mu;
   static std::map<long long, uint64_t> cache;
@@ -855,11 +907,13 @@ static void kernel_shape(int coll, size_t count, int dtype, size_t* kcount, int*
 // fewer wavefronts; a lower residency only ever takes fewer lanes).
 static ringar_result_t plan_for_launch(int coll, size_t count, int dtype, int op, int nranks, int nchannels,
                                 int proto, const ringar_config_t* cfg, Plan* P, bool captured = false) {
-  ringar_result_t r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, 0, P);
+  ringar_result_t r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, 0, P, captured);
   if (r != RINGAR_SUCCESS) return r;
   if (count > 0 && nranks > 1) {
-    const uint64_t cap = capacity_waves(P->kind, dtype, op, P->proto, captured);
-    if (cap && (r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, cap, P)) != RINGAR_SUCCESS)
+    const uint64_t cap =
+        capacity_waves(P->kind, dtype, op, P->tree_split ? kSimpleSplitTree : P->proto, captured);
+    if (cap && (r = make_plan(coll, count, dtype, nranks, nchannels, proto, cfg, cap, P, captured)) !=
+                   RINGAR_SUCCESS)
       return r;
   }
   return RINGAR_SUCCESS;
@@ -897,6 +951,8 @@ ringar_result_t ringar_plan_coll(ringar_coll_t coll, size_t count, ringar_dtype_
   out->algo = P.kind == kTreeAllReduce ? RINGAR_ALGO_TREE : RINGAR_ALGO_RING;
   out->direct = P.direct ? 1 : 0;
   out->xcd_major = P.xcd_major ? 1 : 0;
+  out->tree_split = P.tree_split ? 1 : 0;
+  out->tree_waves_per_lane = P.tree_split ? P.tree_waves : 0;
   return RINGAR_SUCCESS;
 }
 
@@ -1112,12 +1168,14 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   for (int q = 0; q < nranks; q++)
     if (((uintptr_t)sendbuffs[q] | (uintptr_t)recvbuffs[q]) % 16) vec = 0;
   const bool small = P.small && vec;
-  const long long okey = ((((long long)P.kind * 8 + dtype) * 5 + op) * 3 + P.proto) * 4096 +
+  // the kernel's selector: the protocol, or the split tree's own entry
+  const int kproto = P.tree_split ? kSimpleSplitTree : P.proto;
+  const long long okey = ((((long long)P.kind * 8 + dtype) * 5 + op) * 4 + kproto) * 4096 +
                          (captured ? 2048 : 0) + (small ? 1024 : 0) + P.block;
   auto oc = g_occupancy.find(okey);
   if (oc == g_occupancy.end()) {
     int per_cu = 0;
-    HIP_TRY(max_active_blocks(P.kind, dtype, op, P.proto, small, captured, P.block, &per_cu));
+    HIP_TRY(max_active_blocks(P.kind, dtype, op, kproto, small, captured, P.block, &per_cu));
     oc = g_occupancy.emplace(okey, per_cu).first;
   }
   if ((long long)oc->second * num_cus < P.grid) return RINGAR_ERR_INVALID_USAGE;
@@ -1209,7 +1267,11 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
         T.child[t][1][v] = (int8_t)c1;
         if (u < 0) T.root[t] = v;
       }
-    HIP_TRY(launch_tree(dtype, op, P.proto, small, captured, T, P.grid, P.block, st));
+    if (P.tree_split) {
+      T.nroles = P.tree_waves;
+      for (int t = 0; t < 2; t++) tree_split_roles(nranks, t, T.role_of[t]);
+    }
+    HIP_TRY(launch_tree(dtype, op, kproto, small, captured, T, P.grid, P.block, st));
   } else {
     HIP_TRY(launch_ring(coll, dtype, op, P.proto, small, captured, A, P.grid, P.block, st));
   }

@@ -278,8 +278,9 @@ def test_block_map_rule_and_grid():
                     cfg = ra.make_config(algo=algo)
                     plan = ra.ringar_plan(nbytes // 4, "float32", 8, nch, proto, cfg)
                     assert plan.xcd_major == int(nbytes <= limit), (proto, algo, nbytes, nch)
-                    members = 15 if algo == "tree" else 8
-                    groups = plan.nchannels * (plan.lanes // min(plan.lanes, 4))
+                    members = (plan.tree_waves_per_lane if plan.tree_split else 15) if algo == "tree" else 8
+                    lpb = 4 if plan.lanes % 4 == 0 else 2 if plan.lanes % 2 == 0 else 1
+                    groups = plan.nchannels * (plan.lanes // lpb)
                     want = 8 * members * -(-groups // 8) if plan.xcd_major else members * groups
                     assert plan.workgroups == want, (proto, algo, nbytes, nch)
     for m in (1, 2):

@@ -36,6 +36,25 @@ def test_tree_query_errors():
             ra.ringar_tree(*args)
 
 
+def split_waves(n):
+    """Wavefronts per (channel, lane) of the split form: every vertex's
+    reduce role and every other vertex's broadcast role, twice for the root's
+    reduce role and for either role of a vertex with two children (both
+    trees have the same count)."""
+    counts = []
+    for t in (0, 1):
+        c = 0
+        for v in range(n):
+            parent, c0, c1 = ra.ringar_tree(n, t, v)
+            kids = (c0 >= 0) + (c1 >= 0)
+            c += 2 if (parent < 0 or kids == 2) else 1
+            if parent >= 0:
+                c += 2 if kids == 2 else 1
+        counts.append(c)
+    assert counts[0] == counts[1]
+    return counts[0]
+
+
 @pytest.mark.parametrize("n,count,nch,proto", [(8, 1 << 24, 16, "Simple"), (8, 1 << 15, 8, "LL"),
                                                (5, 1000, 3, "LL128"), (2, 17, 1, "Simple")])
 def test_tree_plan_geometry(n, count, nch, proto):
@@ -43,11 +62,16 @@ def test_tree_plan_geometry(n, count, nch, proto):
     p = ra.ringar_plan(count, "float32", n, nch, proto, cfg)
     assert p.algo == 1
     assert p.nchannels == nch
-    lanes_per_block = min(p.lanes, 4)
+    # whole workgroups of 4, 2 or 1 lanes
+    lanes_per_block = 4 if p.lanes % 4 == 0 else 2 if p.lanes % 2 == 0 else 1
     assert p.threads_per_group == 64 * lanes_per_block
     groups = nch * (p.lanes // lanes_per_block)
-    # the XCD-major mapping of small calls pads the groups to whole rounds of 8
-    assert p.workgroups == (2 * n - 1) * (-(-groups // 8) * 8 if p.xcd_major else groups)
+    # 2n - 1 roles per (channel, lane), or the split form's count; the
+    # XCD-major mapping of small calls pads the groups to whole rounds of 8
+    members = p.tree_waves_per_lane if p.tree_split else 2 * n - 1
+    if p.tree_split:
+        assert members == split_waves(n)
+    assert p.workgroups == members * (-(-groups // 8) * 8 if p.xcd_major else groups)
     # the tree moves one chunk of the channel per step: a lane part is at
     # most half the FIFO
     slot = {"Simple": 32768, "LL": 8192, "LL128": 30720}[proto] // 4
@@ -207,3 +231,22 @@ def test_tree_chunk_rule():
     assert p.chunk_elems * 4 == 512 << 10
     # the bench shape: 64 MiB per rank, 16 channels -> 128 KiB
     assert ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", cfg).chunk_elems * 4 == 128 << 10
+
+
+def test_split_form_rule():
+    """The split form runs eager Simple tree calls of at least 256 KiB per
+    channel; line protocols and smaller channels keep one wavefront a role."""
+    cfg = ra.make_config(algo="tree")
+    for nbytes, nch, want in [(8 << 20, 32, 1), (4 << 20, 32, 0), (4 << 20, 16, 1), (64 << 20, 32, 1),
+                              ((8 << 20) - 4096, 32, 0)]:
+        p = ra.ringar_plan(nbytes // 4, "float32", 8, nch, "Simple", cfg)
+        assert p.tree_split == want, (nbytes, nch)
+        assert p.tree_waves_per_lane == (split_waves(8) if want else 0)
+        # every wavefront of the launch is resident at once
+        assert p.lanes * p.nchannels * (p.tree_waves_per_lane or 15) <= 4096
+    for proto in ("LL", "LL128"):
+        p = ra.ringar_plan((64 << 20) // 4, "float32", 8, 32, proto, cfg)
+        assert p.tree_split == 0 and p.tree_waves_per_lane == 0
+    # the ring never splits
+    p = ra.ringar_plan((64 << 20) // 4, "float32", 8, 32, "Simple", ra.make_config(algo="ring"))
+    assert p.tree_split == 0
