@@ -349,8 +349,10 @@ struct Lane {
 // Role profile (a diagnostic build, never the library's own): per wavefront
 // of a tree launch, its first and last wall-clock tick, the ticks its Simple
 // slices waited for their inputs and for free output slots, the slices, and
-// its role.  Written by lane 0 of every wavefront of the eager Simple tree
-// kernels of one element type's translation unit.
+// its role (vertex, broadcast bit, children, root bit; in the split form
+// whether the role splits and which half this is).  Written by lane 0 of
+// every wavefront of the eager Simple tree kernels of one element type's
+// translation unit.
 constexpr int kRoleProfileWaves = 4096;
 static __device__ unsigned long long g_role_profile[kRoleProfileWaves][8];
 #endif
@@ -1505,6 +1507,10 @@ __device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
   L.head_seen[0] = L.head_seen[1] = 0;
   L.tail2_seen[0] = L.tail2_seen[1] = 0;
   L.head2_seen[0] = L.head2_seen[1] = 0;
+#ifdef RINGAR_ROLE_PROFILE
+  L.w_in = L.w_out = L.n_sl = 0;
+  const uint64_t tstart = wall_clock64();
+#endif
   L.src = a.send[v];
   L.dst = a.recv[v];
   const int s0 = ta.child[t][0][v], s1 = ta.child[t][1][v];
@@ -1565,6 +1571,23 @@ __device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
     else if (nk == 1) tree_chunks<E, OP, PROTO, false, kRecv | kDst | kSend | S>(L, lo, len, l, es);
     else tree_chunks<E, OP, PROTO, false, kRecv | kDst | kSend | kSend2 | S>(L, lo, len, l, es);
   }
+#ifdef RINGAR_ROLE_PROFILE
+  if (L.lane == 0) {
+    const uint32_t id = blockIdx.x * (blockDim.x / 64) + wave;
+    if (id < (uint32_t)kRoleProfileWaves) {
+      unsigned long long* r = g_role_profile[id];
+      r[0] = tstart;
+      r[1] = wall_clock64();
+      r[2] = L.w_in;
+      r[3] = L.w_out;
+      r[4] = L.n_sl;
+      r[5] = (uint64_t)v | ((uint64_t)bcast << 8) | ((uint64_t)nk << 16) | ((uint64_t)(v == root) << 24) |
+             ((uint64_t)L.my_split << 32) | ((uint64_t)L.my_half << 33);
+      r[6] = (uint64_t)c;
+      r[7] = (uint64_t)l;
+    }
+  }
+#endif
 }
 
 template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>

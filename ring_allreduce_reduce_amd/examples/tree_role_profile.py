@@ -3,7 +3,9 @@
 Uses a diagnostic build of the library whose Simple tree kernels record,
 per wavefront, its first and last wall-clock tick, the ticks its slices
 waited for their inputs (the children's, or the parent's on the way down)
-and for free output slots, and its role.  Prints, per kind of role, the
+and for free output slots, and its role (in the split form, the two halves
+of a split role apart).  RINGAR_TREE_SPLIT=0 in the environment profiles
+the form with one wavefront a role.  Prints, per kind of role, the
 mean over its wavefronts.  The diagnostic build is never the library the
 package loads by default.
 
@@ -47,13 +49,17 @@ def main(lib_path):
         assert lib.ringar_role_profile(buf.ctypes.data, buf.nbytes, 0) == 0
         rows = buf[buf[:, 1] > 0].astype(np.int64)
         t0, t1 = rows[:, 0].min(), rows[:, 1].max()
-        print(f"\n{nbytes >> 20} MiB per rank, {nch} channels, {plan.lanes} lanes, chunk {plan.chunk_bytes >> 10} KiB: "
+        form = f"split form, {plan.tree_waves_per_lane} wavefronts per lane" if plan.tree_split else "one wavefront a role"
+        print(f"\n{nbytes >> 20} MiB per rank, {nch} channels, {plan.lanes} lanes, chunk {plan.chunk_bytes >> 10} KiB, {form}: "
               f"{len(rows)} wavefronts, first start to last end {(t1 - t0) / ticks_per_us:.1f} us")
         groups = collections.defaultdict(list)
         for r in rows:
             info = int(r[5])
             nk, bc, root = (info >> 16) & 255, (info >> 8) & 255, (info >> 24) & 1
+            split, half = (info >> 32) & 1, (info >> 33) & 1
             kind = ("broadcast" if bc else "root" if root else "reduce") + f", {nk} children"
+            if split:
+                kind += f", half {half}"
             groups[kind].append(((r[1] - r[0]) / ticks_per_us, r[2] / ticks_per_us, r[3] / ticks_per_us, r[4],
                                  (r[0] - t0) / ticks_per_us, (t1 - r[1]) / ticks_per_us))
         print(f"  {'role':22s} {'waves':>6s} {'busy':>8s} {'wait in':>8s} {'wait out':>8s} {'slices':>7s} "
