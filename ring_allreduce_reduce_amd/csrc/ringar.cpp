@@ -447,6 +447,10 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   P.nch = nchannels > 0 ? nchannels : (n == 1 ? 1 : auto_channels(m, n, P.proto, bytes, maxc, !tree));
   P.per_channel = channel_len(count, P.nch, (uint32_t)es);
   P.chunk_bytes = chunk_bytes ? chunk_bytes : m.default_chunk_bytes[P.proto];
+  // The split tree form (below) is wanted for eager Simple tree calls of at
+  // least kTreeSplitMinChannelBytes per channel.
+  const bool split_wanted = tree && P.proto == kSimple && !captured && E.tree_split && n > 1 &&
+                            P.per_channel * es >= kTreeSplitMinChannelBytes;
   if (tree && !chunk_bytes) {
     // The tree moves a whole chunk up and then down, so a channel needs
     // several chunks for the two directions to overlap: a quarter of the
@@ -456,10 +460,15 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
     // 512 KiB chunks, 2 MiB per rank 47.5 -> 37.9 us, 8 MiB 133.7 -> 99.4
     // us, 64 MiB 620 -> 534 us; at 64 MiB the best chunk is 64 KiB at 32
     // channels (529 us), 128 KiB at 16 (550 against 593 us at 64 KiB) and
-    // 256 KiB at 8 (531 against 659 us).
+    // 256 KiB at 8 (531 against 659 us).  The split form keeps twice that
+    // in flight, in chunks of half the channel: at 64 MiB, 32 channels,
+    // 128 KiB chunks take 483 us against 495 at 64 KiB; 8 MiB 83 against
+    // 86 us; n = 5 318 against 351 us.
     const uint64_t lo = P.proto == kLL ? 4096 : 8192;
-    const uint64_t hi = std::min<uint64_t>(std::max<uint64_t>(65536, (2u << 20) / (uint64_t)P.nch), P.chunk_bytes);
-    P.chunk_bytes = std::min(hi, std::max(lo, align_up(P.per_channel * es / 4, 16)));
+    const uint64_t in_flight = split_wanted ? (4u << 20) : (2u << 20);
+    const uint64_t hi = std::min<uint64_t>(std::max<uint64_t>(split_wanted ? 131072 : 65536, in_flight / (uint64_t)P.nch),
+                                           P.chunk_bytes);
+    P.chunk_bytes = std::min(hi, std::max(lo, align_up(P.per_channel * es / (split_wanted ? 2 : 4), 16)));
   }
   if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)
     return RINGAR_ERR_INVALID_ARGUMENT;
@@ -550,8 +559,7 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // it takes 2-8% off calls of 256 KiB per channel and more, and adds 3-29%
   // to smaller ones, whose fewer lanes cost more than the halves gain.
   P.tree_split = false;
-  if (tree && P.proto == kSimple && !captured && E.tree_split && n > 1 &&
-      P.per_channel * es >= kTreeSplitMinChannelBytes) {
+  if (split_wanted) {
     uint8_t roles[2][4 * kMaxRanks];
     const int r0 = tree_split_roles(n, 0, roles[0]), r1 = tree_split_roles(n, 1, roles[1]);
     const uint64_t wpl2 = (uint64_t)r0 * P.nch;

@@ -212,25 +212,31 @@ def test_direct_form_is_planned_only_where_it_applies():
 def test_tree_chunk_rule():
     # without a configured chunk the tree takes a quarter of a channel's
     # bytes, between 8 KiB (LL: 4 KiB) and 2 MiB / channels (at least 64 KiB),
-    # and never above the protocol's default chunk
+    # and never above the protocol's default chunk; where the split form is
+    # wanted (Simple, 256 KiB per channel or more) half a channel, up to
+    # 4 MiB / channels (at least 128 KiB)
     cfg = ra.make_config(algo="tree")
     defaults = dict(zip(("LL", "LL128", "Simple"), golden_model_dict()["default_chunk_bytes"]))
     for proto in ("LL", "LL128", "Simple"):
         for nch in (1, 2, 4, 8, 16, 32):
-            for mib in (0.25, 1, 4, 64):
+            for mib in (0.25, 1, 4, 8, 64):
                 count = int(mib * (1 << 18))
                 p = ra.ringar_plan(count, "float32", 8, nch, proto, cfg)
                 per = -(-count // nch)
                 per = -(-per // 4) * 4
-                hi = min(max(64 << 10, (2 << 20) // nch), defaults[proto])
+                split = proto == "Simple" and per * 4 >= 256 << 10
+                hi = min(max((128 if split else 64) << 10, ((4 if split else 2) << 20) // nch), defaults[proto])
                 lo = 4096 if proto == "LL" else 8192
-                quarter = -(-(per * 4 // 4) // 16) * 16
-                assert p.chunk_elems * 4 == min(hi, max(lo, quarter)), (proto, nch, mib)
+                part = -(-(per * 4 // (2 if split else 4)) // 16) * 16
+                assert p.chunk_elems * 4 == min(hi, max(lo, part)), (proto, nch, mib)
+                assert p.tree_split == int(split), (proto, nch, mib)
     # a configured chunk is taken as it is
     p = ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", ra.make_config(algo="tree", chunk_bytes=512 << 10))
     assert p.chunk_elems * 4 == 512 << 10
-    # the bench shape: 64 MiB per rank, 16 channels -> 128 KiB
-    assert ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", cfg).chunk_elems * 4 == 128 << 10
+    # the bench shape: 64 MiB per rank, 16 channels -> 256 KiB (split form)
+    assert ra.ringar_plan(1 << 24, "float32", 8, 16, "Simple", cfg).chunk_elems * 4 == 256 << 10
+    # a line protocol never splits and keeps the quarter rule
+    assert ra.ringar_plan(1 << 24, "float32", 8, 16, "LL128", cfg).chunk_elems * 4 == 128 << 10
 
 
 def test_split_form_rule():
