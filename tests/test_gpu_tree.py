@@ -90,6 +90,29 @@ def test_ragged_shapes(proto, dtype, form):
               force_general=int(form == "general"), inplace=bool(i % 4 == 1))
 
 
+# The split form (Simple, 256 KiB per channel or more): ragged tails, chunks
+# that leave odd slice sizes (the halves cut at 16-byte units), forced lanes
+# and FIFO depths.  (n, channels, KiB per channel, tail elements, chunk units
+# of 16 B, lanes, FIFO depth)
+SPLIT = [
+    (2, 1, 300, 3, 0, 0, 0), (3, 2, 256, 1, 100, 1, 0), (5, 3, 400, 5, 0, 0, 4), (8, 2, 512, 9, 777, 2, 0),
+    (8, 4, 260, 15, 0, 0, 8), (16, 1, 300, 1, 0, 0, 2), (6, 1, 1024, 7, 301, 4, 2), (8, 1, 256, 0, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_form_ragged(dtype):
+    es = W.ELEM_BYTES[dtype]
+    for i, (n, nch, kib, tail, units, lanes, depth) in enumerate(SPLIT):
+        count = (kib << 10) * nch // es + tail
+        op = W.CONFIG5_OPS[i % len(W.CONFIG5_OPS)]
+        dist = ("uniform", 0.9, 1.1) if op == "prod" and dtype in W.FLOATS else ("uniform", -4, 4)
+        xs = W.inputs(f"tree-split-{dtype}-{i}", n, count, dtype, *dist)
+        outs, plan = check(xs, dtype, op, "Simple", nch, units * 16, lanes=lanes, fifo_depth=depth,
+                           inplace=bool(i % 3 == 2))
+        assert plan.tree_split == 1, (n, nch, kib, units, lanes)
+
+
 @pytest.mark.parametrize("proto", ["LL", "Simple"])
 @pytest.mark.parametrize("n", [2, 3, 8])
 def test_small_form_every_op_and_dtype(proto, n):
