@@ -256,3 +256,20 @@ def test_split_form_rule():
     # the ring never splits
     p = ra.ringar_plan((64 << 20) // 4, "float32", 8, 32, "Simple", ra.make_config(algo="ring"))
     assert p.tree_split == 0
+
+
+def test_split_form_env_switch():
+    # RINGAR_TREE_SPLIT=0 keeps one wavefront a role (and the quarter chunk
+    # rule); read in a child process because the library caches its
+    # environment
+    root = ROOT
+    code = ("import sys; sys.path.insert(0, %r); import ring_allreduce_reduce_amd as ra;"
+            "p = ra.ringar_plan(1 << 24, 'float32', 8, 32, 'Simple', ra.make_config(algo='tree'));"
+            "print(p.tree_split, p.chunk_elems * 4, p.lanes)" % root)
+    out = {}
+    for v in ("0", "1"):
+        env = dict(os.environ, RINGAR_TREE_SPLIT=v)
+        out[v] = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                                check=True).stdout.split()
+    assert out["0"][:2] == ["0", str(64 << 10)]
+    assert out["1"][:2] == ["1", str(128 << 10)]
