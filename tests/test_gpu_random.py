@@ -159,3 +159,50 @@ def test_random_halves(coll):
             assert np.array_equal(_bits(W.from_torch(recvs[r], dtype)), _bits(want[r])), (desc, r)
         ran += 1
     assert ran >= CASES * 3 // 4, (ran, skipped)
+
+
+def test_random_split_tree():
+    """Random calls that the tree runs in its split form (eager Simple, at
+    least 256 KiB per channel), every other knob drawn as above."""
+    rng = np.random.default_rng(606)
+    ran = split = 0
+    for i in range(40):
+        n = int(rng.integers(2, 17)) if rng.random() < 0.9 else int(rng.integers(17, 33))
+        dtype = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        es = W.ELEM_BYTES[dtype]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        nch = int(rng.integers(1, 9))
+        count = int(rng.integers((256 << 10) * nch // es, (1 << 20) * nch // es + 1)) + int(rng.integers(0, 17))
+        cfg = dict(algo="tree",
+                   chunk_bytes=0 if rng.random() < 0.5 else int(rng.integers(64, 16384)) * 16,
+                   lanes=0 if rng.random() < 0.7 else int(2 ** rng.integers(0, 4)),
+                   fifo_depth=0 if rng.random() < 0.7 else int([2, 4, 8][rng.integers(0, 3)]),
+                   block_map=int(rng.integers(0, 3)))
+        inplace = rng.random() < 0.2
+        unaligned = (not inplace) and rng.random() < 0.15
+        try:
+            plan = ra.ringar_plan(count, dtype, n, nch, "Simple", ra.make_config(**cfg))
+        except ra.RingarError:
+            continue
+        desc = (f"split tree case {i}: n={n} count={count} {dtype} {op} nch={nch} {cfg} inplace={inplace} "
+                f"unaligned={unaligned} -> split={plan.tree_split} lanes={plan.lanes} depth={plan.fifo_depth} "
+                f"chunk={plan.chunk_elems * es}")
+        print(desc, flush=True)
+        xs = W.inputs(f"grand-split-{i}", n, count, dtype, *_dist(op, dtype))
+        sends, recvs = _tensors(xs, dtype, count, count, unaligned)
+        if recvs is None:
+            recvs = sends if inplace else [torch.zeros_like(t) for t in sends]
+        try:
+            ra.allreduce(sends, recvs, op=op, nchannels=nch, proto="Simple", **cfg)
+        except ra.RingarError as e:
+            # e.g. a forced XCD-major mapping whose padded grid exceeds residency
+            assert e.code == ra.INVALID_USAGE, desc
+            continue
+        code = _finish()
+        assert code == 0, (desc, ra.ringar_result_string(code))
+        want = oracle.tree_allreduce(xs, dtype, op, plan.nchannels, plan.chunk_elems)
+        for r in range(n):
+            assert np.array_equal(_bits(W.from_torch(recvs[r], dtype)), _bits(want[r])), (desc, r)
+        ran += 1
+        split += plan.tree_split
+    assert ran >= 28 and split >= ran * 3 // 4, (ran, split)
