@@ -201,9 +201,13 @@ typedef struct {
  *                    place; otherwise the call runs with FIFOs as usual.
  *   block_map:       which workgroup runs which (rank, channel, lane): 0 =
  *                    by size (the XCD-major mapping up to 512 KiB per rank,
- *                    LL128 up to 32 KiB, else linear), 1 = linear, 2 =
+ *                    LL128 up to 32 KiB, else linear; linear too where the
+ *                    XCD-major grid, padded to whole rounds of 8 groups,
+ *                    would not be resident at once), 1 = linear, 2 =
  *                    XCD-major (every rank of a channel on one of MI355X's
- *                    8 XCDs).  Changes speed only, never a result. */
+ *                    8 XCDs; RINGAR_ERR_INVALID_USAGE where its padded grid
+ *                    is not resident at once).  Changes speed only, never
+ *                    a result. */
 typedef struct {
   size_t chunk_bytes;
   const int* ring_order;

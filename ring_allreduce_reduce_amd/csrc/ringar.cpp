@@ -630,7 +630,19 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   const int block_map = (cfg && cfg->block_map) ? cfg->block_map : E.block_map;
   if (block_map < 0 || block_map > 2) return RINGAR_ERR_INVALID_ARGUMENT;
   P.xcd_major = block_map ? block_map == 2 : (uint64_t)bytes <= xcd_limit;
-  P.grid = launch_grid(P.tree_split ? P.tree_waves : tree ? tree_roles(n) : n, groups, P.xcd_major);
+  const int members = P.tree_split ? P.tree_waves : tree ? tree_roles(n) : n;
+  P.grid = launch_grid(members, groups, P.xcd_major);
+  // The XCD-major grid pads the groups to whole rounds of 8 so that every
+  // XCD takes the same number of workgroups; the padded grid must still be
+  // resident at once (workgroup b runs on XCD b mod 8, so a round that does
+  // not fit stalls the dispatch).  By size, such a call takes the linear
+  // mapping; a forced XCD-major mapping is refused.
+  const uint64_t resident = std::min<uint64_t>(kTargetWaves, capacity_waves ? capacity_waves : 4096);
+  if (P.xcd_major && (uint64_t)P.grid * P.lanes_per_block > resident) {
+    if (block_map == 2) return RINGAR_ERR_INVALID_USAGE;
+    P.xcd_major = false;
+    P.grid = launch_grid(members, groups, false);
+  }
   P.conns = (uint64_t)P.nch * n * lanes * (tree ? 2 : 1);
 
   // Upper bound of FIFO steps any connection takes in this call.

@@ -292,6 +292,36 @@ def test_block_map_rule_and_grid():
         assert e.value.code == ra.INVALID_ARGUMENT
 
 
+def test_xcd_major_padding_stays_resident():
+    # the XCD-major grid pads the groups to whole rounds of 8; by size, a call
+    # whose padded grid would exceed the 4096 resident wavefronts takes the
+    # linear mapping, and a forced XCD-major mapping of it is refused
+    seen_fallback = False
+    for n in (2, 3, 5, 8, 10, 12, 16, 23, 33, 64):
+        for nbytes in (8, 4096, 131072, 262144, 524288):
+            for proto in ("auto", "LL", "Simple"):
+                for algo in ("ring", "tree", "auto"):
+                    cfg = ra.make_config(algo=algo)
+                    try:
+                        p = ra.ringar_plan(max(1, nbytes // 4), "float32", n, 0, proto, cfg)
+                    except ra.RingarError:
+                        continue
+                    assert p.workgroups * p.threads_per_group // 64 <= 4096, (n, nbytes, proto, algo)
+                    try:
+                        f = ra.ringar_plan(max(1, nbytes // 4), "float32", n, 0, proto,
+                                           ra.make_config(algo=algo, block_map=2))
+                        assert f.xcd_major and f.workgroups * f.threads_per_group // 64 <= 4096
+                    except ra.RingarError as e:
+                        assert e.code == ra.INVALID_USAGE
+                        assert not p.xcd_major, (n, nbytes, proto, algo)
+                        seen_fallback = True
+    assert seen_fallback
+    # n = 10, 128 KiB: the tree's 25 channels x 2 lane blocks pad to 56 groups
+    p = ra.ringar_plan(1 << 15, "float32", 10, 0, "Simple", ra.make_config(algo="tree"))
+    assert (p.nchannels, p.lanes, p.xcd_major) == (25, 8, 0)
+    assert p.workgroups == 19 * 50
+
+
 def test_halves_buffer_rules_before_any_device_call():
     n, count = 4, 1000
     E = ra

@@ -52,3 +52,27 @@ def test_block_map_matches_oracle(algo, proto, block_map):
         want = run(xs, dtype, op, plan.nchannels, plan.chunk_elems)
         for r in range(n):
             assert np.array_equal(_bits(W.from_torch(recvs[r], dtype)), _bits(want[r])), (algo, proto, j, r)
+
+
+@pytest.mark.parametrize("n,nbytes", [(10, 1 << 19), (12, 1 << 18), (17, 1 << 18), (24, 1 << 19)])
+def test_padding_beyond_residency_takes_the_linear_mapping(n, nbytes):
+    # small enough for the XCD-major mapping by size, but its padded grid
+    # would exceed the resident wavefronts: the plan takes the linear one,
+    # and the automatic call runs (it used to be refused at launch)
+    count = nbytes // 4
+    cfg = dict(algo="auto")
+    plan = ra.ringar_plan(count, "float32", n, 0, "auto", ra.make_config(**cfg))
+    assert not plan.xcd_major
+    print(f"case padding n={n} bytes={nbytes} algo={plan.algo} proto={plan.proto} nch={plan.nchannels} "
+          f"lanes={plan.lanes} xcd_major={plan.xcd_major} grid={plan.workgroups}", flush=True)
+    xs = W.inputs(f"blockmap-pad-{n}-{nbytes}", n, count, "float32", "uniform", -4, 4)
+    sends = [W.to_torch(x, "float32", DEV) for x in xs]
+    recvs = [torch.zeros_like(s) for s in sends]
+    ra.allreduce(sends, recvs, op="sum", nchannels=0, proto="auto", **cfg)
+    torch.cuda.synchronize()
+    code = ra.ringar_get_async_error(torch.cuda.current_stream().cuda_stream)
+    assert code == 0, ra.ringar_result_string(code)
+    run = oracle.tree_allreduce if plan.algo == 1 else oracle.ring_allreduce
+    want = run(xs, "float32", "sum", plan.nchannels, plan.chunk_elems)
+    for r in range(n):
+        assert np.array_equal(_bits(W.from_torch(recvs[r], "float32")), _bits(want[r])), r
