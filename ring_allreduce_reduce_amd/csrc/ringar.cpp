@@ -466,8 +466,9 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
     // 86 us; n = 5 318 against 351 us.
     const uint64_t lo = P.proto == kLL ? 4096 : 8192;
     const uint64_t in_flight = split_wanted ? (4u << 20) : (2u << 20);
-    const uint64_t hi = std::min<uint64_t>(std::max<uint64_t>(split_wanted ? 131072 : 65536, in_flight / (uint64_t)P.nch),
-                                           P.chunk_bytes);
+    // (whole 16-byte units: channel counts that are not powers of two)
+    const uint64_t hi = std::min<uint64_t>(
+        std::max<uint64_t>(split_wanted ? 131072 : 65536, in_flight / (uint64_t)P.nch / 16 * 16), P.chunk_bytes);
     P.chunk_bytes = std::min(hi, std::max(lo, align_up(P.per_channel * es / (split_wanted ? 2 : 4), 16)));
   }
   if (P.chunk_bytes == 0 || P.chunk_bytes % 16 != 0 || P.chunk_bytes % es != 0)

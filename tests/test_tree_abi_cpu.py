@@ -273,3 +273,18 @@ def test_split_form_env_switch():
                                 check=True).stdout.split()
     assert out["0"][:2] == ["0", str(64 << 10)]
     assert out["1"][:2] == ["1", str(128 << 10)]
+
+
+def test_every_automatic_plan_is_accepted():
+    # no forced knob: every rank count, size, algorithm, protocol and channel
+    # count has a plan (the tree's chunk cap of 2 or 4 MiB / channels is cut
+    # to whole 16-byte units, which channel counts that are not powers of two
+    # need: n = 9..15 at 16 MiB used to be refused)
+    sizes = [8, 1024, 32768, 131072, 262144, 524288, 1 << 20, 4 << 20, 16 << 20, (64 << 20) + 48]
+    for n in range(2, 65):
+        for nbytes in sizes:
+            for algo in ("auto", "ring", "tree"):
+                for proto in ("auto", "LL", "LL128", "Simple"):
+                    for nch in (0, 3, 7, 13, 32):
+                        p = ra.ringar_plan(max(1, nbytes // 4), "float32", n, nch, proto, ra.make_config(algo=algo))
+                        assert p.chunk_bytes % 16 == 0
