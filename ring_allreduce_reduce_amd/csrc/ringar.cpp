@@ -577,7 +577,8 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
       P.tree_waves = r0;
     }
   }
-  if (slices_for(lanes) > kMaxSlicesPerPart)
+  // (one rank moves no FIFO slot: its call is a copy, whatever the knobs)
+  if (n > 1 && slices_for(lanes) > kMaxSlicesPerPart)
     return forced_lanes ? RINGAR_ERR_INVALID_USAGE : RINGAR_ERR_INVALID_ARGUMENT;
   P.lanes = lanes;
 
@@ -587,7 +588,7 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   const uint64_t step_bytes =
       fifo_bytes_for(P.proto, std::min<uint64_t>(lane_part(first_chunk, lanes, (uint32_t)es, P.proto), slot) * es);
   if (depth) {
-    if ((uint64_t)slices_for(lanes) > (uint64_t)depth / 2) return RINGAR_ERR_INVALID_USAGE;
+    if (n > 1 && (uint64_t)slices_for(lanes) > (uint64_t)depth / 2) return RINGAR_ERR_INVALID_USAGE;
     P.depth = depth;
   } else {
     P.depth = kMaxSteps;

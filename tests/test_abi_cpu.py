@@ -397,3 +397,15 @@ def _halves_time(m, n, nch, p, nbytes):
         bus *= m["eff"][2]
     steps = n - 1
     return m["base_lat_us"][p] + steps * m["hw_lat_us"][p] + nbytes / (1000.0 * bus * n / steps)
+
+
+def test_one_rank_ignores_fifo_knobs():
+    # one rank's call is a copy: a forced lane count or FIFO depth that its
+    # parts would not fit is not a reason to refuse it
+    for proto in ("LL", "LL128", "Simple"):
+        ra.ringar_plan(1 << 20, "int32", 1, 1, proto, ra.make_config(fifo_depth=2))
+        ra.ringar_plan(1 << 20, "int32", 1, 1, proto, ra.make_config(lanes=1))
+    # with two ranks the same knobs are refused
+    with pytest.raises(ra.RingarError) as e:
+        ra.ringar_plan(1 << 20, "int32", 2, 1, "Simple", ra.make_config(lanes=1))
+    assert e.value.code == ra.INVALID_USAGE
