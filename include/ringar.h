@@ -170,8 +170,10 @@ typedef struct {
  *   lanes:           wavefronts working in parallel on each (rank, channel),
  *                    each with its own FIFO; 0 = chosen by size (a power of
  *                    two, or a multiple of 4 when that saves a FIFO slice).
- *                    A forced count must be a power of two, at most 32.
- *                    Does not change any result.
+ *                    A forced count must be a power of two, at most 32;
+ *                    one whose grid the GPU cannot hold at once is refused
+ *                    with RINGAR_ERR_INVALID_USAGE (by ringar_plan too when
+ *                    a device is visible).  Does not change any result.
  *   spin_limit_ms:   a wait that lasts longer ends the kernel with
  *                    RINGAR_ERR_TIMEOUT (reported by ringar_get_async_error);
  *                    0 = default (env RINGAR_SPIN_LIMIT_MS, else 2000 ms).

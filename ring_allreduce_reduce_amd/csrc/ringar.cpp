@@ -645,6 +645,11 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
     P.xcd_major = false;
     P.grid = launch_grid(members, groups, false);
   }
+  // A forced lane count whose grid the GPU cannot hold at once is refused
+  // here, as the launch would refuse it (the kernel's residency is known
+  // only with a device; without one the launch decides).
+  if (forced_lanes && capacity_waves && (uint64_t)P.grid * P.lanes_per_block > capacity_waves)
+    return RINGAR_ERR_INVALID_USAGE;
   P.conns = (uint64_t)P.nch * n * lanes * (tree ? 2 : 1);
 
   // Upper bound of FIFO steps any connection takes in this call.
