@@ -119,6 +119,11 @@ def test_random_halves(coll):
     ran = skipped = 0
     for i in range(CASES):
         n, count, dtype, op, proto, nch, cfg, inplace, unaligned = _draw(rng, halves=True)
+        try:
+            ra.ringar_plan_coll(coll, count, dtype, n, nch, proto, ra.make_config(**cfg))
+        except ra.RingarError:
+            skipped += 1
+            continue
         desc = (f"{coll} case {i}: n={n} count={count} {dtype} {op} {proto} nch={nch} {cfg} "
                 f"inplace={inplace} unaligned={unaligned}")
         print(desc, flush=True)
@@ -138,15 +143,10 @@ def test_random_halves(coll):
                 recvs = full
             else:
                 recvs = [torch.zeros(recv_count, dtype=sends[0].dtype, device=DEV) for _ in range(n)]
-        try:
-            if rs:
-                ra.reduce_scatter(sends, recvs, op=op, nchannels=nch, proto=proto, **cfg)
-            else:
-                ra.all_gather(sends, recvs, nchannels=nch, proto=proto, **cfg)
-        except ra.RingarError as e:
-            assert e.code in (ra.INVALID_ARGUMENT, ra.INVALID_USAGE), desc
-            skipped += 1
-            continue
+        if rs:
+            ra.reduce_scatter(sends, recvs, op=op, nchannels=nch, proto=proto, **cfg)
+        else:
+            ra.all_gather(sends, recvs, nchannels=nch, proto=proto, **cfg)
         code = _finish()
         assert code == 0, (desc, ra.ringar_result_string(code))
         if rs:
