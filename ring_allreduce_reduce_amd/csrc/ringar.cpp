@@ -1122,6 +1122,15 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   if (captured && (r = plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, cfg, &P, true)) !=
                       RINGAR_SUCCESS)
     return r;
+  // Connections an eager call allocates on the stream: its own, and in the
+  // split tree form also those of the captured (unsplit) form of the same
+  // call, which takes other lanes, so that the stream can capture it next.
+  uint64_t hold_conns = P.conns;
+  if (!captured && !noalloc && P.tree_split) {
+    Plan Q;
+    if (plan_for_launch(coll, kcount, dtype, op, nranks, nchannels, proto, cfg, &Q, true) == RINGAR_SUCCESS)
+      hold_conns = std::max(hold_conns, Q.conns);
+  }
 
   // the direct form needs every rank out of place
   bool direct = P.direct;
@@ -1227,7 +1236,7 @@ static ringar_result_t run_collective(int coll, void* const* sendbuffs, void* co
   } else if (!captured) {
     // (the library's own direct choice still allocates the FIFOs, so that
     // the stream can capture the same call, which keeps them)
-    if ((r = ensure_conns(*R, st, P.proto, P.conns, direct && !P.direct_auto)) != RINGAR_SUCCESS) return r;
+    if ((r = ensure_conns(*R, st, P.proto, hold_conns, direct && !P.direct_auto)) != RINGAR_SUCCESS) return r;
     // LL flags are 32-bit step numbers: restart the numbering before it wraps.
     if (R->base + P.max_steps + 1 >= 0xFFFFFFF0ull)
       if ((r = reset_steps(*R, st)) != RINGAR_SUCCESS) return r;

@@ -452,3 +452,41 @@ def test_replay_error_is_reported_after_an_eager_error_and_the_graph_recovers():
             assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
             _check(recvs, _want(xs2, shape), shape)
         del g_bad, g_good
+
+
+@pytest.mark.parametrize("shape", [(16, 1 << 20, "float32", "avg", "Simple", 8, "tree"),
+                                   (8, 1 << 21, "bfloat16", "sum", "Simple", 4, "tree")])
+def test_split_tree_call_captured_after_one_eager_call(shape):
+    # eagerly the tree runs these calls in its split form, whose lane count
+    # differs from the captured (unsplit) form's; one eager call on a fresh
+    # stream must still leave the connections the captured form needs
+    n, count, dtype = shape[:3]
+    plan = ra.ringar_plan(count, dtype, n, shape[5], shape[4], _cfg(shape))
+    assert plan.tree_split == 1
+    st = torch.cuda.Stream()
+    xs = _inputs(shape, "cap-split-warm")
+    sends = [W.to_torch(x, dtype, DEV) for x in xs]
+    recvs = [torch.zeros_like(s) for s in sends]
+    print(f"case capture split warm-up {shape}", flush=True)
+    with torch.cuda.stream(st):
+        assert _raw(sends, recvs, shape, st) == ra.SUCCESS
+    st.synchronize()
+    assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+    _check(recvs, _want(xs, shape), shape)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        code = _raw(sends, recvs, shape, st)
+    assert code == ra.SUCCESS, ra.ringar_result_string(code)
+    for rep in range(3):
+        xs = _inputs(shape, f"cap-split-rep{rep}")
+        with torch.cuda.stream(st):
+            for t, x in zip(sends, xs):
+                t.copy_(W.to_torch(x, dtype, DEV))
+            for t in recvs:
+                t.zero_()
+        st.synchronize()
+        print(f"case capture split replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ra.ringar_get_async_error(st.cuda_stream) == ra.SUCCESS
+        _check(recvs, _want(xs, shape), shape)
