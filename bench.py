@@ -474,6 +474,11 @@ def main():
                      "copy_bytes": int(b_alg // 2) // 4096 * 4096 * 2,
                      "copy_in_cache_gbs": round(copy_cache_gbs, 1)},
         "cpu_baseline": cpu,
+        # The figures the pages give for NVIDIA systems ([ARCH] introduction),
+        # quoted beside the measurement as model constants: none was measured here.
+        "pages_model_constants": {"source": "[ARCH] introduction", "kind": "model constants, not measurements",
+                                  "nvlink_bidirectional_gbs_per_gpu": {"A100": 600, "H100": 900},
+                                  "protocol_payload_efficiency": {"Simple": 1.0, "LL128": 0.94, "LL": 0.5}},
     }
     print(json.dumps(out), flush=True)
 
