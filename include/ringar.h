@@ -284,7 +284,10 @@ typedef struct {
  *       shape first (else RINGAR_ERR_INVALID_USAGE).  The captured kernels
  *       may hold fewer wavefronts per CU, so a captured call can take fewer
  *       lanes than the same call made eagerly (same results); a forced lane
- *       count beyond what they hold is RINGAR_ERR_INVALID_USAGE.  A call that
+ *       count beyond what they hold is RINGAR_ERR_INVALID_USAGE.  The tree
+ *       never runs its split form under capture (it may then take more
+ *       lanes and another chunk, same results); an eager call in the split
+ *       form allocates the connections of both forms.  A call that
  *       asks for the direct form is refused under capture
  *       (RINGAR_ERR_INVALID_USAGE, nothing enqueued); one for which the
  *       library chose it keeps its FIFOs.
