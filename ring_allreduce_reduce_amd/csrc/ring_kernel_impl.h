@@ -1461,10 +1461,6 @@ __device__ __forceinline__ void tree_body(const TreeArgs& ta) {
 #endif
 }
 
-
-// The tree's Simple kernels carry the ring's launch bound (4 workgroups of
-// 256 per CU, so at most 128 VGPRs: the 3840-wavefront launches of large
-// calls need occupancy 4); the line protocols keep their registers.
 // ----------------------------------------------------------------- split tree (Simple)
 // The split form of the tree AllReduce: every role that moves four or more
 // units of its channel per element (the root's reduce role, the reduce and
@@ -1590,6 +1586,10 @@ __device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
 #endif
 }
 
+// The tree's Simple kernels (both forms) carry the ring's launch bound (4
+// workgroups of 256 per CU, so at most 128 VGPRs: the launches of large
+// calls fill the GPU's 4096 wavefronts, which needs occupancy 4); the line
+// protocols keep their registers.
 template <class E, int OP, int PROTO, bool SMALL, bool CAP = false>
 __global__ void __launch_bounds__(256, 4) tree_kernel_simple(const TreeArgs ta) {
   static_assert(PROTO == kSimple, "the line protocols run tree_kernel");
