@@ -3,7 +3,7 @@
 The tuning table of `calibrate` times each (algorithm, protocol) pair with
 HIP events around each call.  This tool evidences the same choices with the
 kernels' own durations as rocprofv3 records them: `run` makes, for every size
-of the table (8 B to 128 MiB per rank, n = 8, fp32 sum) and every pair, a few
+of the table (8 B to 128 MiB per rank, n = 8 or --nranks, fp32 sum) and every pair, a few
 warm-up calls and then K timed calls with the built-in model's channel count
 (Ring Simple from 256 KiB per rank in the direct form, which the library runs
 when the model takes Simple on the ring), and writes the list of calls it
@@ -33,7 +33,6 @@ PAIRS = [("Tree", q) for q in PROTOS] + [("Ring", q) for q in PROTOS]
 SIZES = [1 << sh for sh in range(3, 29, 2)]       # 8 B .. 128 MiB per rank
 DIRECT_AUTO_MIN_BYTES = 256 << 10                # the library's own direct choice
 WARMUP, TIMED = 3, 20
-N = 8
 
 
 def alg_bytes(nbytes: int, n: int, proto: str, direct: bool) -> float:
@@ -43,13 +42,13 @@ def alg_bytes(nbytes: int, n: int, proto: str, direct: bool) -> float:
     return float(nbytes) * (2 * n + 4 * (n - 1) * e)
 
 
-def run(calls_path: str) -> int:
+def run(calls_path: str, n: int = 8) -> int:
     import torch
     import ring_allreduce_reduce_amd as ra
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     biggest = max(SIZES) // 4
-    sends = [torch.randn(biggest, device=dev) for _ in range(N)]
+    sends = [torch.randn(biggest, device=dev) for _ in range(n)]
     recvs = [torch.empty_like(s) for s in sends]
     sp = [s.data_ptr() for s in sends]
     rp = [r.data_ptr() for r in recvs]
@@ -59,10 +58,10 @@ def run(calls_path: str) -> int:
         for algo, proto in PAIRS:
             direct = int((algo, proto) == ("Ring", "Simple") and nbytes >= DIRECT_AUTO_MIN_BYTES)
             cfg = ra.make_config(algo=algo.lower(), direct=direct)
-            plan = ra.ringar_plan(count, "float32", N, 0, proto, cfg)
-            auto = ra.ringar_plan(count, "float32", N, 0, "auto", ra.make_config(algo="auto"))
+            plan = ra.ringar_plan(count, "float32", n, 0, proto, cfg)
+            auto = ra.ringar_plan(count, "float32", n, 0, "auto", ra.make_config(algo="auto"))
             for _ in range(WARMUP + TIMED):
-                code = ra.ringar_allreduce_ex(sp, rp, count, "float32", "sum", N, 0, proto, stream.cuda_stream, cfg)
+                code = ra.ringar_allreduce_ex(sp, rp, count, "float32", "sum", n, 0, proto, stream.cuda_stream, cfg)
                 if code:
                     raise ra.RingarError(code, "ringar_allreduce_ex")
             torch.cuda.synchronize()
@@ -76,7 +75,7 @@ def run(calls_path: str) -> int:
                           "dispatches": WARMUP + TIMED})
         print(f"{nbytes} B done", flush=True)
     with open(calls_path, "w") as f:
-        json.dump({"n": N, "warmup": WARMUP, "timed": TIMED, "calls": calls}, f, indent=1)
+        json.dump({"n": n, "warmup": WARMUP, "timed": TIMED, "calls": calls}, f, indent=1)
     return 0
 
 
@@ -104,14 +103,15 @@ def summarize(trace_path: str, calls_path: str, out_path: str | None) -> int:
             return 1
         c["kernel_us"] = statistics.median(durs)
         c["gbs"] = alg_bytes(c["bytes"], n, c["proto"], bool(c["direct"])) / (c["kernel_us"] * 1e3)
-    out = ["# the selector's choices against kernel time: n = 8, fp32 sum, one MI355X; per (algorithm, protocol)",
+    out = [f"# the selector's choices against kernel time: n = {n}, fp32 sum, one MI355X; per (algorithm, protocol)",
            "# the model's channel count, the median rocprofv3 kernel duration of 20 calls (after 3 warm-up",
            "# calls) and the achieved memory GB/s (algorithmic bytes over kernel time; '/d' = the direct form,",
            "# S (5n - 4) bytes); the model's pick (algorithm = auto, protocol = auto) and the fastest kernels",
            "# commands (from the repository root on the MI355X box):",
            "#   cd /tmp && export TMPDIR=/tmp PYTHONPATH=<repo> && \\",
            "#     rocprofv3 --kernel-trace --output-format csv -d <dir> -o run -- \\",
-           "#     python3 -m ring_allreduce_reduce_amd.tuning_trace run --calls <calls.json>",
+           f"#     python3 -m ring_allreduce_reduce_amd.tuning_trace run --calls <calls.json>" +
+           ("" if n == 8 else f" --nranks {n}"),
            "#   python3 -m ring_allreduce_reduce_amd.tuning_trace summarize --trace <dir>/run_kernel_trace.csv \\",
            "#     --calls <calls.json> --out <this file>",
            ""]
@@ -144,13 +144,14 @@ def main(argv=None) -> int:
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--calls", required=True, help="write the list of calls made here (JSON)")
+    r.add_argument("--nranks", type=int, default=8)
     s = sub.add_parser("summarize")
     s.add_argument("--trace", required=True, help="rocprofv3 run_kernel_trace.csv of the run")
     s.add_argument("--calls", required=True)
     s.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "run":
-        return run(args.calls)
+        return run(args.calls, args.nranks)
     return summarize(args.trace, args.calls, args.out)
 
 
