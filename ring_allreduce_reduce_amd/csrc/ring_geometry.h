@@ -243,4 +243,53 @@ RA_HD bool tree_role_splits(bool bcast, bool is_root, int nchildren) {
   return bcast ? nchildren == 2 : (is_root || nchildren == 2);
 }
 
+// The split form's handshake of one role (vertex v of tree t, its reduce or
+// broadcast role): whether it splits, whether the producer of each of its
+// inputs splits (then it waits for both tail words) and whether the consumer
+// of each of its outputs splits (then it waits for both head words); inputs
+// and outputs in the primitives' order, children in child-slot order.
+struct SplitRole {
+  bool my_split;
+  bool in_split[2];
+  bool out_split[2];
+};
+RA_HD int tree_children(const TreeArgs& ta, int t, int u) {
+  return (ta.child[t][0][u] >= 0 ? 1 : 0) + (ta.child[t][1][u] >= 0 ? 1 : 0);
+}
+RA_HD SplitRole tree_split_role(const TreeArgs& ta, int t, int v, bool bcast) {
+  const int root = ta.root[t];
+  const int s0 = ta.child[t][0][v], s1 = ta.child[t][1][v];
+  const int k0 = s0 >= 0 ? s0 : s1;
+  const int k1 = s0 >= 0 ? s1 : -1;
+  const int nk = (k0 >= 0 ? 1 : 0) + (k1 >= 0 ? 1 : 0);
+  SplitRole r;
+  r.my_split = tree_role_splits(bcast, v == root, nk);
+  // the children's roles: their reduce roles send up, their broadcast roles
+  // take the way down
+  const bool up0 = k0 >= 0 && tree_role_splits(false, false, tree_children(ta, t, k0));
+  const bool up1 = k1 >= 0 && tree_role_splits(false, false, tree_children(ta, t, k1));
+  const bool down0 = k0 >= 0 && tree_role_splits(true, false, tree_children(ta, t, k0));
+  const bool down1 = k1 >= 0 && tree_role_splits(true, false, tree_children(ta, t, k1));
+  if (!bcast) {
+    r.in_split[0] = up0;
+    r.in_split[1] = up1;
+    if (v == root) {
+      r.out_split[0] = down0;
+      r.out_split[1] = down1;
+    } else {
+      // the parent's reduce role reads the up connection
+      const int p = ta.parent[t][v];
+      r.out_split[0] = r.out_split[1] = tree_role_splits(false, p == root, tree_children(ta, t, p));
+    }
+  } else {
+    // the down connection is written by the parent's broadcast role, or by
+    // the root's reduce role
+    const int p = ta.parent[t][v];
+    r.in_split[0] = r.in_split[1] = tree_role_splits(p != root, p == root, tree_children(ta, t, p));
+    r.out_split[0] = down0;
+    r.out_split[1] = down1;
+  }
+  return r;
+}
+
 }  // namespace ringar

@@ -1490,7 +1490,6 @@ __device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
   if (v == a.skip_ring_index) return;
   const uint32_t es = sizeof(typename E::T);
 
-  auto nkids = [&](int u) { return (ta.child[t][0][u] >= 0 ? 1 : 0) + (ta.child[t][1][u] >= 0 ? 1 : 0); };
   Lane L;
   L.a = &a;
   L.w.a = &a;
@@ -1514,40 +1513,33 @@ __device__ __forceinline__ void tree_body_split(const TreeArgs& ta) {
   const int k1 = s0 >= 0 ? s1 : -1;
   const int nk = (k0 >= 0 ? 1 : 0) + (k1 >= 0 ? 1 : 0);
   const int k0c = k0 >= 0 ? k0 : v, k1c = k1 >= 0 ? k1 : k0c;
-  L.my_split = tree_role_splits(bcast, v == root, nk);
+  const SplitRole sr = tree_split_role(ta, t, v, bcast);
+  L.my_split = sr.my_split;
   L.my_half = (entry >> 7) & 1;
-  L.in_split[0] = L.in_split[1] = false;
-  L.out_split[0] = L.out_split[1] = false;
+  L.in_split[0] = sr.in_split[0];
+  L.in_split[1] = sr.in_split[1];
+  L.out_split[0] = sr.out_split[0];
+  L.out_split[1] = sr.out_split[1];
   if (!bcast) {
     // inputs: the children's up connections, written by their reduce roles
     L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kUp, l, n, a.lanes));
     L.in[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kUp, l, n, a.lanes));
-    L.in_split[0] = k0 >= 0 && tree_role_splits(false, false, nkids(k0));
-    L.in_split[1] = k1 >= 0 && tree_role_splits(false, false, nkids(k1));
     if (v == root) {
       // outputs: the children's down connections, read by their broadcast roles
       L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
       L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
-      L.out_split[0] = k0 >= 0 && tree_role_splits(true, false, nkids(k0));
-      L.out_split[1] = k1 >= 0 && tree_role_splits(true, false, nkids(k1));
     } else {
       // output: the up connection to the parent, read by its reduce role
-      const int p = ta.parent[t][v];
       L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kUp, l, n, a.lanes));
       L.out[1] = L.out[0];
-      L.out_split[0] = L.out_split[1] = tree_role_splits(false, p == root, nkids(p));
     }
   } else {
     // input: the down connection from the parent (its broadcast role, or the
     // root's reduce role); outputs: the children's down connections
-    const int p = ta.parent[t][v];
     L.in[0] = conn_at<PROTO>(a, tree_conn_index(c, v, kDown, l, n, a.lanes));
     L.in[1] = L.in[0];
-    L.in_split[0] = L.in_split[1] = tree_role_splits(p != root, p == root, nkids(p));
     L.out[0] = conn_at<PROTO>(a, tree_conn_index(c, k0c, kDown, l, n, a.lanes));
     L.out[1] = conn_at<PROTO>(a, tree_conn_index(c, k1c, kDown, l, n, a.lanes));
-    L.out_split[0] = k0 >= 0 && tree_role_splits(true, false, nkids(k0));
-    L.out_split[1] = k1 >= 0 && tree_role_splits(true, false, nkids(k1));
   }
 
   uint64_t lo, hi;
