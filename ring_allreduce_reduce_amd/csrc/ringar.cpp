@@ -556,9 +556,11 @@ ringar_result_t make_plan(int coll, size_t count, int dtype, int n, int nchannel
   // kTreeSplitMinChannelBytes per channel): the roles that move four or more
   // units per element run as two wavefronts, so a lane takes more
   // wavefronts and the grid's 4096 fewer lanes, of any count (whole
-  // workgroups of 4, 2 or 1 wavefronts).  Measured at n = 3..16 on MI355X,
-  // it takes 2-8% off calls of 256 KiB per channel and more, and adds 3-29%
-  // to smaller ones, whose fewer lanes cost more than the halves gain.
+  // workgroups of 4, 2 or 1 wavefronts).  Measured on MI355X (fp32, with
+  // its chunk rule above, against one wavefront a role): 2-17% off calls of
+  // 64 MiB per rank at n = 2..16; at 256 KiB per channel n = 2, 3 and 8 gain
+  // 2-4% while n = 4 and 6 lose 5-8%; below 256 KiB per channel the fewer
+  // lanes cost more than the halves gain (3-29% slower at n = 8).
   P.tree_split = false;
   if (split_wanted) {
     uint8_t roles[2][4 * kMaxRanks];
