@@ -54,6 +54,13 @@ BYTES_PER_RANK = 64 << 20
 NCHANNELS = 16
 CHUNK_BYTES = 512 * 1024
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ring_simple_fp32_64MiB_n8_traffic.txt")
+# counter summaries of the other 64 MiB AllReduce forms, by (algorithm, direct, protocol, dtype)
+TRAFFIC_FILES = {
+    ("ring", False, "Simple", "float32"): TRAFFIC_FILE,
+    ("ring", True, "Simple", "float32"): os.path.join(ROOT, "profiles", "ring_direct_fp32_64MiB_n8_traffic.txt"),
+    ("ring", False, "LL128", "bfloat16"): os.path.join(ROOT, "profiles", "ring_ll128_bf16_64MiB_n8_traffic.txt"),
+    ("tree", False, "Simple", "float32"): os.path.join(ROOT, "profiles", "tree_simple_fp32_64MiB_n8_traffic.txt"),
+}
 
 
 def log(msg):
@@ -81,12 +88,12 @@ def plan_key(cfg):
     return f"lanes={cfg['lanes']} fifo_depth={cfg['fifo_depth']} workgroups={cfg['workgroups']}"
 
 
-def read_traffic(cfg):
-    """Measured HBM bytes per launch from the committed counter summary, if it
+def read_traffic(cfg, path=TRAFFIC_FILE):
+    """Measured HBM bytes per launch from a committed counter summary, if it
     was taken on the current kernel code with the same launch shape."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
     m_plan = re.search(r"plan:\s*([^\n]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -367,8 +374,10 @@ def main():
     algbw = s / (ms_per_step * 1e-3) / 1e9
     bus_factor = (2 if coll == "allreduce" else 1) * (NRANKS - 1) / NRANKS
     busbw = algbw * bus_factor
+    tfile = TRAFFIC_FILES.get((algo, bool(direct), pname, dtype)) \
+        if coll == "allreduce" and s == BYTES_PER_RANK else None
     traffic = read_traffic({"lanes": plan.lanes, "fifo_depth": plan.fifo_depth,
-                            "workgroups": plan.workgroups}) if headline else None
+                            "workgroups": plan.workgroups}, tfile)
 
     def run_oracle(threaded=False, threads=1):
         if coll == "allreduce" and algo == "tree":
